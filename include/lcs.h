@@ -1,0 +1,181 @@
+/*
+ * lcs.h -- C ABI of the MI355X (gfx950) hybrid compressed attention forward (CSA + HCA).
+ *
+ * The method is the DeepSeek-V4 attention described on page 1 ("DeepSeek V4 ..." walk-through,
+ * section "hybrid attention", CSA steps 1-4, the HCA paragraph, Q/KV normalization, partial RoPE,
+ * the sliding-window branch and the attention sink) and page 4 ("DeepSeek-V4开源解读",
+ * section 3.1 "Hybrid Attention: CSA + HCA", the Flash constants).
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers owned by the caller.  The library allocates nothing on the
+ *     device and keeps no state between calls (the optional timing facility at the end aside).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and runs asynchronously;
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - bf16 = uint16_t bit pattern; fp8 = uint8_t OCP E4M3FN; positions are int64 token indices.
+ *   - Tensors are row-major and contiguous, shapes given in [] with the fastest axis last.
+ *     Caches carry an explicit per-sequence row count ("ld"): row r of sequence b starts at
+ *     element (b*ld + r) * width.
+ *   - Return value: LCS_OK, or an error code below; on error nothing has been enqueued.
+ *   - Device-side preconditions that would need a synchronisation to check are documented, not
+ *     checked: finite inputs, indices in range, positions inside the buffers.
+ *   - Same inputs give bitwise-identical outputs (no floating-point atomics anywhere).
+ *
+ * Readings of the pages that fix the arithmetic (page 1, section "hybrid attention", unless noted):
+ *   pooling  entry i = sum_j softmax(s[S_i])_j x_j over tokens S_i = [i*m - ov, (i+1)*m), j >= 0
+ *   norm     RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps) on pooled entries, window tokens, q heads
+ *   rope     dims 448..511 as adjacent pairs (448+2j, 449+2j), angle = pos * theta^(-j/32);
+ *            entry i at pos (i+1)*m - 1 + rope_offset, window token j at j + rope_offset, query t at
+ *            t + rope_offset; the output's last 64 dims are rotated by -(t + rope_offset)
+ *   visible  entry i is visible to the query at token t iff (i+1)*m <= t  (n_vis = t / m)
+ *   window   tokens [max(0, t-window+1), t]; one joint softmax over compressed keys + window + sink
+ *   sink     p = e^l / (e^z_h + sum e^l), l = scale * qhat . k (scale normally 1/sqrt(512))
+ *   indexer  I_s = sum_h w_h * max(0, q_h . k_s)   (page 1 CSA step 2; page 4 section 3.1)
+ */
+#ifndef LCS_H_
+#define LCS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCS_OK 0
+#define LCS_ERR_ARG 1          /* NULL pointer, non-positive size, bad stride or misalignment  */
+#define LCS_ERR_UNSUPPORTED 2  /* shape or dtype this build does not implement                */
+#define LCS_ERR_WORKSPACE 3    /* workspace NULL or smaller than the *_workspace() query      */
+#define LCS_ERR_HIP 4          /* a HIP launch error                                          */
+
+#define LCS_IK_BF16 0          /* indexer keys stored as bf16, no scale                        */
+#define LCS_IK_FP8 1           /* indexer keys stored as E4M3FN codes + one fp32 scale per key */
+
+#define LCS_HEAD_DIM 512       /* c, fixed (page 1, CSA step 4: "c set to 512")                */
+#define LCS_MAX_HEADS 64
+#define LCS_MAX_TOPK 2048
+
+int lcs_version(void);
+const char* lcs_status_string(int status);
+
+/*
+ * csa_compress_kv -- CSA step 1 (page 1, "hybrid attention", CSA step 1; page 4 section 3.1, m = 4):
+ * pools m-token blocks with an overlap of `overlap` earlier tokens into one K=V entry each, then
+ * RMSNorm(gamma_kv) and RoPE at the block's last token.  With ik_tok != NULL the indexer key of the
+ * block is pooled the same way with its own logits ik_score (no norm, no RoPE) and stored as bf16
+ * (ik_dtype = LCS_IK_BF16) or as E4M3FN codes with scale = absmax/448 (LCS_IK_FP8).
+ *
+ *   kv_tok   [B, T, c] bf16   raw per-token K=V vectors of tokens tok0 .. tok0+T-1
+ *   kv_score [B, T]    fp32   one pooling logit per token
+ *   ik_tok   [B, T, dI] bf16, ik_score [B, T] fp32   (both NULL: no indexer keys)
+ *   blocks blk_begin .. blk_begin+n_blk-1 are produced; every token they pool must lie in
+ *   [tok0, tok0+T) (tokens < 0 are dropped), else LCS_ERR_ARG.
+ *   kv_out   [B, kv_ld, c] bf16: entry i goes to row i (ring_cap = 0) or row i % ring_cap; with a
+ *            ring, one call writes at most ring_cap entries (else LCS_ERR_ARG).
+ *   ik_out   [B, ik_ld, dI] (uint8 codes or bf16), ik_scale [B, ik_ld] fp32 (fp8 only), row i.
+ *   Requirements: c = 512, m >= 1, 0 <= overlap <= 4*m, m + overlap <= 1024, dI in {64, 128}.
+ */
+int csa_compress_kv(const uint16_t* kv_tok, const float* kv_score,
+                    const uint16_t* ik_tok, const float* ik_score,
+                    int B, int T, int64_t tok0, int64_t blk_begin, int n_blk,
+                    int m, int overlap, int c, int dI,
+                    const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
+                    uint16_t* kv_out, int64_t kv_ld, int64_t ring_cap,
+                    void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype,
+                    void* stream);
+
+/*
+ * hca_compress_kv -- HCA compression (page 1, HCA paragraph: m' = 128, no overlap) and, with m = 1,
+ * the sliding-window fill (page 1, "sliding window": uncompressed tokens, each normed and rotated
+ * to its own position).  Same arguments and layout as csa_compress_kv without indexer keys.
+ */
+int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score,
+                    int B, int T, int64_t tok0, int64_t blk_begin, int n_blk, int m, int c,
+                    const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
+                    uint16_t* kv_out, int64_t kv_ld, int64_t ring_cap, void* stream);
+
+/*
+ * csa_index_topk -- CSA step 2 (page 1, CSA step 2: lightning indexer + top-k; page 4 section 3.1:
+ * 64 indexer heads of dim 128, top-k 512): for each query at token t = q_pos[b, tq] the score of
+ * every visible entry s < n_vis = min(t / m, n_cap) is I_s = sum_h w_h * max(0, q_h . k_s); the
+ * min(k, n_vis) largest (ties to the lower index) are written ascending, padded with -1.
+ * fp8 mode quantises each query head row to E4M3FN (scale absmax/448, round to nearest even,
+ * computed in fp32) and multiplies codes on the fp8 matrix cores; accumulation is fp32.
+ *
+ *   q_idx  [B, Tq, H_I, dI] bf16;  w_idx [B, Tq, H_I] bf16
+ *   ik_cache [B, ik_ld, dI] (codes or bf16), ik_scale [B, ik_ld] fp32 (fp8), n_cap <= ik_ld
+ *   q_pos  [B, Tq] int64 (device)
+ *   topk_idx [B, Tq, k] int32; topk_score [B, Tq, k] fp32 (may be NULL; -inf where padded)
+ *   ws     device workspace of at least csa_index_topk_workspace(B, Tq, n_cap, k) bytes
+ *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1.
+ */
+size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
+int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx,
+                   const void* ik_cache, const float* ik_scale, int64_t ik_ld, int ik_dtype,
+                   const int64_t* q_pos, int64_t n_cap,
+                   int B, int Tq, int H_I, int dI, int m, int k,
+                   int32_t* topk_idx, float* topk_score,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_attend -- CSA step 3 (page 1, CSA step 3: multi-query attention over the selected entries;
+ * Q/KV normalization; partial RoPE with the -i output rotation; sliding window; sink):
+ * per query, qhat_h = RoPE_t(RMSNorm_gamma_q(q_h)); keys = the selected entries of kv_cache
+ * (topk_idx >= 0) plus window tokens [t-window+1, t] read from win_ring; K = V.
+ *
+ *   q [B, Tq, H, c] bf16 raw;  gamma_q [c] bf16
+ *   kv_cache [B, kv_ld, c] bf16 (normed + rotated entries); topk_idx [B, Tq, k] int32
+ *   win_ring [B, win_ld, c] bf16 (normed + rotated tokens): token j at row j (ring_cap = 0) or
+ *            j % ring_cap; the caller keeps every window token of every query present.
+ *   sink [H] fp32;  q_pos [B, Tq] int64 (device)
+ *   out [B, Tq, H, c] bf16
+ *   ws     device workspace of at least lcs_attend_workspace(B, Tq, H, k + window) bytes
+ *   Requirements: c = 512, 1 <= H <= 64, window >= 0, k <= 2048.
+ */
+size_t lcs_attend_workspace(int B, int Tq, int H, int64_t max_keys);
+int csa_attend(const uint16_t* q, const uint16_t* gamma_q,
+               const uint16_t* kv_cache, int64_t kv_ld, const int32_t* topk_idx, int k,
+               const uint16_t* win_ring, int64_t win_ld, int64_t ring_cap, int window,
+               const float* sink, const int64_t* q_pos, int64_t rope_offset,
+               int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+               uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attend -- HCA core attention (page 1, HCA paragraph: dense attention over every compressed
+ * entry): as csa_attend, but the compressed keys are all visible entries 0 .. n_vis-1 with
+ * n_vis = min(t / m, n_cap).  With m = 4 on a CSA cache this is CSA with top-k >= n_vis.
+ * Workspace: lcs_attend_workspace(B, Tq, H, n_cap + window).
+ */
+int hca_attend(const uint16_t* q, const uint16_t* gamma_q,
+               const uint16_t* kv_cache, int64_t kv_ld, int64_t n_cap, int m,
+               const uint16_t* win_ring, int64_t win_ld, int64_t ring_cap, int window,
+               const float* sink, const int64_t* q_pos, int64_t rope_offset,
+               int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+               uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * grouped_out_proj -- CSA step 4 (page 1, CSA step 4: the n_h heads are split into g groups, each
+ * group projected to d_g, and the concatenation projected to d):
+ *   z[:, j*d_g:(j+1)*d_g] = o[:, heads of group j] . W_g[j]^T   (rounded to bf16)
+ *   y = z . W_o^T
+ *   o [M, H*c] bf16;  w_g [g, d_g, (H/g)*c] bf16;  w_o [d, g*d_g] bf16;  y [M, d] bf16
+ *   ws: grouped_out_proj_workspace(M, g, d_g) bytes (holds z).
+ *   Requirements: H % g == 0, d_g % 16 == 0, d % 16 == 0, (H/g)*c % 32 == 0.
+ */
+size_t grouped_out_proj_workspace(int M, int g, int d_g);
+int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o,
+                     int M, int H, int c, int g, int d_g, int d, uint16_t* y,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing (measurement facility, off by default).  While enabled, every kernel launch made
+ * by the library is bracketed by two hipEvents recorded on the launch stream; lcs_timing_read
+ * synchronises those events and returns the summed duration and launch count of the kernels whose
+ * name contains `name`.  Not for use under stream capture.  lcs_timing_enable(0) drops the events.
+ */
+int lcs_timing_enable(int on);
+int lcs_timing_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCS_H_ */

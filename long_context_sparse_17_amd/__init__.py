@@ -1,0 +1,215 @@
+"""Python binding of liblcs.so, the gfx950 hybrid compressed attention forward (CSA + HCA).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI declared in
+include/lcs.h.  Tensors are torch tensors on the GPU (torch supplies device memory and the
+stream); shapes are read off the tensors and passed as plain sizes and pointers.  There is no
+fallback: if liblcs.so is missing or fails to load, the functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
+
+LCS_OK, LCS_ERR_ARG, LCS_ERR_UNSUPPORTED, LCS_ERR_WORKSPACE, LCS_ERR_HIP = 0, 1, 2, 3, 4
+LCS_IK_BF16, LCS_IK_FP8 = 0, 1
+HEAD_DIM = 512
+
+# exported symbols and their C signatures (see include/lcs.h)
+_P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "lcs_version": (_I, []),
+    "lcs_status_string": (ctypes.c_char_p, [_I]),
+    "csa_compress_kv": (_I, [_P, _P, _P, _P, _I, _I, _I64, _I64, _I, _I, _I, _I, _I, _P, _F, _F, _I64,
+                             _P, _I64, _I64, _P, _P, _I64, _I, _P]),
+    "hca_compress_kv": (_I, [_P, _P, _I, _I, _I64, _I64, _I, _I, _I, _P, _F, _F, _I64, _P, _I64, _I64, _P]),
+    "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
+    "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "lcs_attend_workspace": (_SZ, [_I, _I, _I, _I64]),
+    "csa_attend": (_I, [_P, _P, _P, _I64, _P, _I, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F, _F, _F,
+                        _P, _P, _SZ, _P]),
+    "hca_attend": (_I, [_P, _P, _P, _I64, _I64, _I, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F, _F,
+                        _F, _P, _P, _SZ, _P]),
+    "grouped_out_proj_workspace": (_SZ, [_I, _I, _I]),
+    "grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "lcs_timing_enable": (_I, [_I]),
+    "lcs_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+}
+
+_lib = None
+
+
+class LcsError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib().lcs_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load liblcs.so once and declare the C signatures; raises if the library is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_sparse_17_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+# --------------------------------------------------------------------------------- marshalling
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != LCS_OK:
+        raise LcsError(fn, status)
+
+
+def _bits(t, name):
+    """bf16 tensors are passed as their 16-bit patterns; accept bfloat16 or int16/uint16 views."""
+    import torch
+    if t is None:
+        return None
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16")
+    return t
+
+
+def _dt(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    return t
+
+
+def workspace(nbytes, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------------- entry points
+def csa_compress_kv(kv_tok, kv_score, ik_tok, ik_score, *, tok0, blk_begin, n_blk, m, overlap, gamma_kv,
+                    kv_out, ring_cap=0, ik_out=None, ik_scale=None, ik_fp8=True, eps=1e-6,
+                    rope_theta=10000.0, rope_offset=0, stream=None):
+    """kv_tok [B,T,512] bf16, kv_score [B,T] f32, ik_tok [B,T,dI] bf16 | None, kv_out [B,kv_ld,512]."""
+    import torch
+    B, T, c = kv_tok.shape
+    _bits(kv_tok, "kv_tok"); _bits(gamma_kv, "gamma_kv"); _bits(kv_out, "kv_out")
+    _dt(kv_score, torch.float32, "kv_score"); _dt(ik_score, torch.float32, "ik_score")
+    dI = ik_tok.shape[-1] if ik_tok is not None else 0
+    ik_ld = ik_out.shape[1] if ik_out is not None else 0
+    st = lib().csa_compress_kv(_ptr(kv_tok), _ptr(kv_score), _ptr(ik_tok), _ptr(ik_score), B, T, tok0, blk_begin,
+                               n_blk, m, overlap, c, dI, _ptr(gamma_kv), eps, rope_theta, rope_offset,
+                               _ptr(kv_out), kv_out.shape[1], ring_cap, _ptr(ik_out), _ptr(ik_scale), ik_ld,
+                               LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16, _stream(stream))
+    _check("csa_compress_kv", st)
+
+
+def hca_compress_kv(kv_tok, kv_score, *, tok0, blk_begin, n_blk, m, gamma_kv, kv_out, ring_cap=0, eps=1e-6,
+                    rope_theta=10000.0, rope_offset=0, stream=None):
+    """HCA compression (m = 128) or the window fill (m = 1, ring_cap = ring size)."""
+    import torch
+    B, T, c = kv_tok.shape
+    _bits(kv_tok, "kv_tok"); _dt(kv_score, torch.float32, "kv_score")
+    st = lib().hca_compress_kv(_ptr(kv_tok), _ptr(kv_score), B, T, tok0, blk_begin, n_blk, m, c, _ptr(gamma_kv),
+                               eps, rope_theta, rope_offset, _ptr(kv_out), kv_out.shape[1], ring_cap,
+                               _stream(stream))
+    _check("hca_compress_kv", st)
+
+
+def csa_index_topk_workspace(B, Tq, n_cap, k):
+    return lib().csa_index_topk_workspace(B, Tq, n_cap, k)
+
+
+def csa_index_topk(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, topk_score=None,
+                   ws=None, stream=None):
+    """q_idx [B,Tq,H_I,dI] bf16, w_idx [B,Tq,H_I] bf16, ik_cache [B,ik_ld,dI] uint8 (fp8) or bf16."""
+    import torch
+    B, Tq, H_I, dI = q_idx.shape
+    fp8 = ik_cache.dtype == torch.uint8
+    _dt(q_pos, torch.int64, "q_pos"); _dt(topk_idx, torch.int32, "topk_idx")
+    if ws is None:
+        ws = workspace(csa_index_topk_workspace(B, Tq, n_cap, k), q_idx.device)
+    st = lib().csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(ik_cache), _ptr(ik_scale), ik_cache.shape[1],
+                              LCS_IK_FP8 if fp8 else LCS_IK_BF16, _ptr(q_pos), n_cap, B, Tq, H_I, dI, m, k,
+                              _ptr(topk_idx), _ptr(topk_score), _ptr(ws), ws.numel(), _stream(stream))
+    _check("csa_index_topk", st)
+
+
+def attend_workspace(B, Tq, H, max_keys):
+    return lib().lcs_attend_workspace(B, Tq, H, max_keys)
+
+
+def csa_attend(q, gamma_q, kv_cache, topk_idx, win_ring, sink, q_pos, *, window, ring_cap, out, scale=None,
+               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, stream=None):
+    """q [B,Tq,H,512] bf16 raw; kv_cache [B,kv_ld,512]; topk_idx [B,Tq,k] int32; win_ring [B,win_ld,512]."""
+    B, Tq, H, c = q.shape
+    k = topk_idx.shape[-1]
+    scale = 1.0 / (c ** 0.5) if scale is None else scale
+    if ws is None:
+        ws = workspace(attend_workspace(B, Tq, H, k + window), q.device)
+    st = lib().csa_attend(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), kv_cache.shape[1], _ptr(topk_idx), k,
+                          _ptr(win_ring), win_ring.shape[1] if win_ring is not None else 0, ring_cap, window,
+                          _ptr(sink), _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps, rope_theta, _ptr(out),
+                          _ptr(ws), ws.numel(), _stream(stream))
+    _check("csa_attend", st)
+
+
+def hca_attend(q, gamma_q, kv_cache, win_ring, sink, q_pos, *, n_cap, m, window, ring_cap, out, scale=None,
+               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, stream=None):
+    """Dense attention over entries 0 .. min(t/m, n_cap)-1 plus the window."""
+    B, Tq, H, c = q.shape
+    scale = 1.0 / (c ** 0.5) if scale is None else scale
+    if ws is None:
+        ws = workspace(attend_workspace(B, Tq, H, n_cap + window), q.device)
+    st = lib().hca_attend(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), kv_cache.shape[1], n_cap, m, _ptr(win_ring),
+                          win_ring.shape[1] if win_ring is not None else 0, ring_cap, window, _ptr(sink),
+                          _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps, rope_theta, _ptr(out), _ptr(ws),
+                          ws.numel(), _stream(stream))
+    _check("hca_attend", st)
+
+
+def grouped_out_proj_workspace(M, g, d_g):
+    return lib().grouped_out_proj_workspace(M, g, d_g)
+
+
+def grouped_out_proj(o, w_g, w_o, *, H, y, ws=None, stream=None):
+    """o [M, H*512] bf16; w_g [g, d_g, (H/g)*512]; w_o [d, g*d_g]; y [M, d]."""
+    M = o.shape[0]
+    g, d_g, _ = w_g.shape
+    d = w_o.shape[0]
+    if ws is None:
+        ws = workspace(grouped_out_proj_workspace(M, g, d_g), o.device)
+    st = lib().grouped_out_proj(_ptr(o), _ptr(w_g), _ptr(w_o), M, H, HEAD_DIM, g, d_g, d, _ptr(y), _ptr(ws),
+                                ws.numel(), _stream(stream))
+    _check("grouped_out_proj", st)
+
+
+def timing_enable(on=True):
+    _check("lcs_timing_enable", lib().lcs_timing_enable(1 if on else 0))
+
+
+def timing_read(name):
+    """(total milliseconds, launches) of the library's kernels whose name contains `name`."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check("lcs_timing_read", lib().lcs_timing_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

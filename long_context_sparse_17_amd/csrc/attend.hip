@@ -1,0 +1,471 @@
+// Core multi-query attention over compressed entries plus the sliding window, with a per-head sink
+// (page 1, "hybrid attention": CSA step 3, the HCA paragraph, Q/KV normalization, partial RoPE with
+// the output rotated by -i, the sliding-window branch, the attention sink; page 4 section 3.1).
+//
+// For a query at token t and head h:  qhat = RoPE_t(RMSNorm(q_h)),  l_j = scale * qhat . k_j,
+// o_h = sum_j e^{l_j} k_j / (e^{z_h} + sum_j e^{l_j})  (K = V),  then o_h[448:] rotated by -t.
+// Keys: the selected entries (CSA) or every visible entry (HCA), followed by tokens [t-W+1, t].
+//
+// All query heads share each 1 KiB K=V row, so per key the work is 64 heads x 512 dims twice
+// (QK^T and PV): ~128 flop per byte, above the fp32-vector ridge, hence bf16 MFMA for both.
+// Workgroup = 4 waves; wave w owns dims [128w, 128w+128) of every key, for all heads:
+//   - its K slice comes straight from HBM into MFMA A-fragments (16 B loads, 256 B per key),
+//   - partial logits over its 128 dims are summed across the 4 waves through LDS,
+//   - wave w' < HB runs the online softmax of head block w' and publishes P (bf16) and the
+//     rescale factors,
+//   - every wave then accumulates O[:, its 128 dims] += P V with V read back from its own LDS copy
+//     of the slice, laid out so the k-major V fragment reads hit 32 distinct banks.
+// Keys are split across workgroups (split-K); partial (max, sum, O) are merged by merge_kernel,
+// which adds the sink once.  With one split the workgroup finishes the output itself.
+#include "common.h"
+#include "kernels.h"
+
+namespace lcs {
+
+namespace {
+
+constexpr int kTile = 32;                 // keys per tile
+constexpr int kVtStride = 136;            // bf16 per LDS row of the V slice (128 + 8 pad)
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnK {
+  const uint16_t* q; const uint16_t* gamma_q;
+  const uint16_t* kv; int64_t kv_ld;
+  const int32_t* topk; int k;
+  int64_t n_cap; int m;
+  const uint16_t* win; int64_t win_ld, ring_cap; int window;
+  const float* sink; const int64_t* q_pos; int64_t rope_offset;
+  int Tq, H; float scale_log2, eps, theta;
+  uint16_t* out; float* part_o; float* part_ml;
+  int nsplit, keys_per_split;
+};
+
+struct RowKeys {
+  int64_t t, nc, nk;                      // query token, compressed keys in the list, total keys
+};
+
+__device__ __forceinline__ const uint16_t* key_row(const AttnK& a, int64_t b, int64_t r, const RowKeys& rk,
+                                                   int64_t e, bool* valid) {
+  if (e >= rk.nk) { *valid = false; return a.kv; }
+  if (e < rk.nc) {
+    int64_t idx = e;
+    if (a.topk) idx = a.topk[r * a.k + e];
+    *valid = idx >= 0;
+    return a.kv + (b * a.kv_ld + (idx >= 0 ? idx : 0)) * kHeadDim;
+  }
+  const int64_t j = rk.t - a.window + 1 + (e - rk.nc);
+  *valid = j >= 0;
+  const int64_t jj = j >= 0 ? j : 0;
+  const int64_t row = a.ring_cap > 0 ? jj % a.ring_cap : jj;
+  return a.win + (b * a.win_ld + row) * kHeadDim;
+}
+
+// LDS row of the V-slice copy for tile key (block kb, row r16 of the 16x16 MFMA block).
+__device__ __forceinline__ int vt_row(int kb, int r16) { return 2 * (r16 >> 2) + 8 * (r16 & 3) + kb; }
+
+template <int HB>
+__global__ void __launch_bounds__(256, 1)
+attend_kernel(AttnK a) {
+  __shared__ float4 s_part[4 * 2 * HB * kWave];            // partial logits [wave][kb][hb][lane]
+  __shared__ uint16_t s_vt[4][kTile * kVtStride];         // per-wave V slice
+  __shared__ uint4 s_p[HB * kWave];                        // P fragments [hb][lane]
+  __shared__ float s_alpha[HB * 16];
+  __shared__ float s_fac[HB * 16];
+  __shared__ float s_ssq[4][HB * 16];
+  __shared__ float s_cos[32], s_sin[32];
+  __shared__ int s_nsel;
+
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t r = blockIdx.y;
+  const int64_t b = r / a.Tq;
+  const int split = blockIdx.x;
+  const int head0 = 0;
+
+  RowKeys rk;
+  rk.t = a.q_pos[r];
+  if (a.topk) {
+    // compressed keys in the list: up to the last non-negative index
+    if (threadIdx.x == 0) s_nsel = 0;
+    __syncthreads();
+    int last = 0;
+    for (int i = threadIdx.x; i < a.k; i += 256)
+      if (a.topk[r * a.k + i] >= 0) last = i + 1;
+    atomicMax(&s_nsel, last);
+    __syncthreads();
+    rk.nc = s_nsel;
+  } else {
+    int64_t nv = rk.t >= 0 ? rk.t / a.m : 0;
+    rk.nc = nv < a.n_cap ? nv : a.n_cap;
+  }
+  rk.nk = rk.nc + a.window;
+  const int64_t e_begin = (int64_t)split * a.keys_per_split;
+  int64_t e_end = e_begin + a.keys_per_split;
+  if (e_end > rk.nk) e_end = rk.nk;
+
+  // rope table for this query position (same angles for every head)
+  const double pos = (double)(rk.t + a.rope_offset);
+  if (threadIdx.x < 32) {
+    float cs, sn;
+    rope_cs(pos, threadIdx.x, a.theta, &cs, &sn);
+    s_cos[threadIdx.x] = cs;
+    s_sin[threadIdx.x] = sn;
+  }
+
+  // ---- qhat fragments: B operand of S^T = K qhat^T, lane holds head c16 of block hb,
+  //      dims 128w + 32ks + 8g .. +8 ----
+  uint4 qf[HB][4];
+  {
+    float ss[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = head0 + hb * 16 + c16;
+      const bool hv = head < a.H;
+      float acc = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d = 128 * w + 32 * ks + 8 * g;
+        uint4 x = hv ? *reinterpret_cast<const uint4*>(a.q + (r * a.H + head) * kHeadDim + d) : make_uint4(0, 0, 0, 0);
+        qf[hb][ks] = x;
+        const float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
+                            bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j] * v[j];
+      }
+      acc += __shfl_xor(acc, 16, kWave);
+      acc += __shfl_xor(acc, 32, kWave);
+      ss[hb] = acc;
+      if (g == 0) s_ssq[w][hb * 16 + c16] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const float tot = s_ssq[0][hb * 16 + c16] + s_ssq[1][hb * 16 + c16] + s_ssq[2][hb * 16 + c16] +
+                        s_ssq[3][hb * 16 + c16];
+      const float rstd = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d = 128 * w + 32 * ks + 8 * g;
+        const uint4 x = qf[hb][ks];
+        const uint4 gm = *reinterpret_cast<const uint4*>(a.gamma_q + d);
+        float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
+                      bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
+        const float gv[8] = {bf2f_lo(gm.x), bf2f_hi(gm.x), bf2f_lo(gm.y), bf2f_hi(gm.y),
+                             bf2f_lo(gm.z), bf2f_hi(gm.z), bf2f_lo(gm.w), bf2f_hi(gm.w)};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = v[j] * rstd * gv[j];
+        if (d >= kRopeStart) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int jr = (d + 2 * p - kRopeStart) >> 1;
+            const float cs = s_cos[jr], sn = s_sin[jr];
+            const float a0 = v[2 * p], a1 = v[2 * p + 1];
+            v[2 * p] = a0 * cs - a1 * sn;
+            v[2 * p + 1] = a0 * sn + a1 * cs;
+          }
+        }
+        qf[hb][ks] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                pack_bf2(v[6], v[7]));
+      }
+    }
+    (void)ss;
+  }
+
+  floatx4 o[HB][8];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;      // softmax state of head (16w + c16), waves w < HB
+
+  const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
+
+  // ---- tile loads: this lane feeds MFMA rows kb*16 + c16 ----
+  uint4 kcur[2][4];
+  uint32_t vcur = 0;
+  auto load_tile = [&](int64_t e0, uint4 (&kf)[2][4], uint32_t& vmask) {
+    bool valid = false;
+    const uint16_t* p = key_row(a, b, r, rk, e0 + (lane & 31), &valid);
+    if (e0 + (lane & 31) >= e_end) valid = false;
+    vmask = (uint32_t)__ballot(valid && lane < 32);
+    const uint64_t pv = reinterpret_cast<uint64_t>(p);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int src = kb * 16 + c16;
+      const uint64_t pp = ((uint64_t)(uint32_t)__shfl((int)(pv >> 32), src, kWave) << 32) |
+                          (uint64_t)(uint32_t)__shfl((int)(uint32_t)pv, src, kWave);
+      const bool v = (vmask >> src) & 1u;
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(pp);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[kb][ks] = v ? *reinterpret_cast<const uint4*>(row + 128 * w + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (ntiles > 0) load_tile(e_begin, kcur, vcur);
+
+  for (int it = 0; it < ntiles; ++it) {
+    uint4 knext[2][4];
+    uint32_t vnext = 0;
+    if (it + 1 < ntiles) load_tile(e_begin + (int64_t)(it + 1) * kTile, knext, vnext);
+
+    // partial S^T over this wave's 128 dims
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(kcur[kb][ks], qf[hb][ks], acc);
+        s_part[((w * 2 + kb) * HB + hb) * kWave + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+      const int vr = vt_row(kb, c16);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<uint4*>(&s_vt[w][vr * kVtStride + 32 * ks + 8 * g]) = kcur[kb][ks];
+    }
+    __syncthreads();
+
+    if (w < HB) {
+      float s[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float4 t0 = s_part[((0 * 2 + kb) * HB + w) * kWave + lane];
+        float4 t1 = s_part[((1 * 2 + kb) * HB + w) * kWave + lane];
+        float4 t2 = s_part[((2 * 2 + kb) * HB + w) * kWave + lane];
+        float4 t3 = s_part[((3 * 2 + kb) * HB + w) * kWave + lane];
+        s[kb][0] = (t0.x + t1.x) + (t2.x + t3.x);
+        s[kb][1] = (t0.y + t1.y) + (t2.y + t3.y);
+        s[kb][2] = (t0.z + t1.z) + (t2.z + t3.z);
+        s[kb][3] = (t0.w + t1.w) + (t2.w + t3.w);
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool v = (vcur >> (kb * 16 + 4 * g + i)) & 1u;
+          s[kb][i] = v ? s[kb][i] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, s[kb][i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run, tmax);
+      float alpha = 1.f;
+      uint32_t pk[4] = {0u, 0u, 0u, 0u};
+      float psum = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run - m_new);
+        float p[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[kb * 4 + i] = exp2f(s[kb][i] - m_new);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pk[j] = pack_bf2(p[2 * j], p[2 * j + 1]);
+          psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+        }
+      }
+      psum += __shfl_xor(psum, 16, kWave);
+      psum += __shfl_xor(psum, 32, kWave);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      s_p[w * kWave + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      if (g == 0) s_alpha[w * 16 + c16] = alpha;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const float4 al = *reinterpret_cast<const float4*>(&s_alpha[hb * 16 + 4 * g]);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        o[hb][db][0] *= al.x;
+        o[hb][db][1] *= al.y;
+        o[hb][db][2] *= al.z;
+        o[hb][db][3] *= al.w;
+      }
+    }
+    uint4 pf[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) pf[hb] = s_p[hb * kWave + lane];
+    const uint16_t* vt = s_vt[w];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int col = 16 * db + c16;
+      uint32_t vv[4];
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const int j0 = 2 * j2, j1 = 2 * j2 + 1;
+        const uint32_t lo = vt[(2 * g + 8 * (j0 & 3) + (j0 >> 2)) * kVtStride + col];
+        const uint32_t hi = vt[(2 * g + 8 * (j1 & 3) + (j1 >> 2)) * kVtStride + col];
+        vv[j2] = lo | (hi << 16);
+      }
+      const uint4 vf = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) o[hb][db] = mfma_bf16(pf[hb], vf, o[hb][db]);
+    }
+
+    if (it + 1 < ntiles) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kcur[kb][ks] = knext[kb][ks];
+      vcur = vnext;
+    }
+  }
+
+  if (a.nsplit == 1) {
+    // finish here: add the sink, normalise, rotate the last 64 dims by -(t + offset), store bf16
+    if (w < HB) {
+      const int head = head0 + w * 16 + c16;
+      const float z = head < a.H ? a.sink[head] * kLog2e : -INFINITY;
+      const float M = fmaxf(m_run, z);
+      float f = 0.f;
+      if (M != -INFINITY) {
+        const float L = l_run * exp2f(m_run - M) + exp2f(z - M);
+        f = exp2f(m_run - M) / L;
+      }
+      if (g == 0) s_fac[w * 16 + c16] = f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int d = 128 * w + 16 * db + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hl = hb * 16 + 4 * g + i;
+          float v = o[hb][db][i] * s_fac[hl];
+          const float pv = __shfl_xor(v, 1, kWave);
+          if (d >= kRopeStart) {
+            const int jr = (d - kRopeStart) >> 1;
+            const float cs = s_cos[jr], sn = s_sin[jr];
+            v = (c16 & 1) ? (-pv * sn + v * cs) : (v * cs + pv * sn);
+          }
+          const int head = head0 + hl;
+          if (head < a.H) a.out[(r * a.H + head) * kHeadDim + d] = (uint16_t)f2bf(v);
+        }
+      }
+    }
+  } else {
+    const int64_t base = (r * a.nsplit + split) * a.H;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int d = 128 * w + 16 * db + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int head = head0 + hb * 16 + 4 * g + i;
+          if (head < a.H) a.part_o[(base + head) * kHeadDim + d] = o[hb][db][i];
+        }
+      }
+    if (w < HB && g == 0) {
+      const int head = head0 + w * 16 + c16;
+      if (head < a.H) {
+        a.part_ml[(base + head) * 2 + 0] = m_run;
+        a.part_ml[(base + head) * 2 + 1] = l_run;
+      }
+    }
+  }
+}
+
+// Merge split-K partials with the sink; one workgroup of 128 threads per (query, head).
+__global__ void __launch_bounds__(128)
+merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
+             const float* __restrict__ sink, const int64_t* __restrict__ q_pos, int64_t rope_offset,
+             float theta, uint16_t* __restrict__ out) {
+  const int64_t r = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float z = sink[h] * kLog2e;
+  float M = z;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((r * nsplit + s) * H + h) * 2]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  if (M != -INFINITY) {
+    L = exp2f(z - M);
+    for (int s = 0; s < nsplit; ++s) {
+      const int64_t base = (r * nsplit + s) * H + h;
+      const float ms = part_ml[base * 2], ls = part_ml[base * 2 + 1];
+      const float f = exp2f(ms - M);
+      L += f * ls;
+      const float4 v = *reinterpret_cast<const float4*>(part_o + base * kHeadDim + 4 * tid);
+      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  float y0 = acc.x * inv, y1 = acc.y * inv, y2 = acc.z * inv, y3 = acc.w * inv;
+  const int d0 = 4 * tid;
+  if (d0 >= kRopeStart) {
+    const double pos = (double)(q_pos[r] + rope_offset);
+    float c, s;
+    rope_cs(pos, (d0 - kRopeStart) / 2, theta, &c, &s);
+    const float r0 = y0 * c + y1 * s, r1 = -y0 * s + y1 * c;
+    rope_cs(pos, (d0 - kRopeStart) / 2 + 1, theta, &c, &s);
+    const float r2 = y2 * c + y3 * s, r3 = -y2 * s + y3 * c;
+    y0 = r0; y1 = r1; y2 = r2; y3 = r3;
+  }
+  uint2 o;
+  o.x = pack_bf2(y0, y1);
+  o.y = pack_bf2(y2, y3);
+  *reinterpret_cast<uint2*>(out + (r * H + h) * kHeadDim + d0) = o;
+}
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int head_blocks(int H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
+
+// Keys per split: aim for >= 512 workgroups with at least 4 tiles (128 keys) each.
+int keys_per_split(int R, int64_t max_keys) {
+  const int64_t tiles = (max_keys + kTile - 1) / kTile;
+  if (tiles <= 0) return kTile;
+  int64_t want_splits = (512 + R - 1) / R;
+  if (want_splits < 1) want_splits = 1;
+  int64_t tps = (tiles + want_splits - 1) / want_splits;
+  if (tps < 4) tps = 4;
+  if (tps > tiles) tps = tiles;
+  return (int)(tps * kTile);
+}
+
+}  // namespace
+
+size_t attend_workspace(int B, int Tq, int H, int64_t max_keys) {
+  const int R = B * Tq;
+  const int kps = keys_per_split(R, max_keys);
+  const int64_t nsplit = max_keys > 0 ? (max_keys + kps - 1) / kps : 1;
+  if (nsplit <= 1) return 256;
+  return al256((size_t)R * nsplit * H * kHeadDim * 4) + al256((size_t)R * nsplit * H * 2 * 4);
+}
+
+int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
+  const int R = x.B * x.Tq;
+  AttnK a;
+  a.q = x.q; a.gamma_q = x.gamma_q; a.kv = x.kv; a.kv_ld = x.kv_ld; a.topk = x.topk; a.k = x.k;
+  a.n_cap = x.n_cap; a.m = x.m; a.win = x.win; a.win_ld = x.win_ld; a.ring_cap = x.ring_cap;
+  a.window = x.window; a.sink = x.sink; a.q_pos = x.q_pos; a.rope_offset = x.rope_offset;
+  a.Tq = x.Tq; a.H = x.H; a.scale_log2 = x.scale * kLog2e; a.eps = x.eps; a.theta = x.theta;
+  a.out = x.out;
+  a.keys_per_split = keys_per_split(R, max_keys);
+  a.nsplit = max_keys > 0 ? (int)((max_keys + a.keys_per_split - 1) / a.keys_per_split) : 1;
+  if (a.nsplit < 1) a.nsplit = 1;
+  a.part_o = static_cast<float*>(x.ws);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
+                                       al256((size_t)R * a.nsplit * x.H * kHeadDim * 4));
+  dim3 grid((unsigned)a.nsplit, (unsigned)R);
+  switch (head_blocks(x.H)) {
+    case 1: LCS_LAUNCH("attend_kernel", attend_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 2: LCS_LAUNCH("attend_kernel", attend_kernel<2>, grid, dim3(256), 0, st, a); break;
+    default: LCS_LAUNCH("attend_kernel", attend_kernel<4>, grid, dim3(256), 0, st, a); break;
+  }
+  if (a.nsplit > 1) {
+    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(128), 0, st,
+               a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.q_pos, x.rope_offset, x.theta, x.out);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // namespace lcs

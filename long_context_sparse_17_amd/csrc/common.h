@@ -1,0 +1,103 @@
+// Device helpers shared by the gfx950 kernels of the hybrid compressed attention forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcs {
+
+constexpr int kHeadDim = 512;            // c (page 1, "hybrid attention", CSA step 4)
+constexpr int kRopeDims = 64;            // RoPE on the last 64 dims (page 1 "Partial RoPE"; page 4 section 3.1)
+constexpr int kRopeStart = kHeadDim - kRopeDims;
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// ----------------------------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// fp32 -> OCP E4M3FN code: round to nearest, ties to even, saturating at +-448; -0 -> +0.
+// Written from the format's definition: bias 7, 3 mantissa bits, subnormal quantum 2^-9.
+__device__ __forceinline__ uint32_t f2e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                           // below the smallest normal 2^-6
+    code = (uint32_t)__builtin_rintf(a * 512.0f); // exact scaling, RNE to a multiple of 2^-9 (8 -> 0x08)
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);             // keep 3 mantissa bits, RNE, carry into exponent
+    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  }
+  return code ? (sign | code) : 0u;
+}
+
+// Order-preserving map fp32 -> uint32 (larger float <-> larger key; +0 canonical).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ----------------------------------------------------------------------------------- RoPE
+// cos/sin of pos * theta^(-j/32), formed in fp64 so that positions near 2^20 keep their phase.
+__device__ __forceinline__ void rope_cs(double pos, int j, float theta, float* c, float* s) {
+  const double inv = pow((double)theta, -(double)j / (double)(kRopeDims / 2));
+  double sd, cd;
+  sincos(pos * inv, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
+// ----------------------------------------------------------------------------------- MFMA
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds A row l%16 / B column l%16 with
+// the 8 k-values of group l/16; D: lane l holds column l%16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), unit block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ floatx4 mfma_fp8(intx8 a, intx8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ----------------------------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+}  // namespace lcs
+
+// ----------------------------------------------------------------------------------- host side
+namespace lcs {
+// Launch timing hooks (no-ops unless lcs_timing_enable(1)).
+void timing_before(const char* name, hipStream_t s);
+void timing_after(const char* name, hipStream_t s);
+}  // namespace lcs
+
+#define LCS_LAUNCH(name, kern, grid, block, shmem, stream, ...)                 \
+  do {                                                                          \
+    lcs::timing_before(name, stream);                                           \
+    hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);          \
+    lcs::timing_after(name, stream);                                            \
+  } while (0)

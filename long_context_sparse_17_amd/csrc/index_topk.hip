@@ -1,0 +1,605 @@
+// Lightning-indexer scoring and per-query top-k block selection (page 1, "hybrid attention",
+// CSA step 2; page 4 section 3.1: 64 indexer heads of dim 128, top-k 512; page 1: top-k 1024 at
+// 1M context).  Score of entry s for the query at token t:  I_s = sum_h w_h * max(0, q_h . k_s),
+// over the entries visible to t (s < t / m).  The min(k, n_vis) largest are kept, ties going to
+// the lower index, and written ascending with -1 padding.
+//
+// Scoring is a dense contraction (query heads x entries x d_I) and runs on the matrix cores:
+// E4M3FN codes on the gfx950 scaled fp8 MFMA (16x16x128, unit scales), or bf16 MFMA (16x16x32).
+// Query rows are quantised in-kernel (absmax/448 per head row, RNE), their scales folded into the
+// head weights, the key scale applied after the head sum (relu commutes with a positive scale).
+//
+// Selection is an exact radix select on the order-preserving uint32 image of the fp32 scores,
+// extended by the complemented entry index so that every key is distinct:
+//   decode (few query rows):  score kernel also histograms the top 11 bits of every score
+//       (LDS, then integer atomics to a per-row global histogram) -> filter kernel, many
+//       workgroups per row, appends entries of bins above the k-th's bin to the result and those of
+//       its bin to a candidate list -> final kernel, one workgroup per row, resolves the
+//       candidates digit by digit, sorts the result ascending and writes it out.
+//   prefill (many query rows): one workgroup per row does histogram, filter and the same final.
+#include <limits.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace lcs {
+
+namespace {
+
+constexpr int kBins = 2048;                 // top 11 bits of the score key
+constexpr int kBinShift = 21;
+constexpr int kScoreChunk = 1024;           // entries per scoring workgroup
+constexpr int kFilterChunk = 4096;          // entries per filter workgroup
+constexpr int kSelThreads = 256;
+constexpr int kBitmapWords = 16384;         // 64 KiB LDS bitmap: sort by set bits for n_vis <= 2^19
+constexpr int kMaxTopk = 2048;
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Ws {
+  float* scores;      // [R, nsp]
+  uint32_t* hist;     // [R, kBins + 4]: histogram, then sel count, cand count
+  int32_t* sel;       // [R, k]
+  int32_t* cand;      // [R, nsp]
+  int64_t nsp;
+};
+
+Ws carve(void* ws, int R, int64_t n_cap, int k) {
+  Ws w;
+  w.nsp = (n_cap + 63) & ~(int64_t)63;
+  char* p = static_cast<char*>(ws);
+  w.scores = reinterpret_cast<float*>(p);
+  p += al256((size_t)R * w.nsp * 4);
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += al256((size_t)R * (kBins + 4) * 4);
+  w.sel = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)R * k * 4);
+  w.cand = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+__device__ __forceinline__ int64_t n_visible(const int64_t* q_pos, int64_t r, int m, int64_t n_cap) {
+  int64_t t = q_pos[r];
+  int64_t n = t >= 0 ? t / m : 0;
+  return n < n_cap ? n : n_cap;
+}
+
+// ------------------------------------------------------------------------------------ clear
+__global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// ------------------------------------------------------------------------------------ scoring
+// Workgroup: 4 waves.  QW = query rows per wave.  QW == 1: one query per workgroup, the waves split
+// the chunk's entries (decode).  QW == 4: 16 queries per workgroup, every wave scores the whole
+// chunk for its 4 queries (prefill; entries are re-read from L1/L2, not HBM).
+template <bool FP8, int KS, int HBI, int QW>
+__global__ void __launch_bounds__(256)
+index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
+                   const void* __restrict__ ik, const float* __restrict__ ik_scale, int64_t ik_ld,
+                   const int64_t* __restrict__ q_pos, int64_t n_cap, int Tq, int H_I, int dI, int m,
+                   float* __restrict__ scores, uint32_t* __restrict__ hist, int64_t nsp) {
+  constexpr int QWAVES = QW == 1 ? 1 : 4;       // waves that split the queries
+  constexpr int QTILE = QW * QWAVES;
+  constexpr bool HIST = (QW == 1);
+  __shared__ uint32_t lhist[HIST ? kBins : 1];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int tiles_per_b = (Tq + QTILE - 1) / QTILE;
+  const int b = blockIdx.y / tiles_per_b;
+  const int tq0 = (blockIdx.y % tiles_per_b) * QTILE;
+  const int64_t c0 = (int64_t)blockIdx.x * kScoreChunk;
+
+  // entry limit of this workgroup = max n_vis over its queries
+  int64_t nv_max = 0;
+  for (int i = 0; i < QTILE; ++i) {
+    const int tq = tq0 + i;
+    if (tq < Tq) {
+      const int64_t nv = n_visible(q_pos, (int64_t)b * Tq + tq, m, n_cap);
+      nv_max = nv > nv_max ? nv : nv_max;
+    }
+  }
+  if (c0 >= nv_max) return;                    // uniform across the workgroup
+
+  if (HIST) {
+    for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0u;
+    __syncthreads();
+  }
+
+  // ---- per-query operands: A fragments (head rows) and folded head weights ----
+  const int qgroup = wave % QWAVES;
+  const int kpart = wave / QWAVES;
+  constexpr int KWAVES = 4 / QWAVES;
+  typedef typename std::conditional<FP8, intx8, uint4>::type AFrag;
+  AFrag afr[QW][HBI][KS];
+  float wq[QW][HBI][4];
+  int64_t nvis[QW];
+  int64_t rowq[QW];
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) {
+    const int tq = tq0 + qgroup * QW + qw;
+    const bool qvalid = tq < Tq;
+    const int64_t r = (int64_t)b * Tq + (qvalid ? tq : 0);
+    rowq[qw] = r;
+    nvis[qw] = qvalid ? n_visible(q_pos, r, m, n_cap) : 0;
+#pragma unroll
+    for (int hb = 0; hb < HBI; ++hb) {
+      const int head = hb * 16 + c16;
+      const bool hv = qvalid && head < H_I;
+      const uint16_t* qrow = q_idx + (r * H_I + (hv ? head : 0)) * dI;
+      float wh = hv ? bf2f(w_idx[r * H_I + head]) : 0.f;
+      if (FP8) {
+        // dims [32g, 32g+32) of this head row
+        uint4 raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          raw[u] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * u) : make_uint4(0, 0, 0, 0);
+        float v[32];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[8 * u + 0] = bf2f_lo(raw[u].x); v[8 * u + 1] = bf2f_hi(raw[u].x);
+          v[8 * u + 2] = bf2f_lo(raw[u].y); v[8 * u + 3] = bf2f_hi(raw[u].y);
+          v[8 * u + 4] = bf2f_lo(raw[u].z); v[8 * u + 5] = bf2f_hi(raw[u].z);
+          v[8 * u + 6] = bf2f_lo(raw[u].w); v[8 * u + 7] = bf2f_hi(raw[u].w);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        intx8 codes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t b0 = f2e4m3(__fdiv_rn(v[4 * j + 0], s));
+          const uint32_t b1 = f2e4m3(__fdiv_rn(v[4 * j + 1], s));
+          const uint32_t b2 = f2e4m3(__fdiv_rn(v[4 * j + 2], s));
+          const uint32_t b3 = f2e4m3(__fdiv_rn(v[4 * j + 3], s));
+          codes[j] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+        }
+        if (!hv) codes = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+        afr[qw][hb][0] = *reinterpret_cast<AFrag*>(&codes);
+        wh *= s;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 a = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+          afr[qw][hb][ks] = *reinterpret_cast<AFrag*>(&a);
+        }
+      }
+      // the D fragment of this lane holds heads 16hb + 4g + i: fetch their weights
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[qw][hb][i] = __shfl(wh, 4 * g + i, kWave);
+    }
+  }
+
+  // ---- entry loop ----
+  const int64_t span = kScoreChunk / KWAVES;
+  int64_t e_lo = c0 + kpart * span;
+  int64_t e_hi = e_lo + span;
+  if (e_hi > nv_max) e_hi = nv_max;
+  const uint8_t* ik8 = static_cast<const uint8_t*>(ik) + (int64_t)b * ik_ld * dI;
+  const uint16_t* ik16 = static_cast<const uint16_t*>(ik) + (int64_t)b * ik_ld * dI;
+  const float* ksc = ik_scale ? ik_scale + (int64_t)b * ik_ld : nullptr;
+
+  for (int64_t e0 = e_lo; e0 < e_hi; e0 += 64) {
+    typedef typename std::conditional<FP8, intx8, uint4>::type BFrag;
+    BFrag bfr[4][KS];
+    float kscale[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = e0 + 16 * u + c16;
+      const bool ev = e < e_hi;
+      if (FP8) {
+        intx8 v = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (ev) {
+          const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 32 * g);
+          const uint4 x0 = p[0], x1 = p[1];
+          v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+        bfr[u][0] = *reinterpret_cast<BFrag*>(&v);
+        kscale[u] = ev ? ksc[e] : 0.f;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 v = ev ? *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+          bfr[u][ks] = *reinterpret_cast<BFrag*>(&v);
+        }
+        kscale[u] = 1.f;
+      }
+    }
+#pragma unroll
+    for (int qw = 0; qw < QW; ++qw) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float part = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HBI; ++hb) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (FP8)
+              acc = mfma_fp8(*reinterpret_cast<intx8*>(&afr[qw][hb][ks]), *reinterpret_cast<intx8*>(&bfr[u][ks]), acc);
+            else
+              acc = mfma_bf16(*reinterpret_cast<uint4*>(&afr[qw][hb][ks]), *reinterpret_cast<uint4*>(&bfr[u][ks]), acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part += wq[qw][hb][i] * fmaxf(acc[i], 0.f);
+        }
+        part += __shfl_xor(part, 16, kWave);
+        part += __shfl_xor(part, 32, kWave);
+        const int64_t e = e0 + 16 * u + c16;
+        if (g == 0 && e < nvis[qw]) {
+          const float sc = part * kscale[u] + 0.0f;
+          scores[rowq[qw] * nsp + e] = sc;
+          if (HIST) atomicAdd(&lhist[float_key(sc) >> kBinShift], 1u);
+        }
+      }
+    }
+  }
+
+  if (HIST) {
+    __syncthreads();
+    uint32_t* gh = hist + rowq[0] * (kBins + 4);
+    for (int i = threadIdx.x; i < kBins; i += 256) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(gh + i, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------ selection
+// Threshold bin from a complete 2048-bin histogram: the bin T holding the k-th largest score and
+// the number of scores in bins above it.  256 threads, 8 bins each, suffix scan across threads.
+__device__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* scratch) {
+  const int tid = threadIdx.x;
+  uint32_t loc[8];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { loc[j] = h[tid * 8 + j]; sum += loc[j]; }
+  // exclusive suffix sum over threads (higher thread index = higher bins = counted first)
+  scratch[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    uint32_t v = tid + off < kSelThreads ? scratch[tid + off] : 0u;
+    __syncthreads();
+    scratch[tid] += v;
+    __syncthreads();
+  }
+  const uint32_t incl = scratch[tid];           // bins >= 8*tid
+  const uint32_t excl = incl - sum;             // bins >= 8*(tid+1)
+  if (excl < (uint32_t)k && incl >= (uint32_t)k) {
+    uint32_t cum = excl;
+    for (int j = 7; j >= 0; --j) {
+      if (cum + loc[j] >= (uint32_t)k) { *T_out = tid * 8 + j; *above_out = (int)cum; break; }
+      cum += loc[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Wave-aggregated append of `pred` lanes' values to a global list with a global counter.
+__device__ __forceinline__ void wave_append(bool pred, int32_t val, uint32_t* counter, int32_t* list) {
+  const uint64_t mask = __ballot(pred);
+  if (!mask) return;
+  const int lane = lane_id();
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+  base = __shfl(base, leader, kWave);
+  if (pred) list[base + __popcll(mask & ((1ull << lane) - 1ull))] = val;
+}
+
+// Decode filter: many workgroups per row.
+__global__ void __launch_bounds__(kSelThreads)
+topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist, int32_t* __restrict__ sel,
+                   int32_t* __restrict__ cand, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
+                   int64_t n_cap, int k) {
+  __shared__ uint32_t scratch[kSelThreads];
+  __shared__ int sT, sAbove;
+  const int64_t r = blockIdx.y;
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
+  if (c0 >= nv) return;
+  uint32_t* h = hist + r * (kBins + 4);
+  int T = -1;
+  if (nv > k) {
+    if (threadIdx.x == 0) { sT = kBins - 1; sAbove = 0; }
+    __syncthreads();
+    find_threshold(h, k, &sT, &sAbove, scratch);
+    T = sT;
+  }
+  const float* srow = scores + r * nsp;
+  int64_t c1 = c0 + kFilterChunk;
+  if (c1 > nv) c1 = nv;
+  for (int64_t base = c0; base < c1; base += kSelThreads) {
+    const int64_t e = base + threadIdx.x;
+    bool is_sel = false, is_cand = false;
+    if (e < c1) {
+      if (T < 0) {
+        is_sel = true;
+      } else {
+        const int bin = (int)(float_key(srow[e]) >> kBinShift);
+        is_sel = bin > T;
+        is_cand = bin == T;
+      }
+    }
+    wave_append(is_sel, (int32_t)e, h + kBins + 0, sel + r * k);
+    wave_append(is_cand, (int32_t)e, h + kBins + 1, cand + r * nsp);
+  }
+}
+
+__device__ __forceinline__ uint64_t cand_key(const float* srow, int32_t s) {
+  return ((uint64_t)(float_key(srow[s]) & 0x1FFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
+}
+
+struct SelShared {
+  uint32_t h256[256];
+  uint32_t wsum[4];
+  int nsel;
+  int remaining;
+  int done;
+  int thr_shift;
+  unsigned long long prefix;
+  uint32_t bitmap[kBitmapWords];
+  uint32_t scan[kSelThreads];
+};
+
+// Resolve `need` winners among `ncand` candidates (all in the threshold bin) digit by digit over
+// the 53-bit key (21 low score bits, complemented index) and append them to s.sel_list.
+__device__ void refine_candidates(const float* srow, const int32_t* cand, int ncand, int need,
+                                  int32_t* sel_list, SelShared& s) {
+  const int tid = threadIdx.x;
+  if (tid == 0) { s.remaining = need; s.done = 0; s.prefix = 0ull; s.thr_shift = 0; }
+  __syncthreads();
+  int shift = 53;
+  for (int pass = 0; pass < 7; ++pass) {
+    const int width = shift >= 8 ? 8 : shift;
+    shift -= width;
+    for (int i = tid; i < 256; i += kSelThreads) s.h256[i] = 0u;
+    __syncthreads();
+    const unsigned long long pre = s.prefix;
+    for (int i = tid; i < ncand; i += kSelThreads) {
+      const uint64_t key = cand_key(srow, cand[i]);
+      if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane j covers digits 255-4j .. 252-4j (top first)
+      uint32_t c[4];
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { c[u] = s.h256[255 - 4 * tid - u]; lsum += c[u]; }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, kWave);
+        if (tid >= o) incl += v;
+      }
+      const uint32_t rem = (uint32_t)s.remaining;
+      const uint64_t hit = __ballot(incl >= rem);
+      const int first = __ffsll((unsigned long long)hit) - 1;
+      if (tid == first) {
+        uint32_t cum = incl - lsum;
+        for (int u = 0; u < 4; ++u) {
+          if (cum + c[u] >= rem) {
+            const uint32_t d = 255u - 4u * tid - u;
+            const uint32_t left = rem - cum;
+            s.remaining = (int)left;
+            s.prefix = (s.prefix << width) | d;
+            if (c[u] == left || shift == 0) { s.done = 1; s.thr_shift = shift; }
+            break;
+          }
+          cum += c[u];
+        }
+      }
+      if (tid == 0 && shift == 0 && !s.done) { s.done = 1; s.thr_shift = 0; }
+    }
+    __syncthreads();
+    if (s.done) break;
+  }
+  const unsigned long long thr = s.prefix;
+  const int ts = s.thr_shift;
+  for (int i = tid; i < ncand; i += kSelThreads) {
+    const int32_t e = cand[i];
+    if ((cand_key(srow, e) >> ts) >= thr) {
+      const int pos = atomicAdd(&s.nsel, 1);
+      if (pos < kMaxTopk) sel_list[pos] = e;
+    }
+  }
+  __syncthreads();
+}
+
+// Write the selected entries (unordered, count n) ascending into out[0..k), -1 padded.
+__device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const float* srow,
+                               int32_t* out_idx, float* out_score, SelShared& s) {
+  const int tid = threadIdx.x;
+  if (nv <= (int64_t)kBitmapWords * 32) {
+    const int words = (int)((nv + 31) / 32);
+    for (int i = tid; i < words; i += kSelThreads) s.bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const int32_t e = list[i];
+      if (e >= 0 && (int64_t)e < nv) atomicOr(&s.bitmap[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    const int per = (words + kSelThreads - 1) / kSelThreads;
+    const int w0 = tid * per;
+    uint32_t cnt = 0;
+    for (int i = 0; i < per; ++i) if (w0 + i < words) cnt += __popc(s.bitmap[w0 + i]);
+    s.scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kSelThreads; off <<= 1) {
+      const uint32_t v = tid >= off ? s.scan[tid - off] : 0u;
+      __syncthreads();
+      s.scan[tid] += v;
+      __syncthreads();
+    }
+    int pos = (int)(s.scan[tid] - cnt);
+    for (int i = 0; i < per; ++i) {
+      if (w0 + i >= words) break;
+      uint32_t bits = s.bitmap[w0 + i];
+      while (bits) {
+        const int bpos = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int32_t e = (w0 + i) * 32 + bpos;
+        out_idx[pos] = e;
+        if (out_score) out_score[pos] = srow[e];
+        ++pos;
+      }
+    }
+  } else {
+    // bitonic sort of up to 2048 indices
+    int P = 2;
+    while (P < n) P <<= 1;
+    for (int i = tid; i < P; i += kSelThreads) if (i >= n) list[i] = INT_MAX;
+    __syncthreads();
+    for (int kk = 2; kk <= P; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += kSelThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int32_t a = list[i], bb = list[ixj];
+            const bool up = (i & kk) == 0;
+            if ((a > bb) == up) { list[i] = bb; list[ixj] = a; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < n; i += kSelThreads) {
+      out_idx[i] = list[i];
+      if (out_score) out_score[i] = srow[list[i]];
+    }
+  }
+  for (int i = n + tid; i < k; i += kSelThreads) {
+    out_idx[i] = -1;
+    if (out_score) out_score[i] = -INFINITY;
+  }
+}
+
+// Decode final: one workgroup per row.
+__global__ void __launch_bounds__(kSelThreads)
+topk_final_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+                  const int32_t* __restrict__ sel, const int32_t* __restrict__ cand, int64_t nsp,
+                  const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
+                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  __shared__ SelShared s;
+  __shared__ int32_t list[kMaxTopk];
+  const int64_t r = blockIdx.x;
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const uint32_t* h = hist + r * (kBins + 4);
+  const int nsel = (int)h[kBins + 0];
+  const int ncand = (int)h[kBins + 1];
+  const float* srow = scores + r * nsp;
+  for (int i = threadIdx.x; i < nsel; i += kSelThreads) list[i] = sel[r * k + i];
+  if (threadIdx.x == 0) s.nsel = nsel;
+  __syncthreads();
+  if (nv > k) refine_candidates(srow, cand + r * nsp, ncand, k - nsel, list, s);
+  __syncthreads();
+  const int n = s.nsel < k ? s.nsel : k;
+  sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
+}
+
+// Prefill: one workgroup per row does histogram, filter, refine, sort.
+__global__ void __launch_bounds__(kSelThreads)
+topk_rowwise_kernel(const float* __restrict__ scores, int32_t* __restrict__ cand, int64_t nsp,
+                    const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
+                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  __shared__ SelShared s;
+  __shared__ int32_t list[kMaxTopk];
+  __shared__ uint32_t h[kBins];
+  __shared__ int sT, sAbove, sCand;
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const float* srow = scores + r * nsp;
+  if (nv <= k) {
+    for (int64_t i = tid; i < k; i += kSelThreads) {
+      topk_idx[r * k + i] = i < nv ? (int32_t)i : -1;
+      if (topk_score) topk_score[r * k + i] = i < nv ? srow[i] : -INFINITY;
+    }
+    return;
+  }
+  for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
+  if (tid == 0) { s.nsel = 0; sCand = 0; sT = kBins - 1; sAbove = 0; }
+  __syncthreads();
+  for (int64_t e = tid; e < nv; e += kSelThreads) atomicAdd(&h[float_key(srow[e]) >> kBinShift], 1u);
+  __syncthreads();
+  find_threshold(h, k, &sT, &sAbove, s.scan);
+  const int T = sT;
+  int32_t* crow = cand + r * nsp;
+  for (int64_t e = tid; e < nv; e += kSelThreads) {
+    const int bin = (int)(float_key(srow[e]) >> kBinShift);
+    if (bin > T) list[atomicAdd(&s.nsel, 1)] = (int32_t)e;
+    else if (bin == T) crow[atomicAdd(&sCand, 1)] = (int32_t)e;
+  }
+  __syncthreads();
+  const int nsel = s.nsel;
+  refine_candidates(srow, crow, sCand, k - nsel, list, s);
+  const int n = s.nsel < k ? s.nsel : k;
+  sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
+}
+
+template <bool FP8, int KS, int HBI, int QW>
+void launch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  constexpr int QTILE = QW == 1 ? 1 : 16;
+  const int tiles = (a.Tq + QTILE - 1) / QTILE;
+  dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));
+  LCS_LAUNCH("index_score_kernel", (index_score_kernel<FP8, KS, HBI, QW>), grid, dim3(256), 0, st,
+             a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m,
+             w.scores, w.hist, w.nsp);
+}
+
+template <bool FP8, int KS, int QW>
+void dispatch_hbi(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  if (a.H_I <= 16) launch_score<FP8, KS, 1, QW>(a, w, st);
+  else if (a.H_I <= 32) launch_score<FP8, KS, 2, QW>(a, w, st);
+  else launch_score<FP8, KS, 4, QW>(a, w, st);
+}
+
+template <int QW>
+void dispatch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  if (a.ik_fp8) dispatch_hbi<true, 1, QW>(a, w, st);
+  else if (a.dI == 64) dispatch_hbi<false, 2, QW>(a, w, st);
+  else dispatch_hbi<false, 4, QW>(a, w, st);
+}
+
+}  // namespace
+
+size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
+  const int64_t R = (int64_t)B * Tq;
+  const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
+  return al256((size_t)R * nsp * 4) + al256((size_t)R * (kBins + 4) * 4) + al256((size_t)R * k * 4) +
+         al256((size_t)R * nsp * 4);
+}
+
+int launch_index_topk(const IndexArgs& a, hipStream_t st) {
+  const int R = a.B * a.Tq;
+  Ws w = carve(a.ws, R, a.n_cap, a.k);
+  // Few rows: spread every row over many workgroups (decode).  Many rows: row-per-workgroup.
+  const bool decode = R < 64;
+  if (decode) {
+    const int64_t n = (int64_t)R * (kBins + 4);
+    LCS_LAUNCH("topk_clear_kernel", clear_u32_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
+               dim3(256), 0, st, w.hist, n);
+    dispatch_score<1>(a, w, st);
+    dim3 gf((unsigned)((a.n_cap + kFilterChunk - 1) / kFilterChunk), (unsigned)R);
+    LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.sel,
+               w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k);
+    LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
+               w.hist, w.sel, w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
+  } else {
+    dispatch_score<4>(a, w, st);
+    LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
+               w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // namespace lcs

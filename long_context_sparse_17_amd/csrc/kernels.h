@@ -1,0 +1,50 @@
+// Internal launcher interface between the C-ABI layer and the kernels (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcs {
+
+struct CompressArgs {
+  const uint16_t* kv_tok; const float* kv_score; const uint16_t* ik_tok; const float* ik_score;
+  int B, T; int64_t tok0, blk_begin; int n_blk, m, ov, dI;
+  const uint16_t* gamma; float eps, theta; int64_t rope_offset;
+  uint16_t* kv_out; int64_t kv_ld, ring_cap;
+  void* ik_out; float* ik_scale; int64_t ik_ld; int ik_fp8;
+};
+int launch_compress(const CompressArgs& a, hipStream_t stream);
+
+struct IndexArgs {
+  const uint16_t* q_idx; const uint16_t* w_idx;
+  const void* ik; const float* ik_scale; int64_t ik_ld; int ik_fp8;
+  const int64_t* q_pos; int64_t n_cap;
+  int B, Tq, H_I, dI, m, k;
+  int32_t* topk_idx; float* topk_score;
+  void* ws; size_t ws_bytes;
+};
+size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
+int launch_index_topk(const IndexArgs& a, hipStream_t stream);
+
+struct AttendArgs {
+  const uint16_t* q; const uint16_t* gamma_q;
+  const uint16_t* kv; int64_t kv_ld;
+  const int32_t* topk; int k;          // CSA: selected entries (topk != nullptr)
+  int64_t n_cap; int m;                // HCA: all visible entries
+  const uint16_t* win; int64_t win_ld, ring_cap; int window;
+  const float* sink; const int64_t* q_pos; int64_t rope_offset;
+  int B, Tq, H; float scale, eps, theta;
+  uint16_t* out; void* ws; size_t ws_bytes;
+};
+size_t attend_workspace(int B, int Tq, int H, int64_t max_keys);
+int launch_attend(const AttendArgs& a, int64_t max_keys, hipStream_t stream);
+
+struct OutProjArgs {
+  const uint16_t* o; const uint16_t* w_g; const uint16_t* w_o;
+  int M, H, c, g, d_g, d; uint16_t* y; void* ws; size_t ws_bytes;
+};
+size_t out_proj_workspace(int M, int g, int d_g);
+int launch_out_proj(const OutProjArgs& a, hipStream_t stream);
+
+}  // namespace lcs

@@ -1,0 +1,209 @@
+"""Decode-step drivers for one CSA or HCA layer, composed from the C-ABI entry points only.
+
+A layer holds its device state (compressed caches, window ring, raw-token staging, weights,
+workspaces) and `step()` enqueues one decode step for the query at token t = ctx of every
+sequence, in the order the method runs it (page 1, "hybrid attention", CSA steps 1-4 / HCA):
+
+  CSA: window fill (token t) -> compress the block that ended at t-1 (kv entry + fp8 indexer key)
+       -> indexer scores + top-k -> attention over the selected entries + window + sink
+       -> grouped output projection
+  HCA: window fill -> compress the 128-token block that ended at t-1 -> dense attention
+       -> grouped output projection
+
+Re-compressing the last finished block every step writes the same values again; it stands for the
+compression work a real decoder does once per m (CSA) or 128 (HCA) steps and is counted every step.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (csa_attend, csa_compress_kv, csa_index_topk, csa_index_topk_workspace, attend_workspace,
+               grouped_out_proj, grouped_out_proj_workspace, hca_attend, hca_compress_kv, workspace)
+
+RING = 256          # window ring rows (>= the 128-token window)
+
+
+class _Common:
+    def __init__(self, B, ctx, H, W, g, d_g, d, device, weights_std, seed):
+        self.B, self.ctx, self.H, self.W = B, ctx, H, W
+        self.g, self.d_g, self.d = g, d_g, d
+        self.dev = device
+        self.t = ctx
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+
+        def nrm(shape, std):
+            x = torch.empty(shape, dtype=torch.float32, device=device)
+            x.normal_(0.0, std, generator=gen)
+            return x
+
+        self._nrm = nrm
+        self.gamma = torch.ones(512, dtype=torch.bfloat16, device=device)
+        self.ring = torch.zeros((B, RING, 512), dtype=torch.bfloat16, device=device)
+        self.q_pos = torch.full((B, 1), ctx, dtype=torch.int64, device=device)
+        self.sink = nrm((H,), 1.0)
+        self.o = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=device)
+        self.y = torch.empty((B, d), dtype=torch.bfloat16, device=device)
+        self.w_g = nrm((g, d_g, H * 512 // g), weights_std).to(torch.bfloat16)
+        self.w_o = nrm((d, g * d_g), weights_std).to(torch.bfloat16)
+        self.ws_proj = workspace(grouped_out_proj_workspace(B, g, d_g), device)
+        self.new_tok = nrm((B, 1, 512), 1.28).to(torch.bfloat16)
+        self.new_score = nrm((B, 1), 1.28)
+        self.q = nrm((B, 1, H, 512), 1.28).to(torch.bfloat16)
+
+    def fill_ring(self, tok, score, t0):
+        """Window tokens [t0, t0 + T) of raw per-token vectors into the ring (m = 1 compression)."""
+        T = tok.shape[1]
+        hca_compress_kv(tok, score, tok0=t0, blk_begin=t0, n_blk=T, m=1, gamma_kv=self.gamma, kv_out=self.ring,
+                        ring_cap=RING)
+
+    def _window_and_proj_tail(self):
+        grouped_out_proj(self.o.view(self.B, self.H * 512), self.w_g, self.w_o, H=self.H, y=self.y,
+                         ws=self.ws_proj)
+
+
+class CsaDecodeLayer(_Common):
+    """One CSA layer (m = 4 with an overlap of 4, fp8 indexer 64 x 128, top-k k)."""
+
+    def __init__(self, B, ctx, k=1024, H=64, H_I=64, dI=128, W=128, g=8, d_g=1024, d=4096, m=4, ov=4,
+                 device="cuda", weights_std=0.02, seed=0):
+        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed)
+        self.k, self.H_I, self.dI, self.m, self.ov = k, H_I, dI, m, ov
+        self.n_cap = ctx // m
+        nrm = self._nrm
+        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
+        self.ik_cache = torch.empty((B, self.n_cap, dI), dtype=torch.uint8, device=device)
+        self.ik_scale = torch.empty((B, self.n_cap), dtype=torch.float32, device=device)
+        self.stage_kv = nrm((B, m + ov, 512), 1.28).to(torch.bfloat16)
+        self.stage_s = nrm((B, m + ov), 1.28)
+        self.stage_ik = nrm((B, m + ov, dI), 1.28).to(torch.bfloat16)
+        self.stage_is = nrm((B, m + ov), 1.28)
+        self.q_idx = nrm((B, 1, H_I, dI), 1.28).to(torch.bfloat16)
+        self.w_idx = nrm((B, 1, H_I), 1.28).to(torch.bfloat16)
+        self.topk = torch.empty((B, 1, k), dtype=torch.int32, device=device)
+        self.ws_index = workspace(csa_index_topk_workspace(B, 1, self.n_cap, k), device)
+        self.ws_attn = workspace(attend_workspace(B, 1, H, k + W), device)
+
+    def build_caches(self, block_tokens=65536, seed=1):
+        """Fill the compressed caches for tokens [0, ctx) from seeded raw per-token data on the device,
+        through csa_compress_kv (bulk path), and the window ring for tokens [ctx-W+1, ctx)."""
+        B, m, ov = self.B, self.m, self.ov
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(seed)
+        nb_per = block_tokens // m
+        for blk0 in range(0, self.n_cap, nb_per):
+            nb = min(nb_per, self.n_cap - blk0)
+            t0 = max(0, blk0 * m - ov)
+            T = (blk0 + nb) * m - t0
+            kv = torch.empty((B, T, 512), device=self.dev).normal_(0, 1.28, generator=gen).to(torch.bfloat16)
+            ks = torch.empty((B, T), device=self.dev).normal_(0, 1.28, generator=gen)
+            ik = torch.empty((B, T, self.dI), device=self.dev).normal_(0, 1.28, generator=gen).to(torch.bfloat16)
+            iks = torch.empty((B, T), device=self.dev).normal_(0, 1.28, generator=gen)
+            csa_compress_kv(kv, ks, ik, iks, tok0=t0, blk_begin=blk0, n_blk=nb, m=m, overlap=ov, gamma_kv=self.gamma,
+                            kv_out=self.kv_cache, ik_out=self.ik_cache, ik_scale=self.ik_scale, ik_fp8=True)
+            if blk0 + nb == self.n_cap:
+                w0 = max(0, self.ctx - self.W + 1)
+                self.fill_ring(kv[:, w0 - t0:], ks[:, w0 - t0:], w0)
+            del kv, ks, ik, iks
+
+    def step(self):
+        t, m = self.t, self.m
+        self.fill_ring(self.new_tok, self.new_score, t)
+        blk = t // m - 1
+        t0 = blk * m - self.ov
+        csa_compress_kv(self.stage_kv, self.stage_s, self.stage_ik, self.stage_is, tok0=t0, blk_begin=blk, n_blk=1,
+                        m=m, overlap=self.ov, gamma_kv=self.gamma, kv_out=self.kv_cache, ik_out=self.ik_cache,
+                        ik_scale=self.ik_scale, ik_fp8=True)
+        csa_index_topk(self.q_idx, self.w_idx, self.ik_cache, self.ik_scale, self.q_pos, n_cap=self.n_cap, m=m,
+                       k=self.k, topk_idx=self.topk, ws=self.ws_index)
+        csa_attend(self.q, self.gamma, self.kv_cache, self.topk, self.ring, self.sink, self.q_pos, window=self.W,
+                   ring_cap=RING, out=self.o, ws=self.ws_attn)
+        self._window_and_proj_tail()
+
+    def bytes_per_step(self):
+        """Algorithmic HBM bytes of one step (each key/entry/weight read once, outputs written once)."""
+        B, k, W, H = self.B, self.k, self.W, self.H
+        n_vis = min(self.t // self.m, self.n_cap)
+        index = B * n_vis * (self.dI + 4) + B * self.H_I * (self.dI * 2 + 2)
+        attend = B * (min(k, n_vis) + W) * 1024 + B * H * 512 * 2 * 2 + B * k * 4
+        proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
+        compress = B * ((self.m + self.ov) * (512 + self.dI) * 2 + 512 * 2 + self.dI + 4) + B * 512 * 4
+        return {"index": index, "attend": attend, "proj": proj, "compress": compress}
+
+
+class HcaDecodeLayer(_Common):
+    """One HCA layer (m' = 128, no overlap, dense attention over every visible entry)."""
+
+    def __init__(self, B, ctx, H=64, W=128, g=8, d_g=1024, d=4096, m=128, device="cuda", weights_std=0.02, seed=0):
+        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed)
+        self.m = m
+        self.n_cap = ctx // m
+        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
+        self.stage_kv = self._nrm((B, m, 512), 1.28).to(torch.bfloat16)
+        self.stage_s = self._nrm((B, m), 1.28)
+        self.ws_attn = workspace(attend_workspace(B, 1, H, self.n_cap + W), device)
+
+    def build_caches(self, block_tokens=65536, seed=1):
+        B, m = self.B, self.m
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(seed)
+        nb_per = block_tokens // m
+        for blk0 in range(0, self.n_cap, nb_per):
+            nb = min(nb_per, self.n_cap - blk0)
+            t0 = blk0 * m
+            T = nb * m
+            kv = torch.empty((B, T, 512), device=self.dev).normal_(0, 1.28, generator=gen).to(torch.bfloat16)
+            ks = torch.empty((B, T), device=self.dev).normal_(0, 1.28, generator=gen)
+            hca_compress_kv(kv, ks, tok0=t0, blk_begin=blk0, n_blk=nb, m=m, gamma_kv=self.gamma, kv_out=self.kv_cache)
+            if blk0 + nb == self.n_cap:
+                w0 = max(0, self.ctx - self.W + 1)
+                self.fill_ring(kv[:, w0 - t0:], ks[:, w0 - t0:], w0)
+            del kv, ks
+
+    def step(self):
+        t, m = self.t, self.m
+        self.fill_ring(self.new_tok, self.new_score, t)
+        blk = t // m - 1
+        hca_compress_kv(self.stage_kv, self.stage_s, tok0=blk * m, blk_begin=blk, n_blk=1, m=m, gamma_kv=self.gamma,
+                        kv_out=self.kv_cache)
+        hca_attend(self.q, self.gamma, self.kv_cache, self.ring, self.sink, self.q_pos, n_cap=self.n_cap, m=m,
+                   window=self.W, ring_cap=RING, out=self.o, ws=self.ws_attn)
+        self._window_and_proj_tail()
+
+    def bytes_per_step(self):
+        B, W, H = self.B, self.W, self.H
+        n_vis = min(self.t // self.m, self.n_cap)
+        attend = B * (n_vis + W) * 1024 + B * H * 512 * 2 * 2
+        proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
+        compress = B * (self.m * (512 * 2 + 4) + 512 * 2) + B * 512 * 4
+        return {"attend": attend, "proj": proj, "compress": compress}
+
+
+def hybrid_stack(B=8, ctx=1 << 20, k=1024, device="cuda", build=True):
+    """The 4-layer decode stack (CSA, HCA, CSA, HCA) at one GPU's share of the hybrid configuration."""
+    layers = []
+    for i, kind in enumerate(("csa", "hca", "csa", "hca")):
+        L = CsaDecodeLayer(B, ctx, k=k, device=device, seed=100 + i) if kind == "csa" else \
+            HcaDecodeLayer(B, ctx, device=device, seed=100 + i)
+        if build:
+            L.build_caches(seed=200 + i)
+        layers.append(L)
+    return layers
+
+
+def flops_per_step(layer):
+    """Algorithmic flops: indexer dots (2 d_I per head-entry), QK^T + PV (4 c per head-key), projections."""
+    B, H = layer.B, layer.H
+    proj = 2 * B * (layer.w_g.numel() + layer.w_o.numel())
+    if isinstance(layer, CsaDecodeLayer):
+        n_vis = min(layer.t // layer.m, layer.n_cap)
+        return {"index": 2 * B * n_vis * layer.H_I * layer.dI,
+                "attend": 4 * 512 * B * H * (min(layer.k, n_vis) + layer.W), "proj": proj}
+    n_vis = min(layer.t // layer.m, layer.n_cap)
+    return {"attend": 4 * 512 * B * H * (n_vis + layer.W), "proj": proj}
+
+
+__all__ = ["CsaDecodeLayer", "HcaDecodeLayer", "hybrid_stack", "flops_per_step", "RING"]
+_ = math

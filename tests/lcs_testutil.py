@@ -1,0 +1,95 @@
+"""Comparison helpers shared by the parity tests (no method arithmetic beyond what the oracle does).
+
+Tolerances (bf16 outputs, from the stated parity bar): the maximum absolute error, taken relative to
+max(1, rms(reference)) so that bf16 rounding of outputs larger than 1 is not counted against the
+kernel, must be <= 2e-2, and the relative L2 error <= 5e-3.  fp8-indexer outputs compared with an
+oracle that does not quantise the indexer: relative L2 <= 5e-2.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+import synth
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+REL_L2_FP8_VS_EXACT = 5e-2
+
+
+def to_np_bf16(t):
+    """bf16 torch tensor (any device) -> float64 numpy, exactly."""
+    import torch
+    return synth.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def from_bits(bits, device="cuda"):
+    """uint16 bf16 patterns (numpy) -> torch bfloat16 tensor on device."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = got - ref
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    max_abs = float(np.max(np.abs(d))) / max(1.0, rms) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)) if d.size else 0.0
+    return max_abs, rel
+
+
+def assert_close(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
+    ma, rl = errors(got, ref)
+    assert ma <= max_abs and rl <= rel_l2, f"{what}: max-abs {ma:.3e} (<= {max_abs}), rel-L2 {rl:.3e} (<= {rel_l2})"
+    return ma, rl
+
+
+def check_topk_row(gpu_idx, oracle_scores, k, bound):
+    """Validate one GPU top-k row against the oracle's float64 scores of the same inputs.
+
+    gpu_idx [k] int (ascending, -1 padded); oracle_scores [n_vis]; bound [n_vis] = per-entry fp32
+    accumulation error bound.  Sets must agree wherever the score gap to the k-th exceeds the bound.
+    Returns the number of entries that differ inside the band.
+    """
+    n = oracle_scores.shape[0]
+    want = min(k, n)
+    g = np.asarray(gpu_idx)
+    valid = g[g >= 0]
+    assert valid.shape[0] == want, f"selected {valid.shape[0]} entries, expected {want}"
+    assert np.all(g[want:] == -1), "padding must be -1"
+    assert np.all(np.diff(valid) > 0), "indices must be strictly ascending"
+    assert valid.size == 0 or (valid.min() >= 0 and valid.max() < n), "index out of the visible range"
+    if want == 0:
+        return 0
+    ref = O.topk_select(oracle_scores, k)
+    ref = ref[ref >= 0]
+    if np.array_equal(ref, valid):
+        return 0
+    order = np.lexsort((np.arange(n), -oracle_scores))
+    kth = oracle_scores[order[want - 1]]
+    extra = np.setdiff1d(valid, ref)        # chosen by the GPU, not by the oracle
+    missing = np.setdiff1d(ref, valid)      # chosen by the oracle, not by the GPU
+    tau = 1e-6 * max(1.0, abs(kth))
+    for s in extra:
+        assert oracle_scores[s] >= kth - max(tau, bound[s]), f"GPU picked {s}: {oracle_scores[s]} vs kth {kth}"
+    for s in missing:
+        assert oracle_scores[s] <= kth + max(tau, bound[s]), f"GPU dropped {s}: {oracle_scores[s]} vs kth {kth}"
+    return int(extra.size)
+
+
+def index_oracle_row(q_idx_bits, w_idx_bits, k_deq, fp8):
+    """Oracle scores for one query row (inputs as given to the GPU) and their fp32 error bounds.
+
+    q_idx_bits [H_I, dI] bf16 patterns; w_idx_bits [H_I]; k_deq [n, dI] float64 dequantised keys.
+    In fp8 mode the query rows are quantised with the kernel's fp32 decision rule.
+    """
+    q = synth.bf16_bits_to_f64(q_idx_bits)
+    w = synth.bf16_bits_to_f64(w_idx_bits)
+    if fp8:
+        _, _, q = O.fp8_quantize_rows(q, kernel_fp32=True)
+    sc = O.index_scores(q, w, k_deq)
+    mag = (np.abs(k_deq) @ np.abs(q).T) @ np.abs(w)
+    H, dI = q.shape
+    bound = mag * (dI + H + 8) * 2.0 ** -23
+    return sc, bound

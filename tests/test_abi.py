@@ -1,0 +1,129 @@
+"""C-ABI contract tests (no GPU): the library loads, exports every symbol include/lcs.h declares, and
+rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_17_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcs.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("liblcs.so is not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"binding misses {n}"
+    assert set(L.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lcs_version() >= 10000
+    for code, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small")]:
+        assert lib.lcs_status_string(code) == txt
+
+
+def test_workspace_queries_are_positive_and_monotone(lib):
+    a = lib.csa_index_topk_workspace(8, 1, 262144, 1024)
+    b = lib.csa_index_topk_workspace(8, 1, 262145, 1024)
+    assert 0 < a <= b
+    assert lib.csa_index_topk_workspace(0, 1, 10, 1) == 0
+    assert lib.lcs_attend_workspace(8, 1, 64, 8192 + 128) > 8 * 64 * 512 * 4
+    assert lib.grouped_out_proj_workspace(8, 8, 1024) >= 8 * 8 * 1024 * 2
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+
+
+def test_attend_rejects_bad_arguments(lib):
+    args = [FAKE, FAKE, FAKE, 100, FAKE, 16, FAKE, 200, 0, 128, FAKE, FAKE, 0, 1, 1, 64, 512, 0.04, 1e-6, 1e4,
+            FAKE, FAKE, 1 << 30, None]
+    bad_c = list(args); bad_c[16] = 256
+    assert lib.csa_attend(*bad_c) == L.LCS_ERR_UNSUPPORTED
+    bad_h = list(args); bad_h[15] = 65
+    assert lib.csa_attend(*bad_h) == L.LCS_ERR_UNSUPPORTED
+    null_q = list(args); null_q[0] = None
+    assert lib.csa_attend(*null_q) == L.LCS_ERR_ARG
+    small_ws = list(args); small_ws[22] = 0
+    assert lib.csa_attend(*small_ws) == L.LCS_ERR_WORKSPACE
+    mis = list(args); mis[0] = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.csa_attend(*mis) == L.LCS_ERR_ARG
+    big_k = list(args); big_k[5] = 4096
+    assert lib.csa_attend(*big_k) == L.LCS_ERR_UNSUPPORTED
+    neg_scale = list(args); neg_scale[17] = -1.0
+    assert lib.csa_attend(*neg_scale) == L.LCS_ERR_ARG
+
+
+def test_index_rejects_bad_arguments(lib):
+    base = [FAKE, FAKE, FAKE, FAKE, 1000, L.LCS_IK_FP8, FAKE, 1000, 2, 1, 64, 128, 4, 64, FAKE, None, FAKE,
+            1 << 30, None]
+    assert lib.csa_index_topk(*[a if i != 11 else 64 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
+    assert lib.csa_index_topk(*[a if i != 10 else 65 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
+    assert lib.csa_index_topk(*[a if i != 13 else 4096 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
+    assert lib.csa_index_topk(*[a if i != 17 else 16 for i, a in enumerate(base)]) == L.LCS_ERR_WORKSPACE
+    assert lib.csa_index_topk(*[a if i != 4 else 999 for i, a in enumerate(base)]) == L.LCS_ERR_ARG
+    assert lib.csa_index_topk(*[a if i != 5 else 7 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
+    assert lib.csa_index_topk(*[a if i != 3 else None for i, a in enumerate(base)]) == L.LCS_ERR_ARG
+
+
+def test_compress_rejects_tokens_outside_the_given_columns(lib):
+    # blocks 10..11 of m=4, ov=4 need tokens 36..47; columns start at tok0 = 40
+    args = [FAKE, FAKE, None, None, 1, 8, 40, 10, 2, 4, 4, 512, 0, FAKE, 1e-6, 1e4, 0, FAKE, 100, 0, None, None, 0,
+            0, None]
+    assert lib.csa_compress_kv(*args) == L.LCS_ERR_ARG
+    ok_cols = list(args); ok_cols[6] = 36; ok_cols[5] = 12
+    bad_c = list(ok_cols); bad_c[11] = 128
+    assert lib.csa_compress_kv(*bad_c) == L.LCS_ERR_UNSUPPORTED
+    bad_ld = list(ok_cols); bad_ld[18] = 11
+    assert lib.csa_compress_kv(*bad_ld) == L.LCS_ERR_ARG
+    bad_ov = list(ok_cols); bad_ov[10] = 17
+    assert lib.csa_compress_kv(*bad_ov) == L.LCS_ERR_UNSUPPORTED
+    # HCA path: overlap is always 0; m = 128 blocks need 128 columns each
+    assert lib.hca_compress_kv(FAKE, FAKE, 1, 100, 0, 0, 1, 128, 512, FAKE, 1e-6, 1e4, 0, FAKE, 10, 0, None) == \
+        L.LCS_ERR_ARG
+
+
+def test_out_proj_rejects_bad_grouping(lib):
+    assert lib.grouped_out_proj(FAKE, FAKE, FAKE, 8, 64, 512, 7, 1024, 4096, FAKE, FAKE, 1 << 30, None) == \
+        L.LCS_ERR_UNSUPPORTED
+    assert lib.grouped_out_proj(FAKE, FAKE, FAKE, 8, 64, 512, 8, 1000, 4096, FAKE, FAKE, 1 << 30, None) == \
+        L.LCS_ERR_UNSUPPORTED
+    assert lib.grouped_out_proj(FAKE, FAKE, FAKE, 8, 64, 512, 8, 1024, 4096, FAKE, FAKE, 16, None) == \
+        L.LCS_ERR_WORKSPACE
+
+
+def test_timing_facility_without_launches(lib):
+    assert lib.lcs_timing_enable(1) == 0
+    ms = ctypes.c_double(-1)
+    n = ctypes.c_int64(-1)
+    assert lib.lcs_timing_read(b"attend", ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.lcs_timing_enable(0) == 0
+
+
+def test_product_path_has_no_fallback():
+    """The binding loads only liblcs.so; nothing in the package imports the oracle."""
+    pkg = os.path.dirname(L.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(root, f), encoding="utf-8").read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

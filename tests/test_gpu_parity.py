@@ -1,0 +1,310 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle on small seeded inputs.
+
+Sizes span several tiles / chunks and a ragged tail; edge cases: n_vis = 0, n_vis < k, ties,
+-1 padding, ring-buffer windows, one split and many splits, heads < 16.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_17_amd as L
+import oracle as O
+import synth
+from lcs_testutil import (REL_L2_FP8_VS_EXACT, assert_close, check_topk_row, errors, from_bits,
+                          index_oracle_row, to_np_bf16)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def dev_i64(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(DEV)
+
+
+# ----------------------------------------------------------------------------------- fp8 quantiser
+def test_fp8_quantiser_bit_exact_exhaustive():
+    """Every bf16 value in [-448, 448] through the device quantiser (m = 1 compression of the
+    indexer key, scale exactly 1) against the oracle's E4M3FN encoder; plus random rows."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = synth.bf16_bits_to_f32(bits)
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    bits = bits[keep]
+    per = 127
+    R = (bits.size + per - 1) // per
+    pad = np.full(R * per - bits.size, bits[0], dtype=np.uint16)
+    rows = np.concatenate([bits, pad]).reshape(R, per)
+    rows = np.concatenate([rows, np.full((R, 1), synth.f32_to_bf16_bits(np.float32(448.0)), np.uint16)], 1)
+    rnd = synth.normal_bf16((64, 128), 1.28, 900, 1)
+    ik_bits = np.concatenate([rows, rnd], 0)
+    T = ik_bits.shape[0]
+    ik = from_bits(ik_bits[None])
+    kv = torch.zeros((1, T, 512), dtype=torch.bfloat16, device=DEV)
+    zs = torch.zeros((1, T), dtype=torch.float32, device=DEV)
+    gamma = torch.ones(512, dtype=torch.bfloat16, device=DEV)
+    kv_out = torch.empty((1, T, 512), dtype=torch.bfloat16, device=DEV)
+    ik_out = torch.empty((1, T, 128), dtype=torch.uint8, device=DEV)
+    ik_sc = torch.empty((1, T), dtype=torch.float32, device=DEV)
+    L.csa_compress_kv(kv, zs, ik, zs, tok0=0, blk_begin=0, n_blk=T, m=1, overlap=0, gamma_kv=gamma,
+                      kv_out=kv_out, ik_out=ik_out, ik_scale=ik_sc, ik_fp8=True)
+    torch.cuda.synchronize()
+    codes, s, _ = O.fp8_quantize_rows(synth.bf16_bits_to_f64(ik_bits), kernel_fp32=True)
+    got = ik_out[0].cpu().numpy()
+    np.testing.assert_array_equal(ik_sc[0].cpu().numpy(), s.astype(np.float32))
+    np.testing.assert_array_equal(got, codes)
+
+
+# ----------------------------------------------------------------------------------- compression
+def _compress_inputs(B, T, dI, cfg):
+    kv = synth.normal_bf16((B, T, 512), 1.28, cfg, 1)
+    ks = synth.normal_f32((B, T), 1.28, cfg, 2)
+    ik = synth.normal_bf16((B, T, dI), 1.28, cfg, 3)
+    iks = synth.normal_f32((B, T), 1.28, cfg, 4)
+    gamma = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 5).random(512, dtype=np.float32))
+    return kv, ks, ik, iks, gamma
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_csa_compress_parity(fp8):
+    B, T, m, ov, dI = 2, 777, 4, 4, 128 if fp8 else 64
+    kv, ks, ik, iks, gamma = _compress_inputs(B, T, dI, 11)
+    nb = T // m
+    kv_out = torch.zeros((B, nb + 3, 512), dtype=torch.bfloat16, device=DEV)
+    ik_out = torch.zeros((B, nb + 3, dI), dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
+    ik_sc = torch.zeros((B, nb + 3), dtype=torch.float32, device=DEV)
+    off = 4321
+    # first half from all columns, second half from a column window that starts later (tok0 > 0)
+    h = nb // 2
+    L.csa_compress_kv(from_bits(kv), dev_f32(ks), from_bits(ik), dev_f32(iks), tok0=0, blk_begin=0, n_blk=h, m=m,
+                      overlap=ov, gamma_kv=from_bits(gamma), kv_out=kv_out, ik_out=ik_out,
+                      ik_scale=ik_sc if fp8 else None, ik_fp8=fp8, rope_offset=off)
+    t0 = h * m - ov
+    L.csa_compress_kv(from_bits(kv[:, t0:]), dev_f32(ks[:, t0:]), from_bits(ik[:, t0:]), dev_f32(iks[:, t0:]),
+                      tok0=t0, blk_begin=h, n_blk=nb - h, m=m, overlap=ov, gamma_kv=from_bits(gamma),
+                      kv_out=kv_out, ik_out=ik_out, ik_scale=ik_sc if fp8 else None, ik_fp8=fp8,
+                      rope_offset=off)
+    torch.cuda.synchronize()
+    g64 = synth.bf16_bits_to_f64(gamma)
+    for b in range(B):
+        x = synth.bf16_bits_to_f64(kv[b])
+        ref = O.compress_kv(x, ks[b].astype(np.float64), m, ov, g64, 1e-6, 10000.0, off)
+        assert_close(to_np_bf16(kv_out[b, :nb]), ref, f"kv entries b={b}")
+        e = O.pool(synth.bf16_bits_to_f64(ik[b]), iks[b].astype(np.float64), m, ov)
+        if fp8:
+            codes, s, deq = O.fp8_quantize_rows(e)
+            got = O.e4m3_decode(ik_out[b, :nb].cpu().numpy()) * ik_sc[b, :nb].cpu().numpy()[:, None]
+            np.testing.assert_allclose(ik_sc[b, :nb].cpu().numpy(), s, rtol=1e-5)
+            gc = ik_out[b, :nb].cpu().numpy().astype(int)
+            diff = np.abs((gc & 0x7F) - (codes.astype(int) & 0x7F))
+            assert diff.max() <= 1                          # fp32 vs fp64 pooling: at most one code apart
+            assert (diff > 0).mean() < 0.01
+            _, rl = errors(got, deq)
+            assert rl < 1e-2
+        else:
+            assert_close(to_np_bf16(ik_out[b, :nb]), e, f"bf16 indexer keys b={b}")
+
+
+def test_hca_compress_and_window_ring_parity():
+    B, T = 3, 600
+    kv, ks, _, _, gamma = _compress_inputs(B, T, 64, 12)
+    g64 = synth.bf16_bits_to_f64(gamma)
+    nb = T // 128
+    out = torch.zeros((B, nb, 512), dtype=torch.bfloat16, device=DEV)
+    L.hca_compress_kv(from_bits(kv), dev_f32(ks), tok0=0, blk_begin=0, n_blk=nb, m=128, gamma_kv=from_bits(gamma),
+                      kv_out=out)
+    # window fill into a ring of 160 rows: tokens 280..599 in two calls of 160 (the second overwrites)
+    ring = torch.zeros((B, 160, 512), dtype=torch.bfloat16, device=DEV)
+    for t0 in (280, 440):
+        L.hca_compress_kv(from_bits(kv[:, t0:]), dev_f32(ks[:, t0:]), tok0=t0, blk_begin=t0, n_blk=160, m=1,
+                          gamma_kv=from_bits(gamma), kv_out=ring, ring_cap=160)
+    with pytest.raises(L.LcsError):
+        L.hca_compress_kv(from_bits(kv[:, 200:]), dev_f32(ks[:, 200:]), tok0=200, blk_begin=200, n_blk=161, m=1,
+                          gamma_kv=from_bits(gamma), kv_out=ring, ring_cap=160)
+    torch.cuda.synchronize()
+    for b in range(B):
+        x = synth.bf16_bits_to_f64(kv[b])
+        assert_close(to_np_bf16(out[b]), O.compress_kv(x, ks[b], 128, 0, g64), f"hca entries b={b}")
+        win = O.window_entries(x, g64)
+        got = to_np_bf16(ring[b])
+        ref = np.stack([win[j] for j in range(440, 600)])
+        rows = np.array([j % 160 for j in range(440, 600)])
+        assert_close(got[rows], ref, f"window ring b={b}")
+
+
+# ----------------------------------------------------------------------------------- indexer + top-k
+def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False):
+    q = synth.normal_bf16((B, Tq, H_I, dI), 1.28, cfg, 21)
+    w = synth.normal_bf16((B, Tq, H_I), 1.28, cfg, 22)
+    ik_ld = n_cap + 5
+    if fp8:
+        codes = synth.fp8_codes((B, ik_ld, dI), cfg, 23)
+        scale = synth.positive_scales((B, ik_ld), cfg, 24)
+        if ties:
+            codes[:, : n_cap // 2] = codes[:, :1]
+            scale[:, : n_cap // 2] = scale[:, :1]
+        kdeq = O.e4m3_decode(codes) * scale[..., None].astype(np.float64)
+        ik = torch.from_numpy(codes).to(DEV)
+        iks = dev_f32(scale)
+    else:
+        kb = synth.normal_bf16((B, ik_ld, dI), 1.28, cfg, 23)
+        if ties:
+            kb[:, : n_cap // 2] = kb[:, :1]
+        kdeq = synth.bf16_bits_to_f64(kb)
+        ik = from_bits(kb)
+        iks = None
+    pos = np.array(positions, dtype=np.int64).reshape(B, Tq)
+    idx = torch.full((B, Tq, k), -7, dtype=torch.int32, device=DEV)
+    sc = torch.zeros((B, Tq, k), dtype=torch.float32, device=DEV)
+    L.csa_index_topk(from_bits(q), from_bits(w), ik, iks, dev_i64(pos), n_cap=n_cap, m=m, k=k, topk_idx=idx,
+                     topk_score=sc)
+    torch.cuda.synchronize()
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    band = 0
+    for b in range(B):
+        for t in range(Tq):
+            nv = min(pos[b, t] // m, n_cap)
+            ref, bound = index_oracle_row(q[b, t], w[b, t], kdeq[b, :nv], fp8)
+            band += check_topk_row(gi[b, t], ref, k, bound)
+            sel = gi[b, t][gi[b, t] >= 0]
+            # scores agree within the fp32 accumulation bound of each selected entry
+            assert np.all(np.abs(gs[b, t, : sel.size] - ref[sel]) <= bound[sel] + 1e-30)
+            assert np.all(np.isneginf(gs[b, t, sel.size:]))
+    return band
+
+
+def test_index_topk_decode_fp8():
+    # n_cap spans 3 score chunks and a ragged tail; rows with n_vis = 0, < k, == k, > k
+    n_cap, k = 2600, 64
+    pos = [0, 3, 100, 256, 257, 4 * 2600 + 9, 5000, 4 * 2600]
+    band = _index_case(8, 1, n_cap, 64, 128, k, 4, True, pos, 31)
+    assert band <= 2
+
+
+def test_index_topk_prefill_fp8_rowwise():
+    Tq, n_cap, k = 80, 1500, 100
+    pos = list(range(4 * 1500 - 79, 4 * 1500 + 1)) + list(range(0, 800, 10))
+    band = _index_case(2, Tq, n_cap, 64, 128, k, 4, True, pos, 32)
+    assert band <= 4
+
+
+def test_index_topk_bf16_small_heads():
+    # the prefill-2k shape family: 8 heads x 64 dims, bf16 keys, top-k 128
+    Tq, n_cap, k = 70, 512, 128
+    pos = list(range(2048 - Tq, 2048))
+    _index_case(1, Tq, n_cap, 8, 64, k, 4, False, pos, 33)
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_index_topk_exact_ties_go_to_lower_index(fp8):
+    n_cap, k = 3000, 40
+    _index_case(2, 1, n_cap, 16 if fp8 else 8, 128 if fp8 else 64, k, 4, fp8, [12000, 9000], 34, ties=True)
+
+
+def test_index_topk_all_equal_scores():
+    """Identical keys: every score ties, the k lowest indices must be returned."""
+    B, n_cap, k = 2, 5000, 77
+    q = synth.normal_bf16((B, 1, 64, 128), 1.28, 35, 1)
+    w = synth.normal_bf16((B, 1, 64), 1.28, 35, 2)
+    codes = np.repeat(synth.fp8_codes((B, 1, 128), 35, 3), n_cap, axis=1)
+    scale = np.full((B, n_cap), 0.01, dtype=np.float32)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    L.csa_index_topk(from_bits(q), from_bits(w), torch.from_numpy(codes).to(DEV), dev_f32(scale),
+                     dev_i64(np.array([[4 * n_cap], [4 * 3000 + 3]])), n_cap=n_cap, m=4, k=k, topk_idx=idx)
+    got = idx.cpu().numpy()
+    np.testing.assert_array_equal(got[0, 0], np.arange(k))
+    np.testing.assert_array_equal(got[1, 0], np.arange(k))
+
+
+# ----------------------------------------------------------------------------------- attention
+def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_inf=False, rope_offset=0):
+    q = synth.normal_bf16((B, Tq, H, 512), 1.28, cfg, 41)
+    gq = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 42).random(512, dtype=np.float32))
+    kv_ld = n_cap + 3
+    cache = synth.normal_bf16((B, kv_ld, 512), 1.0, cfg, 43)
+    pos = np.array(positions, dtype=np.int64).reshape(B, Tq)
+    max_t = int(pos.max())
+    win_ld = ring_cap if ring_cap else max_t + 1
+    win_tok = synth.normal_bf16((B, win_ld, 512), 1.0, cfg, 44)   # row j % ring_cap holds token j
+    sink = np.full(H, -np.inf, np.float32) if sink_inf else synth.normal_f32((H,), 1.0, cfg, 45)
+    out = torch.zeros((B, Tq, H, 512), dtype=torch.bfloat16, device=DEV)
+    scale = 1.0 / math.sqrt(512)
+    if kind == "csa":
+        g = synth.rng(cfg, 46)
+        topk = -np.ones((B, Tq, k), dtype=np.int32)
+        for b in range(B):
+            for t in range(Tq):
+                nv = min(pos[b, t] // m, n_cap)
+                sel = np.sort(g.choice(nv, size=min(k, nv), replace=False)) if nv else np.zeros(0, int)
+                topk[b, t, : sel.size] = sel
+        L.csa_attend(from_bits(q), from_bits(gq), from_bits(cache), torch.from_numpy(topk).to(DEV),
+                     from_bits(win_tok), dev_f32(sink), dev_i64(pos), window=W, ring_cap=ring_cap, out=out,
+                     rope_offset=rope_offset)
+    else:
+        L.hca_attend(from_bits(q), from_bits(gq), from_bits(cache), from_bits(win_tok), dev_f32(sink), dev_i64(pos),
+                     n_cap=n_cap, m=m, window=W, ring_cap=ring_cap, out=out, rope_offset=rope_offset)
+    torch.cuda.synchronize()
+    got = to_np_bf16(out)
+    g64 = synth.bf16_bits_to_f64(gq)
+    cache64 = synth.bf16_bits_to_f64(cache)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        for t in range(Tq):
+            tt = int(pos[b, t])
+            nv = min(tt // m, n_cap)
+            keys = [cache64[b, s] for s in (topk[b, t][topk[b, t] >= 0] if kind == "csa" else range(nv))]
+            for j in range(max(0, tt - W + 1), tt + 1):
+                keys.append(synth.bf16_bits_to_f64(win_tok[b, j % ring_cap if ring_cap else j]))
+            K = np.stack(keys) if keys else np.zeros((0, 512))
+            ref = O.attend_one(synth.bf16_bits_to_f64(q[b, t]), g64, K, sink.astype(np.float64), tt, scale,
+                               1e-6, 10000.0, rope_offset)
+            ma, rl = assert_close(got[b, t], ref, f"{kind} b={b} t={tt}")
+            worst = (max(worst[0], ma), max(worst[1], rl))
+    return worst
+
+
+@pytest.mark.parametrize("H", [64, 8, 32])
+def test_csa_attend_parity(H):
+    # k + W keys spread over several tiles; some rows padded with -1 (n_vis < k)
+    pos = [4 * 900 + 2, 37, 4 * 500, 130]
+    _attend_case("csa", 2, 2, H, 200, 900, 4, 128, 256, pos, 51 + H)
+
+
+def test_csa_attend_linear_window_and_minus_inf_sink():
+    _attend_case("csa", 1, 3, 64, 64, 300, 4, 20, 0, [1199, 1000, 5], 52, sink_inf=True)
+
+
+@pytest.mark.parametrize("n_cap,H", [(700, 64), (3000, 64), (60, 16)])
+def test_hca_attend_parity(n_cap, H):
+    # dense over all visible entries: many splits (3000) and a single split (60)
+    pos = [128 * n_cap + 5, 128 * n_cap // 2 + 127, 0]
+    _attend_case("hca", 3, 1, H, 0, n_cap, 128, 128, 128, pos, 53 + n_cap)
+
+
+def test_hca_attend_single_split_finishes_in_kernel():
+    # 60 entries + 64 window keys = 4 tiles: one split, the attention kernel writes the output itself
+    assert L.attend_workspace(2, 1, 16, 124) == 256
+    _attend_case("hca", 2, 1, 16, 0, 60, 128, 64, 64, [128 * 60 + 1, 128 * 30], 55)
+
+
+def test_hca_attend_prefill_rows_with_rope_offset():
+    pos = list(range(4000, 4000 + 40))
+    _attend_case("hca", 1, 40, 64, 0, 40, 128, 128, 0, pos, 54, rope_offset=12345)
+
+
+# ----------------------------------------------------------------------------------- projection
+@pytest.mark.parametrize("M,H,g,d_g,d", [(8, 64, 8, 1024, 4096), (3, 16, 2, 64, 96), (37, 8, 1, 32, 48)])
+def test_grouped_out_proj_parity(M, H, g, d_g, d):
+    cfg = 60 + M
+    o = synth.normal_bf16((M, H * 512), 0.3, cfg, 1)
+    wg = synth.normal_bf16((g, d_g, H * 512 // g), 0.02, cfg, 2)
+    wo = synth.normal_bf16((d, g * d_g), 0.02, cfg, 3)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    L.grouped_out_proj(from_bits(o), from_bits(wg), from_bits(wo), H=H, y=y)
+    torch.cuda.synchronize()
+    _, ref = O.grouped_out_proj(synth.bf16_bits_to_f64(o), synth.bf16_bits_to_f64(wg), synth.bf16_bits_to_f64(wo))
+    assert_close(to_np_bf16(y), ref, "grouped out-proj")
