@@ -208,7 +208,7 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
   if (window > 0 && !win_ring) return LCS_ERR_ARG;
   if (B <= 0 || Tq <= 0 || H <= 0 || kv_ld <= 0 || window < 0 || ring_cap < 0) return LCS_ERR_ARG;
   if (window > 0 && win_ld <= 0) return LCS_ERR_ARG;
-  if (ring_cap > 0 && ring_cap > win_ld) return LCS_ERR_ARG;
+  if (ring_cap > 0 && (ring_cap > win_ld || ring_cap < window)) return LCS_ERR_ARG;
   if (!aligned16(q) || !aligned16(gamma_q) || !aligned16(kv_cache) || !aligned16(out)) return LCS_ERR_ARG;
   if (win_ring && !aligned16(win_ring)) return LCS_ERR_ARG;
   if (!(scale > 0.f) || !(eps >= 0.f) || !(rope_theta > 0.f)) return LCS_ERR_ARG;

@@ -25,6 +25,9 @@ namespace lcs {
 namespace {
 
 constexpr int kTile = 32;                 // keys per tile
+constexpr int kMaxSplitKeys = 2048;       // keys of one split, staged as row indices in LDS
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 GU32x4;   // global address space: global_load, not flat
 constexpr int kVtStride = 136;            // bf16 per LDS row of the V slice (128 + 8 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -36,29 +39,13 @@ struct AttnK {
   const uint16_t* win; int64_t win_ld, ring_cap; int window;
   const float* sink; const int64_t* q_pos; int64_t rope_offset;
   int Tq, H; float scale_log2, eps, theta;
-  uint16_t* out; float* part_o; float* part_ml;
+  uint16_t* out; uint16_t* part_o; float* part_ml;
   int nsplit, keys_per_split;
 };
 
 struct RowKeys {
   int64_t t, nc, nk;                      // query token, compressed keys in the list, total keys
 };
-
-__device__ __forceinline__ const uint16_t* key_row(const AttnK& a, int64_t b, int64_t r, const RowKeys& rk,
-                                                   int64_t e, bool* valid) {
-  if (e >= rk.nk) { *valid = false; return a.kv; }
-  if (e < rk.nc) {
-    int64_t idx = e;
-    if (a.topk) idx = a.topk[r * a.k + e];
-    *valid = idx >= 0;
-    return a.kv + (b * a.kv_ld + (idx >= 0 ? idx : 0)) * kHeadDim;
-  }
-  const int64_t j = rk.t - a.window + 1 + (e - rk.nc);
-  *valid = j >= 0;
-  const int64_t jj = j >= 0 ? j : 0;
-  const int64_t row = a.ring_cap > 0 ? jj % a.ring_cap : jj;
-  return a.win + (b * a.win_ld + row) * kHeadDim;
-}
 
 // LDS row of the V-slice copy for tile key (block kb, row r16 of the 16x16 MFMA block).
 __device__ __forceinline__ int vt_row(int kb, int r16) { return 2 * (r16 >> 2) + 8 * (r16 & 3) + kb; }
@@ -67,6 +54,7 @@ template <int HB>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
   __shared__ float4 s_part[4 * 2 * HB * kWave];            // partial logits [wave][kb][hb][lane]
+  __shared__ uint4 s_q[4][HB][4][kWave];                    // qhat fragments [wave][hb][ks][lane]
   __shared__ uint16_t s_vt[4][kTile * kVtStride];         // per-wave V slice
   __shared__ uint4 s_p[HB * kWave];                        // P fragments [hb][lane]
   __shared__ float s_alpha[HB * 16];
@@ -74,6 +62,8 @@ attend_kernel(AttnK a) {
   __shared__ float s_ssq[4][HB * 16];
   __shared__ float s_cos[32], s_sin[32];
   __shared__ int s_nsel;
+  __shared__ int32_t s_rows[kMaxSplitKeys];                 // per key of this split: cache/ring row, -1 = none
+  __shared__ int s_rescale[2];            // per tile parity: some head's reference max moved
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -83,6 +73,7 @@ attend_kernel(AttnK a) {
   const int split = blockIdx.x;
   const int head0 = 0;
 
+  if (threadIdx.x == 0) { s_rescale[0] = 0; s_rescale[1] = 0; }
   RowKeys rk;
   rk.t = a.q_pos[r];
   if (a.topk) {
@@ -113,6 +104,54 @@ attend_kernel(AttnK a) {
     s_sin[threadIdx.x] = sn;
   }
 
+  const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
+
+  // ---- the split's key rows, staged once: compressed keys (selected index or entry number), then
+  //      window tokens (ring row), -1 where a key does not exist ----
+  const int nkeys = e_end > e_begin ? (int)(e_end - e_begin) : 0;
+  {
+    const int64_t j0 = rk.t - a.window + 1;               // first window token
+    for (int i = threadIdx.x; i < nkeys; i += 256) {
+      const int64_t e = e_begin + i;
+      int32_t row;
+      if (e < rk.nc) {
+        row = a.topk ? a.topk[r * a.k + e] : (int32_t)e;
+      } else {
+        const int64_t j = j0 + (e - rk.nc);
+        row = j < 0 ? -1 : (int32_t)(a.ring_cap > 0 ? j % a.ring_cap : j);
+      }
+      s_rows[i] = row;
+    }
+  }
+  __syncthreads();
+  const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
+  const uint16_t* win_b = a.win ? a.win + b * a.win_ld * kHeadDim : a.kv;
+  const int nc_local = rk.nc > e_begin ? (int)(rk.nc - e_begin) : 0;   // split keys that are compressed
+
+  // ---- tile loads: this lane feeds MFMA rows kb*16 + c16 ----
+  uint4 kcur[2][4];
+  uint32_t vcur = 0;
+  auto load_tile = [&](int i0, uint4 (&kf)[2][4], uint32_t& vmask) {
+    const int i = i0 + (lane & 31);
+    const int32_t row = i < nkeys ? s_rows[i] : -1;
+    vmask = (uint32_t)__ballot(row >= 0 && lane < 32);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int src = kb * 16 + c16;
+      const int32_t rr = __shfl(row, src, kWave);
+      const uint16_t* base = (i0 + src) < nc_local ? kv_b : win_b;
+      // always a readable row (row 0 when the key does not exist): no predicated loads
+      GU32x4* p = reinterpret_cast<GU32x4*>(reinterpret_cast<uintptr_t>(base + (int64_t)(rr > 0 ? rr : 0) * kHeadDim +
+                                                                          128 * w + 8 * g));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {                         // invalid keys are zeroed where consumed
+        const u32x4 x = p[4 * ks];
+        kf[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    }
+  };
+  if (ntiles > 0) load_tile(0, kcur, vcur);                // first tile in flight during the q prologue
+
   // ---- qhat fragments: B operand of S^T = K qhat^T, lane holds head c16 of block hb,
   //      dims 128w + 32ks + 8g .. +8 ----
   uint4 qf[HB][4];
@@ -122,11 +161,13 @@ attend_kernel(AttnK a) {
     for (int hb = 0; hb < HB; ++hb) {
       const int head = head0 + hb * 16 + c16;
       const bool hv = head < a.H;
+      const int hl = hv ? head : a.H - 1;
       float acc = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int d = 128 * w + 32 * ks + 8 * g;
-        uint4 x = hv ? *reinterpret_cast<const uint4*>(a.q + (r * a.H + head) * kHeadDim + d) : make_uint4(0, 0, 0, 0);
+        uint4 x = *reinterpret_cast<const uint4*>(a.q + (r * a.H + hl) * kHeadDim + d);
+        if (!hv) x = make_uint4(0, 0, 0, 0);
         qf[hb][ks] = x;
         const float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
                             bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
@@ -138,6 +179,9 @@ attend_kernel(AttnK a) {
       ss[hb] = acc;
       if (g == 0) s_ssq[w][hb * 16 + c16] = acc;
     }
+    uint4 gmv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) gmv[ks] = *reinterpret_cast<const uint4*>(a.gamma_q + 128 * w + 32 * ks + 8 * g);
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -148,7 +192,7 @@ attend_kernel(AttnK a) {
       for (int ks = 0; ks < 4; ++ks) {
         const int d = 128 * w + 32 * ks + 8 * g;
         const uint4 x = qf[hb][ks];
-        const uint4 gm = *reinterpret_cast<const uint4*>(a.gamma_q + d);
+        const uint4 gm = gmv[ks];
         float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
                       bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
         const float gv[8] = {bf2f_lo(gm.x), bf2f_hi(gm.x), bf2f_lo(gm.y), bf2f_hi(gm.y),
@@ -165,7 +209,7 @@ attend_kernel(AttnK a) {
             v[2 * p + 1] = a0 * sn + a1 * cs;
           }
         }
-        qf[hb][ks] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+        s_q[w][hb][ks][lane] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
                                 pack_bf2(v[6], v[7]));
       }
     }
@@ -179,36 +223,18 @@ attend_kernel(AttnK a) {
     for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;      // softmax state of head (16w + c16), waves w < HB
 
-  const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
-
-  // ---- tile loads: this lane feeds MFMA rows kb*16 + c16 ----
-  uint4 kcur[2][4];
-  uint32_t vcur = 0;
-  auto load_tile = [&](int64_t e0, uint4 (&kf)[2][4], uint32_t& vmask) {
-    bool valid = false;
-    const uint16_t* p = key_row(a, b, r, rk, e0 + (lane & 31), &valid);
-    if (e0 + (lane & 31) >= e_end) valid = false;
-    vmask = (uint32_t)__ballot(valid && lane < 32);
-    const uint64_t pv = reinterpret_cast<uint64_t>(p);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int src = kb * 16 + c16;
-      const uint64_t pp = ((uint64_t)(uint32_t)__shfl((int)(pv >> 32), src, kWave) << 32) |
-                          (uint64_t)(uint32_t)__shfl((int)(uint32_t)pv, src, kWave);
-      const bool v = (vmask >> src) & 1u;
-      const uint16_t* row = reinterpret_cast<const uint16_t*>(pp);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kf[kb][ks] = v ? *reinterpret_cast<const uint4*>(row + 128 * w + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (ntiles > 0) load_tile(e_begin, kcur, vcur);
-
   for (int it = 0; it < ntiles; ++it) {
     uint4 knext[2][4];
     uint32_t vnext = 0;
-    if (it + 1 < ntiles) load_tile(e_begin + (int64_t)(it + 1) * kTile, knext, vnext);
+    if (it + 1 < ntiles) load_tile((it + 1) * kTile, knext, vnext);
 
+    // zero the rows of invalid keys (their loads read a real row so that no load is predicated)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool v = (vcur >> (kb * 16 + c16)) & 1u;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kcur[kb][ks] = v ? kcur[kb][ks] : make_uint4(0, 0, 0, 0);
+    }
     // partial S^T over this wave's 128 dims
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -216,7 +242,7 @@ attend_kernel(AttnK a) {
       for (int hb = 0; hb < HB; ++hb) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(kcur[kb][ks], qf[hb][ks], acc);
+        for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(kcur[kb][ks], s_q[w][hb][ks][lane], acc);
         s_part[((w * 2 + kb) * HB + hb) * kWave + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
       const int vr = vt_row(kb, c16);
@@ -250,12 +276,22 @@ attend_kernel(AttnK a) {
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run, tmax);
+      // Lazy rescaling: the reference max only moves when the tile max exceeds it by more than
+      // 2^8 (p then stays <= 256, exact in the fp32 sums and in bf16's exponent range); the
+      // final normalisation uses the same reference, so the result is unchanged.
+      float m_new = m_run;
       float alpha = 1.f;
+      if (m_run == -INFINITY) {
+        m_new = tmax;                      // nothing accumulated yet: O and l are zero
+      } else if (tmax > m_run + 8.f) {
+        m_new = tmax;
+        alpha = exp2f(m_run - m_new);
+        s_rescale[it & 1] = 1;
+      }
+      if (w == 0 && lane == 0) s_rescale[(it + 1) & 1] = 0;   // read last by the previous tile's PV
       uint32_t pk[4] = {0u, 0u, 0u, 0u};
       float psum = 0.f;
       if (m_new != -INFINITY) {
-        alpha = exp2f(m_run - m_new);
         float p[8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -276,15 +312,17 @@ attend_kernel(AttnK a) {
     }
     __syncthreads();
 
+    if (s_rescale[it & 1]) {               // rare: some head's reference max moved this tile
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const float4 al = *reinterpret_cast<const float4*>(&s_alpha[hb * 16 + 4 * g]);
+      for (int hb = 0; hb < HB; ++hb) {
+        const float4 al = *reinterpret_cast<const float4*>(&s_alpha[hb * 16 + 4 * g]);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        o[hb][db][0] *= al.x;
-        o[hb][db][1] *= al.y;
-        o[hb][db][2] *= al.z;
-        o[hb][db][3] *= al.w;
+        for (int db = 0; db < 8; ++db) {
+          o[hb][db][0] *= al.x;
+          o[hb][db][1] *= al.y;
+          o[hb][db][2] *= al.z;
+          o[hb][db][3] *= al.w;
+        }
       }
     }
     uint4 pf[HB];
@@ -360,7 +398,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int head = head0 + hb * 16 + 4 * g + i;
-          if (head < a.H) a.part_o[(base + head) * kHeadDim + d] = o[hb][db][i];
+          if (head < a.H) a.part_o[(base + head) * kHeadDim + d] = (uint16_t)f2bf(o[hb][db][i]);
         }
       }
     if (w < HB && g == 0) {
@@ -375,7 +413,7 @@ attend_kernel(AttnK a) {
 
 // Merge split-K partials with the sink; one workgroup of 128 threads per (query, head).
 __global__ void __launch_bounds__(128)
-merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
+merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
              const float* __restrict__ sink, const int64_t* __restrict__ q_pos, int64_t rope_offset,
              float theta, uint16_t* __restrict__ out) {
   const int64_t r = blockIdx.x;
@@ -383,18 +421,20 @@ merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml
   const int tid = threadIdx.x;
   const float z = sink[h] * kLog2e;
   float M = z;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((r * nsplit + s) * H + h) * 2]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
   if (M != -INFINITY) {
     L = exp2f(z - M);
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
       const int64_t base = (r * nsplit + s) * H + h;
       const float ms = part_ml[base * 2], ls = part_ml[base * 2 + 1];
       const float f = exp2f(ms - M);
       L += f * ls;
-      const float4 v = *reinterpret_cast<const float4*>(part_o + base * kHeadDim + 4 * tid);
-      acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+      const uint2 v = *reinterpret_cast<const uint2*>(part_o + base * kHeadDim + 4 * tid);
+      acc.x += f * bf2f_lo(v.x); acc.y += f * bf2f_hi(v.x); acc.z += f * bf2f_lo(v.y); acc.w += f * bf2f_hi(v.y);
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
@@ -419,15 +459,17 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int head_blocks(int H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
 
-// Keys per split: aim for >= 512 workgroups with at least 4 tiles (128 keys) each.
+// Keys per split: about one workgroup per CU (256) with at least 2 tiles (64 keys) each; every split
+// adds a 64 KiB partial (bf16 O of 64 heads) that the merge reads back, so splits are kept few.
 int keys_per_split(int R, int64_t max_keys) {
   const int64_t tiles = (max_keys + kTile - 1) / kTile;
   if (tiles <= 0) return kTile;
-  int64_t want_splits = (512 + R - 1) / R;
+  int64_t want_splits = (256 + R - 1) / R;
   if (want_splits < 1) want_splits = 1;
   int64_t tps = (tiles + want_splits - 1) / want_splits;
-  if (tps < 4) tps = 4;
+  if (tps < 2) tps = 2;
   if (tps > tiles) tps = tiles;
+  if (tps > kMaxSplitKeys / kTile) tps = kMaxSplitKeys / kTile;
   return (int)(tps * kTile);
 }
 
@@ -438,7 +480,7 @@ size_t attend_workspace(int B, int Tq, int H, int64_t max_keys) {
   const int kps = keys_per_split(R, max_keys);
   const int64_t nsplit = max_keys > 0 ? (max_keys + kps - 1) / kps : 1;
   if (nsplit <= 1) return 256;
-  return al256((size_t)R * nsplit * H * kHeadDim * 4) + al256((size_t)R * nsplit * H * 2 * 4);
+  return al256((size_t)R * nsplit * H * kHeadDim * 2) + al256((size_t)R * nsplit * H * 2 * 4);
 }
 
 int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
@@ -452,9 +494,9 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.keys_per_split = keys_per_split(R, max_keys);
   a.nsplit = max_keys > 0 ? (int)((max_keys + a.keys_per_split - 1) / a.keys_per_split) : 1;
   if (a.nsplit < 1) a.nsplit = 1;
-  a.part_o = static_cast<float*>(x.ws);
+  a.part_o = static_cast<uint16_t*>(x.ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
-                                       al256((size_t)R * a.nsplit * x.H * kHeadDim * 4));
+                                       al256((size_t)R * a.nsplit * x.H * kHeadDim * 2));
   dim3 grid((unsigned)a.nsplit, (unsigned)R);
   switch (head_blocks(x.H)) {
     case 1: LCS_LAUNCH("attend_kernel", attend_kernel<1>, grid, dim3(256), 0, st, a); break;

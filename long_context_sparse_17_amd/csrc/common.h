@@ -52,13 +52,16 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 // ----------------------------------------------------------------------------------- RoPE
-// cos/sin of pos * theta^(-j/32), formed in fp64 so that positions near 2^20 keep their phase.
+// cos/sin of pos * theta^(-j/32).  The angle is formed in fp64 (positions near 2^20 would lose their
+// phase in fp32), reduced by 2*pi with a two-term Cody-Waite split (error ~1e-10 rad at 1e6 rad),
+// and the reduced angle in [-pi, pi] goes to the fp32 sincos.
 __device__ __forceinline__ void rope_cs(double pos, int j, float theta, float* c, float* s) {
-  const double inv = pow((double)theta, -(double)j / (double)(kRopeDims / 2));
-  double sd, cd;
-  sincos(pos * inv, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  const double inv = exp2(-(double)j * (1.0 / (kRopeDims / 2)) * log2((double)theta));
+  const double phi = pos * inv;
+  const double kq = rint(phi * 0.15915494309189535);
+  double rr = fma(-kq, 6.283185307179586, phi);
+  rr = fma(-kq, 2.4492935982947064e-16, rr);
+  sincosf((float)rr, s, c);
 }
 
 // ----------------------------------------------------------------------------------- MFMA

@@ -34,13 +34,13 @@ __device__ __forceinline__ float block_reduce_max(float v, float* red) {
   return fmaxf(red[0], red[1]);
 }
 
-// Softmax weights of the logits of tokens [lo, hi) (columns lo-tok0 ..) into wt[0 .. hi-lo).
-__device__ void pool_weights(const float* __restrict__ score_row, int64_t lo, int64_t hi, int64_t tok0,
-                             float* wt, float* red) {
-  const int n = (int)(hi - lo);
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < n; j += kThreads) {
-    const float s = score_row[lo - tok0 + j];
+// Softmax weights of n logits into wt[0 .. n).  `first` is this thread's logit j = tid (or -inf),
+// already loaded; the rest (n > 128) are read here.
+__device__ void pool_weights(const float* __restrict__ srow, int n, float first, float* wt, float* red) {
+  float mx = first;
+  if (threadIdx.x < n) wt[threadIdx.x] = first;
+  for (int j = threadIdx.x + kThreads; j < n; j += kThreads) {
+    const float s = srow[j];
     wt[j] = s;
     mx = fmaxf(mx, s);
   }
@@ -56,6 +56,8 @@ __device__ void pool_weights(const float* __restrict__ score_row, int64_t lo, in
   for (int j = threadIdx.x; j < n; j += kThreads) wt[j] *= inv;
   __syncthreads();
 }
+
+constexpr int kPre = 8;    // token rows whose loads are issued before the pooling weights exist
 
 __global__ void __launch_bounds__(kThreads)
 compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ kv_score,
@@ -73,12 +75,53 @@ compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ k
   const int64_t hi = (i + 1) * m;
   const int n = (int)(hi - lo);
   const int tid = threadIdx.x;
+  const bool has_ik = ik_tok != nullptr;
+
+  // ---- every independent load of the first round, issued together ----
+  const float* srow = kv_score + (int64_t)b * T + (lo - tok0);
+  const uint16_t* xb = kv_tok + ((int64_t)b * T + (lo - tok0)) * kHeadDim + tid * 4;
+  const float s0 = srow[tid < n ? tid : n - 1];
+  uint2 pre[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) pre[u] = *reinterpret_cast<const uint2*>(xb + (int64_t)(u < n ? u : n - 1) * kHeadDim);
+  const uint2 gm = *reinterpret_cast<const uint2*>(gamma + tid * 4);
+  const float* isrow = has_ik ? ik_score + (int64_t)b * T + (lo - tok0) : srow;
+  const int dim = tid < dI ? tid : 0;
+  const uint16_t* kb = has_ik ? ik_tok + ((int64_t)b * T + (lo - tok0)) * dI + dim : nullptr;
+  float is0 = 0.f;
+  uint32_t ipre[kPre];
+  if (has_ik) {
+    is0 = isrow[tid < n ? tid : n - 1];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) ipre[u] = kb[(int64_t)(u < n ? u : n - 1) * dI];
+  }
 
   // ---- K=V entry: pool, RMSNorm, RoPE at the block's last token ----
-  pool_weights(kv_score + (int64_t)b * T, lo, hi, tok0, wt, red);
-  const uint16_t* xb = kv_tok + ((int64_t)b * T + (lo - tok0)) * kHeadDim + tid * 4;
+  pool_weights(srow, n, tid < n ? s0 : -INFINITY, wt, red);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < n; ++j) {
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const float w = u < n ? wt[u] : 0.f;
+    a0 += w * bf2f_lo(pre[u].x);
+    a1 += w * bf2f_hi(pre[u].x);
+    a2 += w * bf2f_lo(pre[u].y);
+    a3 += w * bf2f_hi(pre[u].y);
+  }
+  int j = kPre;
+  for (; j + 8 <= n; j += 8) {            // 8 independent row loads in flight
+    uint2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint2*>(xb + (int64_t)(j + u) * kHeadDim);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = wt[j + u];
+      a0 += w * bf2f_lo(v[u].x);
+      a1 += w * bf2f_hi(v[u].x);
+      a2 += w * bf2f_lo(v[u].y);
+      a3 += w * bf2f_hi(v[u].y);
+    }
+  }
+  for (; j < n; ++j) {
     const uint2 v = *reinterpret_cast<const uint2*>(xb + (int64_t)j * kHeadDim);
     const float w = wt[j];
     a0 += w * bf2f_lo(v.x);
@@ -88,9 +131,8 @@ compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ k
   }
   const float ss = block_reduce_sum(a0 * a0 + a1 * a1 + a2 * a2 + a3 * a3, red);
   const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
-  const uint2 g = *reinterpret_cast<const uint2*>(gamma + tid * 4);
-  float y0 = a0 * rstd * bf2f_lo(g.x), y1 = a1 * rstd * bf2f_hi(g.x);
-  float y2 = a2 * rstd * bf2f_lo(g.y), y3 = a3 * rstd * bf2f_hi(g.y);
+  float y0 = a0 * rstd * bf2f_lo(gm.x), y1 = a1 * rstd * bf2f_hi(gm.x);
+  float y2 = a2 * rstd * bf2f_lo(gm.y), y3 = a3 * rstd * bf2f_hi(gm.y);
   const int d0 = tid * 4;
   if (d0 >= kRopeStart) {
     const double pos = (double)((i + 1) * m - 1 + rope_offset);
@@ -107,14 +149,21 @@ compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ k
   o.y = pack_bf2(y2, y3);
   *reinterpret_cast<uint2*>(kv_out + ((int64_t)b * kv_ld + row) * kHeadDim + d0) = o;
 
-  if (ik_tok == nullptr) return;
+  if (!has_ik) return;
   // ---- indexer key: pooled with its own logits, no norm, no RoPE ----
-  pool_weights(ik_score + (int64_t)b * T, lo, hi, tok0, wt, red);
+  pool_weights(isrow, n, tid < n ? is0 : -INFINITY, wt, red);
   float e = 0.f;
-  if (tid < dI) {
-    const uint16_t* kb = ik_tok + ((int64_t)b * T + (lo - tok0)) * dI + tid;
-    for (int j = 0; j < n; ++j) e += wt[j] * bf2f(kb[(int64_t)j * dI]);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) e += (u < n ? wt[u] : 0.f) * bf2f(ipre[u]);
+  int jj = kPre;
+  for (; jj + 8 <= n; jj += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = kb[(int64_t)(jj + u) * dI];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) e += wt[jj + u] * bf2f(v[u]);
   }
+  for (; jj < n; ++jj) e += wt[jj] * bf2f(kb[(int64_t)jj * dI]);
   if (ik_fp8) {
     const float amax = block_reduce_max(tid < dI ? fabsf(e) : 0.f, red);
     const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;

@@ -33,7 +33,6 @@ constexpr int kBinShift = 21;
 constexpr int kScoreChunk = 1024;           // entries per scoring workgroup
 constexpr int kFilterChunk = 4096;          // entries per filter workgroup
 constexpr int kSelThreads = 256;
-constexpr int kBitmapWords = 16384;         // 64 KiB LDS bitmap: sort by set bits for n_vis <= 2^19
 constexpr int kMaxTopk = 2048;
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -253,6 +252,174 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
   }
 }
 
+// Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  The 4 waves quantise
+// one 16-head block each into LDS (codes + folded weights), then stream the chunk in 64-entry groups
+// interleaved across waves, with the next group's loads in flight while the current group's 4*HBI
+// MFMAs run back to back; the epilogue applies relu and the head weights and histograms the scores.
+template <bool FP8, int KS, int HBI>
+__global__ void __launch_bounds__(256, (FP8 || KS * HBI <= 8) ? 2 : 1)
+index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
+                          const void* __restrict__ ik, const float* __restrict__ ik_scale, int64_t ik_ld,
+                          const int64_t* __restrict__ q_pos, int64_t n_cap, int Tq, int H_I, int dI, int m,
+                          int64_t chunk, float* __restrict__ scores, uint32_t* __restrict__ hist, int64_t nsp) {
+  typedef typename std::conditional<FP8, intx8, uint4>::type Frag;
+  __shared__ uint32_t lhist[kBins];
+  __shared__ Frag s_afr[HBI][KS][kWave];
+  __shared__ float s_w[HBI * 16];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t r = blockIdx.y;
+  const int64_t b = r / Tq;
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  if (c0 >= nv) return;                                  // uniform
+  const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
+
+  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0u;
+  if (wave < HBI) {
+    const int head = wave * 16 + c16;
+    const bool hv = head < H_I;
+    const int hl = hv ? head : H_I - 1;
+    const uint16_t* qrow = q_idx + (r * H_I + hl) * dI;
+    float wh = bf2f(w_idx[r * H_I + hl]);
+    if (!hv) wh = 0.f;
+    if (FP8) {
+      uint4 raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * u);
+      float amax = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf2f_lo(wd[j])), fabsf(bf2f_hi(wd[j]))));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+      intx8 codes;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t b0 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j]), sc));
+          const uint32_t b1 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j]), sc));
+          const uint32_t b2 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j + 1]), sc));
+          const uint32_t b3 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j + 1]), sc));
+          codes[2 * u + j] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+        }
+      }
+      if (!hv) codes = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+      s_afr[wave][0][lane] = *reinterpret_cast<Frag*>(&codes);
+      wh *= sc;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 a = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+        if (!hv) a = make_uint4(0, 0, 0, 0);
+        s_afr[wave][ks][lane] = *reinterpret_cast<Frag*>(&a);
+      }
+    }
+    if (g == 0) s_w[wave * 16 + c16] = wh;
+  }
+  __syncthreads();
+  Frag afr[HBI][KS];
+  float wq[HBI][4];
+#pragma unroll
+  for (int hb = 0; hb < HBI; ++hb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) afr[hb][ks] = s_afr[hb][ks][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wq[hb][i] = s_w[hb * 16 + 4 * g + i];
+  }
+
+  const uint8_t* ik8 = static_cast<const uint8_t*>(ik) + b * ik_ld * dI;
+  const uint16_t* ik16 = static_cast<const uint16_t*>(ik) + b * ik_ld * dI;
+  const float* ksc = ik_scale ? ik_scale + b * ik_ld : nullptr;
+  float* srow = scores + r * nsp;
+  const int64_t ngroups = (c1 - c0 + 63) / 64;
+
+  Frag cur[4][KS], nxt[4][KS];
+  float cs[4], ns[4];
+  // Loads are unconditional (entry index clamped into the chunk) so that the compiler keeps them in
+  // flight; out-of-range entries are zeroed by a select and never stored.
+  auto load_group = [&](int64_t gi, Frag (&fr)[4][KS], float (&sc)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int64_t e = c0 + 64 * gi + 16 * u + c16;
+      e = e < c1 ? e : c1 - 1;
+      if (FP8) {
+        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 32 * g);
+        const uint4 x0 = p[0], x1 = p[1];
+        intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        fr[u][0] = *reinterpret_cast<Frag*>(&v);
+        sc[u] = ksc[e];                     // clamped entries are never stored
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 v = *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g);
+          fr[u][ks] = *reinterpret_cast<Frag*>(&v);
+        }
+        sc[u] = 1.f;
+      }
+    }
+  };
+
+  int64_t gi = wave;
+  if (gi < ngroups) load_group(gi, cur, cs);
+  for (; gi < ngroups; gi += 4) {
+    if (gi + 4 < ngroups) load_group(gi + 4, nxt, ns);
+    floatx4 acc[4][HBI];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int hb = 0; hb < HBI; ++hb) {
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (FP8)
+            a = mfma_fp8(*reinterpret_cast<intx8*>(&afr[hb][ks]), *reinterpret_cast<intx8*>(&cur[u][ks]), a);
+          else
+            a = mfma_bf16(*reinterpret_cast<uint4*>(&afr[hb][ks]), *reinterpret_cast<uint4*>(&cur[u][ks]), a);
+        }
+        acc[u][hb] = a;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HBI; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wq[hb][i] * fmaxf(acc[u][hb][i], 0.f);
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      const int64_t e = c0 + 64 * gi + 16 * u + c16;
+      if (g == 0 && e < c1) {
+        const float sc = part * cs[u] + 0.0f;
+        srow[e] = sc;
+        atomicAdd(&lhist[float_key(sc) >> kBinShift], 1u);
+      }
+    }
+    if (gi + 4 < ngroups) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cur[u][ks] = nxt[u][ks];
+        cs[u] = ns[u];
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist + r * (kBins + 4);
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    const uint32_t v = lhist[i];
+    if (v) atomicAdd(gh + i, v);
+  }
+}
+
 // ------------------------------------------------------------------------------------ selection
 // Threshold bin from a complete 2048-bin histogram: the bin T holding the k-th largest score and
 // the number of scores in bins above it.  256 threads, 8 bins each, suffix scan across threads.
@@ -283,60 +450,83 @@ __device__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_
   __syncthreads();
 }
 
-// Wave-aggregated append of `pred` lanes' values to a global list with a global counter.
-__device__ __forceinline__ void wave_append(bool pred, int32_t val, uint32_t* counter, int32_t* list) {
-  const uint64_t mask = __ballot(pred);
-  if (!mask) return;
-  const int lane = lane_id();
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader, kWave);
-  if (pred) list[base + __popcll(mask & ((1ull << lane) - 1ull))] = val;
-}
-
 // Decode filter: many workgroups per row.
 __global__ void __launch_bounds__(kSelThreads)
 topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist, int32_t* __restrict__ sel,
                    int32_t* __restrict__ cand, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
                    int64_t n_cap, int k) {
   __shared__ uint32_t scratch[kSelThreads];
+  __shared__ uint32_t s_cnt[2][kSelThreads / kWave];
+  __shared__ uint32_t s_base[2];
   __shared__ int sT, sAbove;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
   const int64_t r = blockIdx.y;
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
   const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
   if (c0 >= nv) return;
   uint32_t* h = hist + r * (kBins + 4);
+  const float* srow = scores + r * nsp;
+  int64_t c1 = c0 + kFilterChunk;
+  if (c1 > nv) c1 = nv;
+  // this thread's scores first (independent loads in flight during the threshold search)
+  constexpr int kPer = kFilterChunk / kSelThreads;
+  float vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t e = c0 + j * kSelThreads + tid;
+    vals[j] = srow[e < c1 ? e : c1 - 1];
+  }
   int T = -1;
   if (nv > k) {
-    if (threadIdx.x == 0) { sT = kBins - 1; sAbove = 0; }
+    if (tid == 0) { sT = kBins - 1; sAbove = 0; }
     __syncthreads();
     find_threshold(h, k, &sT, &sAbove, scratch);
     T = sT;
   }
-  const float* srow = scores + r * nsp;
-  int64_t c1 = c0 + kFilterChunk;
-  if (c1 > nv) c1 = nv;
-  for (int64_t base = c0; base < c1; base += kSelThreads) {
-    const int64_t e = base + threadIdx.x;
-    bool is_sel = false, is_cand = false;
-    if (e < c1) {
-      if (T < 0) {
-        is_sel = true;
-      } else {
-        const int bin = (int)(float_key(srow[e]) >> kBinShift);
-        is_sel = bin > T;
-        is_cand = bin == T;
-      }
-    }
-    wave_append(is_sel, (int32_t)e, h + kBins + 0, sel + r * k);
-    wave_append(is_cand, (int32_t)e, h + kBins + 1, cand + r * nsp);
+  // classify, count per wave, one global reservation per list for the whole workgroup
+  uint64_t msel[kPer], mcand[kPer];
+  uint32_t nsel_w = 0, ncand_w = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t e = c0 + j * kSelThreads + tid;
+    const bool valid = e < c1;
+    const int bin = (int)(float_key(vals[j]) >> kBinShift);
+    msel[j] = __ballot(valid && bin > T);
+    mcand[j] = __ballot(valid && T >= 0 && bin == T);
+    nsel_w += __popcll(msel[j]);
+    ncand_w += __popcll(mcand[j]);
+  }
+  if (lane == 0) { s_cnt[0][wave] = nsel_w; s_cnt[1][wave] = ncand_w; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t ts = 0, tc = 0;
+    for (int w = 0; w < kSelThreads / kWave; ++w) { ts += s_cnt[0][w]; tc += s_cnt[1][w]; }
+    s_base[0] = ts ? atomicAdd(h + kBins + 0, ts) : 0u;
+    s_base[1] = tc ? atomicAdd(h + kBins + 1, tc) : 0u;
+  }
+  __syncthreads();
+  uint32_t bs = s_base[0], bc = s_base[1];
+  for (int w = 0; w < wave; ++w) { bs += s_cnt[0][w]; bc += s_cnt[1][w]; }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int32_t* sl = sel + r * k;
+  int32_t* cl = cand + r * nsp;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int32_t e = (int32_t)(c0 + j * kSelThreads + tid);
+    if ((msel[j] >> lane) & 1ull) sl[bs + __popcll(msel[j] & below)] = e;
+    if ((mcand[j] >> lane) & 1ull) cl[bc + __popcll(mcand[j] & below)] = e;
+    bs += __popcll(msel[j]);
+    bc += __popcll(mcand[j]);
   }
 }
 
 __device__ __forceinline__ uint64_t cand_key(const float* srow, int32_t s) {
   return ((uint64_t)(float_key(srow[s]) & 0x1FFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
 }
+
+constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
 
 struct SelShared {
   uint32_t h256[256];
@@ -346,17 +536,22 @@ struct SelShared {
   int done;
   int thr_shift;
   unsigned long long prefix;
-  uint32_t bitmap[kBitmapWords];
   uint32_t scan[kSelThreads];
+  unsigned long long ckey[kCandCache];
 };
 
 // Resolve `need` winners among `ncand` candidates (all in the threshold bin) digit by digit over
-// the 53-bit key (21 low score bits, complemented index) and append them to s.sel_list.
+// the 53-bit key (21 low score bits, complemented index) and append them to sel_list.  The
+// candidates' keys are read once into LDS when they fit.
 __device__ void refine_candidates(const float* srow, const int32_t* cand, int ncand, int need,
                                   int32_t* sel_list, SelShared& s) {
   const int tid = threadIdx.x;
+  const bool cached = ncand <= kCandCache;
+  if (cached)
+    for (int i = tid; i < ncand; i += kSelThreads) s.ckey[i] = cand_key(srow, cand[i]);
   if (tid == 0) { s.remaining = need; s.done = 0; s.prefix = 0ull; s.thr_shift = 0; }
   __syncthreads();
+  auto key_of = [&](int i) -> uint64_t { return cached ? (uint64_t)s.ckey[i] : cand_key(srow, cand[i]); };
   int shift = 53;
   for (int pass = 0; pass < 7; ++pass) {
     const int width = shift >= 8 ? 8 : shift;
@@ -365,7 +560,7 @@ __device__ void refine_candidates(const float* srow, const int32_t* cand, int nc
     __syncthreads();
     const unsigned long long pre = s.prefix;
     for (int i = tid; i < ncand; i += kSelThreads) {
-      const uint64_t key = cand_key(srow, cand[i]);
+      const uint64_t key = key_of(i);
       if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
@@ -406,76 +601,41 @@ __device__ void refine_candidates(const float* srow, const int32_t* cand, int nc
   const unsigned long long thr = s.prefix;
   const int ts = s.thr_shift;
   for (int i = tid; i < ncand; i += kSelThreads) {
-    const int32_t e = cand[i];
-    if ((cand_key(srow, e) >> ts) >= thr) {
+    const uint64_t key = key_of(i);
+    if ((key >> ts) >= thr) {
       const int pos = atomicAdd(&s.nsel, 1);
-      if (pos < kMaxTopk) sel_list[pos] = e;
+      if (pos < kMaxTopk) sel_list[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
     }
   }
   __syncthreads();
 }
 
-// Write the selected entries (unordered, count n) ascending into out[0..k), -1 padded.
+// Write the selected entries (unordered, count n <= 2048) ascending into out[0..k), -1 padded:
+// bitonic sort of the list in LDS.
 __device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const float* srow,
                                int32_t* out_idx, float* out_score, SelShared& s) {
   const int tid = threadIdx.x;
-  if (nv <= (int64_t)kBitmapWords * 32) {
-    const int words = (int)((nv + 31) / 32);
-    for (int i = tid; i < words; i += kSelThreads) s.bitmap[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const int32_t e = list[i];
-      if (e >= 0 && (int64_t)e < nv) atomicOr(&s.bitmap[e >> 5], 1u << (e & 31));
-    }
-    __syncthreads();
-    const int per = (words + kSelThreads - 1) / kSelThreads;
-    const int w0 = tid * per;
-    uint32_t cnt = 0;
-    for (int i = 0; i < per; ++i) if (w0 + i < words) cnt += __popc(s.bitmap[w0 + i]);
-    s.scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-      const uint32_t v = tid >= off ? s.scan[tid - off] : 0u;
-      __syncthreads();
-      s.scan[tid] += v;
-      __syncthreads();
-    }
-    int pos = (int)(s.scan[tid] - cnt);
-    for (int i = 0; i < per; ++i) {
-      if (w0 + i >= words) break;
-      uint32_t bits = s.bitmap[w0 + i];
-      while (bits) {
-        const int bpos = __ffs(bits) - 1;
-        bits &= bits - 1;
-        const int32_t e = (w0 + i) * 32 + bpos;
-        out_idx[pos] = e;
-        if (out_score) out_score[pos] = srow[e];
-        ++pos;
-      }
-    }
-  } else {
-    // bitonic sort of up to 2048 indices
-    int P = 2;
-    while (P < n) P <<= 1;
-    for (int i = tid; i < P; i += kSelThreads) if (i >= n) list[i] = INT_MAX;
-    __syncthreads();
-    for (int kk = 2; kk <= P; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P; i += kSelThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const int32_t a = list[i], bb = list[ixj];
-            const bool up = (i & kk) == 0;
-            if ((a > bb) == up) { list[i] = bb; list[ixj] = a; }
-          }
+  (void)nv; (void)s;
+  int P = 2;
+  while (P < n) P <<= 1;
+  for (int i = tid; i < P; i += kSelThreads) if (i >= n) list[i] = INT_MAX;
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kSelThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int32_t a = list[i], bb = list[ixj];
+          const bool up = (i & kk) == 0;
+          if ((a > bb) == up) { list[i] = bb; list[ixj] = a; }
         }
-        __syncthreads();
       }
+      __syncthreads();
     }
-    for (int i = tid; i < n; i += kSelThreads) {
-      out_idx[i] = list[i];
-      if (out_score) out_score[i] = srow[list[i]];
-    }
+  }
+  for (int i = tid; i < n; i += kSelThreads) {
+    out_idx[i] = list[i];
+    if (out_score) out_score[i] = srow[list[i]];
   }
   for (int i = n + tid; i < k; i += kSelThreads) {
     out_idx[i] = -1;
@@ -546,8 +706,25 @@ topk_rowwise_kernel(const float* __restrict__ scores, int32_t* __restrict__ cand
   sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
 }
 
+// Entries per decode scoring workgroup: about two workgroups per CU over the whole call.
+int64_t decode_chunk(int64_t n_cap, int R) {
+  int64_t c = (n_cap * R + 511) / 512;
+  c = (c + 255) & ~(int64_t)255;
+  if (c < 256) c = 256;
+  if (c > 65536) c = 65536;
+  return c;
+}
+
 template <bool FP8, int KS, int HBI, int QW>
 void launch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  if constexpr (QW == 1) {
+    const int64_t chunk = decode_chunk(a.n_cap, a.B * a.Tq);
+    dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * a.Tq));
+    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI>), grid, dim3(256), 0, st,
+               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
+               w.scores, w.hist, w.nsp);
+    return;
+  }
   constexpr int QTILE = QW == 1 ? 1 : 16;
   const int tiles = (a.Tq + QTILE - 1) / QTILE;
   dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));

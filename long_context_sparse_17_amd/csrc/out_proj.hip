@@ -7,8 +7,8 @@
 //
 // Both stages are Y[M, N] = X[M, xoff(n) + 0..K) . W[N, K]^T with output-major weights.  At decode
 // M is the batch (<= 16): the kernel streams W once from HBM straight into MFMA A-fragments
-// (16 B per lane, rows contiguous), X fragments come from L2, the 4 waves of a workgroup split K
-// and are summed through LDS.  One workgroup per 16 output features.
+// (16 B per lane, rows contiguous), X fragments come from L2, the waves of a workgroup split K
+// and are summed through LDS.  One workgroup per 16 output features; its 8 waves split K.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,18 +17,19 @@ namespace lcs {
 namespace {
 
 constexpr int kUnroll = 8;
+constexpr int kWaves = 8;                 // waves per workgroup, splitting K
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kWaves * 64)
 rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W,
                      uint16_t* __restrict__ Y, int64_t y_ld, int M, int N, int K, int n_per_group) {
-  __shared__ float4 red[4][kWave];
+  __shared__ float4 red[kWaves][kWave];
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int g = lane >> 4, c16 = lane & 15;
   const int n0 = blockIdx.x * 16;
   const int64_t xoff = (int64_t)(n0 / n_per_group) * K;
   const int ksteps = K / 32;
-  const int per_wave = (ksteps + 3) / 4;
+  const int per_wave = (ksteps + kWaves - 1) / kWaves;
   const int ks0 = w * per_wave;
   int ks1 = ks0 + per_wave;
   if (ks1 > ksteps) ks1 = ksteps;
@@ -37,7 +38,7 @@ rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
   for (int m0 = 0; m0 < M; m0 += 16) {
     const int mrow = m0 + c16;
     const bool mv = mrow < M;
-    const uint16_t* xrow = X + (int64_t)(mv ? mrow : 0) * x_ld + xoff + 8 * g;
+    const uint16_t* xrow = X + (int64_t)(mv ? mrow : M - 1) * x_ld + xoff + 8 * g;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     int ks = ks0;
     for (; ks + kUnroll <= ks1; ks += kUnroll) {
@@ -45,25 +46,28 @@ rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         wa[u] = *reinterpret_cast<const uint4*>(wrow + 32 * (ks + u));
-        xb[u] = mv ? *reinterpret_cast<const uint4*>(xrow + 32 * (ks + u)) : make_uint4(0, 0, 0, 0);
+        const uint4 xv = *reinterpret_cast<const uint4*>(xrow + 32 * (ks + u));
+        xb[u] = mv ? xv : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) acc = mfma_bf16(wa[u], xb[u], acc);
     }
     for (; ks < ks1; ++ks) {
       const uint4 wa = *reinterpret_cast<const uint4*>(wrow + 32 * ks);
-      const uint4 xb = mv ? *reinterpret_cast<const uint4*>(xrow + 32 * ks) : make_uint4(0, 0, 0, 0);
+      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + 32 * ks);
+      const uint4 xb = mv ? xv : make_uint4(0, 0, 0, 0);
       acc = mfma_bf16(wa, xb, acc);
     }
     // acc: lane holds column m0 + c16, rows n0 + 4g .. +3
     red[w][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
     if (w == 0) {
-      const float4 a0 = red[0][lane], a1 = red[1][lane], a2 = red[2][lane], a3 = red[3][lane];
-      const float y0 = (a0.x + a1.x) + (a2.x + a3.x);
-      const float y1 = (a0.y + a1.y) + (a2.y + a3.y);
-      const float y2 = (a0.z + a1.z) + (a2.z + a3.z);
-      const float y3 = (a0.w + a1.w) + (a2.w + a3.w);
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float4 a = red[v][lane];
+        y0 += a.x; y1 += a.y; y2 += a.z; y3 += a.w;
+      }
       if (mv) {
         uint2 o;
         o.x = pack_bf2(y0, y1);
@@ -85,9 +89,9 @@ int launch_out_proj(const OutProjArgs& a, hipStream_t st) {
   uint16_t* z = static_cast<uint16_t*>(a.ws);
   const int kg = a.H / a.g * a.c;
   const int nz = a.g * a.d_g;
-  LCS_LAUNCH("out_proj_group_kernel", rowblock_gemm_kernel, dim3((unsigned)(nz / 16)), dim3(256), 0, st,
+  LCS_LAUNCH("out_proj_group_kernel", rowblock_gemm_kernel, dim3((unsigned)(nz / 16)), dim3(kWaves * 64), 0, st,
              a.o, (int64_t)a.H * a.c, a.w_g, z, (int64_t)nz, a.M, nz, kg, a.d_g);
-  LCS_LAUNCH("out_proj_out_kernel", rowblock_gemm_kernel, dim3((unsigned)(a.d / 16)), dim3(256), 0, st,
+  LCS_LAUNCH("out_proj_out_kernel", rowblock_gemm_kernel, dim3((unsigned)(a.d / 16)), dim3(kWaves * 64), 0, st,
              z, (int64_t)nz, a.w_o, a.y, (int64_t)a.d, a.M, a.d, nz, a.d);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -105,7 +105,7 @@ class CsaDecodeLayer(_Common):
                             kv_out=self.kv_cache, ik_out=self.ik_cache, ik_scale=self.ik_scale, ik_fp8=True)
             if blk0 + nb == self.n_cap:
                 w0 = max(0, self.ctx - self.W + 1)
-                self.fill_ring(kv[:, w0 - t0:], ks[:, w0 - t0:], w0)
+                self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
             del kv, ks, ik, iks
 
     def step(self):
@@ -159,7 +159,7 @@ class HcaDecodeLayer(_Common):
             hca_compress_kv(kv, ks, tok0=t0, blk_begin=blk0, n_blk=nb, m=m, gamma_kv=self.gamma, kv_out=self.kv_cache)
             if blk0 + nb == self.n_cap:
                 w0 = max(0, self.ctx - self.W + 1)
-                self.fill_ring(kv[:, w0 - t0:], ks[:, w0 - t0:], w0)
+                self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
             del kv, ks
 
     def step(self):

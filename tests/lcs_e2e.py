@@ -78,8 +78,9 @@ def run_csa(B=2, t=600, H=64, H_I=64, dI=128, k=64, W=128, cfg=700, rope_offset=
         res["ref_sel"].append(sel[0])
         res["ref_scores"].append(sc[0])
         if fp8:
-            o_ex, _, _ = O.csa_layer(*args, **dict(kw, fp8=False))
+            o_ex, sel_ex, _ = O.csa_layer(*args, **dict(kw, fp8=False))
             res["ref_o_exact_indexer"].append(o_ex[0])
+            res.setdefault("ref_sel_exact", []).append(sel_ex[0])
         # oracle attention on the GPU's selection (used where the sets differ inside the tie band)
         ent = O.compress_kv(args[0], args[1], m, ov, ones, 1e-6, 10000.0, rope_offset)
         win = O.window_entries(args[0], ones, 1e-6, 10000.0, rope_offset)
@@ -136,5 +137,13 @@ def csa_report(res, k):
     out["o"] = errors(res["gpu_o"], ref_o)
     out["y"] = errors(res["gpu_y"], res["ref_y"])
     if res["ref_o_exact_indexer"]:
-        out["o_vs_exact_indexer"] = errors(res["gpu_o"], np.stack(res["ref_o_exact_indexer"]))
+        ex = np.stack(res["ref_o_exact_indexer"])
+        out["o_vs_exact_indexer"] = errors(res["gpu_o"], ex)
+        out["oracle_fp8_vs_exact"] = errors(res["ref_o"], ex)
+        ov = []
+        for b in range(B):
+            a, e = res["gpu_topk"][b], res["ref_sel_exact"][b]
+            a, e = a[a >= 0], e[e >= 0]
+            ov.append(np.intersect1d(a, e).size / max(1, e.size))
+        out["selection_overlap_vs_exact"] = float(min(ov))
     return out
