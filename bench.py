@@ -213,6 +213,21 @@ def main():
         wb = layers[0].w_g.numel() * 2
         per_kernel_gbs["out_proj_group_kernel"] = round(wb / (kernels["out_proj_group_kernel"]["avg_us"] * 1e-6) / 1e9, 1)
 
+    # reference: a plain device-to-device copy of 1 GiB (read + write bytes / time)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
     cpu = None
     if not args.no_cpu:
         rate, secs, threads, sample = cpu_baseline(layers, args.cpu_seqs)
@@ -231,7 +246,7 @@ def main():
         "step_hbm": {"bytes": step_bytes, "achieved_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "flops": step_flops},
-        "kernels": kernels, "kernel_gbs": per_kernel_gbs,
+        "kernels": kernels, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
     }
     _ = hca

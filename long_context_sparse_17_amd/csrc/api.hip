@@ -2,6 +2,7 @@
 // kernel launches on the caller's stream.  Declarations and the contract are in include/lcs.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -41,6 +42,12 @@ Timing& timing() {
 }  // namespace
 
 namespace lcs {
+RopeFreq rope_freq(float theta) {
+  RopeFreq f;
+  for (int j = 0; j < kRopeDims / 2; ++j) f.inv[j] = std::pow((double)theta, -(double)j / (kRopeDims / 2));
+  return f;
+}
+
 void timing_before(const char*, hipStream_t s) {
   Timing& t = timing();
   if (!t.on) return;

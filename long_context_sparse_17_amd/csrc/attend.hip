@@ -38,9 +38,10 @@ struct AttnK {
   int64_t n_cap; int m;
   const uint16_t* win; int64_t win_ld, ring_cap; int window;
   const float* sink; const int64_t* q_pos; int64_t rope_offset;
-  int Tq, H; float scale_log2, eps, theta;
+  int Tq, H; float scale_log2, eps;
+  RopeFreq rf;
   uint16_t* out; uint16_t* part_o; float* part_ml;
-  int nsplit, keys_per_split;
+  int nsplit, keys_per_split, hgroups;
 };
 
 struct RowKeys {
@@ -70,8 +71,14 @@ attend_kernel(AttnK a) {
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t r = blockIdx.y;
   const int64_t b = r / a.Tq;
-  const int split = blockIdx.x;
-  const int head0 = 0;
+  // Block ids are grouped 8 at a time so that the head-group workgroups of one split have ids 8 apart
+  // and therefore run on the same XCD (workgroups are dealt to the 8 XCDs round-robin): the second
+  // one finds the key tiles in that XCD's L2.
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * a.hgroups), rem = bid % (8 * a.hgroups);
+  const int split = grp * 8 + rem % 8;
+  if (split >= a.nsplit) return;                           // padding workgroup (uniform)
+  const int head0 = (rem / 8) * 16 * HB;
 
   if (threadIdx.x == 0) { s_rescale[0] = 0; s_rescale[1] = 0; }
   RowKeys rk;
@@ -81,8 +88,18 @@ attend_kernel(AttnK a) {
     if (threadIdx.x == 0) s_nsel = 0;
     __syncthreads();
     int last = 0;
-    for (int i = threadIdx.x; i < a.k; i += 256)
-      if (a.topk[r * a.k + i] >= 0) last = i + 1;
+    constexpr int kPer = 2048 / 256;     // k <= 2048: all loads in flight together
+    int32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      v[u] = a.topk[r * a.k + (i < a.k ? i : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < a.k && v[u] >= 0) last = i + 1;
+    }
     atomicMax(&s_nsel, last);
     __syncthreads();
     rk.nc = s_nsel;
@@ -99,7 +116,7 @@ attend_kernel(AttnK a) {
   const double pos = (double)(rk.t + a.rope_offset);
   if (threadIdx.x < 32) {
     float cs, sn;
-    rope_cs(pos, threadIdx.x, a.theta, &cs, &sn);
+    rope_cs(pos, a.rf.inv[threadIdx.x], &cs, &sn);
     s_cos[threadIdx.x] = cs;
     s_sin[threadIdx.x] = sn;
   }
@@ -111,16 +128,27 @@ attend_kernel(AttnK a) {
   const int nkeys = e_end > e_begin ? (int)(e_end - e_begin) : 0;
   {
     const int64_t j0 = rk.t - a.window + 1;               // first window token
-    for (int i = threadIdx.x; i < nkeys; i += 256) {
-      const int64_t e = e_begin + i;
-      int32_t row;
-      if (e < rk.nc) {
-        row = a.topk ? a.topk[r * a.k + e] : (int32_t)e;
-      } else {
-        const int64_t j = j0 + (e - rk.nc);
-        row = j < 0 ? -1 : (int32_t)(a.ring_cap > 0 ? j % a.ring_cap : j);
+    constexpr int kPer = kMaxSplitKeys / 256;
+    int32_t sel[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {                     // the selected indices: one round trip
+      const int64_t e = e_begin + threadIdx.x + 256 * u;
+      sel[u] = a.topk ? a.topk[r * a.k + (e < rk.nc ? e : 0)] : 0;   // unconditional (clamped) load
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + 256 * u;
+      if (i < nkeys) {
+        const int64_t e = e_begin + i;
+        int32_t row;
+        if (e < rk.nc) {
+          row = a.topk ? sel[u] : (int32_t)e;
+        } else {
+          const int64_t j = j0 + (e - rk.nc);
+          row = j < 0 ? -1 : (int32_t)(a.ring_cap > 0 ? j % a.ring_cap : j);
+        }
+        s_rows[i] = row;
       }
-      s_rows[i] = row;
     }
   }
   __syncthreads();
@@ -223,17 +251,19 @@ attend_kernel(AttnK a) {
     for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;      // softmax state of head (16w + c16), waves w < HB
 
-  for (int it = 0; it < ntiles; ++it) {
-    uint4 knext[2][4];
-    uint32_t vnext = 0;
-    if (it + 1 < ntiles) load_tile((it + 1) * kTile, knext, vnext);
+  // One 32-key tile: QK^T partials, softmax, PV.  kf holds the tile's fragments, vm its key mask.
+  auto process = [&](uint4 (&kf)[2][4], uint32_t vm, int it) {
+    // opaque zero: keeps the qhat fragment reads inside the tile (hoisting them would pin 16*HB
+    // registers for the whole loop)
+    int qz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(qz));
 
     // zero the rows of invalid keys (their loads read a real row so that no load is predicated)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bool v = (vcur >> (kb * 16 + c16)) & 1u;
+      const bool v = (vm >> (kb * 16 + c16)) & 1u;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kcur[kb][ks] = v ? kcur[kb][ks] : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) kf[kb][ks] = v ? kf[kb][ks] : make_uint4(0, 0, 0, 0);
     }
     // partial S^T over this wave's 128 dims
 #pragma unroll
@@ -242,13 +272,13 @@ attend_kernel(AttnK a) {
       for (int hb = 0; hb < HB; ++hb) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(kcur[kb][ks], s_q[w][hb][ks][lane], acc);
+        for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(kf[kb][ks], s_q[w][hb][ks][lane + qz], acc);
         s_part[((w * 2 + kb) * HB + hb) * kWave + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
       const int vr = vt_row(kb, c16);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<uint4*>(&s_vt[w][vr * kVtStride + 32 * ks + 8 * g]) = kcur[kb][ks];
+        *reinterpret_cast<uint4*>(&s_vt[w][vr * kVtStride + 32 * ks + 8 * g]) = kf[kb][ks];
     }
     __syncthreads();
 
@@ -270,7 +300,7 @@ attend_kernel(AttnK a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool v = (vcur >> (kb * 16 + 4 * g + i)) & 1u;
+          const bool v = (vm >> (kb * 16 + 4 * g + i)) & 1u;
           s[kb][i] = v ? s[kb][i] * a.scale_log2 : -INFINITY;
           tmax = fmaxf(tmax, s[kb][i]);
         }
@@ -345,12 +375,25 @@ attend_kernel(AttnK a) {
       for (int hb = 0; hb < HB; ++hb) o[hb][db] = mfma_bf16(pf[hb], vf, o[hb][db]);
     }
 
-    if (it + 1 < ntiles) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kcur[kb][ks] = knext[kb][ks];
-      vcur = vnext;
+  };
+
+  // Two register buffers rotate by unrolling (a copy between buffers would wait for the loads in
+  // flight): the next tile's loads are in flight while the current one is processed.  A load past
+  // the end re-reads the last tile (never processed).
+  uint4 k1[2][4];
+  uint32_t v1 = 0;
+  auto tile0 = [&](int t) { return (t < ntiles ? t : ntiles - 1) * kTile; };
+  if (ntiles > 0) {
+    for (int t = 0; t < ntiles; t += 2) {
+      load_tile(tile0(t + 1), k1, v1);
+      __builtin_amdgcn_sched_barrier(0);
+      process(kcur, vcur, t);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 >= ntiles) break;
+      load_tile(tile0(t + 2), kcur, vcur);
+      __builtin_amdgcn_sched_barrier(0);
+      process(k1, v1, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -415,7 +458,7 @@ attend_kernel(AttnK a) {
 __global__ void __launch_bounds__(128)
 merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
              const float* __restrict__ sink, const int64_t* __restrict__ q_pos, int64_t rope_offset,
-             float theta, uint16_t* __restrict__ out) {
+             RopeFreq rf, uint16_t* __restrict__ out) {
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -443,9 +486,9 @@ merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part
   if (d0 >= kRopeStart) {
     const double pos = (double)(q_pos[r] + rope_offset);
     float c, s;
-    rope_cs(pos, (d0 - kRopeStart) / 2, theta, &c, &s);
+    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2], &c, &s);
     const float r0 = y0 * c + y1 * s, r1 = -y0 * s + y1 * c;
-    rope_cs(pos, (d0 - kRopeStart) / 2 + 1, theta, &c, &s);
+    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2 + 1], &c, &s);
     const float r2 = y2 * c + y3 * s, r3 = -y2 * s + y3 * c;
     y0 = r0; y1 = r1; y2 = r2; y3 = r3;
   }
@@ -457,7 +500,10 @@ merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int head_blocks(int H) { return H <= 16 ? 1 : (H <= 32 ? 2 : 4); }
+// 16-head blocks per workgroup (at most 2: 32 heads keep the tile loop within the register file)
+// and the number of head-group workgroups per key split.
+int head_blocks(int H) { return H <= 16 ? 1 : 2; }
+int head_groups(int H) { return (H + 16 * head_blocks(H) - 1) / (16 * head_blocks(H)); }
 
 // Keys per split: about one workgroup per CU (256) with at least 2 tiles (64 keys) each; every split
 // adds a 64 KiB partial (bf16 O of 64 heads) that the merge reads back, so splits are kept few.
@@ -477,7 +523,7 @@ int keys_per_split(int R, int64_t max_keys) {
 
 size_t attend_workspace(int B, int Tq, int H, int64_t max_keys) {
   const int R = B * Tq;
-  const int kps = keys_per_split(R, max_keys);
+  const int kps = keys_per_split(R * head_groups(H), max_keys);
   const int64_t nsplit = max_keys > 0 ? (max_keys + kps - 1) / kps : 1;
   if (nsplit <= 1) return 256;
   return al256((size_t)R * nsplit * H * kHeadDim * 2) + al256((size_t)R * nsplit * H * 2 * 4);
@@ -489,23 +535,23 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.q = x.q; a.gamma_q = x.gamma_q; a.kv = x.kv; a.kv_ld = x.kv_ld; a.topk = x.topk; a.k = x.k;
   a.n_cap = x.n_cap; a.m = x.m; a.win = x.win; a.win_ld = x.win_ld; a.ring_cap = x.ring_cap;
   a.window = x.window; a.sink = x.sink; a.q_pos = x.q_pos; a.rope_offset = x.rope_offset;
-  a.Tq = x.Tq; a.H = x.H; a.scale_log2 = x.scale * kLog2e; a.eps = x.eps; a.theta = x.theta;
+  a.Tq = x.Tq; a.H = x.H; a.scale_log2 = x.scale * kLog2e; a.eps = x.eps; a.rf = rope_freq(x.theta);
   a.out = x.out;
-  a.keys_per_split = keys_per_split(R, max_keys);
+  a.hgroups = head_groups(x.H);
+  a.keys_per_split = keys_per_split(R * a.hgroups, max_keys);
   a.nsplit = max_keys > 0 ? (int)((max_keys + a.keys_per_split - 1) / a.keys_per_split) : 1;
   if (a.nsplit < 1) a.nsplit = 1;
   a.part_o = static_cast<uint16_t*>(x.ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
                                        al256((size_t)R * a.nsplit * x.H * kHeadDim * 2));
-  dim3 grid((unsigned)a.nsplit, (unsigned)R);
-  switch (head_blocks(x.H)) {
-    case 1: LCS_LAUNCH("attend_kernel", attend_kernel<1>, grid, dim3(256), 0, st, a); break;
-    case 2: LCS_LAUNCH("attend_kernel", attend_kernel<2>, grid, dim3(256), 0, st, a); break;
-    default: LCS_LAUNCH("attend_kernel", attend_kernel<4>, grid, dim3(256), 0, st, a); break;
-  }
+  dim3 grid((unsigned)(((a.nsplit + 7) / 8) * 8 * a.hgroups), (unsigned)R);
+  if (head_blocks(x.H) == 1)
+    LCS_LAUNCH("attend_kernel", attend_kernel<1>, grid, dim3(256), 0, st, a);
+  else
+    LCS_LAUNCH("attend_kernel", attend_kernel<2>, grid, dim3(256), 0, st, a);
   if (a.nsplit > 1) {
     LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(128), 0, st,
-               a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.q_pos, x.rope_offset, x.theta, x.out);
+               a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.q_pos, x.rope_offset, a.rf, x.out);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -52,12 +52,17 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 // ----------------------------------------------------------------------------------- RoPE
-// cos/sin of pos * theta^(-j/32).  The angle is formed in fp64 (positions near 2^20 would lose their
-// phase in fp32), reduced by 2*pi with a two-term Cody-Waite split (error ~1e-10 rad at 1e6 rad),
-// and the reduced angle in [-pi, pi] goes to the fp32 sincos.
-__device__ __forceinline__ void rope_cs(double pos, int j, float theta, float* c, float* s) {
-  const double inv = exp2(-(double)j * (1.0 / (kRopeDims / 2)) * log2((double)theta));
-  const double phi = pos * inv;
+// Inverse frequencies theta^(-j/32) of the 32 rotated pairs, computed once on the host in fp64 and
+// passed by value in the kernel arguments.
+struct RopeFreq {
+  double inv[kRopeDims / 2];
+};
+
+// cos/sin of pos * inv_j.  The angle is formed in fp64 (positions near 2^20 would lose their phase
+// in fp32), reduced by 2*pi with a two-term Cody-Waite split (error ~1e-10 rad at 1e6 rad), and the
+// reduced angle in [-pi, pi] goes to the fp32 sincos.
+__device__ __forceinline__ void rope_cs(double pos, double inv_j, float* c, float* s) {
+  const double phi = pos * inv_j;
   const double kq = rint(phi * 0.15915494309189535);
   double rr = fma(-kq, 6.283185307179586, phi);
   rr = fma(-kq, 2.4492935982947064e-16, rr);
@@ -93,6 +98,7 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 
 // ----------------------------------------------------------------------------------- host side
 namespace lcs {
+RopeFreq rope_freq(float theta);
 // Launch timing hooks (no-ops unless lcs_timing_enable(1)).
 void timing_before(const char* name, hipStream_t s);
 void timing_after(const char* name, hipStream_t s);

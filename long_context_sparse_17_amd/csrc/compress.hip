@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(kThreads)
 compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ kv_score,
                 const uint16_t* __restrict__ ik_tok, const float* __restrict__ ik_score,
                 int T, int64_t tok0, int64_t blk_begin, int m, int ov, int dI,
-                const uint16_t* __restrict__ gamma, float eps, float theta, int64_t rope_offset,
+                const uint16_t* __restrict__ gamma, float eps, RopeFreq rf, int64_t rope_offset,
                 uint16_t* __restrict__ kv_out, int64_t kv_ld, int64_t ring_cap,
                 void* __restrict__ ik_out, float* __restrict__ ik_scale, int64_t ik_ld, int ik_fp8) {
   __shared__ float wt[kMaxSpan];
@@ -137,9 +137,9 @@ compress_kernel(const uint16_t* __restrict__ kv_tok, const float* __restrict__ k
   if (d0 >= kRopeStart) {
     const double pos = (double)((i + 1) * m - 1 + rope_offset);
     float c, s;
-    rope_cs(pos, (d0 - kRopeStart) / 2, theta, &c, &s);
+    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2], &c, &s);
     const float r0 = y0 * c - y1 * s, r1 = y0 * s + y1 * c;
-    rope_cs(pos, (d0 - kRopeStart) / 2 + 1, theta, &c, &s);
+    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2 + 1], &c, &s);
     const float r2 = y2 * c - y3 * s, r3 = y2 * s + y3 * c;
     y0 = r0; y1 = r1; y2 = r2; y3 = r3;
   }
@@ -184,7 +184,7 @@ int launch_compress(const CompressArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.n_blk, (unsigned)a.B);
   LCS_LAUNCH("compress_kernel", compress_kernel, grid, dim3(kThreads), 0, stream,
              a.kv_tok, a.kv_score, a.ik_tok, a.ik_score, a.T, a.tok0, a.blk_begin, a.m, a.ov, a.dI,
-             a.gamma, a.eps, a.theta, a.rope_offset, a.kv_out, a.kv_ld, a.ring_cap, a.ik_out,
+             a.gamma, a.eps, rope_freq(a.theta), a.rope_offset, a.kv_out, a.kv_ld, a.ring_cap, a.ik_out,
              a.ik_scale, a.ik_ld, a.ik_fp8);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -38,10 +38,10 @@ constexpr int kMaxTopk = 2048;
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
-  float* scores;      // [R, nsp]
-  uint32_t* hist;     // [R, kBins + 4]: histogram, then sel count, cand count
-  int32_t* sel;       // [R, k]
-  int32_t* cand;      // [R, nsp]
+  float* scores;                  // [R, nsp]
+  uint32_t* hist;                 // [R, kBins + 4]: histogram, then sel count, cand count
+  int32_t* sel;                   // [R, k]
+  unsigned long long* cand;       // [R, nsp]: 53-bit candidate keys (see cand_key)
   int64_t nsp;
 };
 
@@ -55,7 +55,7 @@ Ws carve(void* ws, int R, int64_t n_cap, int k) {
   p += al256((size_t)R * (kBins + 4) * 4);
   w.sel = reinterpret_cast<int32_t*>(p);
   p += al256((size_t)R * k * 4);
-  w.cand = reinterpret_cast<int32_t*>(p);
+  w.cand = reinterpret_cast<unsigned long long*>(p);
   return w;
 }
 
@@ -342,8 +342,8 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   float* srow = scores + r * nsp;
   const int64_t ngroups = (c1 - c0 + 63) / 64;
 
-  Frag cur[4][KS], nxt[4][KS];
-  float cs[4], ns[4];
+  Frag cur[4][KS], nxt[4][KS], nx2[4][KS];
+  float cs[4], ns[4], n2[4];
   // Loads are unconditional (entry index clamped into the chunk) so that the compiler keeps them in
   // flight; out-of-range entries are zeroed by a select and never stored.
   auto load_group = [&](int64_t gi, Frag (&fr)[4][KS], float (&sc)[4]) {
@@ -368,10 +368,12 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     }
   };
 
-  int64_t gi = wave;
-  if (gi < ngroups) load_group(gi, cur, cs);
-  for (; gi < ngroups; gi += 4) {
-    if (gi + 4 < ngroups) load_group(gi + 4, nxt, ns);
+  // Groups of this wave: wave + 4t, t = 0 .. nt-1.  Three register buffers rotate by unrolling (a
+  // copy between buffers would wait for the loads in flight); two groups stay in flight ahead of the
+  // one being computed.  Loads past the end re-read the last group (never computed).
+  const int64_t nt = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
+  auto gidx = [&](int64_t t) -> int64_t { return wave + 4 * (t < nt ? t : nt - 1); };
+  auto compute_group = [&](const Frag (&fr)[4][KS], const float (&sc)[4], int64_t gi) {
     floatx4 acc[4][HBI];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -381,9 +383,9 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (FP8)
-            a = mfma_fp8(*reinterpret_cast<intx8*>(&afr[hb][ks]), *reinterpret_cast<intx8*>(&cur[u][ks]), a);
+            a = mfma_fp8(*reinterpret_cast<const intx8*>(&afr[hb][ks]), *reinterpret_cast<const intx8*>(&fr[u][ks]), a);
           else
-            a = mfma_bf16(*reinterpret_cast<uint4*>(&afr[hb][ks]), *reinterpret_cast<uint4*>(&cur[u][ks]), a);
+            a = mfma_bf16(*reinterpret_cast<const uint4*>(&afr[hb][ks]), *reinterpret_cast<const uint4*>(&fr[u][ks]), a);
         }
         acc[u][hb] = a;
       }
@@ -398,18 +400,24 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       part += __shfl_xor(part, 32, kWave);
       const int64_t e = c0 + 64 * gi + 16 * u + c16;
       if (g == 0 && e < c1) {
-        const float sc = part * cs[u] + 0.0f;
-        srow[e] = sc;
-        atomicAdd(&lhist[float_key(sc) >> kBinShift], 1u);
+        const float v = part * sc[u] + 0.0f;
+        srow[e] = v;
+        atomicAdd(&lhist[float_key(v) >> kBinShift], 1u);
       }
     }
-    if (gi + 4 < ngroups) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cur[u][ks] = nxt[u][ks];
-        cs[u] = ns[u];
-      }
+  };
+  if (nt > 0) {
+    load_group(gidx(0), cur, cs);
+    load_group(gidx(1), nxt, ns);
+    for (int64_t t = 0; t < nt; t += 3) {
+      load_group(gidx(t + 2), nx2, n2);
+      compute_group(cur, cs, gidx(t));
+      if (t + 1 >= nt) break;
+      load_group(gidx(t + 3), cur, cs);
+      compute_group(nxt, ns, gidx(t + 1));
+      if (t + 2 >= nt) break;
+      load_group(gidx(t + 4), nxt, ns);
+      compute_group(nx2, n2, gidx(t + 2));
     }
   }
   __syncthreads();
@@ -450,10 +458,18 @@ __device__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_
   __syncthreads();
 }
 
-// Decode filter: many workgroups per row.
+// 53-bit candidate key: the 21 score-key bits below the bin, then the complemented entry index, so
+// that larger score wins and, among equal scores, the lower index wins; every key is distinct.
+__device__ __forceinline__ unsigned long long cand_key(uint32_t key32, int32_t s) {
+  return ((unsigned long long)(key32 & 0x1FFFFFu) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)s);
+}
+
+// Decode filter: many workgroups per row.  Entries of bins above the threshold bin go to the result
+// list, those of the threshold bin (with their full keys) to the candidate list; one global
+// reservation per list per workgroup.
 __global__ void __launch_bounds__(kSelThreads)
 topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist, int32_t* __restrict__ sel,
-                   int32_t* __restrict__ cand, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
+                   unsigned long long* __restrict__ cand, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
                    int64_t n_cap, int k) {
   __shared__ uint32_t scratch[kSelThreads];
   __shared__ uint32_t s_cnt[2][kSelThreads / kWave];
@@ -470,13 +486,12 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
   const float* srow = scores + r * nsp;
   int64_t c1 = c0 + kFilterChunk;
   if (c1 > nv) c1 = nv;
-  // this thread's scores first (independent loads in flight during the threshold search)
   constexpr int kPer = kFilterChunk / kSelThreads;
-  float vals[kPer];
+  uint32_t keys[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int64_t e = c0 + j * kSelThreads + tid;
-    vals[j] = srow[e < c1 ? e : c1 - 1];
+    keys[j] = float_key(srow[e < c1 ? e : c1 - 1]);
   }
   int T = -1;
   if (nv > k) {
@@ -485,14 +500,13 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
     find_threshold(h, k, &sT, &sAbove, scratch);
     T = sT;
   }
-  // classify, count per wave, one global reservation per list for the whole workgroup
   uint64_t msel[kPer], mcand[kPer];
   uint32_t nsel_w = 0, ncand_w = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int64_t e = c0 + j * kSelThreads + tid;
     const bool valid = e < c1;
-    const int bin = (int)(float_key(vals[j]) >> kBinShift);
+    const int bin = (int)(keys[j] >> kBinShift);
     msel[j] = __ballot(valid && bin > T);
     mcand[j] = __ballot(valid && T >= 0 && bin == T);
     nsel_w += __popcll(msel[j]);
@@ -511,47 +525,60 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
   for (int w = 0; w < wave; ++w) { bs += s_cnt[0][w]; bc += s_cnt[1][w]; }
   const uint64_t below = (1ull << lane) - 1ull;
   int32_t* sl = sel + r * k;
-  int32_t* cl = cand + r * nsp;
+  unsigned long long* cl = cand + r * nsp;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int32_t e = (int32_t)(c0 + j * kSelThreads + tid);
     if ((msel[j] >> lane) & 1ull) sl[bs + __popcll(msel[j] & below)] = e;
-    if ((mcand[j] >> lane) & 1ull) cl[bc + __popcll(mcand[j] & below)] = e;
+    if ((mcand[j] >> lane) & 1ull) cl[bc + __popcll(mcand[j] & below)] = cand_key(keys[j], e);
     bs += __popcll(msel[j]);
     bc += __popcll(mcand[j]);
   }
 }
 
-__device__ __forceinline__ uint64_t cand_key(const float* srow, int32_t s) {
-  return ((uint64_t)(float_key(srow[s]) & 0x1FFFFFu) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
-}
-
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
+constexpr int kBitmapEntries = 1 << 18;     // rows up to this many entries are ordered through an LDS bitmap
+constexpr int kBitmapWords = kBitmapEntries / 32;
 
 struct SelShared {
   uint32_t h256[256];
-  uint32_t wsum[4];
+  uint32_t scan[kSelThreads];
+  uint32_t wtot[kSelThreads / kWave];
   int nsel;
   int remaining;
   int done;
   int thr_shift;
   unsigned long long prefix;
-  uint32_t scan[kSelThreads];
-  unsigned long long ckey[kCandCache];
+  union {
+    unsigned long long ckey[kCandCache];      // refine phase
+    uint32_t bitmap[kBitmapWords];            // ordering phase
+  } u;
 };
 
-// Resolve `need` winners among `ncand` candidates (all in the threshold bin) digit by digit over
-// the 53-bit key (21 low score bits, complemented index) and append them to sel_list.  The
-// candidates' keys are read once into LDS when they fit.
-__device__ void refine_candidates(const float* srow, const int32_t* cand, int ncand, int need,
-                                  int32_t* sel_list, SelShared& s) {
+// Resolve `need` winners among `ncand` candidate keys (all in the threshold bin) digit by digit and
+// append their entry indices to sel_list.  Keys are read once into LDS when they fit.
+__device__ void refine_candidates(const unsigned long long* cand, int ncand, int need, int32_t* sel_list,
+                                  SelShared& s) {
   const int tid = threadIdx.x;
   const bool cached = ncand <= kCandCache;
-  if (cached)
-    for (int i = tid; i < ncand; i += kSelThreads) s.ckey[i] = cand_key(srow, cand[i]);
+  if (cached) {                          // all loads first, then the LDS stores (one round trip)
+    constexpr int kPer = kCandCache / kSelThreads;
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      v[u] = cand[i < ncand ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < ncand) s.u.ckey[i] = v[u];
+    }
+  }
   if (tid == 0) { s.remaining = need; s.done = 0; s.prefix = 0ull; s.thr_shift = 0; }
   __syncthreads();
-  auto key_of = [&](int i) -> uint64_t { return cached ? (uint64_t)s.ckey[i] : cand_key(srow, cand[i]); };
+  // the key source is chosen outside the loops (a per-element select would issue the global load too)
+  const unsigned long long* src = cand;
   int shift = 53;
   for (int pass = 0; pass < 7; ++pass) {
     const int width = shift >= 8 ? 8 : shift;
@@ -559,9 +586,16 @@ __device__ void refine_candidates(const float* srow, const int32_t* cand, int nc
     for (int i = tid; i < 256; i += kSelThreads) s.h256[i] = 0u;
     __syncthreads();
     const unsigned long long pre = s.prefix;
-    for (int i = tid; i < ncand; i += kSelThreads) {
-      const uint64_t key = key_of(i);
-      if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+    if (cached) {
+      for (int i = tid; i < ncand; i += kSelThreads) {
+        const uint64_t key = s.u.ckey[i];
+        if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+      }
+    } else {
+      for (int i = tid; i < ncand; i += kSelThreads) {
+        const uint64_t key = src[i];
+        if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+      }
     }
     __syncthreads();
     if (tid < kWave) {
@@ -600,42 +634,106 @@ __device__ void refine_candidates(const float* srow, const int32_t* cand, int nc
   }
   const unsigned long long thr = s.prefix;
   const int ts = s.thr_shift;
-  for (int i = tid; i < ncand; i += kSelThreads) {
-    const uint64_t key = key_of(i);
+  auto take = [&](uint64_t key) {
     if ((key >> ts) >= thr) {
       const int pos = atomicAdd(&s.nsel, 1);
       if (pos < kMaxTopk) sel_list[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
     }
+  };
+  if (cached) {
+    for (int i = tid; i < ncand; i += kSelThreads) take(s.u.ckey[i]);
+  } else {
+    for (int i = tid; i < ncand; i += kSelThreads) take(src[i]);
   }
   __syncthreads();
 }
 
-// Write the selected entries (unordered, count n <= 2048) ascending into out[0..k), -1 padded:
-// bitonic sort of the list in LDS.
+// Write the selected entries (unordered, distinct, count n <= 2048) ascending into out[0..k), -1
+// padded.  Rows of up to 2^18 entries: set bits in an LDS bitmap and compact it in index order, each
+// wave scanning a contiguous range of words 64 at a time.  Longer rows: bitonic sort of the list.
 __device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const float* srow,
                                int32_t* out_idx, float* out_score, SelShared& s) {
   const int tid = threadIdx.x;
-  (void)nv; (void)s;
-  int P = 2;
-  while (P < n) P <<= 1;
-  for (int i = tid; i < P; i += kSelThreads) if (i >= n) list[i] = INT_MAX;
-  __syncthreads();
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kSelThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t a = list[i], bb = list[ixj];
-          const bool up = (i & kk) == 0;
-          if ((a > bb) == up) { list[i] = bb; list[ixj] = a; }
-        }
-      }
-      __syncthreads();
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  if (nv <= kBitmapEntries) {
+    const int words = (int)((nv + 31) / 32);
+    for (int i = tid; i < words; i += kSelThreads) s.u.bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const int32_t e = list[i];
+      if (e >= 0 && (int64_t)e < nv) atomicOr(&s.u.bitmap[e >> 5], 1u << (e & 31));
     }
-  }
-  for (int i = tid; i < n; i += kSelThreads) {
-    out_idx[i] = list[i];
-    if (out_score) out_score[i] = srow[list[i]];
+    __syncthreads();
+    constexpr int kWaves = kSelThreads / kWave;
+    const int seg = ((words + kWaves * kWave - 1) / (kWaves * kWave)) * kWave;   // words per wave
+    const int w0 = wave * seg;
+    int w1 = w0 + seg;
+    if (w1 > words) w1 = words;
+    uint32_t cnt_total = 0;
+    for (int base = w0; base < w1; base += kWave) {
+      const int wi = base + lane;
+      cnt_total += wi < w1 ? (uint32_t)__popc(s.u.bitmap[wi]) : 0u;
+    }
+    cnt_total = (uint32_t)wave_sum((float)cnt_total);          // exact: counts <= 2048
+    if (lane == 0) s.wtot[wave] = cnt_total;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += s.wtot[w];
+    for (int base = w0; base < w1; base += kWave) {
+      const int wi = base + lane;
+      uint32_t bits = wi < w1 ? s.u.bitmap[wi] : 0u;
+      const uint32_t c = (uint32_t)__popc(bits);
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      uint32_t pos = off + incl - c;
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int32_t e = wi * 32 + b;
+        out_idx[pos] = e;
+        if (out_score) out_score[pos] = srow[e];
+        ++pos;
+      }
+      off += __shfl(incl, kWave - 1, kWave);
+    }
+  } else {
+    int P = 2;
+    while (P < n) P <<= 1;
+    for (int i = tid; i < P; i += kSelThreads) if (i >= n) list[i] = INT_MAX;
+    __syncthreads();
+    constexpr int kPairs = kMaxTopk / 2 / kSelThreads;         // pairs per thread per phase (<= 4)
+    for (int kk = 2; kk <= P; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        int32_t x[kPairs], y[kPairs];
+        int ii[kPairs];
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {                     // all reads of the phase first
+          const int p = tid + u * kSelThreads;
+          ii[u] = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+          const bool act = p < (P >> 1);
+          x[u] = act ? list[ii[u]] : 0;
+          y[u] = act ? list[ii[u] + j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+          const int p = tid + u * kSelThreads;
+          if (p < (P >> 1)) {
+            const bool up = (ii[u] & kk) == 0;
+            if ((x[u] > y[u]) == up) { list[ii[u]] = y[u]; list[ii[u] + j] = x[u]; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < n; i += kSelThreads) {
+      out_idx[i] = list[i];
+      if (out_score) out_score[i] = srow[list[i]];
+    }
   }
   for (int i = n + tid; i < k; i += kSelThreads) {
     out_idx[i] = -1;
@@ -646,7 +744,7 @@ __device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const fl
 // Decode final: one workgroup per row.
 __global__ void __launch_bounds__(kSelThreads)
 topk_final_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ hist,
-                  const int32_t* __restrict__ sel, const int32_t* __restrict__ cand, int64_t nsp,
+                  const int32_t* __restrict__ sel, const unsigned long long* __restrict__ cand, int64_t nsp,
                   const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelShared s;
@@ -657,10 +755,23 @@ topk_final_kernel(const float* __restrict__ scores, const uint32_t* __restrict__
   const int nsel = (int)h[kBins + 0];
   const int ncand = (int)h[kBins + 1];
   const float* srow = scores + r * nsp;
-  for (int i = threadIdx.x; i < nsel; i += kSelThreads) list[i] = sel[r * k + i];
+  {
+    constexpr int kPer = kMaxTopk / kSelThreads;
+    int32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kSelThreads;
+      v[u] = sel[r * k + (i < nsel ? i : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kSelThreads;
+      if (i < nsel) list[i] = v[u];
+    }
+  }
   if (threadIdx.x == 0) s.nsel = nsel;
   __syncthreads();
-  if (nv > k) refine_candidates(srow, cand + r * nsp, ncand, k - nsel, list, s);
+  if (nv > k) refine_candidates(cand + r * nsp, ncand, k - nsel, list, s);
   __syncthreads();
   const int n = s.nsel < k ? s.nsel : k;
   sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
@@ -668,7 +779,7 @@ topk_final_kernel(const float* __restrict__ scores, const uint32_t* __restrict__
 
 // Prefill: one workgroup per row does histogram, filter, refine, sort.
 __global__ void __launch_bounds__(kSelThreads)
-topk_rowwise_kernel(const float* __restrict__ scores, int32_t* __restrict__ cand, int64_t nsp,
+topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __restrict__ cand, int64_t nsp,
                     const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelShared s;
@@ -693,15 +804,16 @@ topk_rowwise_kernel(const float* __restrict__ scores, int32_t* __restrict__ cand
   __syncthreads();
   find_threshold(h, k, &sT, &sAbove, s.scan);
   const int T = sT;
-  int32_t* crow = cand + r * nsp;
+  unsigned long long* crow = cand + r * nsp;
   for (int64_t e = tid; e < nv; e += kSelThreads) {
-    const int bin = (int)(float_key(srow[e]) >> kBinShift);
+    const uint32_t key = float_key(srow[e]);
+    const int bin = (int)(key >> kBinShift);
     if (bin > T) list[atomicAdd(&s.nsel, 1)] = (int32_t)e;
-    else if (bin == T) crow[atomicAdd(&sCand, 1)] = (int32_t)e;
+    else if (bin == T) crow[atomicAdd(&sCand, 1)] = cand_key(key, (int32_t)e);
   }
   __syncthreads();
   const int nsel = s.nsel;
-  refine_candidates(srow, crow, sCand, k - nsel, list, s);
+  refine_candidates(crow, sCand, k - nsel, list, s);
   const int n = s.nsel < k ? s.nsel : k;
   sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
 }
@@ -753,7 +865,7 @@ size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   const int64_t R = (int64_t)B * Tq;
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
   return al256((size_t)R * nsp * 4) + al256((size_t)R * (kBins + 4) * 4) + al256((size_t)R * k * 4) +
-         al256((size_t)R * nsp * 4);
+         al256((size_t)R * nsp * 8);
 }
 
 int launch_index_topk(const IndexArgs& a, hipStream_t st) {

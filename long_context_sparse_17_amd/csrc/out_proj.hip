@@ -16,7 +16,7 @@ namespace lcs {
 
 namespace {
 
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 constexpr int kWaves = 8;                 // waves per workgroup, splitting K
 
 __global__ void __launch_bounds__(kWaves * 64)
