@@ -36,7 +36,7 @@ __device__ __forceinline__ float block_reduce_max(float v, float* red) {
 
 // Softmax weights of n logits into wt[0 .. n).  `first` is this thread's logit j = tid (or -inf),
 // already loaded; the rest (n > 128) are read here.
-__device__ void pool_weights(const float* __restrict__ srow, int n, float first, float* wt, float* red) {
+__device__ __forceinline__ void pool_weights(const float* __restrict__ srow, int n, float first, float* wt, float* red) {
   float mx = first;
   if (threadIdx.x < n) wt[threadIdx.x] = first;
   for (int j = threadIdx.x + kThreads; j < n; j += kThreads) {

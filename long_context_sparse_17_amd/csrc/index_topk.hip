@@ -431,7 +431,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
 // ------------------------------------------------------------------------------------ selection
 // Threshold bin from a complete 2048-bin histogram: the bin T holding the k-th largest score and
 // the number of scores in bins above it.  256 threads, 8 bins each, suffix scan across threads.
-__device__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* scratch) {
+__device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* scratch) {
   const int tid = threadIdx.x;
   uint32_t loc[8];
   uint32_t sum = 0;
@@ -549,7 +549,7 @@ struct SelShared {
   int done;
   int thr_shift;
   unsigned long long prefix;
-  union {
+  union alignas(16) {
     unsigned long long ckey[kCandCache];      // refine phase
     uint32_t bitmap[kBitmapWords];            // ordering phase
   } u;
@@ -557,7 +557,7 @@ struct SelShared {
 
 // Resolve `need` winners among `ncand` candidate keys (all in the threshold bin) digit by digit and
 // append their entry indices to sel_list.  Keys are read once into LDS when they fit.
-__device__ void refine_candidates(const unsigned long long* cand, int ncand, int need, int32_t* sel_list,
+__device__ __forceinline__ void refine_candidates(const unsigned long long* cand, int ncand, int need, int32_t* sel_list,
                                   SelShared& s) {
   const int tid = threadIdx.x;
   const bool cached = ncand <= kCandCache;
@@ -651,7 +651,7 @@ __device__ void refine_candidates(const unsigned long long* cand, int ncand, int
 // Write the selected entries (unordered, distinct, count n <= 2048) ascending into out[0..k), -1
 // padded.  Rows of up to 2^18 entries: set bits in an LDS bitmap and compact it in index order, each
 // wave scanning a contiguous range of words 64 at a time.  Longer rows: bitonic sort of the list.
-__device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const float* srow,
+__device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const float* srow,
                                int32_t* out_idx, float* out_score, SelShared& s) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -665,41 +665,44 @@ __device__ void sort_and_write(int32_t* list, int n, int64_t nv, int k, const fl
       if (e >= 0 && (int64_t)e < nv) atomicOr(&s.u.bitmap[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
-    constexpr int kWaves = kSelThreads / kWave;
-    const int seg = ((words + kWaves * kWave - 1) / (kWaves * kWave)) * kWave;   // words per wave
-    const int w0 = wave * seg;
-    int w1 = w0 + seg;
-    if (w1 > words) w1 = words;
-    uint32_t cnt_total = 0;
-    for (int base = w0; base < w1; base += kWave) {
-      const int wi = base + lane;
-      cnt_total += wi < w1 ? (uint32_t)__popc(s.u.bitmap[wi]) : 0u;
-    }
-    cnt_total = (uint32_t)wave_sum((float)cnt_total);          // exact: counts <= 2048
-    if (lane == 0) s.wtot[wave] = cnt_total;
-    __syncthreads();
-    uint32_t off = 0;
-    for (int w = 0; w < wave; ++w) off += s.wtot[w];
-    for (int base = w0; base < w1; base += kWave) {
-      const int wi = base + lane;
-      uint32_t bits = wi < w1 ? s.u.bitmap[wi] : 0u;
-      const uint32_t c = (uint32_t)__popc(bits);
-      uint32_t incl = c;
+    // Thread t owns words [32t, 32t + 32) (entries 1024t ..): its bits go to registers, one block-wide
+    // exclusive scan of the per-thread counts gives its output offset, then it writes its entries
+    // in index order.
+    constexpr int kWordsPerThread = kBitmapWords / kSelThreads;            // 32
+    static_assert(kWordsPerThread % 4 == 0, "whole uint4 reads per thread");
+    uint32_t bits[kWordsPerThread];
+    const int w0 = tid * kWordsPerThread;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += v;
-      }
-      uint32_t pos = off + incl - c;
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        const int32_t e = wi * 32 + b;
+    for (int q = 0; q < kWordsPerThread / 4; ++q) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&s.u.bitmap[w0 + 4 * q]);
+      bits[4 * q + 0] = w0 + 4 * q + 0 < words ? x.x : 0u;
+      bits[4 * q + 1] = w0 + 4 * q + 1 < words ? x.y : 0u;
+      bits[4 * q + 2] = w0 + 4 * q + 2 < words ? x.z : 0u;
+      bits[4 * q + 3] = w0 + 4 * q + 3 < words ? x.w : 0u;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kWordsPerThread; ++q) cnt += (uint32_t)__popc(bits[q]);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == kWave - 1) s.wtot[wave] = incl;
+    __syncthreads();
+    uint32_t pos = incl - cnt;
+    for (int v = 0; v < wave; ++v) pos += s.wtot[v];
+#pragma unroll
+    for (int q = 0; q < kWordsPerThread; ++q) {
+      uint32_t b = bits[q];
+      while (b) {
+        const int e = (w0 + q) * 32 + __ffs(b) - 1;
+        b &= b - 1;
         out_idx[pos] = e;
         if (out_score) out_score[pos] = srow[e];
         ++pos;
       }
-      off += __shfl(incl, kWave - 1, kWave);
     }
   } else {
     int P = 2;

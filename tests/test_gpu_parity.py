@@ -221,11 +221,20 @@ def test_index_topk_all_equal_scores():
 
 
 # ----------------------------------------------------------------------------------- attention
-def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_inf=False, rope_offset=0):
+def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_inf=False, rope_offset=0,
+                 block_scale=None, gamma_scale=1.0, eps=1e-6, q_signs=False):
     q = synth.normal_bf16((B, Tq, H, 512), 1.28, cfg, 41)
-    gq = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 42).random(512, dtype=np.float32))
+    if q_signs:   # entries +-1: with eps = 0 the normalised query is gamma * q, exact in bf16
+        q = synth.f32_to_bf16_bits(np.where(synth.bf16_bits_to_f64(q) >= 0, 1.0, -1.0).astype(np.float32))
+    gq = synth.f32_to_bf16_bits(gamma_scale * (0.5 + synth.rng(cfg, 42).random(512, dtype=np.float32)))
     kv_ld = n_cap + 3
     cache = synth.normal_bf16((B, kv_ld, 512), 1.0, cfg, 43)
+    if block_scale is not None:
+        # entries in alternating blocks of 32 scaled by (small, big): the logit range jumps by far more
+        # than the lazy-rescale margin from one tile to the next
+        small, big = block_scale
+        f = np.where((np.arange(kv_ld) // 32) % 2 == 0, small, big)[None, :, None]
+        cache = synth.f32_to_bf16_bits((synth.bf16_bits_to_f64(cache) * f).astype(np.float32))
     pos = np.array(positions, dtype=np.int64).reshape(B, Tq)
     max_t = int(pos.max())
     win_ld = ring_cap if ring_cap else max_t + 1
@@ -243,10 +252,10 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
                 topk[b, t, : sel.size] = sel
         L.csa_attend(from_bits(q), from_bits(gq), from_bits(cache), torch.from_numpy(topk).to(DEV),
                      from_bits(win_tok), dev_f32(sink), dev_i64(pos), window=W, ring_cap=ring_cap, out=out,
-                     rope_offset=rope_offset)
+                     rope_offset=rope_offset, eps=eps)
     else:
         L.hca_attend(from_bits(q), from_bits(gq), from_bits(cache), from_bits(win_tok), dev_f32(sink), dev_i64(pos),
-                     n_cap=n_cap, m=m, window=W, ring_cap=ring_cap, out=out, rope_offset=rope_offset)
+                     n_cap=n_cap, m=m, window=W, ring_cap=ring_cap, out=out, rope_offset=rope_offset, eps=eps)
     torch.cuda.synchronize()
     got = to_np_bf16(out)
     g64 = synth.bf16_bits_to_f64(gq)
@@ -261,7 +270,7 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
                 keys.append(synth.bf16_bits_to_f64(win_tok[b, j % ring_cap if ring_cap else j]))
             K = np.stack(keys) if keys else np.zeros((0, 512))
             ref = O.attend_one(synth.bf16_bits_to_f64(q[b, t]), g64, K, sink.astype(np.float64), tt, scale,
-                               1e-6, 10000.0, rope_offset)
+                               eps, 10000.0, rope_offset)
             ma, rl = assert_close(got[b, t], ref, f"{kind} b={b} t={tt}")
             worst = (max(worst[0], ma), max(worst[1], rl))
     return worst
@@ -283,6 +292,18 @@ def test_hca_attend_parity(n_cap, H):
     # dense over all visible entries: many splits (3000) and a single split (60)
     pos = [128 * n_cap + 5, 128 * n_cap // 2 + 127, 0]
     _attend_case("hca", 3, 1, H, 0, n_cap, 128, 128, 128, pos, 53 + n_cap)
+
+
+def test_hca_attend_running_max_jumps_rescale_accumulators():
+    # Every split sees a tile of tiny logits followed by one of large logits (a 6x query gamma, keys
+    # scaled 0.02 / 1 in alternating blocks of 32), so the running max moves by far more than the
+    # kernel's lazy margin and the accumulated output is rescaled mid-split.  Logits this large would
+    # turn the bf16 rounding of the normalised query into percent-level output differences, so the
+    # query is made exactly representable: entries +-1, eps = 0 and position 0 after the offset
+    # (the rotation is the identity), which leaves qhat = gamma * q.
+    t = 128 * 700 + 5
+    _attend_case("hca", 2, 1, 64, 0, 700, 128, 128, 128, [t, t], 56, block_scale=(0.02, 1.0), gamma_scale=6.0,
+                 eps=0.0, q_signs=True, rope_offset=-t)
 
 
 def test_hca_attend_single_split_finishes_in_kernel():
