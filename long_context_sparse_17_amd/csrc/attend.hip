@@ -62,6 +62,7 @@ __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
   __shared__ uint4 s_p[2][kWaves * kWave];                  // P fragments [slot][head block][lane]
+  __shared__ uint4 s_gamma[kHeadDim / 8];                  // gamma_q (bf16)
   __shared__ int s_redo;                                    // some head's running max jumped: second pass
   __shared__ float s_fac[kHeadSlots];
   __shared__ float s_cos[32], s_sin[32];
@@ -82,6 +83,33 @@ attend_kernel(AttnK a) {
   const int64_t e_begin = (int64_t)split * a.keys_per_split;
   if (threadIdx.x == 0) s_redo = 0;          // read after the first pass's last barrier
 
+  const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
+  // HCA: the first two tiles are loaded speculatively at once, as entries e_begin .. e_begin+63
+  // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
+  // is checked once the query position is known (otherwise they are loaded again).
+  uint4 kb0[2][4], kb1[2][4];
+  uint32_t vb0 = 0, vb1 = 0;
+  if (!LIST) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t e0 = e_begin + kb * 16 + c16, e1 = e0 + kTile;
+      GU32x4* p0 = reinterpret_cast<GU32x4*>(reinterpret_cast<uintptr_t>(
+          kv_b + (e0 < a.kv_ld ? e0 : a.kv_ld - 1) * kHeadDim + 128 * w + 8 * g));
+      GU32x4* p1 = reinterpret_cast<GU32x4*>(reinterpret_cast<uintptr_t>(
+          kv_b + (e1 < a.kv_ld ? e1 : a.kv_ld - 1) * kHeadDim + 128 * w + 8 * g));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 x = p0[4 * ks];
+        kb0[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 x = p1[4 * ks];
+        kb1[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    }
+  }
+
   // ---- one round trip: query position, this split's list slots, q and gamma ----
   const int64_t t_q = a.q_pos[r];
   constexpr int kPer = kMaxSplitKeys / 256;
@@ -99,9 +127,8 @@ attend_kernel(AttnK a) {
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
-  uint4 gmv[16];
-#pragma unroll
-  for (int kk = 0; kk < 16; ++kk) gmv[kk] = *reinterpret_cast<const uint4*>(a.gamma_q + 32 * kk + 8 * g);
+  if (threadIdx.x < kHeadDim / 8)          // gamma: 1 KiB, staged once in LDS
+    s_gamma[threadIdx.x] = *reinterpret_cast<const uint4*>(a.gamma_q + 8 * threadIdx.x);
   __builtin_amdgcn_sched_barrier(0);
 
   int64_t nc;                                             // compressed key slots of the row
@@ -145,7 +172,6 @@ attend_kernel(AttnK a) {
     }
   }
   __syncthreads();
-  const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
   const uint16_t* win_b = a.win ? a.win + b * a.win_ld * kHeadDim : a.kv;
   const int nc_local = nc > e_begin ? (int)(nc - e_begin) : 0;   // split keys that are compressed
 
@@ -176,14 +202,16 @@ attend_kernel(AttnK a) {
     tile_rows(i0, rr, vmask);
     issue_tile(i0, rr, kf);
   };
-  // Two register buffers, issued unconditionally (an empty split reads row 0; a load under a branch
-  // would make every later wait assume the shorter queue of the other path).  A load past the end
-  // re-reads the last tile, whose copy is never scored.
+  // Two register buffers; an empty split reads row 0.  A load past the end re-reads the last
+  // tile, whose copy is never scored.
   auto tile0 = [&](int t) { return (t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0)) * kTile; };
-  uint4 kb0[2][4], kb1[2][4];
-  uint32_t vb0 = 0, vb1 = 0;
-  load_tile(tile0(0), kb0, vb0);
-  load_tile(tile0(1), kb1, vb1);
+  if (!LIST && nkeys >= 2 * kTile && nc_local >= 2 * kTile) {
+    vb0 = 0xFFFFFFFFu;                     // the speculative loads are these tiles
+    vb1 = 0xFFFFFFFFu;
+  } else {
+    load_tile(tile0(0), kb0, vb0);
+    load_tile(tile0(1), kb1, vb1);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- qhat = RoPE(RMSNorm(q) * gamma) for head c16 of block w (zero for a padding head) ----
@@ -200,12 +228,11 @@ attend_kernel(AttnK a) {
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
     const float rstd = head_ok ? 1.0f / sqrtf(acc * (1.0f / kHeadDim) + a.eps) : 0.f;
-    __syncthreads();                       // rope table
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int d = 32 * kk + 8 * g;
       const uint4 x = qf[kk];
-      const uint4 gm = gmv[kk];
+      const uint4 gm = s_gamma[4 * kk + g];   // dims 32kk + 8g .. +8
       float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
                     bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
       const float gv[8] = {bf2f_lo(gm.x), bf2f_hi(gm.x), bf2f_lo(gm.y), bf2f_hi(gm.y),
@@ -237,8 +264,10 @@ attend_kernel(AttnK a) {
   bool jumped = false;
 
   // Tile registers -> this wave's LDS slice of `slot` (invalid keys zeroed), then the buffer is
-  // refilled with the tile at next_i0.  Returns the tile's key mask.
-  auto stage = [&](uint4 (&kf)[2][4], uint32_t& vmask, int slot, int next_i0) -> uint32_t {
+  // refilled with the tile at next_i0, whose rows rn and mask vn were looked up earlier.  Returns
+  // the staged tile's key mask.
+  auto stage = [&](uint4 (&kf)[2][4], uint32_t& vmask, int slot, int next_i0, const int32_t (&rn)[2],
+                   uint32_t vn) -> uint32_t {
     const uint32_t vm = vmask;
     if (vm != 0xFFFFFFFFu) {               // ragged or missing keys: zero their rows
 #pragma unroll
@@ -255,26 +284,41 @@ attend_kernel(AttnK a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(&sl[vr * kVtStride + 32 * ks + 8 * g]) = kf[kb][ks];
     }
-    load_tile(next_i0, kf, vmask);
+    issue_tile(next_i0, rn, kf);
+    vmask = vn;
     return vm;
   };
 
   // Logits of head block w for the tile in `slot`, online softmax, P and rescale factors out.
   auto score = [&](int slot, uint32_t vm) {
     floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    // 8 steps of 64 dims (slice h >> 1, ks 2(h & 1) .. +1): the fragments of step h + 1 are read
+    // while the MFMAs of step h run (two sets of 4 fragments, 32 registers)
+    auto kread = [&](int h, uint4 (&f)[2][2]) {
+      const uint16_t* sl = s_kv[slot][h >> 1];
 #pragma unroll
-    for (int s = 0; s < kWaves; ++s) {   // one slice (8 fragments, 32 registers) at a time
-      const uint16_t* sl = s_kv[slot][s];
-      uint4 kfrag[2][4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          kfrag[kb][ks] = *reinterpret_cast<const uint4*>(&sl[vt_row(kb, c16) * kVtStride + 32 * ks + 8 * g]);
+          f[kb][j] = *reinterpret_cast<const uint4*>(&sl[vt_row(kb, c16) * kVtStride + 32 * (2 * (h & 1) + j) + 8 * g]);
+    };
+    uint4 fa[2][2], fb[2][2];
+    kread(0, fa);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+    for (int h = 0; h < 8; h += 2) {
+      kread(h + 1, fb);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_bf16(kfrag[kb][ks], qf[4 * s + ks], acc[kb]);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_bf16(fa[kb][j], qf[2 * h + j], acc[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (h + 2 < 8) kread(h + 2, fa);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_bf16(fb[kb][j], qf[2 * h + 2 + j], acc[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
     float sc[2][4];
@@ -354,19 +398,24 @@ attend_kernel(AttnK a) {
     for (int hb = 0; hb < kWaves; ++hb)
 #pragma unroll
       for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-    uint32_t vm0 = stage(kb0, vb0, 0, tile0(2));    // tile 0 -> slot 0, buffer 0 <- tile 2
+    int32_t rn[2];
+    uint32_t vn;
+    tile_rows(tile0(2), rn, vn);
+    uint32_t vm0 = stage(kb0, vb0, 0, tile0(2), rn, vn);   // tile 0 -> slot 0, buffer 0 <- tile 2
     uint32_t vm1 = 0;
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
+      tile_rows(tile0(t + 3), rn, vn);              // row lookups first: their latency hides under QK
       score(0, vm0);
       if (t > 0) accumulate(1);
-      vm1 = stage(kb1, vb1, 1, tile0(t + 3));       // tile t+1 -> slot 1, buffer 1 <- tile t+3
+      vm1 = stage(kb1, vb1, 1, tile0(t + 3), rn, vn);      // tile t+1 -> slot 1, buffer 1 <- tile t+3
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 >= ntiles) break;
+      tile_rows(tile0(t + 4), rn, vn);
       score(1, vm1);
       accumulate(0);
-      vm0 = stage(kb0, vb0, 0, tile0(t + 4));       // tile t+2 -> slot 0, buffer 0 <- tile t+4
+      vm0 = stage(kb0, vb0, 0, tile0(t + 4), rn, vn);      // tile t+2 -> slot 0, buffer 0 <- tile t+4
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -436,49 +485,94 @@ attend_kernel(AttnK a) {
 }
 
 // Merge split-K partials with the sink; one workgroup of 128 threads per (query, head), 4 dims per
-// thread.  Splits are folded 16 at a time (all their loads in flight together) with a running max.
-constexpr int kMergeChunk = 16;
+// thread.  The reference M = max(sink, split maxima) is found first (one split per thread), then the
+// split weights 2^(m_s - M) go through LDS and every thread folds the partial O rows, 32 splits'
+// loads in flight at a time (the first 32 are issued before the weights are known).
+constexpr int kMergeThreads = 128;
+constexpr int kMergeChunk = 32;
+constexpr int kMergeBlock = 1024;          // split weights held in LDS at a time
 
-__global__ void __launch_bounds__(128)
+__device__ __forceinline__ float block_max_128(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const float r = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_sum_128(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const float r = red[0] + red[1];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
              const float* __restrict__ sink, uint16_t* __restrict__ out) {
+  __shared__ float s_f[kMergeBlock];
+  __shared__ float2 s_ml[kMergeBlock];     // (max, sum) of the first kMergeBlock splits
+  __shared__ float s_red[2];
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
+  auto o_at = [&](int sp) {                // this thread's 4 dims of split sp's partial
+    return *reinterpret_cast<const uint2*>(part_o + ((r * nsplit + sp) * H + h) * kHeadDim + 4 * tid);
+  };
+  auto ml_at = [&](int sp) { return *reinterpret_cast<const float2*>(part_ml + ((r * nsplit + sp) * H + h) * 2); };
+
+  uint2 v[kMergeChunk];
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u) v[u] = o_at(u < nsplit ? u : nsplit - 1);   // in flight early
+
   const float z = sink[h] * kLog2e;
-  float M = z;                                   // running reference (log2 domain)
-  float L = z == -INFINITY ? 0.f : 1.f;          // e^(sink - M)
+  float mloc = -INFINITY;
+  for (int sp = tid; sp < nsplit; sp += kMergeThreads) {
+    const float2 ml = ml_at(sp);
+    if (sp < kMergeBlock) s_ml[sp] = ml;
+    mloc = fmaxf(mloc, ml.x);
+  }
+  const float M = fmaxf(block_max_128(mloc, s_red), z);
+
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < nsplit; c0 += kMergeChunk) {
-    float2 ml[kMergeChunk];
-    uint2 v[kMergeChunk];
-#pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {      // unconditional (clamped) loads
-      const int s = c0 + u < nsplit ? c0 + u : nsplit - 1;
-      const int64_t base = (r * nsplit + s) * H + h;
-      ml[u] = *reinterpret_cast<const float2*>(part_ml + base * 2);
-      v[u] = *reinterpret_cast<const uint2*>(part_o + base * kHeadDim + 4 * tid);
+  float lloc = 0.f;
+  for (int b0 = 0; b0 < nsplit; b0 += kMergeBlock) {
+    const int nb = nsplit - b0 < kMergeBlock ? nsplit - b0 : kMergeBlock;
+    auto weight = [&](int i, float2 ml) {
+      const float f = M == -INFINITY ? 0.f : exp2f(ml.x - M);
+      s_f[i] = f;
+      lloc += f * ml.y;
+    };
+    if (b0 == 0) {                         // s_ml is visible after the max's barriers
+      for (int i = tid; i < nb; i += kMergeThreads) weight(i, s_ml[i]);
+    } else {
+      for (int i = tid; i < nb; i += kMergeThreads) weight(i, ml_at(b0 + i));
     }
-    float mc = -INFINITY;
+    __syncthreads();
+    for (int c = 0; c < nb; c += kMergeChunk) {
+      if (b0 + c > 0) {
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u)
-      if (c0 + u < nsplit) mc = fmaxf(mc, ml[u].x);
-    const float Mn = fmaxf(M, mc);
-    if (Mn == -INFINITY) continue;               // no key and no sink so far
-    const float sc = exp2f(M - Mn);
-    L *= sc;
-    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+        for (int u = 0; u < kMergeChunk; ++u) {
+          const int sp = b0 + c + u;
+          v[u] = o_at(sp < nsplit ? sp : nsplit - 1);
+        }
+      }
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
-      if (c0 + u < nsplit) {
-        const float f = exp2f(ml[u].x - Mn);
-        L += f * ml[u].y;
+      for (int u = 0; u < kMergeChunk; ++u) {
+        const float f = c + u < nb ? s_f[c + u] : 0.f;
         acc.x += f * bf2f_lo(v[u].x); acc.y += f * bf2f_hi(v[u].x);
         acc.z += f * bf2f_lo(v[u].y); acc.w += f * bf2f_hi(v[u].y);
       }
     }
-    M = Mn;
+    __syncthreads();
   }
+  float L = block_sum_128(lloc, s_red);
+  if (z != -INFINITY) L += exp2f(z - M);
   const float inv = L > 0.f ? 1.0f / L : 0.f;      // partials are already rotated
   uint2 o;
   o.x = pack_bf2(acc.x * inv, acc.y * inv);
@@ -530,7 +624,7 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   if (x.topk) LCS_LAUNCH("attend_kernel", attend_kernel<true>, grid, dim3(256), 0, st, a);
   else LCS_LAUNCH("attend_kernel", attend_kernel<false>, grid, dim3(256), 0, st, a);
   if (a.nsplit > 1) {
-    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(128), 0, st,
+    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(kMergeThreads), 0, st,
                a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.out);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
