@@ -34,7 +34,7 @@ constexpr int kHeadSlots = 16 * kWaves;   // heads handled by one workgroup (all
 constexpr int kMaxSplitKeys = 2048;       // keys of one split, staged as row indices in LDS
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 GU32x4;   // global address space: global_load, not flat
-constexpr int kVtStride = 136;            // bf16 per LDS row of a 128-dim slice (128 + 8 pad)
+constexpr int kVtStride = 136;            // bf16 per LDS row of a 128-dim slice (128 + 8 pad: rows 4 banks apart)
 constexpr float kLog2e = 1.4426950408889634f;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 LdsV4i16;   // LDS operand of the transpose read
@@ -53,9 +53,9 @@ struct AttnK {
   int nsplit, keys_per_split;
 };
 
-// LDS row of tile key (block kb, row r16 of the 16x16 MFMA block) in a slice.  Keys are permuted so
-// that the 8 keys a lane needs for the V fragment (k-slots 8g..8g+7) sit 2 rows apart per g.
-__device__ __forceinline__ int vt_row(int kb, int r16) { return 2 * (r16 >> 2) + 8 * (r16 & 3) + kb; }
+// LDS row of tile key (block kb, row r16 of the 16x16 MFMA block) in a slice: the key itself.  With
+// rows 272 B apart, the 16 rows a K-fragment read touches start 4 banks apart (no conflicts).
+__device__ __forceinline__ int vt_row(int kb, int r16) { return kb * 16 + r16; }
 
 template <bool LIST>
 __global__ void __launch_bounds__(256, 1)
@@ -369,14 +369,13 @@ attend_kernel(AttnK a) {
     // transpose reads give it: within each 16-lane group, lane j points at 4 consecutive dims
     // (16db + 4(j & 3)) of the key in k-slot 8g + (j >> 2) (then 8g + 4 + (j >> 2)), and lane i
     // receives element i & 3 of the chunks of lanes (i >> 2) + 4q, q = 0..3, i.e. dim 16db + i of
-    // k-slots 8g + q.  k-slot 8g + q is key 4g + q (rows 2g + 8q), 8g + 4 + q is key 16 + 4g + q
-    // (the next row).
-    const LdsU16* vbase = (const LdsU16*)(s_kv[slot][w]) + (2 * g + 8 * (c16 >> 2)) * kVtStride +
+    // k-slots 8g + q.  k-slot 8g + q is key 4g + q, 8g + 4 + q is key 16 + 4g + q (P's order).
+    const LdsU16* vbase = (const LdsU16*)(s_kv[slot][w]) + vt_row(0, 4 * g + (c16 >> 2)) * kVtStride +
                           4 * (c16 & 3);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(vbase + 16 * db));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(vbase + kVtStride + 16 * db));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(vbase + 16 * kVtStride + 16 * db));
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
 #pragma unroll
