@@ -420,29 +420,31 @@ attend_kernel(AttnK a) {
     }
     if (ntiles > 0) accumulate((ntiles - 1) & 1);
     if (jumped) s_redo = 1;
-    __syncthreads();
+    {
+      // this pass's output factor per head: one split finishes here (sink, normalisation); with
+      // several, the partials stay unnormalised
+      float f = 1.f;
+      if (a.nsplit == 1) {
+        const float z = head_ok ? a.sink[head] * kLog2e : -INFINITY;
+        const float M = fmaxf(m_ref, z);
+        f = 0.f;
+        if (M != -INFINITY) {
+          const float L = l_run * exp2f(m_ref - M) + exp2f(z - M);
+          f = exp2f(m_ref - M) / L;
+        }
+      }
+      if (g == 0) s_fac[head] = f;
+    }
+    __syncthreads();                       // s_redo, s_fac; every wave is past its last tile reads
     if (pass > 0 || s_redo == 0) break;
   }
 
-  // Epilogue.  One split finishes the output here (sink, normalisation); with several, the split
-  // stores its partial O and (max, sum).  Either way the last 64 dims are rotated by -(t + offset)
-  // here: the rotation is linear, so rotated partials merge to the rotated output.  O goes through
-  // LDS ([head][dim] bf16, in the tile buffers) so that the global stores are whole 16 B chunks.
+  // Epilogue.  One split finishes the output here (factor s_fac: sink, normalisation); with
+  // several, the split stores its partial O and (max, sum).  Either way the last 64 dims are rotated
+  // by -(t + offset) here: the rotation is linear, so rotated partials merge to the rotated output.
+  // O goes through LDS ([head][dim] bf16, in the tile buffers) so that the global stores are whole
+  // 16 B chunks.
   const bool single = a.nsplit == 1;
-  {
-    float f = 1.f;
-    if (single) {
-      const float z = head_ok ? a.sink[head] * kLog2e : -INFINITY;
-      const float M = fmaxf(m_ref, z);
-      f = 0.f;
-      if (M != -INFINITY) {
-        const float L = l_run * exp2f(m_ref - M) + exp2f(z - M);
-        f = exp2f(m_ref - M) / L;
-      }
-    }
-    if (g == 0) s_fac[head] = f;
-  }
-  __syncthreads();                         // s_fac; every wave is past its last tile reads
   uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][512 dims] bf16 = 64 KiB
   static_assert(sizeof(s_kv) >= kHeadSlots * kHeadDim * 2, "output staging fits the tile buffers");
 #pragma unroll

@@ -21,13 +21,15 @@ __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 
 __device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16, round to nearest even: gfx950 converts a pair in one instruction
+// (v_cvt_pk_bf16_f32); it agrees bit for bit with the rounding rule on finite values, ties and
+// subnormals included, and keeps NaNs NaN.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float floatx2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_hw){lo, hi}, bf16x2_hw));
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf2(f, 0.f) & 0xFFFFu; }
 
 // fp32 -> OCP E4M3FN code: round to nearest, ties to even, saturating at +-448; -0 -> +0.
 // Written from the format's definition: bias 7, 3 mantissa bits, subnormal quantum 2^-9.
