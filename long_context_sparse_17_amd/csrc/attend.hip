@@ -445,29 +445,33 @@ attend_kernel(AttnK a) {
   // O goes through LDS ([head][dim] bf16, in the tile buffers) so that the global stores are whole
   // 16 B chunks.
   const bool single = a.nsplit == 1;
-  uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][512 dims] bf16 = 64 KiB
-  static_assert(sizeof(s_kv) >= kHeadSlots * kHeadDim * 2, "output staging fits the tile buffers");
+  constexpr int kOStride = kHeadDim;
+  uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][512 dims] bf16
+  static_assert(sizeof(s_kv) >= kHeadSlots * kOStride * 2, "output staging fits the tile buffers");
 #pragma unroll
   for (int hb = 0; hb < kWaves; ++hb) {
-    const float4 fac = *reinterpret_cast<const float4*>(&s_fac[hb * 16 + 4 * g]);
+    float4 fac = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (single) fac = *reinterpret_cast<const float4*>(&s_fac[hb * 16 + 4 * g]);   // partials: factor 1
     const float fv[4] = {fac.x, fac.y, fac.z, fac.w};
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int d = 128 * w + 16 * db + c16;
       float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = o[hb][db][i] * fv[i];
-      if (d >= kRopeStart) {               // wave 3, db >= 4: rotate pairs (d, d ^ 1) by -(t + offset)
+      for (int i = 0; i < 4; ++i) v[i] = single ? o[hb][db][i] * fv[i] : o[hb][db][i];
+      if (w == kWaves - 1 && 16 * db >= kRopeStart - 128 * (kWaves - 1)) {
+        // dims >= 448 (last wave, db >= 4): rotate pairs (d, d ^ 1) by -(t + offset); the partner
+        // lane's value comes by a quad permutation [1, 0, 3, 2]
         const int jr = (d - kRopeStart) >> 1;
         const float cs = s_cos[jr], sn = s_sin[jr];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __shfl_xor(v[i], 1, kWave);
+          const float pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
           v[i] = (c16 & 1) ? (v[i] * cs - pv * sn) : (v[i] * cs + pv * sn);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[(hb * 16 + 4 * g + i) * kHeadDim + d] = (uint16_t)f2bf(v[i]);
+      for (int i = 0; i < 4; ++i) s_o[(hb * 16 + 4 * g + i) * kOStride + d] = (uint16_t)f2bf(v[i]);
     }
   }
   __syncthreads();
@@ -477,7 +481,7 @@ attend_kernel(AttnK a) {
   for (int u = 0; u < kHeadSlots * kHeadDim / 8 / 256; ++u) {   // 16 chunks of 8 dims per thread
     const int hl = 4 * u + w;              // one head per wave per step: the check is uniform
     if (hl < a.H) {
-      const uint4 x = *reinterpret_cast<const uint4*>(&s_o[hl * kHeadDim + 8 * lane]);
+      const uint4 x = *reinterpret_cast<const uint4*>(&s_o[hl * kOStride + 8 * lane]);
       *reinterpret_cast<uint4*>(dst + (base + hl) * kHeadDim + 8 * lane) = x;
     }
   }

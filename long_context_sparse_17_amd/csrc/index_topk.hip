@@ -39,23 +39,27 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
   float* scores;                  // [R, nsp]
-  uint32_t* hist;                 // [R, kBins + 4]: histogram, then sel count, cand count
-  int32_t* sel;                   // [R, k]
-  unsigned long long* cand;       // [R, nsp]: 53-bit candidate keys (see cand_key)
+  uint32_t* hist;                 // [R, kBins + 4]: histogram of the top score-key bits
+  unsigned long long* comb;       // [R, nsp]: kept entries per chunk (decode) / candidates (prefill)
+  uint2* counts;                  // [R, nchunk]: per decode chunk (kept, above the threshold bin)
   int64_t nsp;
+  int nchunk;
 };
 
-Ws carve(void* ws, int R, int64_t n_cap, int k) {
+inline int64_t n_chunks(int64_t n_cap) { return (n_cap + kFilterChunk - 1) / kFilterChunk; }
+
+Ws carve(void* ws, int R, int64_t n_cap) {
   Ws w;
   w.nsp = (n_cap + 63) & ~(int64_t)63;
+  w.nchunk = (int)n_chunks(n_cap);
   char* p = static_cast<char*>(ws);
   w.scores = reinterpret_cast<float*>(p);
   p += al256((size_t)R * w.nsp * 4);
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)R * (kBins + 4) * 4);
-  w.sel = reinterpret_cast<int32_t*>(p);
-  p += al256((size_t)R * k * 4);
-  w.cand = reinterpret_cast<unsigned long long*>(p);
+  w.comb = reinterpret_cast<unsigned long long*>(p);
+  p += al256((size_t)R * w.nsp * 8);
+  w.counts = reinterpret_cast<uint2*>(p);
   return w;
 }
 
@@ -429,27 +433,45 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
 }
 
 // ------------------------------------------------------------------------------------ selection
+// Block-wide exclusive prefix sum over the 256 threads; *total receives the sum.  s_w: 4 words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_w, uint32_t* total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_w[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / kWave; ++w) {
+    const uint32_t x = s_w[w];
+    base += w < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();                                // s_w may be reused
+  *total = tot;
+  return base + incl - v;
+}
+
 // Threshold bin from a complete 2048-bin histogram: the bin T holding the k-th largest score and
-// the number of scores in bins above it.  256 threads, 8 bins each, suffix scan across threads.
-__device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* scratch) {
+// the number of scores in bins above it.  256 threads, 8 bins each; T stays as initialised (-1: keep
+// everything) when the histogram holds fewer than k scores.
+__device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* s_w) {
   const int tid = threadIdx.x;
-  uint32_t loc[8];
+  const uint4 a = *reinterpret_cast<const uint4*>(h + tid * 8);
+  const uint4 b = *reinterpret_cast<const uint4*>(h + tid * 8 + 4);
+  const uint32_t loc[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t sum = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { loc[j] = h[tid * 8 + j]; sum += loc[j]; }
-  // exclusive suffix sum over threads (higher thread index = higher bins = counted first)
-  scratch[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    uint32_t v = tid + off < kSelThreads ? scratch[tid + off] : 0u;
-    __syncthreads();
-    scratch[tid] += v;
-    __syncthreads();
-  }
-  const uint32_t incl = scratch[tid];           // bins >= 8*tid
-  const uint32_t excl = incl - sum;             // bins >= 8*(tid+1)
-  if (excl < (uint32_t)k && incl >= (uint32_t)k) {
-    uint32_t cum = excl;
+  for (int j = 0; j < 8; ++j) sum += loc[j];
+  uint32_t total;
+  const uint32_t below = block_excl_scan(sum, s_w, &total);   // bins under this thread's range
+  const uint32_t higher = total - below - sum;                 // bins above it
+  if (higher < (uint32_t)k && higher + sum >= (uint32_t)k) {
+    uint32_t cum = higher;
     for (int j = 7; j >= 0; --j) {
       if (cum + loc[j] >= (uint32_t)k) { *T_out = tid * 8 + j; *above_out = (int)cum; break; }
       cum += loc[j];
@@ -463,77 +485,62 @@ __device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_
 __device__ __forceinline__ unsigned long long cand_key(uint32_t key32, int32_t s) {
   return ((unsigned long long)(key32 & 0x1FFFFFu) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)s);
 }
+constexpr unsigned long long kAbove = 1ull << 63;   // kept entry from a bin above the threshold bin
 
-// Decode filter: many workgroups per row.  Entries of bins above the threshold bin go to the result
-// list, those of the threshold bin (with their full keys) to the candidate list; one global
-// reservation per list per workgroup.
+// Decode filter: one workgroup per chunk of kFilterChunk entries of a row.  The entries whose bin is
+// above the threshold bin or equal to it are written, in index order, at the start of the chunk's
+// own region of the row's list (value: above flag | 53-bit key), with the chunk's counts.  No
+// atomics: the order of the output does not depend on scheduling.
 __global__ void __launch_bounds__(kSelThreads)
-topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist, int32_t* __restrict__ sel,
-                   unsigned long long* __restrict__ cand, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
-                   int64_t n_cap, int k) {
-  __shared__ uint32_t scratch[kSelThreads];
-  __shared__ uint32_t s_cnt[2][kSelThreads / kWave];
-  __shared__ uint32_t s_base[2];
+topk_filter_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+                   unsigned long long* __restrict__ comb, uint2* __restrict__ counts, int64_t nsp, int nchunk,
+                   const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k) {
+  __shared__ uint32_t s_w[kSelThreads / kWave];
   __shared__ int sT, sAbove;
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid / kWave;
   const int64_t r = blockIdx.y;
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
   const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
-  if (c0 >= nv) return;
-  uint32_t* h = hist + r * (kBins + 4);
+  if (c0 >= nv) return;                                      // uniform
+  constexpr int kPer = kFilterChunk / kSelThreads;           // 16 consecutive entries per thread
+  const int64_t e0 = c0 + (int64_t)kPer * tid;
   const float* srow = scores + r * nsp;
-  int64_t c1 = c0 + kFilterChunk;
-  if (c1 > nv) c1 = nv;
-  constexpr int kPer = kFilterChunk / kSelThreads;
+  const int64_t q4max = (nv - 1) >> 2;                       // last readable float4 (nsp is a multiple of 64)
   uint32_t keys[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t e = c0 + j * kSelThreads + tid;
-    keys[j] = float_key(srow[e < c1 ? e : c1 - 1]);
+  for (int q = 0; q < kPer / 4; ++q) {                       // clamped, unconditional loads
+    const int64_t q4 = (e0 >> 2) + q;
+    const float4 x = *reinterpret_cast<const float4*>(srow + 4 * (q4 < q4max ? q4 : q4max));
+    keys[4 * q + 0] = float_key(x.x);
+    keys[4 * q + 1] = float_key(x.y);
+    keys[4 * q + 2] = float_key(x.z);
+    keys[4 * q + 3] = float_key(x.w);
   }
-  int T = -1;
-  if (nv > k) {
-    if (tid == 0) { sT = kBins - 1; sAbove = 0; }
-    __syncthreads();
-    find_threshold(h, k, &sT, &sAbove, scratch);
-    T = sT;
-  }
-  uint64_t msel[kPer], mcand[kPer];
-  uint32_t nsel_w = 0, ncand_w = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t e = c0 + j * kSelThreads + tid;
-    const bool valid = e < c1;
-    const int bin = (int)(keys[j] >> kBinShift);
-    msel[j] = __ballot(valid && bin > T);
-    mcand[j] = __ballot(valid && T >= 0 && bin == T);
-    nsel_w += __popcll(msel[j]);
-    ncand_w += __popcll(mcand[j]);
-  }
-  if (lane == 0) { s_cnt[0][wave] = nsel_w; s_cnt[1][wave] = ncand_w; }
+  if (tid == 0) { sT = -1; sAbove = 0; }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t ts = 0, tc = 0;
-    for (int w = 0; w < kSelThreads / kWave; ++w) { ts += s_cnt[0][w]; tc += s_cnt[1][w]; }
-    s_base[0] = ts ? atomicAdd(h + kBins + 0, ts) : 0u;
-    s_base[1] = tc ? atomicAdd(h + kBins + 1, tc) : 0u;
-  }
-  __syncthreads();
-  uint32_t bs = s_base[0], bc = s_base[1];
-  for (int w = 0; w < wave; ++w) { bs += s_cnt[0][w]; bc += s_cnt[1][w]; }
-  const uint64_t below = (1ull << lane) - 1ull;
-  int32_t* sl = sel + r * k;
-  unsigned long long* cl = cand + r * nsp;
+  if (nv > k) find_threshold(hist + r * (kBins + 4), k, &sT, &sAbove, s_w);
+  const int T = sT;
+  uint32_t keep = 0, above = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int32_t e = (int32_t)(c0 + j * kSelThreads + tid);
-    if ((msel[j] >> lane) & 1ull) sl[bs + __popcll(msel[j] & below)] = e;
-    if ((mcand[j] >> lane) & 1ull) cl[bc + __popcll(mcand[j] & below)] = cand_key(keys[j], e);
-    bs += __popcll(msel[j]);
-    bc += __popcll(mcand[j]);
+  for (int i = 0; i < kPer; ++i) {
+    const bool valid = e0 + i < nv;
+    const int bin = (int)(keys[i] >> kBinShift);
+    keep |= (valid && bin >= T ? 1u : 0u) << i;
+    above |= (valid && bin > T ? 1u : 0u) << i;
   }
+  const uint32_t packed = (uint32_t)__popc(keep) | ((uint32_t)__popc(above) << 16);   // <= 4096 each
+  uint32_t total;
+  const uint32_t base = block_excl_scan(packed, s_w, &total);
+  uint32_t pos = base & 0xFFFFu;
+  unsigned long long* out = comb + r * nsp + c0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if ((keep >> i) & 1u) {
+      out[pos] = ((above >> i) & 1u ? kAbove : 0ull) | cand_key(keys[i], (int32_t)(e0 + i));
+      ++pos;
+    }
+  }
+  if (tid == 0) counts[r * nchunk + blockIdx.x] = make_uint2(total & 0xFFFFu, total >> 16);
 }
 
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
@@ -744,40 +751,212 @@ __device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv,
   }
 }
 
-// Decode final: one workgroup per row.
+// Decode final: one workgroup per row.  The kept entries of the row's chunks, concatenated in chunk
+// order, are the row's candidates in index order; the digit passes find the exact key of the k-th
+// winner among the threshold-bin entries, and the winners are written in that same order, so the
+// result is ascending without a sort.  Up to kFinalCache kept entries are staged in LDS; beyond that
+// every pass reads the list from global memory (each wave walks whole chunks).
+constexpr int kFinalCache = 4096;
+constexpr int kMaxDecodeChunks = 2048;       // rows up to 8M entries take this path
+
 __global__ void __launch_bounds__(kSelThreads)
-topk_final_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ hist,
-                  const int32_t* __restrict__ sel, const unsigned long long* __restrict__ cand, int64_t nsp,
-                  const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
-                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
-  __shared__ SelShared s;
-  __shared__ int32_t list[kMaxTopk];
+topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __restrict__ counts, int64_t nsp,
+                  int nchunk, const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
+                  const float* __restrict__ scores, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  __shared__ unsigned long long s_list[kFinalCache];
+  __shared__ uint32_t s_keep[kMaxDecodeChunks];   // kept entries per chunk
+  __shared__ uint32_t s_pos[kMaxDecodeChunks];    // their offset in the concatenated list / in the output
+  __shared__ uint32_t s_h[256];
+  __shared__ uint32_t s_w[kSelThreads / kWave];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_remaining, s_done, s_shift;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  constexpr int kWaves = kSelThreads / kWave;
   const int64_t r = blockIdx.x;
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
-  const uint32_t* h = hist + r * (kBins + 4);
-  const int nsel = (int)h[kBins + 0];
-  const int ncand = (int)h[kBins + 1];
+  int32_t* out = topk_idx + r * k;
+  float* out_s = topk_score ? topk_score + r * k : nullptr;
   const float* srow = scores + r * nsp;
-  {
-    constexpr int kPer = kMaxTopk / kSelThreads;
-    int32_t v[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kSelThreads;
-      v[u] = sel[r * k + (i < nsel ? i : 0)];
+  if (nv <= k) {                                    // every visible entry, ascending
+    for (int64_t i = tid; i < k; i += kSelThreads) {
+      out[i] = i < nv ? (int32_t)i : -1;
+      if (out_s) out_s[i] = i < nv ? srow[i] : -INFINITY;
     }
+    return;
+  }
+  const int nch = (int)((nv + kFilterChunk - 1) / kFilterChunk);
+  const unsigned long long* lrow = comb + r * nsp;
+
+  // ---- per-chunk counts, their prefix (contiguous chunk ranges per thread) ----
+  constexpr int kPerT = kMaxDecodeChunks / kSelThreads;   // 8
+  uint32_t kc[kPerT];
+  uint32_t ksum = 0, asum = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kSelThreads;
-      if (i < nsel) list[i] = v[u];
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = tid * kPerT + u;
+    const uint2 cc = counts[r * nchunk + (c < nch ? c : 0)];
+    kc[u] = c < nch ? cc.x : 0u;
+    ksum += kc[u];
+    asum += c < nch ? cc.y : 0u;
+  }
+  uint32_t total_keep, total_above;
+  uint32_t off = block_excl_scan(ksum, s_w, &total_keep);
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = tid * kPerT + u;
+    s_keep[c] = kc[u];
+    s_pos[c] = off;
+    off += kc[u];
+  }
+  block_excl_scan(asum, s_w, &total_above);       // (also orders the s_keep / s_pos writes)
+  const bool cached = total_keep <= (uint32_t)kFinalCache;
+
+  // ---- stage the list in LDS: wave w copies chunks w, w + 4, ..., eight chunks' loads in flight ----
+  if (cached) {
+    for (int cb = wave; cb < nch; cb += kWaves * 8) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = cb + kWaves * u;
+        const int n = c < nch ? (int)s_keep[c] : 0;
+        v[u] = lrow[(int64_t)(c < nch ? c : 0) * kFilterChunk + (lane < n ? lane : 0)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = cb + kWaves * u;
+        if (c < nch && lane < (int)s_keep[c]) s_list[s_pos[c] + lane] = v[u];
+      }
+    }
+    for (int c = wave; c < nch; c += kWaves)        // chunks with more than 64 kept entries (rare)
+      for (int j = kWave + lane; j < (int)s_keep[c]; j += kWave) s_list[s_pos[c] + j] = lrow[(int64_t)c * kFilterChunk + j];
+  }
+  if (tid == 0) { s_remaining = k - (int)total_above; s_done = 0; s_prefix = 0ull; s_shift = 0; }
+  __syncthreads();
+
+  // visit every kept entry once: flat over the LDS copy, or chunk by chunk from global memory
+  auto for_each = [&](auto&& f) {
+    if (cached) {
+      for (int i = tid; i < (int)total_keep; i += kSelThreads) f(s_list[i]);
+    } else {
+      for (int c = wave; c < nch; c += kWaves)
+        for (int j = lane; j < (int)s_keep[c]; j += kWave) f(lrow[(int64_t)c * kFilterChunk + j]);
+    }
+  };
+
+  // ---- digit passes over the threshold-bin entries' 53-bit keys (8 bits at a time, top first) ----
+  int shift = 53;
+  for (int pass = 0; pass < 7; ++pass) {
+    const int width = shift >= 8 ? 8 : shift;
+    shift -= width;
+    s_h[tid] = 0u;
+    __syncthreads();
+    const unsigned long long pre = s_prefix;
+    const uint32_t dmask = (1u << width) - 1u;
+    for_each([&](unsigned long long e) {
+      if (!(e & kAbove) && (e >> (shift + width)) == pre) atomicAdd(&s_h[(uint32_t)(e >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    if (tid < kWave) {
+      // lane j covers digits 255-4j .. 252-4j (top first)
+      uint32_t c[4];
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { c[u] = s_h[255 - 4 * tid - u]; lsum += c[u]; }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, kWave);
+        if (tid >= o) incl += v;
+      }
+      const uint32_t rem = (uint32_t)s_remaining;
+      const uint64_t hit = __ballot(incl >= rem);
+      const int first = __ffsll((unsigned long long)hit) - 1;
+      if (tid == first) {
+        uint32_t cum = incl - lsum;
+        for (int u = 0; u < 4; ++u) {
+          if (cum + c[u] >= rem) {
+            const uint32_t d = 255u - 4u * tid - u;
+            const uint32_t left = rem - cum;
+            s_remaining = (int)left;
+            s_prefix = (s_prefix << width) | d;
+            if (c[u] == left || shift == 0) { s_done = 1; s_shift = shift; }
+            break;
+          }
+          cum += c[u];
+        }
+      }
+    }
+    __syncthreads();
+    if (s_done) break;
+  }
+  const unsigned long long thr = s_prefix;
+  const int ts = s_shift;
+  auto wins = [&](unsigned long long e) { return (e & kAbove) || (e >> ts) >= thr; };
+  auto index_of = [](unsigned long long e) { return (int32_t)(0xFFFFFFFFu - (uint32_t)e); };
+
+  // ---- winners in list order = ascending index ----
+  if (cached) {
+    constexpr int kSeg = kFinalCache / kSelThreads;         // 16 consecutive list entries per thread
+    const int i0 = tid * kSeg;
+    uint32_t win = 0;
+#pragma unroll
+    for (int u = 0; u < kSeg; ++u)
+      if (i0 + u < (int)total_keep && wins(s_list[i0 + u])) win |= 1u << u;
+    uint32_t tot;
+    uint32_t pos = block_excl_scan((uint32_t)__popc(win), s_w, &tot);
+#pragma unroll
+    for (int u = 0; u < kSeg; ++u) {
+      if (((win >> u) & 1u) && pos < (uint32_t)k) {   // exactly k winners; the bound is a guard
+        const int32_t e = index_of(s_list[i0 + u]);
+        out[pos] = e;
+        if (out_s) out_s[pos] = srow[e];
+        ++pos;
+      }
+    }
+  } else {
+    // winners per chunk, their output offsets, then each wave writes its chunks in order
+    for (int c = wave; c < nch; c += kWaves) {
+      uint32_t n = 0;
+      for (int j = lane; j < (int)s_keep[c]; j += kWave) n += wins(lrow[(int64_t)c * kFilterChunk + j]) ? 1u : 0u;
+      n = (uint32_t)wave_sum((float)n);                     // exact: counts <= 4096
+      if (lane == 0) s_keep[c] = n;
+    }
+    __syncthreads();
+    uint32_t wsum = 0;
+    uint32_t wc[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      const int c = tid * kPerT + u;
+      wc[u] = c < nch ? s_keep[c] : 0u;
+      wsum += wc[u];
+    }
+    uint32_t tot;
+    uint32_t o2 = block_excl_scan(wsum, s_w, &tot);
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) { s_pos[tid * kPerT + u] = o2; o2 += wc[u]; }
+    __syncthreads();
+    for (int c = wave; c < nch; c += kWaves) {
+      uint32_t base = s_pos[c];
+      for (int j0 = 0; j0 < kFilterChunk; j0 += kWave) {
+        const int j = j0 + lane;
+        // the chunk's list length is the kept count written by the filter, still in counts
+        const int nk = (int)counts[r * nchunk + c].x;
+        if (j0 >= nk) break;
+        const unsigned long long e = lrow[(int64_t)c * kFilterChunk + (j < nk ? j : 0)];
+        const bool wv = j < nk && wins(e);
+        const uint64_t bal = __ballot(wv);
+        const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (wv && p < (uint32_t)k) {
+          const int32_t ix = index_of(e);
+          out[p] = ix;
+          if (out_s) out_s[p] = srow[ix];
+        }
+        base += (uint32_t)__popcll(bal);
+      }
     }
   }
-  if (threadIdx.x == 0) s.nsel = nsel;
-  __syncthreads();
-  if (nv > k) refine_candidates(cand + r * nsp, ncand, k - nsel, list, s);
-  __syncthreads();
-  const int n = s.nsel < k ? s.nsel : k;
-  sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
 }
 
 // Prefill: one workgroup per row does histogram, filter, refine, sort.
@@ -787,7 +966,7 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelShared s;
   __shared__ int32_t list[kMaxTopk];
-  __shared__ uint32_t h[kBins];
+  __shared__ __align__(16) uint32_t h[kBins];
   __shared__ int sT, sAbove, sCand;
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -865,31 +1044,33 @@ void dispatch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
 }  // namespace
 
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
+  (void)k;
   const int64_t R = (int64_t)B * Tq;
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
-  return al256((size_t)R * nsp * 4) + al256((size_t)R * (kBins + 4) * 4) + al256((size_t)R * k * 4) +
-         al256((size_t)R * nsp * 8);
+  return al256((size_t)R * nsp * 4) + al256((size_t)R * (kBins + 4) * 4) + al256((size_t)R * nsp * 8) +
+         al256((size_t)R * n_chunks(n_cap) * 8);
 }
 
 int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   const int R = a.B * a.Tq;
-  Ws w = carve(a.ws, R, a.n_cap, a.k);
-  // Few rows: spread every row over many workgroups (decode).  Many rows: row-per-workgroup.
-  const bool decode = R < 64;
+  Ws w = carve(a.ws, R, a.n_cap);
+  // Few rows: spread every row over many workgroups (decode).  Many rows, or rows longer than the
+  // decode selection stages: row-per-workgroup.
+  const bool decode = R < 64 && w.nchunk <= kMaxDecodeChunks;
   if (decode) {
     const int64_t n = (int64_t)R * (kBins + 4);
     LCS_LAUNCH("topk_clear_kernel", clear_u32_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
                dim3(256), 0, st, w.hist, n);
     dispatch_score<1>(a, w, st);
-    dim3 gf((unsigned)((a.n_cap + kFilterChunk - 1) / kFilterChunk), (unsigned)R);
-    LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.sel,
-               w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k);
-    LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
-               w.hist, w.sel, w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
+    dim3 gf((unsigned)w.nchunk, (unsigned)R);
+    LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.comb,
+               w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k);
+    LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
+               w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
   } else {
     dispatch_score<4>(a, w, st);
     LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
-               w.cand, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
+               w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
