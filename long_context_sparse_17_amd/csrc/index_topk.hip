@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kBins = 2048;                 // top 11 bits of the score key
 constexpr int kBinShift = 21;
+constexpr int kHistRow = 2 * kBins + 4;     // per row: level-1 bins, level-2 bins (candidates' next 11 bits), spare
 constexpr int kScoreChunk = 1024;           // entries per scoring workgroup
 constexpr int kFilterChunk = 4096;          // entries per filter workgroup
 constexpr int kSelThreads = 256;
@@ -39,7 +40,7 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Ws {
   float* scores;                  // [R, nsp]
-  uint32_t* hist;                 // [R, kBins + 4]: histogram of the top score-key bits
+  uint32_t* hist;                 // [R, kHistRow]: histograms of the top score-key bits, then of the next 11
   unsigned long long* comb;       // [R, nsp]: kept entries per chunk (decode) / candidates (prefill)
   uint2* counts;                  // [R, nchunk]: per decode chunk (kept, above the threshold bin)
   int64_t nsp;
@@ -56,7 +57,7 @@ Ws carve(void* ws, int R, int64_t n_cap) {
   w.scores = reinterpret_cast<float*>(p);
   p += al256((size_t)R * w.nsp * 4);
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)R * (kBins + 4) * 4);
+  p += al256((size_t)R * kHistRow * 4);
   w.comb = reinterpret_cast<unsigned long long*>(p);
   p += al256((size_t)R * w.nsp * 8);
   w.counts = reinterpret_cast<uint2*>(p);
@@ -248,7 +249,7 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
 
   if (HIST) {
     __syncthreads();
-    uint32_t* gh = hist + rowq[0] * (kBins + 4);
+    uint32_t* gh = hist + rowq[0] * kHistRow;
     for (int i = threadIdx.x; i < kBins; i += 256) {
       const uint32_t v = lhist[i];
       if (v) atomicAdd(gh + i, v);
@@ -425,7 +426,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     }
   }
   __syncthreads();
-  uint32_t* gh = hist + r * (kBins + 4);
+  uint32_t* gh = hist + r * kHistRow;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     const uint32_t v = lhist[i];
     if (v) atomicAdd(gh + i, v);
@@ -459,11 +460,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_w, u
 // Threshold bin from a complete 2048-bin histogram: the bin T holding the k-th largest score and
 // the number of scores in bins above it.  256 threads, 8 bins each; T stays as initialised (-1: keep
 // everything) when the histogram holds fewer than k scores.
-__device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* s_w) {
+// (the thread's 8 bins, tid*8 .. tid*8+7, already loaded)
+__device__ __forceinline__ void find_threshold_bins(const uint32_t (&loc)[8], int k, int* T_out, int* above_out,
+                                                    uint32_t* s_w) {
   const int tid = threadIdx.x;
-  const uint4 a = *reinterpret_cast<const uint4*>(h + tid * 8);
-  const uint4 b = *reinterpret_cast<const uint4*>(h + tid * 8 + 4);
-  const uint32_t loc[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t sum = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) sum += loc[j];
@@ -480,6 +480,13 @@ __device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_
   __syncthreads();
 }
 
+__device__ __forceinline__ void find_threshold(const uint32_t* h, int k, int* T_out, int* above_out, uint32_t* s_w) {
+  const uint4 a = *reinterpret_cast<const uint4*>(h + threadIdx.x * 8);
+  const uint4 b = *reinterpret_cast<const uint4*>(h + threadIdx.x * 8 + 4);
+  const uint32_t loc[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  find_threshold_bins(loc, k, T_out, above_out, s_w);
+}
+
 // 53-bit candidate key: the 21 score-key bits below the bin, then the complemented entry index, so
 // that larger score wins and, among equal scores, the lower index wins; every key is distinct.
 __device__ __forceinline__ unsigned long long cand_key(uint32_t key32, int32_t s) {
@@ -487,12 +494,283 @@ __device__ __forceinline__ unsigned long long cand_key(uint32_t key32, int32_t s
 }
 constexpr unsigned long long kAbove = 1ull << 63;   // kept entry from a bin above the threshold bin
 
+// Decode selection, per row.  The kept entries of the row's chunks, concatenated in chunk
+// order, are the row's candidates in index order.  The filter's second histogram (the next 11 key
+// bits of the threshold-bin entries) usually pins the k-th winner's key; otherwise digit passes over
+// the remaining key bits finish the job.  The winners are written in list order, so the result is
+// ascending without a sort.  Up to kFinalCache kept entries are staged in LDS (thread t owns list
+// positions 16t .. 16t+15, stored transposed so that both the staging writes and the per-thread
+// reads are free of bank conflicts); beyond that every pass reads the list from global memory.
+constexpr int kFinalCache = 4096;
+constexpr int kFinalSeg = kFinalCache / kSelThreads;        // 16 list positions per thread
+constexpr int kFinalStride = kSelThreads + 1;               // LDS row stride of the transposed list
+constexpr int kMaxDecodeChunks = 2048;                      // rows up to 8M entries take this path
+
+__device__ __forceinline__ int final_slot(int i) { return (i % kFinalSeg) * kFinalStride + i / kFinalSeg; }
+
+struct FinalShared {
+  unsigned long long list[kFinalSeg * kFinalStride];
+  uint32_t keep[kMaxDecodeChunks];   // kept entries per chunk
+  uint32_t pos[kMaxDecodeChunks];    // their offset in the concatenated list / in the output
+  uint32_t h[256];
+  unsigned long long prefix;
+  int remaining, done, shift, T2, above2;
+};
+
+// Row r's selection (nv visible entries).
+__device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int64_t r, int64_t nv,
+                                             const unsigned long long* __restrict__ comb,
+                                             const uint2* __restrict__ counts, const uint32_t* __restrict__ hist,
+                                             int64_t nsp, int nchunk, int k, const float* __restrict__ scores,
+                                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  auto& s_list = sh.list;
+  auto& s_keep = sh.keep;
+  auto& s_pos = sh.pos;
+  auto& s_h = sh.h;
+  auto& s_prefix = sh.prefix;
+  auto& s_remaining = sh.remaining;
+  auto& s_done = sh.done;
+  auto& s_shift = sh.shift;
+  auto& s_T2 = sh.T2;
+  auto& s_above2 = sh.above2;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  constexpr int kWaves = kSelThreads / kWave;
+  int32_t* out = topk_idx + r * k;
+  float* out_s = topk_score ? topk_score + r * k : nullptr;
+  const float* srow = scores + r * nsp;
+  if (nv <= k) {                                    // every visible entry, ascending
+    for (int64_t i = tid; i < k; i += kSelThreads) {
+      out[i] = i < nv ? (int32_t)i : -1;
+      if (out_s) out_s[i] = i < nv ? srow[i] : -INFINITY;
+    }
+    return;
+  }
+  const int nch = (int)((nv + kFilterChunk - 1) / kFilterChunk);
+  const unsigned long long* lrow = comb + r * nsp;
+
+  // ---- one round trip: the per-chunk counts and, speculatively, the first 64 list entries of each
+  //      of the first 64 chunks (wave w: chunks w, w + 4, ...), which usually hold the whole list ----
+  constexpr int kHeadChunks = kWaves * 16;
+  const bool heads = nch <= kHeadChunks;
+  unsigned long long vh[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = min(wave + kWaves * u, nch - 1);
+    vh[u] = lrow[min((int64_t)c * kFilterChunk + lane, nv - 1)];
+  }
+  const uint32_t* h2 = hist + r * kHistRow + kBins;
+  const uint4 h2a = *reinterpret_cast<const uint4*>(h2 + tid * 8);
+  const uint4 h2b = *reinterpret_cast<const uint4*>(h2 + tid * 8 + 4);
+  constexpr int kPerT = kMaxDecodeChunks / kSelThreads;   // 8
+  uint32_t kc[kPerT];
+  uint32_t ksum = 0, asum = 0;
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = tid * kPerT + u;
+    const uint2 cc = counts[r * nchunk + (c < nch ? c : 0)];
+    kc[u] = c < nch ? cc.x : 0u;
+    ksum += kc[u];
+    asum += c < nch ? cc.y : 0u;
+  }
+  uint32_t total_keep, total_above;
+  uint32_t off = block_excl_scan(ksum, s_w, &total_keep);
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = tid * kPerT + u;
+    s_keep[c] = kc[u];
+    s_pos[c] = off;
+    off += kc[u];
+  }
+  block_excl_scan(asum, s_w, &total_above);       // (its barriers also publish s_keep / s_pos)
+  const int need = k - (int)total_above;          // winners among the threshold-bin entries (>= 1)
+  const bool cached = total_keep <= (uint32_t)kFinalCache;
+
+  // ---- stage the list: wave w copies chunks w, w + 4, ...; sixteen chunks' loads in flight ----
+  if (cached && heads) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = wave + kWaves * u;
+      if (c < nch && lane < (int)s_keep[c]) s_list[final_slot((int)s_pos[c] + lane)] = vh[u];
+    }
+  }
+  if (cached && !heads) {
+    for (int cb = wave; cb < nch; cb += kWaves * 16) {
+      unsigned long long v[16];
+      int n[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {               // in-range chunk, unconditional load (no branches)
+        const int c = min(cb + kWaves * u, nch - 1);
+        n[u] = (int)s_keep[c];
+        v[u] = lrow[(int64_t)c * kFilterChunk + min(lane, max(n[u] - 1, 0))];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = cb + kWaves * u;
+        if (c < nch && lane < n[u]) s_list[final_slot((int)s_pos[c] + lane)] = v[u];
+      }
+    }
+  }
+  if (cached) {
+    for (int c = wave; c < nch; c += kWaves)        // chunks with more than 64 kept entries
+      for (int j = kWave + lane; j < (int)s_keep[c]; j += kWave)
+        s_list[final_slot((int)s_pos[c] + j)] = lrow[(int64_t)c * kFilterChunk + j];
+  }
+
+  // ---- level-2 threshold: the bin of the next 11 key bits that holds the need-th winner ----
+  if (tid == 0) { s_T2 = 0; s_above2 = 0; }
+  __syncthreads();
+  {
+    const uint32_t loc[8] = {h2a.x, h2a.y, h2a.z, h2a.w, h2b.x, h2b.y, h2b.z, h2b.w};
+    find_threshold_bins(loc, need, &s_T2, &s_above2, s_w);
+    if (tid == s_T2 / 8) {                          // the thread holding bin T2
+      const int rem = need - s_above2;
+      s_remaining = rem;
+      s_prefix = (unsigned long long)s_T2;
+      s_shift = 42;                                 // candidates' keys >> 42 = their level-2 bin
+      s_done = loc[s_T2 % 8] == (uint32_t)rem ? 1 : 0;
+    }
+  }
+  __syncthreads();
+
+  // visit every kept entry once: the LDS copy (thread t: positions 16t..16t+15), or chunk by chunk
+  // from global memory
+  auto for_each = [&](auto&& f) {
+    if (cached) {
+#pragma unroll
+      for (int u = 0; u < kFinalSeg; ++u)
+        if (tid * kFinalSeg + u < (int)total_keep) f(s_list[u * kFinalStride + tid]);
+    } else {
+      for (int c = wave; c < nch; c += kWaves)
+        for (int j = lane; j < (int)s_keep[c]; j += kWave) f(lrow[(int64_t)c * kFilterChunk + j]);
+    }
+  };
+
+  // ---- digit passes over the rest of the key (10 score bits, then the complemented index) ----
+  if (!s_done) {
+    int shift = 42;
+    for (int pass = 0; pass < 6; ++pass) {
+      const int width = shift >= 8 ? 8 : shift;
+      shift -= width;
+      s_h[tid] = 0u;
+      __syncthreads();
+      const unsigned long long pre = s_prefix;
+      const uint32_t dmask = (1u << width) - 1u;
+      for_each([&](unsigned long long e) {
+        if (!(e & kAbove) && (e >> (shift + width)) == pre) atomicAdd(&s_h[(uint32_t)(e >> shift) & dmask], 1u);
+      });
+      __syncthreads();
+      if (tid < kWave) {
+        // lane j covers digits 255-4j .. 252-4j (top first)
+        uint32_t c[4];
+        uint32_t lsum = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { c[u] = s_h[255 - 4 * tid - u]; lsum += c[u]; }
+        uint32_t incl = lsum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t v = __shfl_up(incl, o, kWave);
+          if (tid >= o) incl += v;
+        }
+        const uint32_t rem = (uint32_t)s_remaining;
+        const uint64_t hit = __ballot(incl >= rem);
+        const int first = __ffsll((unsigned long long)hit) - 1;
+        if (tid == first) {
+          uint32_t cum = incl - lsum;
+          for (int u = 0; u < 4; ++u) {
+            if (cum + c[u] >= rem) {
+              const uint32_t d = 255u - 4u * tid - u;
+              const uint32_t left = rem - cum;
+              s_remaining = (int)left;
+              s_prefix = (s_prefix << width) | d;
+              s_shift = shift;
+              if (c[u] == left || shift == 0) s_done = 1;
+              break;
+            }
+            cum += c[u];
+          }
+        }
+      }
+      __syncthreads();
+      if (s_done) break;
+    }
+  }
+  const unsigned long long thr = s_prefix;
+  const int ts = s_shift;
+  auto wins = [&](unsigned long long e) { return (e & kAbove) || (e >> ts) >= thr; };
+  auto index_of = [](unsigned long long e) { return (int32_t)(0xFFFFFFFFu - (uint32_t)e); };
+
+  // ---- winners in list order = ascending index ----
+  if (cached) {
+    unsigned long long ev[kFinalSeg];
+    uint32_t win = 0;
+#pragma unroll
+    for (int u = 0; u < kFinalSeg; ++u) {
+      ev[u] = s_list[u * kFinalStride + tid];
+      if (tid * kFinalSeg + u < (int)total_keep && wins(ev[u])) win |= 1u << u;
+    }
+    uint32_t tot;
+    uint32_t pos = block_excl_scan((uint32_t)__popc(win), s_w, &tot);
+#pragma unroll
+    for (int u = 0; u < kFinalSeg; ++u) {
+      if (((win >> u) & 1u) && pos < (uint32_t)k) {   // exactly k winners; the bound is a guard
+        const int32_t e = index_of(ev[u]);
+        out[pos] = e;
+        if (out_s) out_s[pos] = srow[e];
+        ++pos;
+      }
+    }
+  } else {
+    // winners per chunk, their output offsets, then each wave writes its chunks in order
+    for (int c = wave; c < nch; c += kWaves) {
+      uint32_t n = 0;
+      for (int j = lane; j < (int)s_keep[c]; j += kWave) n += wins(lrow[(int64_t)c * kFilterChunk + j]) ? 1u : 0u;
+      n = (uint32_t)wave_sum((float)n);                     // exact: counts <= 4096
+      if (lane == 0) s_keep[c] = n;
+    }
+    __syncthreads();
+    uint32_t wsum = 0;
+    uint32_t wc[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      const int c = tid * kPerT + u;
+      wc[u] = c < nch ? s_keep[c] : 0u;
+      wsum += wc[u];
+    }
+    uint32_t tot;
+    uint32_t o2 = block_excl_scan(wsum, s_w, &tot);
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) { s_pos[tid * kPerT + u] = o2; o2 += wc[u]; }
+    __syncthreads();
+    for (int c = wave; c < nch; c += kWaves) {
+      uint32_t base = s_pos[c];
+      const int nk = (int)counts[r * nchunk + c].x;        // the chunk's list length
+      for (int j0 = 0; j0 < nk; j0 += kWave) {
+        const int j = j0 + lane;
+        const unsigned long long e = lrow[(int64_t)c * kFilterChunk + (j < nk ? j : 0)];
+        const bool wv = j < nk && wins(e);
+        const uint64_t bal = __ballot(wv);
+        const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (wv && p < (uint32_t)k) {
+          const int32_t ix = index_of(e);
+          out[p] = ix;
+          if (out_s) out_s[p] = srow[ix];
+        }
+        base += (uint32_t)__popcll(bal);
+      }
+    }
+  }
+}
+
 // Decode filter: one workgroup per chunk of kFilterChunk entries of a row.  The entries whose bin is
 // above the threshold bin or equal to it are written, in index order, at the start of the chunk's
-// own region of the row's list (value: above flag | 53-bit key), with the chunk's counts.  No
-// atomics: the order of the output does not depend on scheduling.
+// own region of the row's list (value: above flag | 53-bit key), with the chunk's counts and the
+// second-level histogram of the threshold-bin entries.  The output order does not depend on
+// scheduling.  (Handing the selection to the last workgroup of a row would need device-scope fences,
+// i.e. an L2 write-back per workgroup, which costs far more than the kernel boundary.)
 __global__ void __launch_bounds__(kSelThreads)
-topk_filter_kernel(const float* __restrict__ scores, const uint32_t* __restrict__ hist,
+topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist,
                    unsigned long long* __restrict__ comb, uint2* __restrict__ counts, int64_t nsp, int nchunk,
                    const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k) {
   __shared__ uint32_t s_w[kSelThreads / kWave];
@@ -518,7 +796,7 @@ topk_filter_kernel(const float* __restrict__ scores, const uint32_t* __restrict_
   }
   if (tid == 0) { sT = -1; sAbove = 0; }
   __syncthreads();
-  if (nv > k) find_threshold(hist + r * (kBins + 4), k, &sT, &sAbove, s_w);
+  if (nv > k) find_threshold(hist + r * kHistRow, k, &sT, &sAbove, s_w);
   const int T = sT;
   uint32_t keep = 0, above = 0;
 #pragma unroll
@@ -533,14 +811,30 @@ topk_filter_kernel(const float* __restrict__ scores, const uint32_t* __restrict_
   const uint32_t base = block_excl_scan(packed, s_w, &total);
   uint32_t pos = base & 0xFFFFu;
   unsigned long long* out = comb + r * nsp + c0;
+  uint32_t* h2 = hist + r * kHistRow + kBins;   // level 2: candidates' next 11 bits
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if ((keep >> i) & 1u) {
-      out[pos] = ((above >> i) & 1u ? kAbove : 0ull) | cand_key(keys[i], (int32_t)(e0 + i));
+      const bool ab = (above >> i) & 1u;
+      out[pos] = (ab ? kAbove : 0ull) | cand_key(keys[i], (int32_t)(e0 + i));
+      if (!ab) atomicAdd(&h2[(keys[i] >> (kBinShift - 11)) & (kBins - 1)], 1u);
       ++pos;
     }
   }
   if (tid == 0) counts[r * nchunk + blockIdx.x] = make_uint2(total & 0xFFFFu, total >> 16);
+}
+
+// Decode final: one workgroup per row runs the selection above.
+__global__ void __launch_bounds__(kSelThreads)
+topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __restrict__ counts,
+                  const uint32_t* __restrict__ hist, int64_t nsp, int nchunk, const int64_t* __restrict__ q_pos,
+                  int m, int64_t n_cap, int k, const float* __restrict__ scores, int32_t* __restrict__ topk_idx,
+                  float* __restrict__ topk_score) {
+  __shared__ FinalShared sh;
+  __shared__ uint32_t s_w[kSelThreads / kWave];
+  const int64_t r = blockIdx.x;
+  final_select(sh, s_w, r, n_visible(q_pos, r, m, n_cap), comb, counts, hist, nsp, nchunk, k, scores, topk_idx,
+               topk_score);
 }
 
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
@@ -751,214 +1045,6 @@ __device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv,
   }
 }
 
-// Decode final: one workgroup per row.  The kept entries of the row's chunks, concatenated in chunk
-// order, are the row's candidates in index order; the digit passes find the exact key of the k-th
-// winner among the threshold-bin entries, and the winners are written in that same order, so the
-// result is ascending without a sort.  Up to kFinalCache kept entries are staged in LDS; beyond that
-// every pass reads the list from global memory (each wave walks whole chunks).
-constexpr int kFinalCache = 4096;
-constexpr int kMaxDecodeChunks = 2048;       // rows up to 8M entries take this path
-
-__global__ void __launch_bounds__(kSelThreads)
-topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __restrict__ counts, int64_t nsp,
-                  int nchunk, const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
-                  const float* __restrict__ scores, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
-  __shared__ unsigned long long s_list[kFinalCache];
-  __shared__ uint32_t s_keep[kMaxDecodeChunks];   // kept entries per chunk
-  __shared__ uint32_t s_pos[kMaxDecodeChunks];    // their offset in the concatenated list / in the output
-  __shared__ uint32_t s_h[256];
-  __shared__ uint32_t s_w[kSelThreads / kWave];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_remaining, s_done, s_shift;
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid / kWave;
-  constexpr int kWaves = kSelThreads / kWave;
-  const int64_t r = blockIdx.x;
-  const int64_t nv = n_visible(q_pos, r, m, n_cap);
-  int32_t* out = topk_idx + r * k;
-  float* out_s = topk_score ? topk_score + r * k : nullptr;
-  const float* srow = scores + r * nsp;
-  if (nv <= k) {                                    // every visible entry, ascending
-    for (int64_t i = tid; i < k; i += kSelThreads) {
-      out[i] = i < nv ? (int32_t)i : -1;
-      if (out_s) out_s[i] = i < nv ? srow[i] : -INFINITY;
-    }
-    return;
-  }
-  const int nch = (int)((nv + kFilterChunk - 1) / kFilterChunk);
-  const unsigned long long* lrow = comb + r * nsp;
-
-  // ---- per-chunk counts, their prefix (contiguous chunk ranges per thread) ----
-  constexpr int kPerT = kMaxDecodeChunks / kSelThreads;   // 8
-  uint32_t kc[kPerT];
-  uint32_t ksum = 0, asum = 0;
-#pragma unroll
-  for (int u = 0; u < kPerT; ++u) {
-    const int c = tid * kPerT + u;
-    const uint2 cc = counts[r * nchunk + (c < nch ? c : 0)];
-    kc[u] = c < nch ? cc.x : 0u;
-    ksum += kc[u];
-    asum += c < nch ? cc.y : 0u;
-  }
-  uint32_t total_keep, total_above;
-  uint32_t off = block_excl_scan(ksum, s_w, &total_keep);
-#pragma unroll
-  for (int u = 0; u < kPerT; ++u) {
-    const int c = tid * kPerT + u;
-    s_keep[c] = kc[u];
-    s_pos[c] = off;
-    off += kc[u];
-  }
-  block_excl_scan(asum, s_w, &total_above);       // (also orders the s_keep / s_pos writes)
-  const bool cached = total_keep <= (uint32_t)kFinalCache;
-
-  // ---- stage the list in LDS: wave w copies chunks w, w + 4, ..., eight chunks' loads in flight ----
-  if (cached) {
-    for (int cb = wave; cb < nch; cb += kWaves * 8) {
-      unsigned long long v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = cb + kWaves * u;
-        const int n = c < nch ? (int)s_keep[c] : 0;
-        v[u] = lrow[(int64_t)(c < nch ? c : 0) * kFilterChunk + (lane < n ? lane : 0)];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = cb + kWaves * u;
-        if (c < nch && lane < (int)s_keep[c]) s_list[s_pos[c] + lane] = v[u];
-      }
-    }
-    for (int c = wave; c < nch; c += kWaves)        // chunks with more than 64 kept entries (rare)
-      for (int j = kWave + lane; j < (int)s_keep[c]; j += kWave) s_list[s_pos[c] + j] = lrow[(int64_t)c * kFilterChunk + j];
-  }
-  if (tid == 0) { s_remaining = k - (int)total_above; s_done = 0; s_prefix = 0ull; s_shift = 0; }
-  __syncthreads();
-
-  // visit every kept entry once: flat over the LDS copy, or chunk by chunk from global memory
-  auto for_each = [&](auto&& f) {
-    if (cached) {
-      for (int i = tid; i < (int)total_keep; i += kSelThreads) f(s_list[i]);
-    } else {
-      for (int c = wave; c < nch; c += kWaves)
-        for (int j = lane; j < (int)s_keep[c]; j += kWave) f(lrow[(int64_t)c * kFilterChunk + j]);
-    }
-  };
-
-  // ---- digit passes over the threshold-bin entries' 53-bit keys (8 bits at a time, top first) ----
-  int shift = 53;
-  for (int pass = 0; pass < 7; ++pass) {
-    const int width = shift >= 8 ? 8 : shift;
-    shift -= width;
-    s_h[tid] = 0u;
-    __syncthreads();
-    const unsigned long long pre = s_prefix;
-    const uint32_t dmask = (1u << width) - 1u;
-    for_each([&](unsigned long long e) {
-      if (!(e & kAbove) && (e >> (shift + width)) == pre) atomicAdd(&s_h[(uint32_t)(e >> shift) & dmask], 1u);
-    });
-    __syncthreads();
-    if (tid < kWave) {
-      // lane j covers digits 255-4j .. 252-4j (top first)
-      uint32_t c[4];
-      uint32_t lsum = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { c[u] = s_h[255 - 4 * tid - u]; lsum += c[u]; }
-      uint32_t incl = lsum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += v;
-      }
-      const uint32_t rem = (uint32_t)s_remaining;
-      const uint64_t hit = __ballot(incl >= rem);
-      const int first = __ffsll((unsigned long long)hit) - 1;
-      if (tid == first) {
-        uint32_t cum = incl - lsum;
-        for (int u = 0; u < 4; ++u) {
-          if (cum + c[u] >= rem) {
-            const uint32_t d = 255u - 4u * tid - u;
-            const uint32_t left = rem - cum;
-            s_remaining = (int)left;
-            s_prefix = (s_prefix << width) | d;
-            if (c[u] == left || shift == 0) { s_done = 1; s_shift = shift; }
-            break;
-          }
-          cum += c[u];
-        }
-      }
-    }
-    __syncthreads();
-    if (s_done) break;
-  }
-  const unsigned long long thr = s_prefix;
-  const int ts = s_shift;
-  auto wins = [&](unsigned long long e) { return (e & kAbove) || (e >> ts) >= thr; };
-  auto index_of = [](unsigned long long e) { return (int32_t)(0xFFFFFFFFu - (uint32_t)e); };
-
-  // ---- winners in list order = ascending index ----
-  if (cached) {
-    constexpr int kSeg = kFinalCache / kSelThreads;         // 16 consecutive list entries per thread
-    const int i0 = tid * kSeg;
-    uint32_t win = 0;
-#pragma unroll
-    for (int u = 0; u < kSeg; ++u)
-      if (i0 + u < (int)total_keep && wins(s_list[i0 + u])) win |= 1u << u;
-    uint32_t tot;
-    uint32_t pos = block_excl_scan((uint32_t)__popc(win), s_w, &tot);
-#pragma unroll
-    for (int u = 0; u < kSeg; ++u) {
-      if (((win >> u) & 1u) && pos < (uint32_t)k) {   // exactly k winners; the bound is a guard
-        const int32_t e = index_of(s_list[i0 + u]);
-        out[pos] = e;
-        if (out_s) out_s[pos] = srow[e];
-        ++pos;
-      }
-    }
-  } else {
-    // winners per chunk, their output offsets, then each wave writes its chunks in order
-    for (int c = wave; c < nch; c += kWaves) {
-      uint32_t n = 0;
-      for (int j = lane; j < (int)s_keep[c]; j += kWave) n += wins(lrow[(int64_t)c * kFilterChunk + j]) ? 1u : 0u;
-      n = (uint32_t)wave_sum((float)n);                     // exact: counts <= 4096
-      if (lane == 0) s_keep[c] = n;
-    }
-    __syncthreads();
-    uint32_t wsum = 0;
-    uint32_t wc[kPerT];
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) {
-      const int c = tid * kPerT + u;
-      wc[u] = c < nch ? s_keep[c] : 0u;
-      wsum += wc[u];
-    }
-    uint32_t tot;
-    uint32_t o2 = block_excl_scan(wsum, s_w, &tot);
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) { s_pos[tid * kPerT + u] = o2; o2 += wc[u]; }
-    __syncthreads();
-    for (int c = wave; c < nch; c += kWaves) {
-      uint32_t base = s_pos[c];
-      for (int j0 = 0; j0 < kFilterChunk; j0 += kWave) {
-        const int j = j0 + lane;
-        // the chunk's list length is the kept count written by the filter, still in counts
-        const int nk = (int)counts[r * nchunk + c].x;
-        if (j0 >= nk) break;
-        const unsigned long long e = lrow[(int64_t)c * kFilterChunk + (j < nk ? j : 0)];
-        const bool wv = j < nk && wins(e);
-        const uint64_t bal = __ballot(wv);
-        const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (wv && p < (uint32_t)k) {
-          const int32_t ix = index_of(e);
-          out[p] = ix;
-          if (out_s) out_s[p] = srow[ix];
-        }
-        base += (uint32_t)__popcll(bal);
-      }
-    }
-  }
-}
-
 // Prefill: one workgroup per row does histogram, filter, refine, sort.
 __global__ void __launch_bounds__(kSelThreads)
 topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __restrict__ cand, int64_t nsp,
@@ -1047,7 +1133,7 @@ size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   (void)k;
   const int64_t R = (int64_t)B * Tq;
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
-  return al256((size_t)R * nsp * 4) + al256((size_t)R * (kBins + 4) * 4) + al256((size_t)R * nsp * 8) +
+  return al256((size_t)R * nsp * 4) + al256((size_t)R * kHistRow * 4) + al256((size_t)R * nsp * 8) +
          al256((size_t)R * n_chunks(n_cap) * 8);
 }
 
@@ -1058,7 +1144,7 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   // decode selection stages: row-per-workgroup.
   const bool decode = R < 64 && w.nchunk <= kMaxDecodeChunks;
   if (decode) {
-    const int64_t n = (int64_t)R * (kBins + 4);
+    const int64_t n = (int64_t)R * kHistRow;
     LCS_LAUNCH("topk_clear_kernel", clear_u32_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
                dim3(256), 0, st, w.hist, n);
     dispatch_score<1>(a, w, st);
@@ -1066,7 +1152,7 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
     LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.comb,
                w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k);
     LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
-               w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
+               w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
   } else {
     dispatch_score<4>(a, w, st);
     LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
