@@ -18,6 +18,8 @@ namespace {
 
 constexpr int kUnroll = 16;
 constexpr int kWaves = 8;                 // waves per workgroup, splitting K
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4v GU32x4v;   // global address space: global_load
 
 __global__ void __launch_bounds__(kWaves * 64)
 rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W,
@@ -79,7 +81,85 @@ rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
   }
 }
 
+// Decode shapes (M <= 8, K = 4096 or 8192): the workgroup's slice of X (M x K) is staged once in
+// LDS, and each wave issues all of its W loads (KS k-steps of 16 B per lane) before the first MFMA,
+// so a CU has its whole share of the weights in flight.  X rows >= M are zero in the B fragments.
+template <int K>
+__global__ void __launch_bounds__(kWaves * 64)
+rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W,
+                     uint16_t* __restrict__ Y, int64_t y_ld, int M, int n_per_group) {
+  constexpr int KS = K / 32 / kWaves;      // k-steps per wave
+  constexpr int kXStride = K + 8;          // bf16 per staged X row (16 B pad)
+  __shared__ __align__(16) uint16_t sx[8 * kXStride];
+  __shared__ float4 red[kWaves][kWave];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int n0 = blockIdx.x * 16;
+  const int64_t xoff = (int64_t)(n0 / n_per_group) * K;
+
+  // all of this wave's W fragments in flight (rows n0 + c16, k-steps w*KS ..)
+  const GU32x4v* wp = reinterpret_cast<const GU32x4v*>(reinterpret_cast<uintptr_t>(
+      W + (int64_t)(n0 + c16) * K + 32 * (w * KS) + 8 * g));
+  uint4 wa[KS];
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    const u32x4v x = wp[4 * u];
+    wa[u] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+  // X slice -> LDS (rows >= M are never read)
+  constexpr int kChunks = 8 * K / 8;       // 16 B chunks of the 8-row slice
+#pragma unroll
+  for (int u = 0; u < kChunks / (kWaves * 64); ++u) {
+    const int i = threadIdx.x + u * kWaves * 64;
+    const int m = i / (K / 8), kc = i % (K / 8);
+    const int ms = m < M ? m : M - 1;                  // always a readable row
+    const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)ms * x_ld + xoff + 8 * kc);
+    *reinterpret_cast<uint4*>(&sx[m * kXStride + 8 * kc]) = x;
+  }
+  __syncthreads();
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bool mv = c16 < M;
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(&sx[(mv ? c16 : 0) * kXStride + 32 * (w * KS + u) + 8 * g]);
+    acc = mfma_bf16(wa[u], mv ? xv : make_uint4(0, 0, 0, 0), acc);
+  }
+  // acc: lane holds column (m) c16, rows n0 + 4g .. +3; sum the 8 waves' K slices
+  red[w][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (w == 0) {
+    float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float4 a = red[v][lane];
+      y0 += a.x; y1 += a.y; y2 += a.z; y3 += a.w;
+    }
+    if (mv) {
+      uint2 o;
+      o.x = pack_bf2(y0, y1);
+      o.y = pack_bf2(y2, y3);
+      *reinterpret_cast<uint2*>(Y + (int64_t)c16 * y_ld + n0 + 4 * g) = o;
+    }
+  }
+}
+
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Y = X . W^T for one stage: the staged-X kernel at the decode shapes, else the general one.
+void launch_stage(const char* name, const uint16_t* X, int64_t x_ld, const uint16_t* W, uint16_t* Y, int64_t y_ld,
+                  int M, int N, int K, int n_per_group, hipStream_t st) {
+  if (M <= 8 && K == 4096) {
+    LCS_LAUNCH(name, rowblock_gemv_kernel<4096>, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y,
+               y_ld, M, n_per_group);
+  } else if (M <= 8 && K == 8192) {
+    LCS_LAUNCH(name, rowblock_gemv_kernel<8192>, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y,
+               y_ld, M, n_per_group);
+  } else {
+    LCS_LAUNCH(name, rowblock_gemm_kernel, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y, y_ld,
+               M, N, K, n_per_group);
+  }
+}
 
 }  // namespace
 
@@ -89,10 +169,8 @@ int launch_out_proj(const OutProjArgs& a, hipStream_t st) {
   uint16_t* z = static_cast<uint16_t*>(a.ws);
   const int kg = a.H / a.g * a.c;
   const int nz = a.g * a.d_g;
-  LCS_LAUNCH("out_proj_group_kernel", rowblock_gemm_kernel, dim3((unsigned)(nz / 16)), dim3(kWaves * 64), 0, st,
-             a.o, (int64_t)a.H * a.c, a.w_g, z, (int64_t)nz, a.M, nz, kg, a.d_g);
-  LCS_LAUNCH("out_proj_out_kernel", rowblock_gemm_kernel, dim3((unsigned)(a.d / 16)), dim3(kWaves * 64), 0, st,
-             z, (int64_t)nz, a.w_o, a.y, (int64_t)a.d, a.M, a.d, nz, a.d);
+  launch_stage("out_proj_group_kernel", a.o, (int64_t)a.H * a.c, a.w_g, z, (int64_t)nz, a.M, nz, kg, a.d_g, st);
+  launch_stage("out_proj_out_kernel", z, (int64_t)nz, a.w_o, a.y, (int64_t)a.d, a.M, a.d, nz, a.d, st);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
