@@ -225,8 +225,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc += v[j] * v[j];
     }
-    acc += __shfl_xor(acc, 16, kWave);
-    acc += __shfl_xor(acc, 32, kWave);
+    acc = sum_rows4(acc);
     const float rstd = head_ok ? 1.0f / sqrtf(acc * (1.0f / kHeadDim) + a.eps) : 0.f;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
@@ -253,7 +252,7 @@ attend_kernel(AttnK a) {
     }
   }
 
-  floatx4 o[kWaves][8];                    // O[head block hb][dims 128w + 16db ..]
+  floatx4 o[kWaves][8];                    // O^T tiles: lane holds head 16hb + c16, dims 128w + 16db + 4g .. +4
   // Softmax state of this lane's head, log2 domain.  m_ref is the reference of the exponentials:
   // the first tile's max (first pass) or the split's max (second pass); it never moves within a
   // pass, so O is only ever touched by MFMA.  A tile whose max exceeds m_ref by more than kJump
@@ -331,8 +330,7 @@ attend_kernel(AttnK a) {
         sc[kb][i] = v ? acc[kb][i] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, sc[kb][i]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    tmax = max_rows4(tmax);
     m_max = fmaxf(m_max, tmax);
     if (m_ref == -INFINITY) {
       m_ref = tmax;                        // first tile with a key: nothing accumulated yet
@@ -354,8 +352,7 @@ attend_kernel(AttnK a) {
         psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
       }
     }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
+    psum = sum_rows4(psum);
     l_run += psum;
     s_p[slot][w * kWave + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   };
@@ -379,7 +376,7 @@ attend_kernel(AttnK a) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
 #pragma unroll
-      for (int hb = 0; hb < kWaves; ++hb) o[hb][db] = mfma_bf16(pf[hb], vf, o[hb][db]);
+      for (int hb = 0; hb < kWaves; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
     }
   };
 
@@ -445,33 +442,31 @@ attend_kernel(AttnK a) {
   // O goes through LDS ([head][dim] bf16, in the tile buffers) so that the global stores are whole
   // 16 B chunks.
   const bool single = a.nsplit == 1;
-  constexpr int kOStride = kHeadDim;
-  uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][512 dims] bf16
+  constexpr int kOStride = kHeadDim + 8;   // 520 bf16: the 16 heads of one 8-byte write start 4 banks apart
+  uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][kOStride] bf16
   static_assert(sizeof(s_kv) >= kHeadSlots * kOStride * 2, "output staging fits the tile buffers");
 #pragma unroll
   for (int hb = 0; hb < kWaves; ++hb) {
-    float4 fac = make_float4(1.f, 1.f, 1.f, 1.f);
-    if (single) fac = *reinterpret_cast<const float4*>(&s_fac[hb * 16 + 4 * g]);   // partials: factor 1
-    const float fv[4] = {fac.x, fac.y, fac.z, fac.w};
+    const int hh = hb * 16 + c16;
+    const float fac = single ? s_fac[hh] : 1.f;   // partials: factor 1
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int d = 128 * w + 16 * db + c16;
+      const int d = 128 * w + 16 * db + 4 * g;     // dims d .. d + 3 of head hh
       float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = single ? o[hb][db][i] * fv[i] : o[hb][db][i];
+      for (int i = 0; i < 4; ++i) v[i] = single ? o[hb][db][i] * fac : o[hb][db][i];
       if (w == kWaves - 1 && 16 * db >= kRopeStart - 128 * (kWaves - 1)) {
-        // dims >= 448 (last wave, db >= 4): rotate pairs (d, d ^ 1) by -(t + offset); the partner
-        // lane's value comes by a quad permutation [1, 0, 3, 2]
-        const int jr = (d - kRopeStart) >> 1;
-        const float cs = s_cos[jr], sn = s_sin[jr];
+        // dims >= 448 (last wave, db >= 4): rotate the pairs (d, d + 1), (d + 2, d + 3) by -(t + offset)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
-          v[i] = (c16 & 1) ? (v[i] * cs - pv * sn) : (v[i] * cs + pv * sn);
+        for (int p = 0; p < 2; ++p) {
+          const int jr = ((d - kRopeStart) >> 1) + p;
+          const float cs = s_cos[jr], sn = s_sin[jr];
+          const float x = v[2 * p], y = v[2 * p + 1];
+          v[2 * p] = x * cs + y * sn;
+          v[2 * p + 1] = y * cs - x * sn;
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[(hb * 16 + 4 * g + i) * kOStride + d] = (uint16_t)f2bf(v[i]);
+      *reinterpret_cast<uint2*>(&s_o[hh * kOStride + d]) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
     }
   }
   __syncthreads();
@@ -498,8 +493,7 @@ constexpr int kMergeChunk = 32;
 constexpr int kMergeBlock = 1024;          // split weights held in LDS at a time
 
 __device__ __forceinline__ float block_max_128(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  v = wave_max(v);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
   const float r = fmaxf(red[0], red[1]);
@@ -508,8 +502,7 @@ __device__ __forceinline__ float block_max_128(float v, float* red) {
 }
 
 __device__ __forceinline__ float block_sum_128(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = wave_sum(v);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
   const float r = red[0] + red[1];

@@ -84,14 +84,39 @@ __device__ __forceinline__ floatx4 mfma_fp8(intx8 a, intx8 b, floatx4 c) {
 }
 
 // ----------------------------------------------------------------------------------- wave ops
+// v_permlane16_swap / v_permlane32_swap (VALU, no LDS round trip): every lane receives the values
+// of the lane pair (l, l ^ 16), resp. (l, l ^ 32), the lower lane's first, so combining the two
+// gives the same bits in both lanes of a pair.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum / max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 row groups of an MFMA fragment).
+__device__ __forceinline__ float sum_rows4(float x) { return sum_xor32(sum_xor16(x)); }
+__device__ __forceinline__ float max_rows4(float x) { return max_xor32(max_xor16(x)); }
+
 __device__ __forceinline__ float wave_sum(float v) {
+  v = sum_rows4(v);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
+  v = max_rows4(v);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

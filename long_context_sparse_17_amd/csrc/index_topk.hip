@@ -154,8 +154,7 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
         float amax = 0.f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        amax = max_rows4(amax);
         const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
         intx8 codes;
 #pragma unroll
@@ -235,8 +234,7 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
 #pragma unroll
           for (int i = 0; i < 4; ++i) part += wq[qw][hb][i] * fmaxf(acc[i], 0.f);
         }
-        part += __shfl_xor(part, 16, kWave);
-        part += __shfl_xor(part, 32, kWave);
+        part = sum_rows4(part);
         const int64_t e = e0 + 16 * u + c16;
         if (g == 0 && e < nvis[qw]) {
           const float sc = part * kscale[u] + 0.0f;
@@ -301,8 +299,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
 #pragma unroll
         for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf2f_lo(wd[j])), fabsf(bf2f_hi(wd[j]))));
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      amax = max_rows4(amax);
       const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
       intx8 codes;
 #pragma unroll
@@ -401,8 +398,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       for (int hb = 0; hb < HBI; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) part += wq[hb][i] * fmaxf(acc[u][hb][i], 0.f);
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
+      part = sum_rows4(part);
       const int64_t e = c0 + 64 * gi + 16 * u + c16;
       if (g == 0 && e < c1) {
         const float v = part * sc[u] + 0.0f;
