@@ -84,6 +84,7 @@ attend_kernel(AttnK a) {
   if (threadIdx.x == 0) s_redo = 0;          // read after the first pass's last barrier
 
   const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
+  const int64_t t_q = a.q_pos[r];                         // first load: the RoPE table waits for it alone
   // HCA: the first two tiles are loaded speculatively at once, as entries e_begin .. e_begin+63
   // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
@@ -110,8 +111,7 @@ attend_kernel(AttnK a) {
     }
   }
 
-  // ---- one round trip: query position, this split's list slots, q and gamma ----
-  const int64_t t_q = a.q_pos[r];
+  // ---- one round trip: this split's list slots, q and gamma ----
   constexpr int kPer = kMaxSplitKeys / 256;
   int32_t sel[kPer];
 #pragma unroll
@@ -127,9 +127,17 @@ attend_kernel(AttnK a) {
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
-  if (threadIdx.x < kHeadDim / 8)          // gamma: 1 KiB, staged once in LDS
-    s_gamma[threadIdx.x] = *reinterpret_cast<const uint4*>(a.gamma_q + 8 * threadIdx.x);
+  const uint4 gam = *reinterpret_cast<const uint4*>(a.gamma_q + 8 * (threadIdx.x % (kHeadDim / 8)));
   __builtin_amdgcn_sched_barrier(0);
+
+  // rope table for this query position (same angles for every head), while the rest is in flight
+  const double pos = (double)(t_q + a.rope_offset);
+  if (threadIdx.x < 32) {
+    float cs, sn;
+    rope_cs(pos, a.rf.inv[threadIdx.x], &cs, &sn);
+    s_cos[threadIdx.x] = cs;
+    s_sin[threadIdx.x] = sn;
+  }
 
   int64_t nc;                                             // compressed key slots of the row
   if (LIST) {
@@ -143,15 +151,6 @@ attend_kernel(AttnK a) {
   if (e_end > nk) e_end = nk;
   const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
   const int nkeys = e_end > e_begin ? (int)(e_end - e_begin) : 0;
-
-  // rope table for this query position (same angles for every head)
-  const double pos = (double)(t_q + a.rope_offset);
-  if (threadIdx.x < 32) {
-    float cs, sn;
-    rope_cs(pos, a.rf.inv[threadIdx.x], &cs, &sn);
-    s_cos[threadIdx.x] = cs;
-    s_sin[threadIdx.x] = sn;
-  }
 
   // ---- the split's key rows: list entry or entry number, then window tokens (ring row); -1 where a
   //      key does not exist ----
@@ -171,17 +170,18 @@ attend_kernel(AttnK a) {
       s_rows[i] = i >= nkeys ? -1 : (e < nc ? crow : wrow);
     }
   }
+  if (threadIdx.x < kHeadDim / 8) s_gamma[threadIdx.x] = gam;   // gamma: 1 KiB, staged once in LDS
   __syncthreads();
   const uint16_t* win_b = a.win ? a.win + b * a.win_ld * kHeadDim : a.kv;
   const int nc_local = nc > e_begin ? (int)(nc - e_begin) : 0;   // split keys that are compressed
 
   // ---- tile loads: lane (g, c16) fetches dims 128w + 32ks + 8g of keys kb*16 + c16 ----
+  // rows of keys kb*16 + c16 (s_rows is -1 past the split's keys; i0 + 32 <= kMaxSplitKeys)
   auto tile_rows = [&](int i0, int32_t (&rr)[2], uint32_t& vmask) {
-    const int i = i0 + (lane & 31);
-    const int32_t row = i < nkeys ? s_rows[i] : -1;
-    vmask = (uint32_t)__ballot(row >= 0 && lane < 32);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) rr[kb] = __shfl(row, kb * 16 + c16, kWave);
+    for (int kb = 0; kb < 2; ++kb) rr[kb] = s_rows[i0 + kb * 16 + c16];
+    const uint32_t b0 = (uint32_t)__ballot(rr[0] >= 0), b1 = (uint32_t)__ballot(rr[1] >= 0);
+    vmask = (b0 & 0xFFFFu) | (b1 << 16);   // bit j: key j of the tile exists (lanes 0..15 hold keys c16)
   };
   auto issue_tile = [&](int i0, const int32_t (&rr)[2], uint4 (&kf)[2][4]) {
 #pragma unroll
@@ -209,8 +209,11 @@ attend_kernel(AttnK a) {
     vb0 = 0xFFFFFFFFu;                     // the speculative loads are these tiles
     vb1 = 0xFFFFFFFFu;
   } else {
-    load_tile(tile0(0), kb0, vb0);
-    load_tile(tile0(1), kb1, vb1);
+    int32_t r0[2], r1[2];
+    tile_rows(tile0(0), r0, vb0);
+    tile_rows(tile0(1), r1, vb1);
+    issue_tile(tile0(0), r0, kb0);
+    issue_tile(tile0(1), r1, kb1);
   }
   __builtin_amdgcn_sched_barrier(0);
 
