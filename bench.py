@@ -121,6 +121,79 @@ def cpu_baseline(layers, n_seq, min_s=10.0, max_s=30.0):
                                    f"copied from the device"
 
 
+def _event_time_us(fn, reps, graph=False):
+    """Average duration of fn() on the current stream, HIP events around reps back-to-back calls.
+    graph=True captures the reps calls into one graph first, so host launch costs do not count."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    run, n = fn, reps
+    if graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        run, n = g.replay, 1
+        run()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def mfma_reference(dev):
+    """Measured dense bf16 matrix-core ceiling: an 8192^3 GEMM (library kernel) in TFLOP/s."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    us = _event_time_us(lambda: torch.matmul(a, b), 10)
+    return 2.0 * n ** 3 / (us * 1e-6) / 1e12
+
+
+def decode_append_rows(dev, B):
+    """kv_decode_append (one token per sequence, the block ends at this token: pooled-state update,
+    window-ring row, entry finished and stored) at batch B, for the CSA layer shape (m = 4, overlap 4,
+    fp8 indexer keys of 128 dims) and the HCA shape (m = 128)."""
+    import torch
+    import long_context_sparse_17_amd as L
+    g = torch.Generator(device=dev).manual_seed(5)
+    kv = (torch.randn(B, 512, device=dev, generator=g) * 1.28).to(torch.bfloat16)
+    ks = torch.randn(B, device=dev, generator=g)
+    ik = (torch.randn(B, 128, device=dev, generator=g) * 1.28).to(torch.bfloat16)
+    iks = torch.randn(B, device=dev, generator=g)
+    gamma = torch.ones(512, device=dev, dtype=torch.bfloat16)
+    pos = torch.full((B,), 4095, dtype=torch.int64, device=dev)
+    state = torch.zeros(L.kv_decode_state_bytes(B), dtype=torch.uint8, device=dev)
+    ring = torch.zeros(B, 256, 512, device=dev, dtype=torch.bfloat16)
+    kv_out = torch.zeros(B, 1024, 512, device=dev, dtype=torch.bfloat16)
+    ik_out = torch.zeros(B, 1024, 128, device=dev, dtype=torch.uint8)
+    ik_sc = torch.zeros(B, 1024, device=dev)
+    csa = _event_time_us(lambda: L.kv_decode_append(kv, ks, ik, iks, pos, m=4, overlap=4, gamma_kv=gamma, state=state,
+                                                    kv_out=kv_out, win=ring, ring_cap=256, ik_out=ik_out,
+                                                    ik_scale=ik_sc), 200, graph=True)
+    hca = _event_time_us(lambda: L.kv_decode_append(kv, ks, None, None, pos, m=128, overlap=0, gamma_kv=gamma,
+                                                    state=state, kv_out=kv_out, win=ring, ring_cap=256), 200,
+                         graph=True)
+    # bytes per sequence: token (1 KiB + 256 B keys + logits), two state slots read and written, ring row,
+    # entry and key written
+    slot = (512 + 128 + 4) * 4
+    csa_bytes = B * (1024 + 256 + 8 + 2 * 2 * slot + 1024 + 1024 + 128 + 4)
+    hca_bytes = B * (1024 + 4 + 2 * (512 + 4) * 4 + 1024 + 1024)
+    return {"what": "kv_decode_append: one token per sequence that ends a block (state update, ring row, "
+                    "entry + key stored)", "batch": B,
+            "csa_us": round(csa, 2), "hca_us": round(hca, 2), "csa_bytes": csa_bytes, "hca_bytes": hca_bytes,
+            "bound": "latency (one workgroup per sequence)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +317,10 @@ def main():
     copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
+    mfma_tflops = mfma_reference(dev)
+    next_rows = {"decode_append": decode_append_rows(dev, B)}
+    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+
     cpu = None
     if not args.no_cpu:
         rate, secs, threads, sample = cpu_baseline(layers, args.cpu_seqs)
@@ -263,6 +340,7 @@ def main():
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "flops": step_flops},
         "kernels": kernels, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
+        "mfma_gemm_bf16_tflops": round(mfma_tflops, 1), "next": next_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -94,6 +94,42 @@ int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score,
                     uint16_t* kv_out, int64_t kv_ld, int64_t ring_cap, void* stream);
 
 /*
+ * kv_decode_append -- one decode step of the compressed-KV state for B sequences, each at its own
+ * position (page 1, "hybrid attention": CSA step 1, the HCA paragraph and the sliding-window branch:
+ * entries pooled from m-token blocks with `overlap` earlier tokens, the nearest tokens kept
+ * uncompressed).  For every b with pos[b] >= 0 the token t = pos[b] is appended:
+ *   - win row t % ring_cap <- RoPE_t(RMSNorm(kv_tok[b]) * gamma_kv)        (win NULL: skipped);
+ *   - the token joins the pooling state of every block containing it (block t / m and, when
+ *     t >= (t/m + 1) m - overlap, the next one): online softmax over the blocks' logits, fp32;
+ *   - when t = (i+1) m - 1, block i is complete: its entry (the softmax-pooled vector, RMSNorm'd,
+ *     rotated to t) goes to kv_out row i (kv_ring = 0) or i % kv_ring, and its indexer key
+ *     (pooled with ik_score, no norm, no RoPE) to ik_out row i as bf16 or E4M3FN + scale.
+ * The result equals what csa_compress_kv / hca_compress_kv produce for the same blocks (up to the
+ * order of fp32 rounding).  pos[b] < 0 leaves sequence b untouched (ragged batches).
+ *
+ *   kv_tok [B, c] bf16, kv_score [B] fp32, ik_tok [B, dI] bf16, ik_score [B] fp32 (NULL: no keys)
+ *   pos    [B] int64 (device)
+ *   state  caller-owned device buffer of >= kv_decode_state_bytes(B) bytes (16-byte aligned), kept
+ *          between calls; it needs no clearing: the first token of a block (max(0, j m - overlap))
+ *          starts that block's state.  A sequence must therefore be appended from the first token
+ *          of its oldest unfinished block; appending a position twice folds the token in twice.
+ *   win    [B, win_ld, c] bf16 ring (win_ld >= ring_cap >= 1); kv_out [B, kv_ld, c] bf16;
+ *   ik_out [B, ik_ld, dI], ik_scale [B, ik_ld] fp32 (fp8).  Rows past kv_ld / ik_ld are not written.
+ *   Requirements: c = 512, m >= 1, 0 <= overlap <= m, dI in {64, 128}.
+ *   Calls for the same state must be ordered (one stream); concurrent calls on one state race.
+ */
+size_t kv_decode_state_bytes(int B);
+int kv_decode_append(const uint16_t* kv_tok, const float* kv_score,
+                     const uint16_t* ik_tok, const float* ik_score,
+                     const int64_t* pos, int B, int m, int overlap, int c, int dI,
+                     const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
+                     float* state, size_t state_bytes,
+                     uint16_t* win, int64_t win_ld, int64_t ring_cap,
+                     uint16_t* kv_out, int64_t kv_ld, int64_t kv_ring,
+                     void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype,
+                     void* stream);
+
+/*
  * csa_index_topk -- CSA step 2 (page 1, CSA step 2: lightning indexer + top-k; page 4 section 3.1:
  * 64 indexer heads of dim 128, top-k 512): for each query at token t = q_pos[b, tq] the score of
  * every visible entry s < n_vis = min(t / m, n_cap) is I_s = sum_h w_h * max(0, q_h . k_s); the

@@ -24,6 +24,9 @@ SIGNATURES = {
     "csa_compress_kv": (_I, [_P, _P, _P, _P, _I, _I, _I64, _I64, _I, _I, _I, _I, _I, _P, _F, _F, _I64,
                              _P, _I64, _I64, _P, _P, _I64, _I, _P]),
     "hca_compress_kv": (_I, [_P, _P, _I, _I, _I64, _I64, _I, _I, _I, _P, _F, _F, _I64, _P, _I64, _I64, _P]),
+    "kv_decode_state_bytes": (_SZ, [_I]),
+    "kv_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _P, _I64, _I64,
+                              _P, _I64, _I64, _P, _P, _I64, _I, _P]),
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "lcs_attend_workspace": (_SZ, [_I, _I, _I, _I64]),
@@ -133,6 +136,29 @@ def hca_compress_kv(kv_tok, kv_score, *, tok0, blk_begin, n_blk, m, gamma_kv, kv
                                eps, rope_theta, rope_offset, _ptr(kv_out), kv_out.shape[1], ring_cap,
                                _stream(stream))
     _check("hca_compress_kv", st)
+
+
+def kv_decode_state_bytes(B):
+    return lib().kv_decode_state_bytes(B)
+
+
+def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gamma_kv, state, kv_out, kv_ring=0,
+                     win=None, ring_cap=0, ik_out=None, ik_scale=None, ik_fp8=True, eps=1e-6, rope_theta=10000.0,
+                     rope_offset=0, stream=None):
+    """Append token pos[b] of every sequence b (pos < 0: skip).  kv_tok [B,512] bf16, kv_score [B] f32,
+    ik_tok [B,dI] bf16 | None, pos [B] int64, state: uint8 buffer of kv_decode_state_bytes(B) bytes."""
+    import torch
+    B, c = kv_tok.shape
+    _bits(kv_tok, "kv_tok"); _bits(gamma_kv, "gamma_kv"); _bits(kv_out, "kv_out"); _bits(win, "win")
+    _dt(kv_score, torch.float32, "kv_score"); _dt(ik_score, torch.float32, "ik_score"); _dt(pos, torch.int64, "pos")
+    dI = ik_tok.shape[-1] if ik_tok is not None else 0
+    ik_ld = ik_out.shape[1] if ik_out is not None else 0
+    st = lib().kv_decode_append(_ptr(kv_tok), _ptr(kv_score), _ptr(ik_tok), _ptr(ik_score), _ptr(pos), B, m, overlap,
+                                c, dI, _ptr(gamma_kv), eps, rope_theta, rope_offset, _ptr(state),
+                                state.numel() * state.element_size(), _ptr(win), win.shape[1] if win is not None else 0,
+                                ring_cap, _ptr(kv_out), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
+                                LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16, _stream(stream))
+    _check("kv_decode_append", st)
 
 
 def csa_index_topk_workspace(B, Tq, n_cap, k):

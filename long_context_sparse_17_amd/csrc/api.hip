@@ -172,6 +172,42 @@ int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score, int B, int T,
                          eps, rope_theta, rope_offset, kv_out, kv_ld, ring_cap, nullptr, nullptr, 0, 0, stream);
 }
 
+// ------------------------------------------------------------------------------ decode append
+size_t kv_decode_state_bytes(int B) { return B > 0 ? lcs::decode_state_bytes(B) : 0; }
+
+int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
+                     const int64_t* pos, int B, int m, int overlap, int c, int dI, const uint16_t* gamma_kv,
+                     float eps, float rope_theta, int64_t rope_offset, float* state, size_t state_bytes,
+                     uint16_t* win, int64_t win_ld, int64_t ring_cap, uint16_t* kv_out, int64_t kv_ld,
+                     int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype, void* stream) {
+  if (!kv_tok || !kv_score || !pos || !gamma_kv || !state || !kv_out) return LCS_ERR_ARG;
+  if (B <= 0 || m <= 0 || overlap < 0 || kv_ld <= 0 || kv_ring < 0) return LCS_ERR_ARG;
+  if (!(eps >= 0.f) || !(rope_theta > 0.f)) return LCS_ERR_ARG;
+  if (!aligned16(kv_tok) || !aligned16(kv_out) || !aligned16(gamma_kv) || !aligned16(state) || !aligned4(kv_score) ||
+      (reinterpret_cast<uintptr_t>(pos) & 7u))
+    return LCS_ERR_ARG;
+  if (c != LCS_HEAD_DIM) return LCS_ERR_UNSUPPORTED;
+  if (overlap > m) return LCS_ERR_UNSUPPORTED;                 // a token lies in at most two blocks
+  if (state_bytes < lcs::decode_state_bytes(B)) return LCS_ERR_WORKSPACE;
+  if (kv_ring > kv_ld) return LCS_ERR_ARG;
+  if (win && (ring_cap <= 0 || win_ld < ring_cap || !aligned16(win))) return LCS_ERR_ARG;
+  const bool has_ik = ik_tok != nullptr;
+  if (has_ik) {
+    if (!ik_score || !ik_out || ik_ld <= 0) return LCS_ERR_ARG;
+    if (ik_dtype != LCS_IK_BF16 && ik_dtype != LCS_IK_FP8) return LCS_ERR_UNSUPPORTED;
+    if (dI != 64 && dI != 128) return LCS_ERR_UNSUPPORTED;
+    if (ik_dtype == LCS_IK_FP8 && !ik_scale) return LCS_ERR_ARG;
+  }
+  lcs::DecodeAppendArgs a;
+  a.kv_tok = kv_tok; a.kv_score = kv_score; a.ik_tok = has_ik ? ik_tok : nullptr; a.ik_score = ik_score;
+  a.pos = pos; a.B = B; a.m = m; a.ov = overlap; a.dI = has_ik ? dI : 0;
+  a.gamma = gamma_kv; a.eps = eps; a.theta = rope_theta; a.rope_offset = rope_offset;
+  a.state = state; a.win = win; a.win_ld = win_ld; a.ring_cap = ring_cap;
+  a.kv_out = kv_out; a.kv_ld = kv_ld; a.kv_ring = kv_ring;
+  a.ik_out = ik_out; a.ik_scale = ik_scale; a.ik_ld = ik_ld; a.ik_fp8 = ik_dtype == LCS_IK_FP8;
+  return lcs::launch_decode_append(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
 // ------------------------------------------------------------------------------ indexer + top-k
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   if (B <= 0 || Tq <= 0 || n_cap <= 0 || k <= 0) return 0;

@@ -1,0 +1,194 @@
+// One decode step of the compressed-KV state for a batch of sequences, each at its own position
+// (page 1, "hybrid attention": CSA step 1, the HCA paragraph and the sliding-window branch).
+//
+// A token t of sequence b is (1) written to the window ring as RoPE_t(RMSNorm(kv)), (2) folded into
+// the pooling state of every block that contains it, and (3) when t is the last token of block i,
+// block i's entry is finished: pooled vector RMSNorm'd, rotated to t and stored, with the indexer
+// key (own logits, no norm, no RoPE) stored as bf16 or E4M3FN codes + scale.  The pooled vector is
+// the same softmax-weighted sum the bulk compression forms, accumulated online as tokens arrive:
+// a running max M, sum l = sum e^{s_j - M} and weighted sums acc = sum e^{s_j - M} x_j (fp32),
+// rescaled when M grows; entry = acc / l.
+//
+// With overlap ov <= m a token belongs to block i = t / m and, when t >= (i+1)m - ov, to block
+// i + 1, so each sequence keeps two state slots (block j uses slot j & 1).  The first token of a
+// block (max(0, jm - ov)) initialises its slot, so the state needs no clearing.
+//
+// One workgroup of 128 threads per sequence; thread x owns K=V dims 4x .. 4x+3 and indexer dim x.
+#include "common.h"
+#include "kernels.h"
+
+namespace lcs {
+
+namespace {
+
+constexpr int kThreads = 128;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const float r = red[0] + red[1];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const float r = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return r;
+}
+
+// RoPE on dims d0 .. d0+3 (d0 >= 448) at position pos; y holds the 4 values.
+__device__ __forceinline__ void rope4(float (&y)[4], int d0, double pos, const RopeFreq& rf) {
+  if (d0 < kRopeStart) return;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float c, s;
+    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2 + p], &c, &s);
+    const float a0 = y[2 * p], a1 = y[2 * p + 1];
+    y[2 * p] = a0 * c - a1 * s;
+    y[2 * p + 1] = a0 * s + a1 * c;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
+  __shared__ float red[2];
+  const int b = blockIdx.x;
+  const int x = threadIdx.x;
+  const int64_t t = a.pos[b];
+  if (t < 0) return;                                   // inactive slot of the batch (uniform)
+  const bool has_ik = a.ik_tok != nullptr;
+
+  // ---- this token ----
+  const uint2 raw = *reinterpret_cast<const uint2*>(a.kv_tok + (int64_t)b * kHeadDim + 4 * x);
+  const uint2 gm = *reinterpret_cast<const uint2*>(a.gamma + 4 * x);
+  const float s = a.kv_score[b];
+  const float v[4] = {bf2f_lo(raw.x), bf2f_hi(raw.x), bf2f_lo(raw.y), bf2f_hi(raw.y)};
+  const float g4[4] = {bf2f_lo(gm.x), bf2f_hi(gm.x), bf2f_lo(gm.y), bf2f_hi(gm.y)};
+  float iv = 0.f, is = 0.f;
+  if (has_ik) {
+    iv = x < a.dI ? bf2f(a.ik_tok[(int64_t)b * a.dI + x]) : 0.f;
+    is = a.ik_score[b];
+  }
+
+  // ---- window ring row t % ring_cap: RoPE_t(RMSNorm(x)) ----
+  if (a.win != nullptr) {
+    const float ss = block_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3], red);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = v[i] * rstd * g4[i];
+    rope4(y, 4 * x, (double)(t + a.rope_offset), rf);
+    const int64_t row = t % a.ring_cap;
+    *reinterpret_cast<uint2*>(a.win + ((int64_t)b * a.win_ld + row) * kHeadDim + 4 * x) =
+        make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+  }
+
+  // ---- pooling state of the blocks containing t: i = t / m and, inside the overlap, i + 1 ----
+  const int64_t i = t / a.m;
+  const bool in_next = a.ov > 0 && t >= (i + 1) * a.m - a.ov;
+  float kv_e[4] = {0.f, 0.f, 0.f, 0.f};                // block i's pooled vector when t ends it
+  float ik_e = 0.f;
+  const bool ends = t == (i + 1) * a.m - 1;
+  // read both slots' running values first: (M, l) is shared by all threads and rewritten below
+  float4 o[2];
+  float2 mlk[2], mli[2];
+  float io[2];
+  bool init[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t j = i + q;
+    const int64_t first = j * a.m - a.ov > 0 ? j * a.m - a.ov : 0;
+    init[q] = t == first;                                        // the block's first token: fresh state
+    const float* st = a.state + ((int64_t)b * 2 + (j & 1)) * kStateFloats;
+    o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    mlk[q] = mli[q] = make_float2(0.f, 0.f);
+    io[q] = 0.f;
+    if ((q == 0 || in_next) && !init[q]) {
+      o[q] = reinterpret_cast<const float4*>(st)[x];
+      mlk[q] = *reinterpret_cast<const float2*>(st + kHeadDim + kMaxIdxDim);
+      if (has_ik) {
+        mli[q] = *reinterpret_cast<const float2*>(st + kHeadDim + kMaxIdxDim + 2);
+        io[q] = x < a.dI ? st[kHeadDim + x] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (q == 1 && !in_next) break;
+    const int64_t j = i + q;
+    float* st = a.state + ((int64_t)b * 2 + (j & 1)) * kStateFloats;
+    float4 A;
+    float Mn, ln, IA = 0.f, IMn = 0.f, Iln = 0.f;
+    if (init[q]) {
+      A = make_float4(v[0], v[1], v[2], v[3]);
+      Mn = s;
+      ln = 1.f;
+      if (has_ik) { IA = iv; IMn = is; Iln = 1.f; }
+    } else {
+      Mn = fmaxf(mlk[q].x, s);
+      const float fo = __expf(mlk[q].x - Mn), fn = __expf(s - Mn);
+      A = make_float4(o[q].x * fo + v[0] * fn, o[q].y * fo + v[1] * fn, o[q].z * fo + v[2] * fn,
+                      o[q].w * fo + v[3] * fn);
+      ln = mlk[q].y * fo + fn;
+      if (has_ik) {
+        IMn = fmaxf(mli[q].x, is);
+        const float gfo = __expf(mli[q].x - IMn), gfn = __expf(is - IMn);
+        IA = io[q] * gfo + iv * gfn;
+        Iln = mli[q].y * gfo + gfn;
+      }
+    }
+    if (q == 0 && ends) {                                        // block i is complete
+      const float inv = 1.0f / ln;
+      kv_e[0] = A.x * inv; kv_e[1] = A.y * inv; kv_e[2] = A.z * inv; kv_e[3] = A.w * inv;
+      if (has_ik) ik_e = IA * (1.0f / Iln);
+    } else {                                                     // keep the running state
+      reinterpret_cast<float4*>(st)[x] = A;
+      if (has_ik && x < a.dI) st[kHeadDim + x] = IA;
+      if (x == 0) {
+        *reinterpret_cast<float2*>(st + kHeadDim + kMaxIdxDim) = make_float2(Mn, ln);
+        if (has_ik) *reinterpret_cast<float2*>(st + kHeadDim + kMaxIdxDim + 2) = make_float2(IMn, Iln);
+      }
+    }
+  }
+  if (!ends) return;                                            // uniform: t is the same for the block
+
+  // ---- block i's entry: RMSNorm, RoPE at its last token t; indexer key ----
+  const float ss = block_sum(kv_e[0] * kv_e[0] + kv_e[1] * kv_e[1] + kv_e[2] * kv_e[2] + kv_e[3] * kv_e[3], red);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  float y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) y[k] = kv_e[k] * rstd * g4[k];
+  rope4(y, 4 * x, (double)(t + a.rope_offset), rf);
+  const int64_t row = a.kv_ring > 0 ? i % a.kv_ring : i;
+  if (row < a.kv_ld)
+    *reinterpret_cast<uint2*>(a.kv_out + ((int64_t)b * a.kv_ld + row) * kHeadDim + 4 * x) =
+        make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+  if (!has_ik) return;
+  const bool ik_row_ok = i < a.ik_ld;
+  if (a.ik_fp8) {
+    const float amax = block_max(x < a.dI ? fabsf(ik_e) : 0.f, red);
+    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (ik_row_ok && x < a.dI)
+      reinterpret_cast<uint8_t*>(a.ik_out)[((int64_t)b * a.ik_ld + i) * a.dI + x] = (uint8_t)f2e4m3(__fdiv_rn(ik_e, sc));
+    if (ik_row_ok && x == 0) a.ik_scale[(int64_t)b * a.ik_ld + i] = sc;
+  } else if (ik_row_ok && x < a.dI) {
+    reinterpret_cast<uint16_t*>(a.ik_out)[((int64_t)b * a.ik_ld + i) * a.dI + x] = (uint16_t)f2bf(ik_e);
+  }
+}
+
+}  // namespace
+
+size_t decode_state_bytes(int B) { return (size_t)B * 2 * kStateFloats * sizeof(float); }
+
+int launch_decode_append(const DecodeAppendArgs& a, hipStream_t stream) {
+  LCS_LAUNCH("decode_append_kernel", decode_append_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a,
+             rope_freq(a.theta));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // namespace lcs

@@ -16,6 +16,23 @@ struct CompressArgs {
 };
 int launch_compress(const CompressArgs& a, hipStream_t stream);
 
+// Decode-step append (per-sequence positions, online pooling state).  State per sequence: two slots
+// of kStateFloats floats: K=V weighted sums [512], indexer weighted sums [kMaxIdxDim], then
+// (M, l) for the K=V and (M, l) for the indexer logits.
+constexpr int kMaxIdxDim = 128;
+constexpr int kStateFloats = 512 + kMaxIdxDim + 4;
+struct DecodeAppendArgs {
+  const uint16_t* kv_tok; const float* kv_score; const uint16_t* ik_tok; const float* ik_score;
+  const int64_t* pos; int B, m, ov, dI;
+  const uint16_t* gamma; float eps, theta; int64_t rope_offset;
+  float* state;
+  uint16_t* win; int64_t win_ld, ring_cap;
+  uint16_t* kv_out; int64_t kv_ld, kv_ring;
+  void* ik_out; float* ik_scale; int64_t ik_ld; int ik_fp8;
+};
+size_t decode_state_bytes(int B);
+int launch_decode_append(const DecodeAppendArgs& a, hipStream_t stream);
+
 struct IndexArgs {
   const uint16_t* q_idx; const uint16_t* w_idx;
   const void* ik; const float* ik_scale; int64_t ik_ld; int ik_fp8;

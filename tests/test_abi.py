@@ -101,6 +101,30 @@ def test_compress_rejects_tokens_outside_the_given_columns(lib):
         L.LCS_ERR_ARG
 
 
+def test_decode_append_rejects_bad_arguments(lib):
+    need = lib.kv_decode_state_bytes(8)
+    assert need == 8 * 2 * (512 + 128 + 4) * 4
+    # kv_tok, kv_score, ik_tok, ik_score, pos, B, m, ov, c, dI, gamma, eps, theta, offset, state, state_bytes,
+    # win, win_ld, ring_cap, kv_out, kv_ld, kv_ring, ik_out, ik_scale, ik_ld, ik_dtype, stream
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 4, 512, 128, FAKE, 1e-6, 1e4, 0, FAKE, need, FAKE, 256, 256, FAKE,
+            1000, 0, FAKE, FAKE, 1000, L.LCS_IK_FP8, None]
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.kv_decode_append(*a)
+    assert call(a15=need - 1) == L.LCS_ERR_WORKSPACE
+    assert call(a7=5) == L.LCS_ERR_UNSUPPORTED            # overlap > m: a token in three blocks
+    assert call(a8=256) == L.LCS_ERR_UNSUPPORTED           # c != 512
+    assert call(a9=96) == L.LCS_ERR_UNSUPPORTED            # dI
+    assert call(a4=None) == L.LCS_ERR_ARG                  # positions
+    assert call(a17=100) == L.LCS_ERR_ARG                  # win_ld < ring_cap
+    assert call(a21=1001) == L.LCS_ERR_ARG                 # kv_ring > kv_ld
+    assert call(a23=None) == L.LCS_ERR_ARG                 # fp8 keys need scales
+    assert call(a25=7) == L.LCS_ERR_UNSUPPORTED            # key dtype
+    assert call(a6=0) == L.LCS_ERR_ARG
+
+
 def test_out_proj_rejects_bad_grouping(lib):
     assert lib.grouped_out_proj(FAKE, FAKE, FAKE, 8, 64, 512, 7, 1024, 4096, FAKE, FAKE, 1 << 30, None) == \
         L.LCS_ERR_UNSUPPORTED

@@ -1,0 +1,134 @@
+"""GPU parity of kv_decode_append, the per-token decode path of the compressed-KV state, in a
+continuous-batching loop: sequences start at different steps, pause (position -1) and stop, so the
+batch is ragged at every step.  After the loop every finished block's entry (and indexer key) must
+equal the oracle's compression of that sequence's token stream, the window ring must hold the last
+tokens normed and rotated, and untouched rows must stay untouched.  The state buffer starts as NaN
+bytes: the first token of a block starts its state, so nothing is read before it is written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_17_amd as L
+import oracle as O
+import synth
+from lcs_testutil import assert_close, errors, from_bits, to_np_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+RING = 160
+
+
+def _schedule(B, steps, m):
+    """Per step and sequence: the token index appended, or -1.  Sequence 0 runs throughout, 1 starts
+    late, 2 pauses for a while, 3 stops early, 4 starts late and pauses."""
+    pos = np.full((steps, B), -1, dtype=np.int64)
+    start = [0, 9, 0, 0, 37]
+    stop = [steps, steps, steps, 100, steps]
+    pause = {2: range(100, 131), 4: range(150, 170)}
+    for b in range(B):
+        n = 0
+        for s in range(start[b], stop[b]):
+            if b in pause and s in pause[b]:
+                continue
+            pos[s, b] = n
+            n += 1
+    return pos
+
+
+@pytest.mark.parametrize("mode", ["csa_fp8", "csa_bf16", "hca"])
+def test_decode_append_serving_loop(mode):
+    m, ov, dI, fp8 = {"csa_fp8": (4, 4, 128, True), "csa_bf16": (4, 4, 64, False), "hca": (128, 0, 0, False)}[mode]
+    B, steps, off = 5, 300, 4321
+    cfg = 60 + len(mode)
+    kv = synth.normal_bf16((B, steps, 512), 1.28, cfg, 1)
+    ks = synth.normal_f32((B, steps), 1.28, cfg, 2)
+    ik = synth.normal_bf16((B, steps, max(dI, 64)), 1.28, cfg, 3)
+    iks = synth.normal_f32((B, steps), 1.28, cfg, 4)
+    gamma = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 5).random(512, dtype=np.float32))
+    pos = _schedule(B, steps, m)
+    n_tok = (pos.max(axis=0) + 1).astype(int)
+
+    # per-step inputs: the token each sequence appends (zeros where inactive)
+    idx = np.where(pos >= 0, pos, 0)
+    b_ix = np.arange(B)[None, :]
+    step_kv = from_bits(np.ascontiguousarray(kv[b_ix, idx]))                     # [steps, B, 512]
+    step_ks = torch.from_numpy(np.ascontiguousarray(ks[b_ix, idx])).to(DEV)
+    step_ik = from_bits(np.ascontiguousarray(ik[b_ix, idx])) if dI else None
+    step_iks = torch.from_numpy(np.ascontiguousarray(iks[b_ix, idx])).to(DEV) if dI else None
+    step_pos = torch.from_numpy(pos).to(DEV)
+
+    nb_cap = steps // m + 2
+    state = torch.full((L.kv_decode_state_bytes(B) // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    ring = torch.zeros((B, RING, 512), dtype=torch.bfloat16, device=DEV)
+    kv_out = torch.zeros((B, nb_cap, 512), dtype=torch.bfloat16, device=DEV)
+    ik_out = ik_sc = None
+    if dI:
+        ik_out = torch.zeros((B, nb_cap, dI), dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
+        ik_sc = torch.zeros((B, nb_cap), dtype=torch.float32, device=DEV)
+    g_dev = from_bits(gamma)
+    for s in range(steps):
+        L.kv_decode_append(step_kv[s], step_ks[s], step_ik[s] if dI else None, step_iks[s] if dI else None,
+                           step_pos[s], m=m, overlap=ov, gamma_kv=g_dev, state=state, kv_out=kv_out, win=ring,
+                           ring_cap=RING, ik_out=ik_out, ik_scale=ik_sc, ik_fp8=fp8, rope_offset=off)
+    torch.cuda.synchronize()
+
+    g64 = synth.bf16_bits_to_f64(gamma)
+    got_kv = to_np_bf16(kv_out)
+    got_ring = to_np_bf16(ring)
+    for b in range(B):
+        n = int(n_tok[b])
+        nb = n // m
+        x = synth.bf16_bits_to_f64(kv[b, :n])
+        ref = O.compress_kv(x, ks[b, :n].astype(np.float64), m, ov, g64, 1e-6, 10000.0, off)[:nb]
+        assert_close(got_kv[b, :nb], ref, f"{mode} entries b={b}")
+        assert np.all(got_kv[b, nb:] == 0), "rows of unfinished blocks must not be written"
+        win = O.window_entries(x, g64, 1e-6, 10000.0, off)
+        last = range(max(0, n - RING), n)
+        assert_close(got_ring[b, [j % RING for j in last]], win[list(last)], f"{mode} ring b={b}")
+        if dI:
+            e = O.pool(synth.bf16_bits_to_f64(ik[b, :n, :dI]), iks[b, :n].astype(np.float64), m, ov)[:nb]
+            if fp8:
+                codes, sc, deq = O.fp8_quantize_rows(e)
+                np.testing.assert_allclose(ik_sc[b, :nb].cpu().numpy(), sc, rtol=1e-5)
+                gc = ik_out[b, :nb].cpu().numpy().astype(int)
+                diff = np.abs((gc & 0x7F) - (codes.astype(int) & 0x7F))
+                assert diff.max() <= 1                       # fp32 online vs fp64 pooling: one code apart at most
+                assert (diff > 0).mean() < 0.01
+                got = O.e4m3_decode(ik_out[b, :nb].cpu().numpy()) * ik_sc[b, :nb].cpu().numpy()[:, None]
+                assert errors(got, deq)[1] < 1e-2
+            else:
+                assert_close(to_np_bf16(ik_out[b, :nb]), e, f"{mode} bf16 keys b={b}")
+
+    # the bulk path on the same streams agrees with the per-token path
+    b = 0
+    n = int(n_tok[b])
+    nb = n // m
+    bulk = torch.zeros((1, nb_cap, 512), dtype=torch.bfloat16, device=DEV)
+    if dI:
+        L.csa_compress_kv(from_bits(kv[b:b + 1, :n]), torch.from_numpy(ks[b:b + 1, :n].copy()).to(DEV),
+                          from_bits(np.ascontiguousarray(ik[b:b + 1, :n, :dI])),
+                          torch.from_numpy(iks[b:b + 1, :n].copy()).to(DEV), tok0=0, blk_begin=0, n_blk=nb, m=m,
+                          overlap=ov, gamma_kv=g_dev, kv_out=bulk,
+                          ik_out=torch.zeros((1, nb_cap, dI), dtype=ik_out.dtype, device=DEV),
+                          ik_scale=torch.zeros((1, nb_cap), dtype=torch.float32, device=DEV), ik_fp8=fp8,
+                          rope_offset=off)
+    else:
+        L.hca_compress_kv(from_bits(kv[b:b + 1, :n]), torch.from_numpy(ks[b:b + 1, :n].copy()).to(DEV), tok0=0,
+                          blk_begin=0, n_blk=nb, m=m, gamma_kv=g_dev, kv_out=bulk, rope_offset=off)
+    torch.cuda.synchronize()
+    assert_close(got_kv[b, :nb], to_np_bf16(bulk[0, :nb]), f"{mode} per-token vs bulk")
+
+
+def test_decode_append_inactive_batch_touches_nothing():
+    B = 3
+    kv = synth.normal_bf16((B, 512), 1.28, 71, 1)
+    state = torch.full((L.kv_decode_state_bytes(B) // 4,), 7.0, dtype=torch.float32, device=DEV)
+    ring = torch.full((B, 8, 512), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((B, 4, 512), 5.0, dtype=torch.bfloat16, device=DEV)
+    pos = torch.full((B,), -1, dtype=torch.int64, device=DEV)
+    L.kv_decode_append(from_bits(kv), torch.zeros(B, device=DEV), None, None, pos, m=1, overlap=0,
+                       gamma_kv=from_bits(synth.f32_to_bf16_bits(np.ones(512, np.float32))), state=state,
+                       kv_out=out, win=ring, ring_cap=8)
+    torch.cuda.synchronize()
+    assert torch.all(state == 7.0) and torch.all(ring == 3.0) and torch.all(out == 5.0)
