@@ -177,17 +177,25 @@ def decode_append_rows(dev, B):
     kv_out = torch.zeros(B, 1024, 512, device=dev, dtype=torch.bfloat16)
     ik_out = torch.zeros(B, 1024, 128, device=dev, dtype=torch.uint8)
     ik_sc = torch.zeros(B, 1024, device=dev)
+    def prime(t0, **kw):                      # append positions t0 .. 4094: the block ending at 4095 is open
+        for t in range(t0, 4095):
+            L.kv_decode_append(kv, ks, kw.get("ik"), kw.get("iks"), torch.full((B,), t, dtype=torch.int64, device=dev),
+                               **{k: v for k, v in kw.items() if k not in ("ik", "iks")})
+    prime(4088, ik=ik, iks=iks, m=4, overlap=4, gamma_kv=gamma, state=state, kv_out=kv_out, win=ring, ring_cap=256,
+          ik_out=ik_out, ik_scale=ik_sc)
     csa = _event_time_us(lambda: L.kv_decode_append(kv, ks, ik, iks, pos, m=4, overlap=4, gamma_kv=gamma, state=state,
                                                     kv_out=kv_out, win=ring, ring_cap=256, ik_out=ik_out,
                                                     ik_scale=ik_sc), 200, graph=True)
+    state.zero_()
+    prime(3968, m=128, overlap=0, gamma_kv=gamma, state=state, kv_out=kv_out, win=ring, ring_cap=256)
     hca = _event_time_us(lambda: L.kv_decode_append(kv, ks, None, None, pos, m=128, overlap=0, gamma_kv=gamma,
                                                     state=state, kv_out=kv_out, win=ring, ring_cap=256), 200,
                          graph=True)
     # bytes per sequence: token (1 KiB + 256 B keys + logits), two state slots read and written, ring row,
     # entry and key written
-    slot = (512 + 128 + 4) * 4
+    slot = (512 + 128 + 8) * 4
     csa_bytes = B * (1024 + 256 + 8 + 2 * 2 * slot + 1024 + 1024 + 128 + 4)
-    hca_bytes = B * (1024 + 4 + 2 * (512 + 4) * 4 + 1024 + 1024)
+    hca_bytes = B * (1024 + 4 + 2 * (512 + 8) * 4 + 1024 + 1024)
     return {"what": "kv_decode_append: one token per sequence that ends a block (state update, ring row, "
                     "entry + key stored)", "batch": B,
             "csa_us": round(csa, 2), "hca_us": round(hca, 2), "csa_bytes": csa_bytes, "hca_bytes": hca_bytes,
@@ -282,7 +290,7 @@ def main():
     kernels = {}
     for name in ("index_score_kernel", "topk_clear_kernel", "topk_filter_kernel", "topk_final_kernel",
                  "attend_kernel", "attend_merge_kernel", "out_proj_group_kernel", "out_proj_out_kernel",
-                 "compress_kernel"):
+                 "compress_kernel", "decode_append_kernel"):
         ms, n = L.timing_read(name)
         if n:
             kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}

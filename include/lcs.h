@@ -110,9 +110,12 @@ int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score,
  *   kv_tok [B, c] bf16, kv_score [B] fp32, ik_tok [B, dI] bf16, ik_score [B] fp32 (NULL: no keys)
  *   pos    [B] int64 (device)
  *   state  caller-owned device buffer of >= kv_decode_state_bytes(B) bytes (16-byte aligned), kept
- *          between calls; it needs no clearing: the first token of a block (max(0, j m - overlap))
- *          starts that block's state.  A sequence must therefore be appended from the first token
- *          of its oldest unfinished block; appending a position twice folds the token in twice.
+ *          between calls: per sequence two slots, each tagged with the block it holds.  The first
+ *          token of a block (max(0, j m - overlap)) starts that block's slot; a block whose first
+ *          token was never appended is not pooled and its entry is not written.  So a sequence
+ *          appended from t = 0 needs no clearing; a sequence resumed mid-stream (its older blocks
+ *          compressed by the bulk path) needs its slots zero-filled once before the first append.
+ *          Appending one position twice folds that token in twice.
  *   win    [B, win_ld, c] bf16 ring (win_ld >= ring_cap >= 1); kv_out [B, kv_ld, c] bf16;
  *   ik_out [B, ik_ld, dI], ik_scale [B, ik_ld] fp32 (fp8).  Rows past kv_ld / ik_ld are not written.
  *   Requirements: c = 512, m >= 1, 0 <= overlap <= m, dI in {64, 128}.

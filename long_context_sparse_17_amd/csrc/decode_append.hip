@@ -10,8 +10,10 @@
 // rescaled when M grows; entry = acc / l.
 //
 // With overlap ov <= m a token belongs to block i = t / m and, when t >= (i+1)m - ov, to block
-// i + 1, so each sequence keeps two state slots (block j uses slot j & 1).  The first token of a
-// block (max(0, jm - ov)) initialises its slot, so the state needs no clearing.
+// i + 1, so each sequence keeps two state slots (block j uses slot j & 1), tagged with the block
+// they hold.  The first token of a block (max(0, jm - ov)) starts its slot and tag; a later token
+// whose slot carries another tag belongs to a block whose first token was never appended (a
+// sequence resumed mid-stream): that block is left alone and its entry is not written.
 //
 // One workgroup of 128 threads per sequence; thread x owns K=V dims 4x .. 4x+3 and indexer dim x.
 #include "common.h"
@@ -97,7 +99,7 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
   float4 o[2];
   float2 mlk[2], mli[2];
   float io[2];
-  bool init[2];
+  bool init[2], valid[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t j = i + q;
@@ -107,7 +109,9 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
     o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     mlk[q] = mli[q] = make_float2(0.f, 0.f);
     io[q] = 0.f;
-    if ((q == 0 || in_next) && !init[q]) {
+    // same value in every thread: the decisions below are uniform
+    valid[q] = init[q] || __float_as_int(st[kHeadDim + kMaxIdxDim + 4]) == (int32_t)(j + 1);
+    if ((q == 0 || in_next) && !init[q] && valid[q]) {
       o[q] = reinterpret_cast<const float4*>(st)[x];
       mlk[q] = *reinterpret_cast<const float2*>(st + kHeadDim + kMaxIdxDim);
       if (has_ik) {
@@ -117,9 +121,11 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
     }
   }
   __syncthreads();
+  bool finish = false;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     if (q == 1 && !in_next) break;
+    if (!valid[q]) continue;                                     // block opened before this sequence's first append
     const int64_t j = i + q;
     float* st = a.state + ((int64_t)b * 2 + (j & 1)) * kStateFloats;
     float4 A;
@@ -143,6 +149,7 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
       }
     }
     if (q == 0 && ends) {                                        // block i is complete
+      finish = true;
       const float inv = 1.0f / ln;
       kv_e[0] = A.x * inv; kv_e[1] = A.y * inv; kv_e[2] = A.z * inv; kv_e[3] = A.w * inv;
       if (has_ik) ik_e = IA * (1.0f / Iln);
@@ -152,10 +159,11 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
       if (x == 0) {
         *reinterpret_cast<float2*>(st + kHeadDim + kMaxIdxDim) = make_float2(Mn, ln);
         if (has_ik) *reinterpret_cast<float2*>(st + kHeadDim + kMaxIdxDim + 2) = make_float2(IMn, Iln);
+        if (init[q]) st[kHeadDim + kMaxIdxDim + 4] = __int_as_float((int32_t)(j + 1));
       }
     }
   }
-  if (!ends) return;                                            // uniform: t is the same for the block
+  if (!finish) return;                                          // uniform (t and the tag are)
 
   // ---- block i's entry: RMSNorm, RoPE at its last token t; indexer key ----
   const float ss = block_sum(kv_e[0] * kv_e[0] + kv_e[1] * kv_e[1] + kv_e[2] * kv_e[2] + kv_e[3] * kv_e[3], red);

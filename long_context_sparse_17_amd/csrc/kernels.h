@@ -18,9 +18,10 @@ int launch_compress(const CompressArgs& a, hipStream_t stream);
 
 // Decode-step append (per-sequence positions, online pooling state).  State per sequence: two slots
 // of kStateFloats floats: K=V weighted sums [512], indexer weighted sums [kMaxIdxDim], then
-// (M, l) for the K=V and (M, l) for the indexer logits.
+// (M, l) for the K=V, (M, l) for the indexer logits, and the tag (block index + 1, int32 bits; 0 =
+// empty) of the block the slot holds; padded to a multiple of 4 floats.
 constexpr int kMaxIdxDim = 128;
-constexpr int kStateFloats = 512 + kMaxIdxDim + 4;
+constexpr int kStateFloats = 512 + kMaxIdxDim + 8;
 struct DecodeAppendArgs {
   const uint16_t* kv_tok; const float* kv_score; const uint16_t* ik_tok; const float* ik_score;
   const int64_t* pos; int B, m, ov, dI;

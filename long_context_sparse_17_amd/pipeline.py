@@ -1,17 +1,19 @@
 """Decode-step drivers for one CSA or HCA layer, composed from the C-ABI entry points only.
 
-A layer holds its device state (compressed caches, window ring, raw-token staging, weights,
+A layer holds its device state (compressed caches, window ring, pooling state, weights,
 workspaces) and `step()` enqueues one decode step for the query at token t = ctx of every
 sequence, in the order the method runs it (page 1, "hybrid attention", CSA steps 1-4 / HCA):
 
-  CSA: window fill (token t) -> compress the block that ended at t-1 (kv entry + fp8 indexer key)
+  CSA: append token t (window-ring row; pooled state of the blocks containing t)
        -> indexer scores + top-k -> attention over the selected entries + window + sink
        -> grouped output projection
-  HCA: window fill -> compress the 128-token block that ended at t-1 -> dense attention
-       -> grouped output projection
+  HCA: append token t -> dense attention -> grouped output projection
 
-Re-compressing the last finished block every step writes the same values again; it stands for the
-compression work a real decoder does once per m (CSA) or 128 (HCA) steps and is counted every step.
+The caches of tokens [0, ctx) come from the bulk compression; the pooled state of the block that is
+still open at t (CSA: tokens ctx-4 .. ctx-1 of its overlap) is primed by appending those tokens to
+empty slots (the block they end was compressed in bulk and is left alone).
+No block ends at t = ctx, so the step finishes no entry; a block's entry is finished by the append
+of its last token, once every m (CSA) or 128 (HCA) steps.
 """
 from __future__ import annotations
 
@@ -20,7 +22,8 @@ import math
 import torch
 
 from . import (csa_attend, csa_compress_kv, csa_index_topk, csa_index_topk_workspace, attend_workspace,
-               grouped_out_proj, grouped_out_proj_workspace, hca_attend, hca_compress_kv, workspace)
+               grouped_out_proj, grouped_out_proj_workspace, hca_attend, hca_compress_kv, kv_decode_append,
+               kv_decode_state_bytes, workspace)
 
 RING = 256          # window ring rows (>= the 128-token window)
 
@@ -43,6 +46,7 @@ class _Common:
         self.gamma = torch.ones(512, dtype=torch.bfloat16, device=device)
         self.ring = torch.zeros((B, RING, 512), dtype=torch.bfloat16, device=device)
         self.q_pos = torch.full((B, 1), ctx, dtype=torch.int64, device=device)
+        self.state = torch.zeros(kv_decode_state_bytes(B), dtype=torch.uint8, device=device)  # empty slots
         self.sink = nrm((H,), 1.0)
         self.o = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=device)
         self.y = torch.empty((B, d), dtype=torch.bfloat16, device=device)
@@ -58,6 +62,21 @@ class _Common:
         T = tok.shape[1]
         hca_compress_kv(tok, score, tok0=t0, blk_begin=t0, n_blk=T, m=1, gamma_kv=self.gamma, kv_out=self.ring,
                         ring_cap=RING)
+
+    def prime(self, tok, score, ik=None, iks=None, t0=0):
+        """Append raw tokens [t0, t0 + T) one position at a time (kv_decode_append), so that the pooled
+        state holds the open blocks' tokens."""
+        for j in range(tok.shape[1]):
+            pos = torch.full((self.B,), t0 + j, dtype=torch.int64, device=self.dev)
+            kv_decode_append(tok[:, j].contiguous(), score[:, j].contiguous(),
+                             None if ik is None else ik[:, j].contiguous(),
+                             None if iks is None else iks[:, j].contiguous(), pos, **self._append_kw())
+
+    def _append(self):
+        ik = getattr(self, "new_ik", None)
+        iks = getattr(self, "new_is", None)
+        kv_decode_append(self.new_tok.view(self.B, 512), self.new_score.view(self.B), ik, iks, self.q_pos.view(self.B),
+                         **self._append_kw())
 
     def _window_and_proj_tail(self):
         grouped_out_proj(self.o.view(self.B, self.H * 512), self.w_g, self.w_o, H=self.H, y=self.y,
@@ -76,10 +95,8 @@ class CsaDecodeLayer(_Common):
         self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
         self.ik_cache = torch.empty((B, self.n_cap, dI), dtype=torch.uint8, device=device)
         self.ik_scale = torch.empty((B, self.n_cap), dtype=torch.float32, device=device)
-        self.stage_kv = nrm((B, m + ov, 512), 1.28).to(torch.bfloat16)
-        self.stage_s = nrm((B, m + ov), 1.28)
-        self.stage_ik = nrm((B, m + ov, dI), 1.28).to(torch.bfloat16)
-        self.stage_is = nrm((B, m + ov), 1.28)
+        self.new_ik = nrm((B, dI), 1.28).to(torch.bfloat16)
+        self.new_is = nrm((B,), 1.28)
         self.q_idx = nrm((B, 1, H_I, dI), 1.28).to(torch.bfloat16)
         self.w_idx = nrm((B, 1, H_I), 1.28).to(torch.bfloat16)
         self.topk = torch.empty((B, 1, k), dtype=torch.int32, device=device)
@@ -106,16 +123,17 @@ class CsaDecodeLayer(_Common):
             if blk0 + nb == self.n_cap:
                 w0 = max(0, self.ctx - self.W + 1)
                 self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
+                p0 = self.ctx - ov                # the open block at t = ctx starts ov tokens earlier
+                self.prime(kv[:, p0 - t0:], ks[:, p0 - t0:], ik[:, p0 - t0:], iks[:, p0 - t0:], p0)
             del kv, ks, ik, iks
 
+    def _append_kw(self):
+        return dict(m=self.m, overlap=self.ov, gamma_kv=self.gamma, state=self.state, kv_out=self.kv_cache,
+                    win=self.ring, ring_cap=RING, ik_out=self.ik_cache, ik_scale=self.ik_scale, ik_fp8=True)
+
     def step(self):
-        t, m = self.t, self.m
-        self.fill_ring(self.new_tok, self.new_score, t)
-        blk = t // m - 1
-        t0 = blk * m - self.ov
-        csa_compress_kv(self.stage_kv, self.stage_s, self.stage_ik, self.stage_is, tok0=t0, blk_begin=blk, n_blk=1,
-                        m=m, overlap=self.ov, gamma_kv=self.gamma, kv_out=self.kv_cache, ik_out=self.ik_cache,
-                        ik_scale=self.ik_scale, ik_fp8=True)
+        m = self.m
+        self._append()
         csa_index_topk(self.q_idx, self.w_idx, self.ik_cache, self.ik_scale, self.q_pos, n_cap=self.n_cap, m=m,
                        k=self.k, topk_idx=self.topk, ws=self.ws_index)
         csa_attend(self.q, self.gamma, self.kv_cache, self.topk, self.ring, self.sink, self.q_pos, window=self.W,
@@ -129,7 +147,9 @@ class CsaDecodeLayer(_Common):
         index = B * n_vis * (self.dI + 4) + B * self.H_I * (self.dI * 2 + 2)
         attend = B * (min(k, n_vis) + W) * 1024 + B * H * 512 * 2 * 2 + B * k * 4
         proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
-        compress = B * ((self.m + self.ov) * (512 + self.dI) * 2 + 512 * 2 + self.dI + 4) + B * 512 * 4
+        # append: token + key + logits read, ring row written, two pooling-state slots (read + write, write)
+        slot = (512 + 128 + 8) * 4
+        compress = B * ((512 + self.dI) * 2 + 8 + 512 * 2 + 3 * slot)
         return {"index": index, "attend": attend, "proj": proj, "compress": compress}
 
 
@@ -141,8 +161,6 @@ class HcaDecodeLayer(_Common):
         self.m = m
         self.n_cap = ctx // m
         self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
-        self.stage_kv = self._nrm((B, m, 512), 1.28).to(torch.bfloat16)
-        self.stage_s = self._nrm((B, m), 1.28)
         self.ws_attn = workspace(attend_workspace(B, 1, H, self.n_cap + W), device)
 
     def build_caches(self, block_tokens=65536, seed=1):
@@ -162,12 +180,13 @@ class HcaDecodeLayer(_Common):
                 self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
             del kv, ks
 
+    def _append_kw(self):
+        return dict(m=self.m, overlap=0, gamma_kv=self.gamma, state=self.state, kv_out=self.kv_cache, win=self.ring,
+                    ring_cap=RING)
+
     def step(self):
-        t, m = self.t, self.m
-        self.fill_ring(self.new_tok, self.new_score, t)
-        blk = t // m - 1
-        hca_compress_kv(self.stage_kv, self.stage_s, tok0=blk * m, blk_begin=blk, n_blk=1, m=m, gamma_kv=self.gamma,
-                        kv_out=self.kv_cache)
+        m = self.m
+        self._append()
         hca_attend(self.q, self.gamma, self.kv_cache, self.ring, self.sink, self.q_pos, n_cap=self.n_cap, m=m,
                    window=self.W, ring_cap=RING, out=self.o, ws=self.ws_attn)
         self._window_and_proj_tail()
@@ -177,7 +196,7 @@ class HcaDecodeLayer(_Common):
         n_vis = min(self.t // self.m, self.n_cap)
         attend = B * (n_vis + W) * 1024 + B * H * 512 * 2 * 2
         proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
-        compress = B * (self.m * (512 * 2 + 4) + 512 * 2) + B * 512 * 4
+        compress = B * (512 * 2 + 4 + 512 * 2 + (512 + 8) * 4)   # token + logit, ring row, state slot written
         return {"attend": attend, "proj": proj, "compress": compress}
 
 

@@ -103,7 +103,7 @@ def test_compress_rejects_tokens_outside_the_given_columns(lib):
 
 def test_decode_append_rejects_bad_arguments(lib):
     need = lib.kv_decode_state_bytes(8)
-    assert need == 8 * 2 * (512 + 128 + 4) * 4
+    assert need == 8 * 2 * (512 + 128 + 8) * 4
     # kv_tok, kv_score, ik_tok, ik_score, pos, B, m, ov, c, dI, gamma, eps, theta, offset, state, state_bytes,
     # win, win_ld, ring_cap, kv_out, kv_ld, kv_ring, ik_out, ik_scale, ik_ld, ik_dtype, stream
     good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 4, 512, 128, FAKE, 1e-6, 1e4, 0, FAKE, need, FAKE, 256, 256, FAKE,

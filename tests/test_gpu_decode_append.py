@@ -120,6 +120,45 @@ def test_decode_append_serving_loop(mode):
     assert_close(got_kv[b, :nb], to_np_bf16(bulk[0, :nb]), f"{mode} per-token vs bulk")
 
 
+@pytest.mark.parametrize("m,ov", [(4, 4), (128, 0), (4, 2)])
+def test_decode_append_resumes_mid_stream(m, ov):
+    """Sequences resumed at t0 > 0 on zero-filled slots: blocks whose first token comes before t0 are
+    left alone (their rows stay as they were); every block that starts at or after t0 and ends
+    within the appended tokens is written and equals the oracle's."""
+    B, n, off = 2, 300, 77
+    t0s = np.array([1001, 37], dtype=np.int64)
+    cfg = 80 + m + ov
+    T = int(t0s.max()) + n
+    kv = synth.normal_bf16((B, T, 512), 1.28, cfg, 1)
+    ks = synth.normal_f32((B, T), 1.28, cfg, 2)
+    gamma = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 5).random(512, dtype=np.float32))
+    nb_cap = T // m + 2
+    state = torch.zeros(L.kv_decode_state_bytes(B), dtype=torch.uint8, device=DEV)
+    ring = torch.zeros((B, RING, 512), dtype=torch.bfloat16, device=DEV)
+    kv_out = torch.zeros((B, nb_cap, 512), dtype=torch.bfloat16, device=DEV)
+    g_dev = from_bits(gamma)
+    for j in range(n):
+        p = t0s + j
+        L.kv_decode_append(from_bits(np.ascontiguousarray(kv[np.arange(B), p])),
+                           torch.from_numpy(np.ascontiguousarray(ks[np.arange(B), p])).to(DEV),
+                           None, None, torch.from_numpy(p).to(DEV), m=m, overlap=ov, gamma_kv=g_dev, state=state,
+                           kv_out=kv_out, win=ring, ring_cap=RING, rope_offset=off)
+    torch.cuda.synchronize()
+    g64 = synth.bf16_bits_to_f64(gamma)
+    got = to_np_bf16(kv_out)
+    for b in range(B):
+        t0, t1 = int(t0s[b]), int(t0s[b]) + n            # appended positions [t0, t1)
+        first = lambda j: max(0, j * m - ov)              # noqa: E731
+        done = [j for j in range(nb_cap) if first(j) >= t0 and (j + 1) * m <= t1]
+        assert done, "the test must finish blocks"
+        x = synth.bf16_bits_to_f64(kv[b, :t1])
+        x[:t0] = 0.0                                      # tokens never appended take no part
+        ref = O.compress_kv(x, ks[b, :t1].astype(np.float64), m, ov, g64, 1e-6, 10000.0, off)
+        assert_close(got[b, done], ref[done], f"resumed entries b={b} m={m} ov={ov}")
+        untouched = [j for j in range(nb_cap) if j not in done]
+        assert np.all(got[b, untouched] == 0), "blocks opened before the first append must not be written"
+
+
 def test_decode_append_inactive_batch_touches_nothing():
     B = 3
     kv = synth.normal_bf16((B, 512), 1.28, 71, 1)
