@@ -12,6 +12,13 @@ Sources (cited by page and section; the pages are web articles on the V4 release
                CSA + HCA": Flash constants m = 4, indexer 64 heads x 128, top-k 512, m' = 128,
                RoPE on the last 64 dims, one sink logit per head, a window branch per layer type.
   [OFP8]       the OCP 8-bit floating point specification (E4M3FN), for the fp8 code table.
+  [P1 mHC]     page 1, section on mHC (给残差集结加层连续, "a constraint on the residual connection"):
+               n_hc parallel residual streams mixed by a matrix B constrained to the doubly
+               stochastic matrices (rows and columns sum to 1) by Sinkhorn-Knopp, alternating row and
+               column normalisation for 20 iterations per layer; input map A and output map C passed
+               through a sigmoid.
+  [P4 3.2]     page 4, section 3.2 "mHC": the residual mapping constrained to the doubly stochastic
+               manifold; parameters generated dynamically (input-dependent and input-independent parts).
 
 Readings where the pages are silent (each is listed in the design doc):
   R1  pooling logits are one scalar per token, given as input; softmax over the block window.
@@ -26,6 +33,10 @@ Readings where the pages are silent (each is listed in the design doc):
       E4M3FN with a per-row absmax/448 scale; top-k ties go to the lower index; ascending, -1 padded.
   R9  grouped projection: group j = heads [j*H/g, (j+1)*H/g); z_j = o_group . W_g[j]^T; y = z . W_o^T
       (weights stored output-major, [out, in]).
+  R10 mHC: per token the mixing logits are given (their generation from the streams is a projection
+      upstream of the kernel); B = Sinkhorn-Knopp of exp(logits), each round dividing every row by
+      its sum and then every column by its sum; A = sigmoid, C = sigmoid; the streams update as
+      X'_i = sum_j B_ij X_j + C_i y and the next layer's input is h = sum_i A_i X'_i.
 
 All arithmetic is float64 unless a function says it follows the kernel's precision to take the
 same integer decision (fp8 codes of the query rows).
@@ -374,3 +385,47 @@ def hca_layer(kv_tok, kv_score, q, sink, positions, *, m=128, W=128, gamma_kv=No
     win = window_entries(kv_tok, gamma_kv, eps, theta, rope_offset)
     return np.stack([hca_attend_one(q[qi], gamma_q, entries, m, win, sink, t, W, scale,
                                     eps, theta, rope_offset) for qi, t in enumerate(positions)])
+
+
+# ---------------------------------------------------------------------------------------------
+# mHC: mixing of the n_hc residual streams  [P1 mHC], [P4 3.2]
+# ---------------------------------------------------------------------------------------------
+MHC_ITERS = 20        # Sinkhorn-Knopp rounds per layer [P1 mHC]
+
+
+def sigmoid(x):
+    """The map that keeps A and C non-negative and bounded [P1 mHC]."""
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def sinkhorn(logits, iters=MHC_ITERS):
+    """Doubly stochastic projection of one n x n matrix of mixing logits [P1 mHC] (R10): start from
+    the positive matrix exp(logits); each round divides every row by its sum, then every column by
+    its sum (so after any round the columns sum to 1 and the rows approach 1)."""
+    M = np.exp(np.asarray(logits, dtype=np.float64))
+    for _ in range(iters):
+        M = M / M.sum(axis=1, keepdims=True)
+        M = M / M.sum(axis=0, keepdims=True)
+    return M
+
+
+def mhc_mix(X, y, logits, iters=MHC_ITERS):
+    """One residual update of the n streams and the next layer's input, per token [P1 mHC] (R10).
+
+    X [T, n, d] streams; y [T, d] the layer's output; logits [T, n*n + 2n] per token: the mixing
+    logits (row-major), then the output-map logits C~, then the next layer's input-map logits A~.
+    Returns (X' [T, n, d] with X'_i = sum_j B_ij X_j + sigmoid(C~_i) y,  h [T, d] = sum_i sigmoid(A~_i) X'_i).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    L = np.asarray(logits, dtype=np.float64)
+    T, n, d = X.shape
+    Xo = np.empty((T, n, d))
+    h = np.empty((T, d))
+    for t in range(T):
+        B = sinkhorn(L[t, : n * n].reshape(n, n), iters)
+        C = sigmoid(L[t, n * n: n * n + n])
+        A = sigmoid(L[t, n * n + n: n * n + 2 * n])
+        Xo[t] = B @ X[t] + C[:, None] * y[t][None, :]
+        h[t] = A @ Xo[t]
+    return Xo, h

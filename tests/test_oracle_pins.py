@@ -356,3 +356,71 @@ def test_grouped_out_proj_g1_is_two_matmuls():
     o, wg, wo = randn(2, 1024), randn(1, 7, 1024), randn(3, 7)
     z, y = O.grouped_out_proj(o, wg, wo)
     np.testing.assert_allclose(y, np.matmul(np.matmul(o, wg[0].T), wo.T), atol=1e-10)
+
+
+# ------------------------------------------------------------------------------- mHC (Sinkhorn-Knopp)
+def test_sigmoid_anchors():
+    assert O.sigmoid(0.0) == 0.5
+    assert abs(O.sigmoid(math.log(3.0)) - 0.75) < 1e-15          # 1 / (1 + 1/3)
+    assert abs(O.sigmoid(-math.log(3.0)) - 0.25) < 1e-15
+
+
+def test_sinkhorn_uniform_and_rank_one_closed_forms():
+    n = 4
+    assert np.allclose(O.sinkhorn(np.zeros((n, n))), 1.0 / n, atol=1e-15)
+    # exp(a_i + b_j) is rank one: one round (rows, then columns) already gives the uniform matrix
+    a, b = randn(n), randn(n)
+    for it in (1, 20):
+        assert np.allclose(O.sinkhorn(a[:, None] + b[None, :], it), 1.0 / n, atol=1e-14)
+
+
+def test_sinkhorn_one_round_by_hand():
+    """[[1,2],[3,4]]: rows -> [[1/3,2/3],[3/7,4/7]]; column sums 16/21, 26/21 -> [[7/16,7/13],[9/16,6/13]].
+    Columns first would give [[3/7,4/7],[9/17,8/17]]: the order of the two normalisations is pinned."""
+    got = O.sinkhorn(np.log(np.array([[1.0, 2.0], [3.0, 4.0]])), 1)
+    want = np.array([[7 / 16, 7 / 13], [9 / 16, 6 / 13]])
+    assert np.allclose(got, want, atol=1e-15, rtol=0)
+
+
+def test_sinkhorn_2x2_limit_is_the_cross_ratio_form():
+    """The doubly stochastic scaling of a positive [[a,b],[c,d]] is [[p,1-p],[1-p,p]] with
+    p / (1-p) = sqrt(ad / bc) (the cross ratio ad/bc is invariant under row and column scaling)."""
+    for a, b, c, d in [(1, 2, 3, 4), (5.0, 0.1, 0.3, 2.0), (1, 1, 1, 7)]:
+        p = math.sqrt(a * d) / (math.sqrt(a * d) + math.sqrt(b * c))
+        got = O.sinkhorn(np.log(np.array([[a, b], [c, d]], dtype=np.float64)), 500)
+        assert np.allclose(got, [[p, 1 - p], [1 - p, p]], atol=1e-12)
+
+
+def test_sinkhorn_rounds_are_row_shift_invariant_and_converge():
+    L = randn(60, 4, 4, std=1.5)
+    shift = randn(60, 4)
+    for i in range(60):
+        B = O.sinkhorn(L[i])
+        assert np.allclose(B.sum(axis=0), 1.0, atol=1e-14)                 # columns: exact after each round
+        assert np.abs(B.sum(axis=1) - 1.0).max() < 5e-2                   # rows: close after 20 rounds
+        # the rows' L1 distance to 1 never grows from one round to the next, and vanishes in the limit
+        errs = [np.abs(O.sinkhorn(L[i], k).sum(axis=1) - 1.0).sum() for k in range(1, 30)]
+        assert all(e1 <= e0 + 1e-15 for e0, e1 in zip(errs, errs[1:]))
+        assert np.abs(O.sinkhorn(L[i], 400).sum(axis=1) - 1.0).max() < 1e-9
+        # a row shift of the logits is a row scaling, removed by the first row normalisation
+        assert np.allclose(O.sinkhorn(L[i] + shift[i][:, None], 3), O.sinkhorn(L[i], 3), atol=1e-14)
+        # a column shift is removed only in the limit
+        assert np.allclose(O.sinkhorn(L[i] + shift[i][None, :], 400), O.sinkhorn(L[i], 400), atol=1e-10)
+
+
+def test_mhc_mix_by_hand_and_stream_sum():
+    """n = 2, one round: B = [[7/16,7/13],[9/16,6/13]] (above), C = sigmoid(log 3) = 3/4,
+    A = sigmoid(0) = 1/2; every output written out by hand."""
+    X = np.array([[[1.0, -2.0, 0.5], [4.0, 0.25, -1.0]]])
+    y = np.array([[2.0, 1.0, -4.0]])
+    L = np.concatenate([np.log([1.0, 2.0, 3.0, 4.0]), [math.log(3.0)] * 2, [0.0, 0.0]])[None, :]
+    Xo, h = O.mhc_mix(X, y, L, iters=1)
+    x0 = 7 / 16 * X[0, 0] + 7 / 13 * X[0, 1] + 0.75 * y[0]
+    x1 = 9 / 16 * X[0, 0] + 6 / 13 * X[0, 1] + 0.75 * y[0]
+    assert np.allclose(Xo[0], [x0, x1], atol=1e-14)
+    assert np.allclose(h[0], 0.5 * (x0 + x1), atol=1e-14)
+    # with y = 0 the streams' sum is kept whatever the rows sum to (columns sum to 1): B X, not B^T X
+    Xr = randn(6, 4, 8)
+    Lr = randn(6, 24, std=2.0)
+    Xo, _ = O.mhc_mix(Xr, np.zeros((6, 8)), Lr, iters=1)
+    assert np.allclose(Xo.sum(axis=1), Xr.sum(axis=1), atol=1e-12)
