@@ -202,6 +202,26 @@ def decode_append_rows(dev, B):
             "bound": "latency (one workgroup per sequence)"}
 
 
+def mhc_row(dev):
+    """mhc_mix on 4096 tokens x 4 streams x 4096 dims, 20 Sinkhorn-Knopp rounds per token: streams
+    and the layer output read once, new streams and the next input written once."""
+    import torch
+    import long_context_sparse_17_amd as L
+    T, n, d = 4096, 4, 4096
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn((T, n, d), device=dev, generator=g).to(torch.bfloat16)
+    y = torch.randn((T, d), device=dev, generator=g).to(torch.bfloat16)
+    lg = torch.randn((T, n * n + 2 * n), device=dev, generator=g)
+    xo = torch.empty_like(x)
+    h = torch.empty_like(y)
+    us = _event_time_us(lambda: L.mhc_mix(x, y, lg, iters=20, x_out=xo, h_out=h), 20)
+    nbytes = T * (2 * n * d * 2 + 2 * d * 2 + (n * n + 2 * n) * 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"what": "mhc_mix: T=4096 tokens, n=4 streams, d=4096, 20 rounds", "us": round(us, 2),
+            "bytes": nbytes, "achieved_gbs": round(gbs, 1), "bound": "hbm",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,7 +346,7 @@ def main():
     del src, dst
 
     mfma_tflops = mfma_reference(dev)
-    next_rows = {"decode_append": decode_append_rows(dev, B)}
+    next_rows = {"decode_append": decode_append_rows(dev, B), "mhc_mix": mhc_row(dev)}
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None

@@ -133,6 +133,30 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score,
                      void* stream);
 
 /*
+ * mhc_sinkhorn -- the doubly stochastic projection of mHC (page 1, section on mHC: the mixing
+ * matrix of the residual streams is held on the doubly stochastic matrices by Sinkhorn-Knopp,
+ * alternating row and column normalisation, 20 rounds per layer; page 4 section 3.2).  For each of
+ * T matrices: M = exp(logits), then `iters` rounds of (every row / its sum, every column / its
+ * sum).  fp32 throughout.
+ *   logits [T, n, n] fp32 (row-major), b_out [T, n, n] fp32.  1 <= n <= 8, 1 <= iters <= 10000.
+ */
+int mhc_sinkhorn(const float* logits, int T, int n, int iters, float* b_out, void* stream);
+
+/*
+ * mhc_mix -- one mHC residual update of the n streams and the next layer's input, per token
+ * (page 1, section on mHC: streams mixed by B, the layer output spread by the output map C and the
+ * layer input taken by the input map A, both through a sigmoid).  For token t:
+ *   B = mhc_sinkhorn(logits[t, 0 : n*n]),  C = sigmoid(logits[t, n*n : n*n+n]),
+ *   A = sigmoid(logits[t, n*n+n : n*n+2n])  (the next layer's input map),
+ *   x_out[t, i] = sum_j B_ij x[t, j] + C_i y[t]   (bf16, rounded to nearest even),
+ *   h_out[t]    = sum_i A_i x_out[t, i]            (from x_out before its rounding; h_out NULL: skipped).
+ *   x, x_out [T, n, d] bf16 (x_out may be x: in place), y, h_out [T, d] bf16,
+ *   logits [T, n*n + 2n] fp32.  1 <= n <= 8, d % 8 == 0, 1 <= iters <= 10000; 16-byte aligned.
+ */
+int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, int n, int d, int iters,
+            uint16_t* x_out, uint16_t* h_out, void* stream);
+
+/*
  * csa_index_topk -- CSA step 2 (page 1, CSA step 2: lightning indexer + top-k; page 4 section 3.1:
  * 64 indexer heads of dim 128, top-k 512): for each query at token t = q_pos[b, tq] the score of
  * every visible entry s < n_vis = min(t / m, n_cap) is I_s = sum_h w_h * max(0, q_h . k_s); the

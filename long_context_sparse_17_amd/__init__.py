@@ -27,6 +27,8 @@ SIGNATURES = {
     "kv_decode_state_bytes": (_SZ, [_I]),
     "kv_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _P, _I64, _I64,
                               _P, _I64, _I64, _P, _P, _I64, _I, _P]),
+    "mhc_sinkhorn": (_I, [_P, _I, _I, _I, _P, _P]),
+    "mhc_mix": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "lcs_attend_workspace": (_SZ, [_I, _I, _I, _I64]),
@@ -159,6 +161,28 @@ def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gam
                                 ring_cap, _ptr(kv_out), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
                                 LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16, _stream(stream))
     _check("kv_decode_append", st)
+
+
+def mhc_sinkhorn(logits, *, iters=20, out, stream=None):
+    """logits [T, n, n] f32 -> out [T, n, n] f32 (doubly stochastic after Sinkhorn-Knopp)."""
+    import torch
+    T, n, n2 = logits.shape
+    if n != n2:
+        raise ValueError("logits must be [T, n, n]")
+    _dt(logits, torch.float32, "logits"); _dt(out, torch.float32, "out")
+    _check("mhc_sinkhorn", lib().mhc_sinkhorn(_ptr(logits), T, n, iters, _ptr(out), _stream(stream)))
+
+
+def mhc_mix(x, y, logits, *, iters=20, x_out, h_out=None, stream=None):
+    """x [T, n, d] bf16 streams, y [T, d] bf16 layer output, logits [T, n*n + 2n] f32 -> x_out, h_out."""
+    import torch
+    T, n, d = x.shape
+    _bits(x, "x"); _bits(y, "y"); _bits(x_out, "x_out"); _bits(h_out, "h_out")
+    _dt(logits, torch.float32, "logits")
+    if logits.shape != (T, n * n + 2 * n):
+        raise ValueError("logits must be [T, n*n + 2n]")
+    _check("mhc_mix", lib().mhc_mix(_ptr(x), _ptr(y), _ptr(logits), T, n, d, iters, _ptr(x_out), _ptr(h_out),
+                                     _stream(stream)))
 
 
 def csa_index_topk_workspace(B, Tq, n_cap, k):

@@ -208,6 +208,27 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
   return lcs::launch_decode_append(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 
+// ------------------------------------------------------------------------------ mHC
+int mhc_sinkhorn(const float* logits, int T, int n, int iters, float* b_out, void* stream) {
+  if (!logits || !b_out || T <= 0 || iters < 1 || iters > 10000) return LCS_ERR_ARG;
+  if (!aligned4(logits) || !aligned4(b_out)) return LCS_ERR_ARG;
+  if (n < 1 || n > 8) return LCS_ERR_UNSUPPORTED;
+  lcs::MhcArgs a{};
+  a.logits = logits; a.T = T; a.n = n; a.iters = iters; a.b_out = b_out;
+  return lcs::launch_mhc(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
+int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, int n, int d, int iters,
+            uint16_t* x_out, uint16_t* h_out, void* stream) {
+  if (!x || !y || !logits || !x_out || T <= 0 || d <= 0 || iters < 1 || iters > 10000) return LCS_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(x_out) || (h_out && !aligned16(h_out)) || !aligned4(logits))
+    return LCS_ERR_ARG;
+  if (n < 1 || n > 8 || d % 8 != 0) return LCS_ERR_UNSUPPORTED;
+  lcs::MhcArgs a{};
+  a.x = x; a.y = y; a.logits = logits; a.T = T; a.n = n; a.d = d; a.iters = iters; a.x_out = x_out; a.h_out = h_out;
+  return lcs::launch_mhc(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
 // ------------------------------------------------------------------------------ indexer + top-k
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   if (B <= 0 || Tq <= 0 || n_cap <= 0 || k <= 0) return 0;

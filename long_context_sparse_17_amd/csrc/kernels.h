@@ -34,6 +34,14 @@ struct DecodeAppendArgs {
 size_t decode_state_bytes(int B);
 int launch_decode_append(const DecodeAppendArgs& a, hipStream_t stream);
 
+// mHC stream mixing (x != nullptr) or the Sinkhorn-Knopp projection alone (x == nullptr).
+struct MhcArgs {
+  const uint16_t* x; const uint16_t* y; const float* logits;
+  int T, n, d, iters;
+  uint16_t* x_out; uint16_t* h_out; float* b_out;
+};
+int launch_mhc(const MhcArgs& a, hipStream_t stream);
+
 struct IndexArgs {
   const uint16_t* q_idx; const uint16_t* w_idx;
   const void* ik; const float* ik_scale; int64_t ik_ld; int ik_fp8;

@@ -1,0 +1,86 @@
+"""GPU parity of the mHC entry points (Sinkhorn-Knopp projection and the fused stream mixing)
+against the fp64 oracle, on seeded inputs: ragged token counts (not a multiple of the tokens per
+workgroup), ragged widths (d not a multiple of the 2048 dims a workgroup covers per pass), every
+supported stream count, one round and the pages' 20, in place and out of place."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_17_amd as L
+import oracle as O
+import synth
+from lcs_testutil import assert_close, from_bits, to_np_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def assert_bf16_rounding(got, ref, what):
+    """The outputs are stored in bf16: every element within one bf16 quantum (2^-8 relative) of the
+    fp64 value plus a small fp32 allowance, and the relative L2 error within the parity bar."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bad = np.abs(got - ref) > 2.0 ** -8 * np.abs(ref) + 1e-4 * rms
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond bf16 rounding"
+    assert_close(got, ref, what, max_abs=np.inf)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("iters", [1, 20])
+def test_sinkhorn_parity(n, iters):
+    T = 1000
+    Lg = synth.normal_f32((T, n, n), 1.5, 90 + n, iters)
+    out = torch.empty((T, n, n), dtype=torch.float32, device=DEV)
+    L.mhc_sinkhorn(torch.from_numpy(Lg).to(DEV), iters=iters, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = np.stack([O.sinkhorn(Lg[t].astype(np.float64), iters) for t in range(T)])
+    assert np.abs(got - ref).max() < 2e-5
+    assert np.abs(got.sum(axis=1) - 1.0).max() < 1e-5          # columns sum to 1 after the last round
+
+
+def test_sinkhorn_one_round_by_hand_on_gpu():
+    Lg = np.log(np.array([[[1.0, 2.0], [3.0, 4.0]]], dtype=np.float32))
+    out = torch.empty((1, 2, 2), dtype=torch.float32, device=DEV)
+    L.mhc_sinkhorn(torch.from_numpy(Lg).to(DEV), iters=1, out=out)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy()[0], [[7 / 16, 7 / 13], [9 / 16, 6 / 13]], rtol=1e-6)
+
+
+@pytest.mark.parametrize("T,n,d,inplace", [(37, 4, 4096, False), (37, 4, 4096, True), (9, 3, 200, False),
+                                           (6, 8, 1024, True), (5, 1, 8, False)])
+def test_mhc_mix_parity(T, n, d, inplace):
+    cfg = 95 + n + d
+    X = synth.normal_bf16((T, n, d), 1.0, cfg, 1)
+    Y = synth.normal_bf16((T, d), 1.0, cfg, 2)
+    Lg = synth.normal_f32((T, n * n + 2 * n), 1.0, cfg, 3)
+    x_dev = from_bits(X)
+    x_out = x_dev if inplace else torch.empty_like(x_dev)
+    h_out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    L.mhc_mix(x_dev, from_bits(Y), torch.from_numpy(Lg).to(DEV), iters=20, x_out=x_out, h_out=h_out)
+    torch.cuda.synchronize()
+    Xo, h = O.mhc_mix(synth.bf16_bits_to_f64(X), synth.bf16_bits_to_f64(Y), Lg.astype(np.float64), 20)
+    assert_bf16_rounding(to_np_bf16(x_out), Xo, f"streams T={T} n={n} d={d}")
+    assert_bf16_rounding(to_np_bf16(h_out), h, f"next input T={T} n={n} d={d}")
+
+
+def test_mhc_mix_full_size_sampled():
+    """4096 tokens x 4 streams x 4096 dims (the measured shape): 64 seeded tokens checked."""
+    T, n, d = 4096, 4, 4096
+    g = torch.Generator(device=DEV).manual_seed(97)
+    x = torch.randn((T, n, d), device=DEV, generator=g).to(torch.bfloat16)
+    y = torch.randn((T, d), device=DEV, generator=g).to(torch.bfloat16)
+    Lg = torch.randn((T, n * n + 2 * n), device=DEV, generator=g)
+    x_out = torch.empty_like(x)
+    h_out = torch.empty_like(y)
+    L.mhc_mix(x, y, Lg, iters=20, x_out=x_out, h_out=h_out)
+    torch.cuda.synchronize()
+    pick = np.sort(np.random.default_rng(97).choice(T, 64, replace=False))
+    f = lambda t: to_np_bf16(t)  # noqa: E731
+    Xo, h = O.mhc_mix(f(x[pick]), f(y[pick]), Lg[pick].cpu().numpy().astype(np.float64), 20)
+    assert_bf16_rounding(f(x_out[pick]), Xo, "full-size streams")
+    assert_bf16_rounding(f(h_out[pick]), h, "full-size next input")
+    assert math.isfinite(float(h_out.float().abs().max()))
