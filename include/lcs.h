@@ -43,12 +43,14 @@ extern "C" {
 
 #define LCS_OK 0
 #define LCS_ERR_ARG 1          /* NULL pointer, non-positive size, bad stride or misalignment  */
-#define LCS_ERR_UNSUPPORTED 2  /* shape or dtype this build does not implement                */
+#define LCS_ERR_UNSUPPORTED 2  /* shape or dtype the library does not implement                */
 #define LCS_ERR_WORKSPACE 3    /* workspace NULL or smaller than the *_workspace() query      */
 #define LCS_ERR_HIP 4          /* a HIP launch error                                          */
 
 #define LCS_IK_BF16 0          /* indexer keys stored as bf16, no scale                        */
 #define LCS_IK_FP8 1           /* indexer keys stored as E4M3FN codes + one fp32 scale per key */
+#define LCS_KV_BF16 0          /* K=V rows (entries, window ring) stored as bf16               */
+#define LCS_KV_FP8 1           /* K=V rows stored as E4M3FN codes + one fp32 scale per row     */
 
 #define LCS_HEAD_DIM 512       /* c, fixed (page 1, CSA step 4: "c set to 512")                */
 #define LCS_MAX_HEADS 64
@@ -116,7 +118,10 @@ int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score,
  *          appended from t = 0 needs no clearing; a sequence resumed mid-stream (its older blocks
  *          compressed by the bulk path) needs its slots zero-filled once before the first append.
  *          Appending one position twice folds that token in twice.
- *   win    [B, win_ld, c] bf16 ring (win_ld >= ring_cap >= 1); kv_out [B, kv_ld, c] bf16;
+ *   kv_dtype LCS_KV_BF16: win [B, win_ld, c] and kv_out [B, kv_ld, c] bf16 (win_scale, kv_scale
+ *          unused); LCS_KV_FP8: the same rows as E4M3FN codes (uint8) with one scale absmax/448 per
+ *          row in win_scale [B, win_ld] / kv_scale [B, kv_ld] fp32 (the quantiser of kv_quantize_fp8
+ *          applied to the fp32 row).  win_ld >= ring_cap >= 1;
  *   ik_out [B, ik_ld, dI], ik_scale [B, ik_ld] fp32 (fp8).  Rows past kv_ld / ik_ld are not written.
  *   Requirements: c = 512, m >= 1, 0 <= overlap <= m, dI in {64, 128}.
  *   Calls for the same state must be ordered (one stream); concurrent calls on one state race.
@@ -126,11 +131,40 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score,
                      const uint16_t* ik_tok, const float* ik_score,
                      const int64_t* pos, int B, int m, int overlap, int c, int dI,
                      const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
-                     float* state, size_t state_bytes,
-                     uint16_t* win, int64_t win_ld, int64_t ring_cap,
-                     uint16_t* kv_out, int64_t kv_ld, int64_t kv_ring,
+                     float* state, size_t state_bytes, int kv_dtype,
+                     void* win, float* win_scale, int64_t win_ld, int64_t ring_cap,
+                     void* kv_out, float* kv_scale, int64_t kv_ld, int64_t kv_ring,
                      void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype,
                      void* stream);
+
+/*
+ * kv_quantize_fp8 -- fp8 storage of K=V rows (page 2, on HCA's mixed FP4 + FP8 precision: the KV
+ * cache in FP8 halves its memory): each of `rows` 512-dim bf16 rows becomes E4M3FN codes with one
+ * scale absmax/448 (1 for an all-zero row), code = RNE(v / scale) saturating at +-448, with the
+ * scale and the division in fp32 (the indexer keys' quantiser).
+ *   kv [rows, 512] bf16 (16-byte aligned), codes [rows, 512] uint8 (16-byte aligned), scales [rows].
+ */
+int kv_quantize_fp8(const uint16_t* kv, int64_t rows, uint8_t* codes, float* scales, void* stream);
+
+/*
+ * csa_attend_kv8 / hca_attend_kv8 -- csa_attend / hca_attend on fp8 K=V storage: the cache and the
+ * window ring hold E4M3FN codes with one fp32 scale per row (kv_quantize_fp8, or kv_decode_append
+ * with LCS_KV_FP8).  Key j is s_j * code_j: its logit is s_j (qhat . code_j) * scale, and
+ * o = sum_j p_j s_j code_j / (e^{z} + sum_j p_j); the codes are converted exactly to bf16 for the
+ * same MFMA path, so only the storage is fp8.  Arguments as csa_attend / hca_attend with
+ *   kv_codes [B, kv_ld, 512] uint8 + kv_scale [B, kv_ld] fp32,
+ *   win_codes [B, win_ld, 512] uint8 + win_scale [B, win_ld] fp32 (16-byte aligned codes).
+ */
+int csa_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv_codes, const float* kv_scale,
+                   int64_t kv_ld, const int32_t* topk_idx, int k, const uint8_t* win_codes, const float* win_scale,
+                   int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
+                   int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+                   uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+int hca_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv_codes, const float* kv_scale,
+                   int64_t kv_ld, int64_t n_cap, int m, const uint8_t* win_codes, const float* win_scale,
+                   int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
+                   int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+                   uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mhc_sinkhorn -- the doubly stochastic projection of mHC (page 1, section on mHC: the mixing

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
 
 LCS_OK, LCS_ERR_ARG, LCS_ERR_UNSUPPORTED, LCS_ERR_WORKSPACE, LCS_ERR_HIP = 0, 1, 2, 3, 4
 LCS_IK_BF16, LCS_IK_FP8 = 0, 1
+LCS_KV_BF16, LCS_KV_FP8 = 0, 1
 HEAD_DIM = 512
 
 # exported symbols and their C signatures (see include/lcs.h)
@@ -25,8 +26,13 @@ SIGNATURES = {
                              _P, _I64, _I64, _P, _P, _I64, _I, _P]),
     "hca_compress_kv": (_I, [_P, _P, _I, _I, _I64, _I64, _I, _I, _I, _P, _F, _F, _I64, _P, _I64, _I64, _P]),
     "kv_decode_state_bytes": (_SZ, [_I]),
-    "kv_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _P, _I64, _I64,
-                              _P, _I64, _I64, _P, _P, _I64, _I, _P]),
+    "kv_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _I, _P, _P, _I64,
+                              _I64, _P, _P, _I64, _I64, _P, _P, _I64, _I, _P]),
+    "kv_quantize_fp8": (_I, [_P, _I64, _P, _P, _P]),
+    "csa_attend_kv8": (_I, [_P, _P, _P, _P, _I64, _P, _I, _P, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F,
+                            _F, _F, _P, _P, _SZ, _P]),
+    "hca_attend_kv8": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F,
+                            _F, _F, _P, _P, _SZ, _P]),
     "mhc_sinkhorn": (_I, [_P, _I, _I, _I, _P, _P]),
     "mhc_mix": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
@@ -146,21 +152,38 @@ def kv_decode_state_bytes(B):
 
 def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gamma_kv, state, kv_out, kv_ring=0,
                      win=None, ring_cap=0, ik_out=None, ik_scale=None, ik_fp8=True, eps=1e-6, rope_theta=10000.0,
-                     rope_offset=0, stream=None):
+                     rope_offset=0, kv_scale=None, win_scale=None, stream=None):
     """Append token pos[b] of every sequence b (pos < 0: skip).  kv_tok [B,512] bf16, kv_score [B] f32,
-    ik_tok [B,dI] bf16 | None, pos [B] int64, state: uint8 buffer of kv_decode_state_bytes(B) bytes."""
+    ik_tok [B,dI] bf16 | None, pos [B] int64, state: uint8 buffer of kv_decode_state_bytes(B) bytes.
+    kv_out / win bf16, or uint8 E4M3FN codes with kv_scale / win_scale [B, ld] f32 (fp8 K=V)."""
     import torch
     B, c = kv_tok.shape
-    _bits(kv_tok, "kv_tok"); _bits(gamma_kv, "gamma_kv"); _bits(kv_out, "kv_out"); _bits(win, "win")
+    kv8 = kv_out.dtype == torch.uint8
+    _bits(kv_tok, "kv_tok"); _bits(gamma_kv, "gamma_kv")
+    if not kv8:
+        _bits(kv_out, "kv_out"); _bits(win, "win")
+    elif win is not None and win.dtype != torch.uint8:
+        raise TypeError("fp8 K=V: win must hold uint8 codes like kv_out")
     _dt(kv_score, torch.float32, "kv_score"); _dt(ik_score, torch.float32, "ik_score"); _dt(pos, torch.int64, "pos")
     dI = ik_tok.shape[-1] if ik_tok is not None else 0
     ik_ld = ik_out.shape[1] if ik_out is not None else 0
     st = lib().kv_decode_append(_ptr(kv_tok), _ptr(kv_score), _ptr(ik_tok), _ptr(ik_score), _ptr(pos), B, m, overlap,
                                 c, dI, _ptr(gamma_kv), eps, rope_theta, rope_offset, _ptr(state),
-                                state.numel() * state.element_size(), _ptr(win), win.shape[1] if win is not None else 0,
-                                ring_cap, _ptr(kv_out), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
+                                state.numel() * state.element_size(), LCS_KV_FP8 if kv8 else LCS_KV_BF16, _ptr(win),
+                                _ptr(win_scale), win.shape[1] if win is not None else 0, ring_cap, _ptr(kv_out),
+                                _ptr(kv_scale), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
                                 LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16, _stream(stream))
     _check("kv_decode_append", st)
+
+
+def kv_quantize_fp8(kv, *, codes, scales, stream=None):
+    """kv [..., 512] bf16 rows -> codes [..., 512] uint8 (E4M3FN) and scales [...] f32 (absmax / 448)."""
+    import torch
+    _bits(kv, "kv"); _dt(codes, torch.uint8, "codes"); _dt(scales, torch.float32, "scales")
+    rows = kv.numel() // 512
+    if codes.numel() != rows * 512 or scales.numel() != rows:
+        raise ValueError("codes / scales do not match kv")
+    _check("kv_quantize_fp8", lib().kv_quantize_fp8(_ptr(kv), rows, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def mhc_sinkhorn(logits, *, iters=20, out, stream=None):
@@ -209,13 +232,23 @@ def attend_workspace(B, Tq, H, max_keys):
 
 
 def csa_attend(q, gamma_q, kv_cache, topk_idx, win_ring, sink, q_pos, *, window, ring_cap, out, scale=None,
-               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, stream=None):
-    """q [B,Tq,H,512] bf16 raw; kv_cache [B,kv_ld,512]; topk_idx [B,Tq,k] int32; win_ring [B,win_ld,512]."""
+               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, kv_scale=None, win_scale=None, stream=None):
+    """q [B,Tq,H,512] bf16 raw; kv_cache [B,kv_ld,512]; topk_idx [B,Tq,k] int32; win_ring [B,win_ld,512].
+    kv_cache / win_ring bf16, or uint8 E4M3FN codes with kv_scale / win_scale [B, ld] f32 (fp8 K=V)."""
+    import torch
     B, Tq, H, c = q.shape
     k = topk_idx.shape[-1]
     scale = 1.0 / (c ** 0.5) if scale is None else scale
     if ws is None:
         ws = workspace(attend_workspace(B, Tq, H, k + window), q.device)
+    if kv_cache.dtype == torch.uint8:
+        st = lib().csa_attend_kv8(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), _ptr(kv_scale), kv_cache.shape[1],
+                                  _ptr(topk_idx), k, _ptr(win_ring), _ptr(win_scale),
+                                  win_ring.shape[1] if win_ring is not None else 0, ring_cap, window, _ptr(sink),
+                                  _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps, rope_theta, _ptr(out), _ptr(ws),
+                                  ws.numel(), _stream(stream))
+        _check("csa_attend_kv8", st)
+        return
     st = lib().csa_attend(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), kv_cache.shape[1], _ptr(topk_idx), k,
                           _ptr(win_ring), win_ring.shape[1] if win_ring is not None else 0, ring_cap, window,
                           _ptr(sink), _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps, rope_theta, _ptr(out),
@@ -224,12 +257,20 @@ def csa_attend(q, gamma_q, kv_cache, topk_idx, win_ring, sink, q_pos, *, window,
 
 
 def hca_attend(q, gamma_q, kv_cache, win_ring, sink, q_pos, *, n_cap, m, window, ring_cap, out, scale=None,
-               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, stream=None):
-    """Dense attention over entries 0 .. min(t/m, n_cap)-1 plus the window."""
+               eps=1e-6, rope_theta=10000.0, rope_offset=0, ws=None, kv_scale=None, win_scale=None, stream=None):
+    """Dense attention over entries 0 .. min(t/m, n_cap)-1 plus the window (bf16 or fp8 K=V, as csa_attend)."""
+    import torch
     B, Tq, H, c = q.shape
     scale = 1.0 / (c ** 0.5) if scale is None else scale
     if ws is None:
         ws = workspace(attend_workspace(B, Tq, H, n_cap + window), q.device)
+    if kv_cache.dtype == torch.uint8:
+        st = lib().hca_attend_kv8(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), _ptr(kv_scale), kv_cache.shape[1], n_cap, m,
+                                  _ptr(win_ring), _ptr(win_scale), win_ring.shape[1] if win_ring is not None else 0,
+                                  ring_cap, window, _ptr(sink), _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps,
+                                  rope_theta, _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+        _check("hca_attend_kv8", st)
+        return
     st = lib().hca_attend(_ptr(q), _ptr(gamma_q), _ptr(kv_cache), kv_cache.shape[1], n_cap, m, _ptr(win_ring),
                           win_ring.shape[1] if win_ring is not None else 0, ring_cap, window, _ptr(sink),
                           _ptr(q_pos), rope_offset, B, Tq, H, c, scale, eps, rope_theta, _ptr(out), _ptr(ws),

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblcs.so")
-SOURCES = ["api.hip", "compress.hip", "decode_append.hip", "mhc.hip", "index_topk.hip", "attend.hip", "out_proj.hip"]
+SOURCES = ["api.hip", "compress.hip", "decode_append.hip", "mhc.hip", "kv_fp8.hip", "index_topk.hip", "attend.hip", "out_proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -178,8 +178,9 @@ size_t kv_decode_state_bytes(int B) { return B > 0 ? lcs::decode_state_bytes(B) 
 int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
                      const int64_t* pos, int B, int m, int overlap, int c, int dI, const uint16_t* gamma_kv,
                      float eps, float rope_theta, int64_t rope_offset, float* state, size_t state_bytes,
-                     uint16_t* win, int64_t win_ld, int64_t ring_cap, uint16_t* kv_out, int64_t kv_ld,
-                     int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype, void* stream) {
+                     int kv_dtype, void* win, float* win_scale, int64_t win_ld, int64_t ring_cap, void* kv_out,
+                     float* kv_scale, int64_t kv_ld, int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld,
+                     int ik_dtype, void* stream) {
   if (!kv_tok || !kv_score || !pos || !gamma_kv || !state || !kv_out) return LCS_ERR_ARG;
   if (B <= 0 || m <= 0 || overlap < 0 || kv_ld <= 0 || kv_ring < 0) return LCS_ERR_ARG;
   if (!(eps >= 0.f) || !(rope_theta > 0.f)) return LCS_ERR_ARG;
@@ -189,6 +190,9 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
   if (c != LCS_HEAD_DIM) return LCS_ERR_UNSUPPORTED;
   if (overlap > m) return LCS_ERR_UNSUPPORTED;                 // a token lies in at most two blocks
   if (state_bytes < lcs::decode_state_bytes(B)) return LCS_ERR_WORKSPACE;
+  if (kv_dtype != LCS_KV_BF16 && kv_dtype != LCS_KV_FP8) return LCS_ERR_UNSUPPORTED;
+  const bool kv8 = kv_dtype == LCS_KV_FP8;
+  if (kv8 && (!kv_scale || !aligned4(kv_scale) || (win && (!win_scale || !aligned4(win_scale))))) return LCS_ERR_ARG;
   if (kv_ring > kv_ld) return LCS_ERR_ARG;
   if (win && (ring_cap <= 0 || win_ld < ring_cap || !aligned16(win))) return LCS_ERR_ARG;
   const bool has_ik = ik_tok != nullptr;
@@ -204,8 +208,17 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
   a.gamma = gamma_kv; a.eps = eps; a.theta = rope_theta; a.rope_offset = rope_offset;
   a.state = state; a.win = win; a.win_ld = win_ld; a.ring_cap = ring_cap;
   a.kv_out = kv_out; a.kv_ld = kv_ld; a.kv_ring = kv_ring;
+  a.kv8 = kv8; a.win_scale = win_scale; a.kv_scale = kv_scale;
   a.ik_out = ik_out; a.ik_scale = ik_scale; a.ik_ld = ik_ld; a.ik_fp8 = ik_dtype == LCS_IK_FP8;
   return lcs::launch_decode_append(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
+// ------------------------------------------------------------------------------ fp8 K=V rows
+int kv_quantize_fp8(const uint16_t* kv, int64_t rows, uint8_t* codes, float* scales, void* stream) {
+  if (!kv || !codes || !scales || rows <= 0) return LCS_ERR_ARG;
+  if (!aligned16(kv) || !aligned16(codes) || !aligned4(scales)) return LCS_ERR_ARG;
+  if (rows > ((int64_t)1 << 33)) return LCS_ERR_UNSUPPORTED;
+  return lcs::launch_kv_quantize(kv, rows, codes, scales, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 
 // ------------------------------------------------------------------------------ mHC
@@ -267,8 +280,11 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
                          const int32_t* topk_idx, int k, int64_t n_cap, int m, const uint16_t* win_ring,
                          int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
                          int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
-                         uint16_t* out, void* ws, size_t ws_bytes, void* stream, int64_t max_keys) {
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream, int64_t max_keys,
+                         const float* kv_scale = nullptr, const float* win_scale = nullptr, bool kv8 = false) {
   if (!q || !gamma_q || !kv_cache || !sink || !q_pos || !out) return LCS_ERR_ARG;
+  if (kv8 && (!kv_scale || !aligned4(kv_scale) || (window > 0 && (!win_scale || !aligned4(win_scale)))))
+    return LCS_ERR_ARG;
   if (window > 0 && !win_ring) return LCS_ERR_ARG;
   if (B <= 0 || Tq <= 0 || H <= 0 || kv_ld <= 0 || window < 0 || ring_cap < 0) return LCS_ERR_ARG;
   if (window > 0 && win_ld <= 0) return LCS_ERR_ARG;
@@ -282,8 +298,11 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
   if (!ws || ws_bytes < lcs::attend_workspace(B, Tq, H, max_keys)) return LCS_ERR_WORKSPACE;
   if (!aligned16(ws)) return LCS_ERR_ARG;
   lcs::AttendArgs a;
-  a.q = q; a.gamma_q = gamma_q; a.kv = kv_cache; a.kv_ld = kv_ld; a.topk = topk_idx; a.k = k; a.n_cap = n_cap;
-  a.m = m; a.win = win_ring; a.win_ld = win_ld; a.ring_cap = ring_cap; a.window = window; a.sink = sink;
+  a.q = q; a.gamma_q = gamma_q; a.kv = kv8 ? nullptr : kv_cache; a.kv_ld = kv_ld; a.topk = topk_idx; a.k = k;
+  a.n_cap = n_cap;
+  a.kv8 = kv8 ? reinterpret_cast<const uint8_t*>(kv_cache) : nullptr; a.kv_scale = kv_scale;
+  a.win8 = kv8 ? reinterpret_cast<const uint8_t*>(win_ring) : nullptr; a.win_scale = win_scale;
+  a.m = m; a.win = kv8 ? nullptr : win_ring; a.win_ld = win_ld; a.ring_cap = ring_cap; a.window = window; a.sink = sink;
   a.q_pos = q_pos; a.rope_offset = rope_offset; a.B = B; a.Tq = Tq; a.H = H; a.scale = scale; a.eps = eps;
   a.theta = rope_theta; a.out = out; a.ws = ws; a.ws_bytes = ws_bytes;
   return lcs::launch_attend(a, max_keys, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
@@ -310,6 +329,32 @@ int hca_attend(const uint16_t* q, const uint16_t* gamma_q, const uint16_t* kv_ca
   return attend_common(q, gamma_q, kv_cache, kv_ld, nullptr, 0, n_cap, m, win_ring, win_ld, ring_cap, window,
                        sink, q_pos, rope_offset, B, Tq, H, c, scale, eps, rope_theta, out, ws, ws_bytes, stream,
                        n_cap + window);
+}
+
+int csa_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv_codes, const float* kv_scale,
+                   int64_t kv_ld, const int32_t* topk_idx, int k, const uint8_t* win_codes, const float* win_scale,
+                   int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
+                   int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+                   uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_idx || k <= 0) return LCS_ERR_ARG;
+  if (!aligned4(topk_idx)) return LCS_ERR_ARG;
+  if (k > LCS_MAX_TOPK) return LCS_ERR_UNSUPPORTED;
+  return attend_common(q, gamma_q, reinterpret_cast<const uint16_t*>(kv_codes), kv_ld, topk_idx, k, 0, 1,
+                       reinterpret_cast<const uint16_t*>(win_codes), win_ld, ring_cap, window, sink, q_pos,
+                       rope_offset, B, Tq, H, c, scale, eps, rope_theta, out, ws, ws_bytes, stream,
+                       (int64_t)k + window, kv_scale, win_scale, true);
+}
+
+int hca_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv_codes, const float* kv_scale,
+                   int64_t kv_ld, int64_t n_cap, int m, const uint8_t* win_codes, const float* win_scale,
+                   int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
+                   int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
+                   uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (m <= 0 || n_cap < 0 || n_cap > kv_ld) return LCS_ERR_ARG;
+  return attend_common(q, gamma_q, reinterpret_cast<const uint16_t*>(kv_codes), kv_ld, nullptr, 0, n_cap, m,
+                       reinterpret_cast<const uint16_t*>(win_codes), win_ld, ring_cap, window, sink, q_pos,
+                       rope_offset, B, Tq, H, c, scale, eps, rope_theta, out, ws, ws_bytes, stream, n_cap + window,
+                       kv_scale, win_scale, true);
 }
 
 // ------------------------------------------------------------------------------ grouped projection

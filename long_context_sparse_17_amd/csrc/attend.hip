@@ -34,6 +34,9 @@ constexpr int kHeadSlots = 16 * kWaves;   // heads handled by one workgroup (all
 constexpr int kMaxSplitKeys = 2048;       // keys of one split, staged as row indices in LDS
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 GU32x4;   // global address space: global_load, not flat
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 GU32x2;
+typedef __bf16 bf16x2_cv __attribute__((ext_vector_type(2)));
 constexpr int kVtStride = 136;            // bf16 per LDS row of a 128-dim slice (128 + 8 pad: rows 4 banks apart)
 constexpr float kLog2e = 1.4426950408889634f;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -43,6 +46,8 @@ typedef __attribute__((address_space(3))) const uint16_t LdsU16;
 struct AttnK {
   const uint16_t* q; const uint16_t* gamma_q;
   const uint16_t* kv; int64_t kv_ld;
+  const uint8_t* kv8; const float* kv_scale;     // fp8 K=V: E4M3FN codes [.., 512] + one scale per row
+  const uint8_t* win8; const float* win_scale;
   const int32_t* topk; int k;
   int64_t n_cap; int m;
   const uint16_t* win; int64_t win_ld, ring_cap; int window;
@@ -57,7 +62,18 @@ struct AttnK {
 // rows 272 B apart, the 16 rows a K-fragment read touches start 4 banks apart (no conflicts).
 __device__ __forceinline__ int vt_row(int kb, int r16) { return kb * 16 + r16; }
 
-template <bool LIST>
+// Four E4M3FN codes (dims 4j .. 4j+3 of a chunk) -> two bf16 pairs, exactly (every E4M3FN value is a
+// bf16 value): the gfx950 conversion with unit scale, byte 0 to the low half.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true)));
+}
+
+// F8: the K=V rows (compressed entries and window ring) are E4M3FN codes with one fp32 scale per row;
+// tiles are converted to bf16 (exactly) when staged in LDS, and each key's scale multiplies its
+// logit and, for PV, its probability (o = sum_j p_j s_j code_j), so the MFMAs are those of the bf16
+// path on the codes.
+template <bool LIST, bool F8>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
@@ -67,6 +83,7 @@ attend_kernel(AttnK a) {
   __shared__ float s_fac[kHeadSlots];
   __shared__ float s_cos[32], s_sin[32];
   __shared__ int32_t s_rows[kMaxSplitKeys];                 // per key of this split: cache/ring row, -1 = none
+  __shared__ float4 s_sc[kWaves][2][kTile / 4];             // F8: each wave's copy of the tile's key scales
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -89,8 +106,31 @@ attend_kernel(AttnK a) {
   // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
   uint4 kb0[2][4], kb1[2][4];
+  float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};           // F8: scales of the buffers' keys kb*16 + c16
   uint32_t vb0 = 0, vb1 = 0;
-  if (!LIST) {
+  if (!LIST && F8) {
+    const uint8_t* kv8_b = a.kv8 + b * a.kv_ld * kHeadDim;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int64_t e0 = e_begin + kb * 16 + c16, e1 = e0 + kTile;
+      e0 = e0 < a.kv_ld ? e0 : a.kv_ld - 1;
+      e1 = e1 < a.kv_ld ? e1 : a.kv_ld - 1;
+      GU32x2* p0 = reinterpret_cast<GU32x2*>(reinterpret_cast<uintptr_t>(kv8_b + e0 * kHeadDim + 128 * w + 8 * g));
+      GU32x2* p1 = reinterpret_cast<GU32x2*>(reinterpret_cast<uintptr_t>(kv8_b + e1 * kHeadDim + 128 * w + 8 * g));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x2 x = p0[4 * ks];
+        kb0[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x2 x = p1[4 * ks];
+        kb1[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
+      }
+      sc0[kb] = a.kv_scale[b * a.kv_ld + e0];
+      sc1[kb] = a.kv_scale[b * a.kv_ld + e1];
+    }
+  } else if (!LIST) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int64_t e0 = e_begin + kb * 16 + c16, e1 = e0 + kTile;
@@ -183,24 +223,36 @@ attend_kernel(AttnK a) {
     const uint32_t b0 = (uint32_t)__ballot(rr[0] >= 0), b1 = (uint32_t)__ballot(rr[1] >= 0);
     vmask = (b0 & 0xFFFFu) | (b1 << 16);   // bit j: key j of the tile exists (lanes 0..15 hold keys c16)
   };
-  auto issue_tile = [&](int i0, const int32_t (&rr)[2], uint4 (&kf)[2][4]) {
+  auto issue_tile = [&](int i0, const int32_t (&rr)[2], uint4 (&kf)[2][4], float (&sf)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint16_t* base = (i0 + kb * 16 + c16) < nc_local ? kv_b : win_b;
-      // always a readable row (row 0 when the key does not exist): no predicated loads
-      GU32x4* p = reinterpret_cast<GU32x4*>(reinterpret_cast<uintptr_t>(
-          base + (int64_t)(rr[kb] > 0 ? rr[kb] : 0) * kHeadDim + 128 * w + 8 * g));
+      const bool comp = (i0 + kb * 16 + c16) < nc_local;
+      const int64_t row = rr[kb] > 0 ? rr[kb] : 0;   // always a readable row (row 0 when the key does not exist)
+      if (F8) {
+        const uint8_t* base = comp ? a.kv8 + b * a.kv_ld * kHeadDim : a.win8 + b * a.win_ld * kHeadDim;
+        GU32x2* p = reinterpret_cast<GU32x2*>(reinterpret_cast<uintptr_t>(base + row * kHeadDim + 128 * w + 8 * g));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 x = p[4 * ks];
-        kf[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x2 x = p[4 * ks];
+          kf[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
+        }
+        sf[kb] = comp ? a.kv_scale[b * a.kv_ld + row] : a.win_scale[b * a.win_ld + row];
+      } else {
+        const uint16_t* base = comp ? kv_b : win_b;
+        // no predicated loads
+        GU32x4* p = reinterpret_cast<GU32x4*>(reinterpret_cast<uintptr_t>(base + row * kHeadDim + 128 * w + 8 * g));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 x = p[4 * ks];
+          kf[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+        }
       }
     }
   };
-  auto load_tile = [&](int i0, uint4 (&kf)[2][4], uint32_t& vmask) {
+  auto load_tile = [&](int i0, uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask) {
     int32_t rr[2];
     tile_rows(i0, rr, vmask);
-    issue_tile(i0, rr, kf);
+    issue_tile(i0, rr, kf, sf);
   };
   // Two register buffers; an empty split reads row 0.  A load past the end re-reads the last
   // tile, whose copy is never scored.
@@ -212,8 +264,8 @@ attend_kernel(AttnK a) {
     int32_t r0[2], r1[2];
     tile_rows(tile0(0), r0, vb0);
     tile_rows(tile0(1), r1, vb1);
-    issue_tile(tile0(0), r0, kb0);
-    issue_tile(tile0(1), r1, kb1);
+    issue_tile(tile0(0), r0, kb0, sc0);
+    issue_tile(tile0(1), r1, kb1, sc1);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -268,9 +320,20 @@ attend_kernel(AttnK a) {
   // Tile registers -> this wave's LDS slice of `slot` (invalid keys zeroed), then the buffer is
   // refilled with the tile at next_i0, whose rows rn and mask vn were looked up earlier.  Returns
   // the staged tile's key mask.
-  auto stage = [&](uint4 (&kf)[2][4], uint32_t& vmask, int slot, int next_i0, const int32_t (&rn)[2],
-                   uint32_t vn) -> uint32_t {
+  auto stage = [&](uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, int slot, int next_i0,
+                   const int32_t (&rn)[2], uint32_t vn) -> uint32_t {
     const uint32_t vm = vmask;
+    if (F8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint2 lo = e4m3x4_to_bf16(kf[kb][ks].x), hi = e4m3x4_to_bf16(kf[kb][ks].y);
+          kf[kb][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        if (g == 0) reinterpret_cast<float*>(s_sc[w][slot])[kb * 16 + c16] = sf[kb];
+      }
+    }
     if (vm != 0xFFFFFFFFu) {               // ragged or missing keys: zero their rows
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -286,7 +349,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(&sl[vr * kVtStride + 32 * ks + 8 * g]) = kf[kb][ks];
     }
-    issue_tile(next_i0, rn, kf);
+    issue_tile(next_i0, rn, kf, sf);
     vmask = vn;
     return vm;
   };
@@ -324,13 +387,21 @@ attend_kernel(AttnK a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     float sc[2][4];
+    float ksc[2][4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};   // F8: scales of keys kb*16 + 4g + i
+    if (F8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 f = s_sc[w][slot][kb * 4 + g];
+        ksc[kb][0] = f.x; ksc[kb][1] = f.y; ksc[kb][2] = f.z; ksc[kb][3] = f.w;
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool v = (vm >> (kb * 16 + 4 * g + i)) & 1u;
-        sc[kb][i] = v ? acc[kb][i] * a.scale_log2 : -INFINITY;
+        sc[kb][i] = v ? acc[kb][i] * (F8 ? ksc[kb][i] * a.scale_log2 : a.scale_log2) : -INFINITY;
         tmax = fmaxf(tmax, sc[kb][i]);
       }
     tmax = max_rows4(tmax);
@@ -349,10 +420,21 @@ attend_kernel(AttnK a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pe[kb * 4 + i] = exp2f(sc[kb][i] - mr);
+      if (F8) {
+        // PV weights bf16(p_j s_j); the normaliser sums the same rounded weights over s_j, so
+        // numerator and denominator see one rounding of p_j, as in the bf16 path
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pk[j] = pack_bf2(pe[2 * j], pe[2 * j + 1]);
-        psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+        for (int j = 0; j < 4; ++j) {
+          const float s0 = ksc[j >> 1][(2 * j) & 3], s1 = ksc[j >> 1][(2 * j + 1) & 3];
+          pk[j] = pack_bf2(pe[2 * j] * s0, pe[2 * j + 1] * s1);
+          psum += bf2f_lo(pk[j]) * __builtin_amdgcn_rcpf(s0) + bf2f_hi(pk[j]) * __builtin_amdgcn_rcpf(s1);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pk[j] = pack_bf2(pe[2 * j], pe[2 * j + 1]);
+          psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+        }
       }
     }
     psum = sum_rows4(psum);
@@ -388,8 +470,8 @@ attend_kernel(AttnK a) {
   // wave before the previous barrier) and issues the loads of tile t+3; one barrier.
   for (int pass = 0;; ++pass) {
     if (pass > 0) {                        // second pass: the first two tiles again
-      load_tile(tile0(0), kb0, vb0);
-      load_tile(tile0(1), kb1, vb1);
+      load_tile(tile0(0), kb0, sc0, vb0);
+      load_tile(tile0(1), kb1, sc1, vb1);
       m_ref = m_max;
       l_run = 0.f;
     }
@@ -400,21 +482,21 @@ attend_kernel(AttnK a) {
     int32_t rn[2];
     uint32_t vn;
     tile_rows(tile0(2), rn, vn);
-    uint32_t vm0 = stage(kb0, vb0, 0, tile0(2), rn, vn);   // tile 0 -> slot 0, buffer 0 <- tile 2
+    uint32_t vm0 = stage(kb0, sc0, vb0, 0, tile0(2), rn, vn);   // tile 0 -> slot 0, buffer 0 <- tile 2
     uint32_t vm1 = 0;
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
       tile_rows(tile0(t + 3), rn, vn);              // row lookups first: their latency hides under QK
       score(0, vm0);
       if (t > 0) accumulate(1);
-      vm1 = stage(kb1, vb1, 1, tile0(t + 3), rn, vn);      // tile t+1 -> slot 1, buffer 1 <- tile t+3
+      vm1 = stage(kb1, sc1, vb1, 1, tile0(t + 3), rn, vn);      // tile t+1 -> slot 1, buffer 1 <- tile t+3
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 >= ntiles) break;
       tile_rows(tile0(t + 4), rn, vn);
       score(1, vm1);
       accumulate(0);
-      vm0 = stage(kb0, vb0, 0, tile0(t + 4), rn, vn);      // tile t+2 -> slot 0, buffer 0 <- tile t+4
+      vm0 = stage(kb0, sc0, vb0, 0, tile0(t + 4), rn, vn);      // tile t+2 -> slot 0, buffer 0 <- tile t+4
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -622,8 +704,15 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
                                        al256((size_t)R * a.nsplit * x.H * kHeadDim * 2));
   const dim3 grid((unsigned)a.nsplit, (unsigned)R);
-  if (x.topk) LCS_LAUNCH("attend_kernel", attend_kernel<true>, grid, dim3(256), 0, st, a);
-  else LCS_LAUNCH("attend_kernel", attend_kernel<false>, grid, dim3(256), 0, st, a);
+  a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
+  const bool f8 = x.kv8 != nullptr;
+  if (x.topk) {
+    if (f8) LCS_LAUNCH("attend_kernel", (attend_kernel<true, true>), grid, dim3(256), 0, st, a);
+    else LCS_LAUNCH("attend_kernel", (attend_kernel<true, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (f8) LCS_LAUNCH("attend_kernel", (attend_kernel<false, true>), grid, dim3(256), 0, st, a);
+    else LCS_LAUNCH("attend_kernel", (attend_kernel<false, false>), grid, dim3(256), 0, st, a);
+  }
   if (a.nsplit > 1) {
     LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(kMergeThreads), 0, st,
                a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.out);

@@ -4,7 +4,8 @@
 // A token t of sequence b is (1) written to the window ring as RoPE_t(RMSNorm(kv)), (2) folded into
 // the pooling state of every block that contains it, and (3) when t is the last token of block i,
 // block i's entry is finished: pooled vector RMSNorm'd, rotated to t and stored, with the indexer
-// key (own logits, no norm, no RoPE) stored as bf16 or E4M3FN codes + scale.  The pooled vector is
+// key (own logits, no norm, no RoPE) stored as bf16 or E4M3FN codes + scale.  Ring rows and
+// entries are stored as bf16, or (kv8) as E4M3FN codes with one scale absmax / 448 per row.  The pooled vector is
 // the same softmax-weighted sum the bulk compression forms, accumulated online as tokens arrive:
 // a running max M, sum l = sum e^{s_j - M} and weighted sums acc = sum e^{s_j - M} x_j (fp32),
 // rescaled when M grows; entry = acc / l.
@@ -55,6 +56,27 @@ __device__ __forceinline__ void rope4(float (&y)[4], int d0, double pos, const R
   }
 }
 
+// Row (b, row) of a [B, ld, 512] K=V store from this thread's 4 dims: bf16, or (kv8) E4M3FN codes with
+// the row's scale absmax / 448 (block-wide max; every thread must call it).  ok = false: not stored.
+__device__ __forceinline__ void store_kv_row(const DecodeAppendArgs& a, void* base, float* scale, int64_t b,
+                                             int64_t ld, int64_t row, bool ok, const float (&y)[4], float* red) {
+  const int x = threadIdx.x;
+  const int64_t off = (b * ld + row) * kHeadDim + 4 * x;
+  if (a.kv8) {
+    const float amax = block_max(fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))), red);
+    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    uint32_t c = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c |= f2e4m3(__fdiv_rn(y[k], sc)) << (8 * k);
+    if (ok) {
+      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + off) = c;
+      if (x == 0) scale[b * ld + row] = sc;
+    }
+  } else if (ok) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
   __shared__ float red[2];
@@ -84,9 +106,7 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = v[i] * rstd * g4[i];
     rope4(y, 4 * x, (double)(t + a.rope_offset), rf);
-    const int64_t row = t % a.ring_cap;
-    *reinterpret_cast<uint2*>(a.win + ((int64_t)b * a.win_ld + row) * kHeadDim + 4 * x) =
-        make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+    store_kv_row(a, a.win, a.win_scale, b, a.win_ld, t % a.ring_cap, true, y, red);
   }
 
   // ---- pooling state of the blocks containing t: i = t / m and, inside the overlap, i + 1 ----
@@ -173,9 +193,7 @@ decode_append_kernel(DecodeAppendArgs a, RopeFreq rf) {
   for (int k = 0; k < 4; ++k) y[k] = kv_e[k] * rstd * g4[k];
   rope4(y, 4 * x, (double)(t + a.rope_offset), rf);
   const int64_t row = a.kv_ring > 0 ? i % a.kv_ring : i;
-  if (row < a.kv_ld)
-    *reinterpret_cast<uint2*>(a.kv_out + ((int64_t)b * a.kv_ld + row) * kHeadDim + 4 * x) =
-        make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+  store_kv_row(a, a.kv_out, a.kv_scale, b, a.kv_ld, row, row < a.kv_ld, y, red);
   if (!has_ik) return;
   const bool ik_row_ok = i < a.ik_ld;
   if (a.ik_fp8) {

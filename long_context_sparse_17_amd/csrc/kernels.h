@@ -27,12 +27,15 @@ struct DecodeAppendArgs {
   const int64_t* pos; int B, m, ov, dI;
   const uint16_t* gamma; float eps, theta; int64_t rope_offset;
   float* state;
-  uint16_t* win; int64_t win_ld, ring_cap;
-  uint16_t* kv_out; int64_t kv_ld, kv_ring;
+  void* win; int64_t win_ld, ring_cap;
+  void* kv_out; int64_t kv_ld, kv_ring;
+  int kv8; float* win_scale; float* kv_scale;   // kv8: ring rows and entries as E4M3FN codes + row scales
   void* ik_out; float* ik_scale; int64_t ik_ld; int ik_fp8;
 };
 size_t decode_state_bytes(int B);
 int launch_decode_append(const DecodeAppendArgs& a, hipStream_t stream);
+
+int launch_kv_quantize(const uint16_t* kv, int64_t rows, uint8_t* codes, float* scales, hipStream_t stream);
 
 // mHC stream mixing (x != nullptr) or the Sinkhorn-Knopp projection alone (x == nullptr).
 struct MhcArgs {
@@ -56,6 +59,8 @@ int launch_index_topk(const IndexArgs& a, hipStream_t stream);
 struct AttendArgs {
   const uint16_t* q; const uint16_t* gamma_q;
   const uint16_t* kv; int64_t kv_ld;
+  const uint8_t* kv8; const float* kv_scale;     // fp8 K=V (kv8 != nullptr): codes + per-row scales
+  const uint8_t* win8; const float* win_scale;   //   for the cache and the window ring
   const int32_t* topk; int k;          // CSA: selected entries (topk != nullptr)
   int64_t n_cap; int m;                // HCA: all visible entries
   const uint16_t* win; int64_t win_ld, ring_cap; int window;

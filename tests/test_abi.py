@@ -105,9 +105,10 @@ def test_decode_append_rejects_bad_arguments(lib):
     need = lib.kv_decode_state_bytes(8)
     assert need == 8 * 2 * (512 + 128 + 8) * 4
     # kv_tok, kv_score, ik_tok, ik_score, pos, B, m, ov, c, dI, gamma, eps, theta, offset, state, state_bytes,
-    # win, win_ld, ring_cap, kv_out, kv_ld, kv_ring, ik_out, ik_scale, ik_ld, ik_dtype, stream
-    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 4, 512, 128, FAKE, 1e-6, 1e4, 0, FAKE, need, FAKE, 256, 256, FAKE,
-            1000, 0, FAKE, FAKE, 1000, L.LCS_IK_FP8, None]
+    # kv_dtype, win, win_scale, win_ld, ring_cap, kv_out, kv_scale, kv_ld, kv_ring, ik_out, ik_scale, ik_ld,
+    # ik_dtype, stream
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 4, 512, 128, FAKE, 1e-6, 1e4, 0, FAKE, need, L.LCS_KV_BF16, FAKE, None,
+            256, 256, FAKE, None, 1000, 0, FAKE, FAKE, 1000, L.LCS_IK_FP8, None]
     def call(**kw):
         a = list(good)
         for i, v in kw.items():
@@ -118,11 +119,26 @@ def test_decode_append_rejects_bad_arguments(lib):
     assert call(a8=256) == L.LCS_ERR_UNSUPPORTED           # c != 512
     assert call(a9=96) == L.LCS_ERR_UNSUPPORTED            # dI
     assert call(a4=None) == L.LCS_ERR_ARG                  # positions
-    assert call(a17=100) == L.LCS_ERR_ARG                  # win_ld < ring_cap
-    assert call(a21=1001) == L.LCS_ERR_ARG                 # kv_ring > kv_ld
-    assert call(a23=None) == L.LCS_ERR_ARG                 # fp8 keys need scales
-    assert call(a25=7) == L.LCS_ERR_UNSUPPORTED            # key dtype
+    assert call(a19=100) == L.LCS_ERR_ARG                  # win_ld < ring_cap
+    assert call(a24=1001) == L.LCS_ERR_ARG                 # kv_ring > kv_ld
+    assert call(a26=None) == L.LCS_ERR_ARG                 # fp8 keys need scales
+    assert call(a28=7) == L.LCS_ERR_UNSUPPORTED            # key dtype
+    assert call(a16=5) == L.LCS_ERR_UNSUPPORTED            # K=V dtype
+    assert call(a16=L.LCS_KV_FP8) == L.LCS_ERR_ARG         # fp8 K=V rows need their scales
+    assert call(a16=L.LCS_KV_FP8, a22=FAKE) == L.LCS_ERR_ARG   # ... the ring's too
     assert call(a6=0) == L.LCS_ERR_ARG
+
+
+def test_kv8_entry_points_reject_bad_arguments(lib):
+    assert lib.kv_quantize_fp8(FAKE, 0, FAKE, FAKE, None) == L.LCS_ERR_ARG
+    assert lib.kv_quantize_fp8(ctypes.c_void_p((1 << 20) + 8), 4, FAKE, FAKE, None) == L.LCS_ERR_ARG   # alignment
+    # csa_attend_kv8 without row scales
+    args = [FAKE, FAKE, FAKE, None, 100, FAKE, 16, FAKE, FAKE, 256, 256, 128, FAKE, FAKE, 0, 1, 1, 64, 512, 0.04,
+            1e-6, 1e4, FAKE, FAKE, 1 << 30, None]
+    assert lib.csa_attend_kv8(*args) == L.LCS_ERR_ARG
+    hargs = [FAKE, FAKE, FAKE, FAKE, 100, 100, 4, FAKE, None, 256, 256, 128, FAKE, FAKE, 0, 1, 1, 64, 512, 0.04,
+             1e-6, 1e4, FAKE, FAKE, 1 << 30, None]
+    assert lib.hca_attend_kv8(*hargs) == L.LCS_ERR_ARG  # window keys without their scales
 
 
 def test_out_proj_rejects_bad_grouping(lib):

@@ -120,6 +120,61 @@ def test_decode_append_serving_loop(mode):
     assert_close(got_kv[b, :nb], to_np_bf16(bulk[0, :nb]), f"{mode} per-token vs bulk")
 
 
+def _fp8_rows_match(codes, scales, ref, what):
+    """fp8 rows written from fp32 values against the oracle's quantisation of its fp64 values:
+    scales to fp32 rounding, codes at most one step apart (< 1 % of them), dequantised rel-L2 < 1e-2."""
+    rc, rs, rdeq = O.fp8_quantize_rows(ref)
+    np.testing.assert_allclose(scales, rs, rtol=1e-5, err_msg=what)
+    diff = np.abs((codes.astype(int) & 0x7F) - (rc.astype(int) & 0x7F))
+    assert diff.max() <= 1 and (diff > 0).mean() < 0.01, what
+    got = O.e4m3_decode(codes) * scales[:, None].astype(np.float64)
+    assert errors(got, rdeq)[1] < 1e-2, what
+
+
+@pytest.mark.parametrize("m,ov", [(4, 4), (128, 0)])
+def test_decode_append_fp8_kv_rows(m, ov):
+    """The same serving loop with fp8 K=V storage: entries and ring rows as E4M3FN codes + scales."""
+    B, steps, off = 5, 300, 99
+    cfg = 170 + m
+    kv = synth.normal_bf16((B, steps, 512), 1.28, cfg, 1)
+    ks = synth.normal_f32((B, steps), 1.28, cfg, 2)
+    gamma = synth.f32_to_bf16_bits(0.5 + synth.rng(cfg, 5).random(512, dtype=np.float32))
+    pos = _schedule(B, steps, m)
+    n_tok = (pos.max(axis=0) + 1).astype(int)
+    idx = np.where(pos >= 0, pos, 0)
+    b_ix = np.arange(B)[None, :]
+    step_kv = from_bits(np.ascontiguousarray(kv[b_ix, idx]))
+    step_ks = torch.from_numpy(np.ascontiguousarray(ks[b_ix, idx])).to(DEV)
+    step_pos = torch.from_numpy(pos).to(DEV)
+    nb_cap = steps // m + 2
+    state = torch.zeros(L.kv_decode_state_bytes(B), dtype=torch.uint8, device=DEV)
+    ring = torch.zeros((B, RING, 512), dtype=torch.uint8, device=DEV)
+    ring_sc = torch.zeros((B, RING), dtype=torch.float32, device=DEV)
+    kv_out = torch.zeros((B, nb_cap, 512), dtype=torch.uint8, device=DEV)
+    kv_sc = torch.zeros((B, nb_cap), dtype=torch.float32, device=DEV)
+    g_dev = from_bits(gamma)
+    for s in range(steps):
+        L.kv_decode_append(step_kv[s], step_ks[s], None, None, step_pos[s], m=m, overlap=ov, gamma_kv=g_dev,
+                           state=state, kv_out=kv_out, kv_scale=kv_sc, win=ring, win_scale=ring_sc, ring_cap=RING,
+                           rope_offset=off)
+    torch.cuda.synchronize()
+    g64 = synth.bf16_bits_to_f64(gamma)
+    codes, sc = kv_out.cpu().numpy(), kv_sc.cpu().numpy()
+    rcodes, rsc = ring.cpu().numpy(), ring_sc.cpu().numpy()
+    for b in range(B):
+        n = int(n_tok[b])
+        nb = n // m
+        x = synth.bf16_bits_to_f64(kv[b, :n])
+        if nb:
+            ref = O.compress_kv(x, ks[b, :n].astype(np.float64), m, ov, g64, 1e-6, 10000.0, off)[:nb]
+            _fp8_rows_match(codes[b, :nb], sc[b, :nb], ref, f"fp8 entries b={b}")
+        assert np.all(codes[b, nb:] == 0) and np.all(sc[b, nb:] == 0)
+        win = O.window_entries(x, g64, 1e-6, 10000.0, off)
+        last = list(range(max(0, n - RING), n))
+        rows = [j % RING for j in last]
+        _fp8_rows_match(rcodes[b, rows], rsc[b, rows], win[last], f"fp8 ring b={b}")
+
+
 @pytest.mark.parametrize("m,ov", [(4, 4), (128, 0), (4, 2)])
 def test_decode_append_resumes_mid_stream(m, ov):
     """Sequences resumed at t0 > 0 on zero-filled slots: blocks whose first token comes before t0 are

@@ -224,7 +224,7 @@ def test_index_topk_all_equal_scores():
 
 # ----------------------------------------------------------------------------------- attention
 def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_inf=False, rope_offset=0,
-                 block_scale=None, gamma_scale=1.0, eps=1e-6, q_signs=False):
+                 block_scale=None, gamma_scale=1.0, eps=1e-6, q_signs=False, kv8=False):
     q = synth.normal_bf16((B, Tq, H, 512), 1.28, cfg, 41)
     if q_signs:   # entries +-1: with eps = 0 the normalised query is gamma * q, exact in bf16
         q = synth.f32_to_bf16_bits(np.where(synth.bf16_bits_to_f64(q) >= 0, 1.0, -1.0).astype(np.float32))
@@ -244,6 +244,14 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
     sink = np.full(H, -np.inf, np.float32) if sink_inf else synth.normal_f32((H,), 1.0, cfg, 45)
     out = torch.zeros((B, Tq, H, 512), dtype=torch.bfloat16, device=DEV)
     scale = 1.0 / math.sqrt(512)
+    cache64 = synth.bf16_bits_to_f64(cache)
+    win64 = synth.bf16_bits_to_f64(win_tok)
+    kv_dev, win_dev, extra = from_bits(cache), from_bits(win_tok), {}
+    if kv8:   # fp8 K=V storage: codes and row scales from the oracle's quantiser (fp32 decisions)
+        ccodes, csc, cache64 = O.fp8_quantize_rows(cache64, kernel_fp32=True)
+        wcodes, wsc, win64 = O.fp8_quantize_rows(win64, kernel_fp32=True)
+        kv_dev, win_dev = torch.from_numpy(ccodes).to(DEV), torch.from_numpy(wcodes).to(DEV)
+        extra = dict(kv_scale=dev_f32(csc), win_scale=dev_f32(wsc))
     if kind == "csa":
         g = synth.rng(cfg, 46)
         topk = -np.ones((B, Tq, k), dtype=np.int32)
@@ -252,16 +260,16 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
                 nv = min(pos[b, t] // m, n_cap)
                 sel = np.sort(g.choice(nv, size=min(k, nv), replace=False)) if nv else np.zeros(0, int)
                 topk[b, t, : sel.size] = sel
-        L.csa_attend(from_bits(q), from_bits(gq), from_bits(cache), torch.from_numpy(topk).to(DEV),
-                     from_bits(win_tok), dev_f32(sink), dev_i64(pos), window=W, ring_cap=ring_cap, out=out,
-                     rope_offset=rope_offset, eps=eps)
+        L.csa_attend(from_bits(q), from_bits(gq), kv_dev, torch.from_numpy(topk).to(DEV),
+                     win_dev, dev_f32(sink), dev_i64(pos), window=W, ring_cap=ring_cap, out=out,
+                     rope_offset=rope_offset, eps=eps, **extra)
     else:
-        L.hca_attend(from_bits(q), from_bits(gq), from_bits(cache), from_bits(win_tok), dev_f32(sink), dev_i64(pos),
-                     n_cap=n_cap, m=m, window=W, ring_cap=ring_cap, out=out, rope_offset=rope_offset, eps=eps)
+        L.hca_attend(from_bits(q), from_bits(gq), kv_dev, win_dev, dev_f32(sink), dev_i64(pos),
+                     n_cap=n_cap, m=m, window=W, ring_cap=ring_cap, out=out, rope_offset=rope_offset, eps=eps,
+                     **extra)
     torch.cuda.synchronize()
     got = to_np_bf16(out)
     g64 = synth.bf16_bits_to_f64(gq)
-    cache64 = synth.bf16_bits_to_f64(cache)
     worst = (0.0, 0.0)
     for b in range(B):
         for t in range(Tq):
@@ -269,7 +277,7 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
             nv = min(tt // m, n_cap)
             keys = [cache64[b, s] for s in (topk[b, t][topk[b, t] >= 0] if kind == "csa" else range(nv))]
             for j in range(max(0, tt - W + 1), tt + 1):
-                keys.append(synth.bf16_bits_to_f64(win_tok[b, j % ring_cap if ring_cap else j]))
+                keys.append(win64[b, j % ring_cap if ring_cap else j])
             K = np.stack(keys) if keys else np.zeros((0, 512))
             ref = O.attend_one(synth.bf16_bits_to_f64(q[b, t]), g64, K, sink.astype(np.float64), tt, scale,
                                eps, 10000.0, rope_offset)
@@ -306,6 +314,48 @@ def test_hca_attend_running_max_jumps_rescale_accumulators():
     t = 128 * 700 + 5
     _attend_case("hca", 2, 1, 64, 0, 700, 128, 128, 128, [t, t], 56, block_scale=(0.02, 1.0), gamma_scale=6.0,
                  eps=0.0, q_signs=True, rope_offset=-t)
+
+
+@pytest.mark.parametrize("kind,H", [("csa", 64), ("csa", 8), ("hca", 64), ("hca", 16)])
+def test_attend_fp8_kv_parity(kind, H):
+    """fp8 K=V storage (codes + one scale per row, cache and ring) against the oracle on the same
+    dequantised keys: the bf16 bar (the codes are converted exactly; only the scales enter the
+    logits and the PV weights)."""
+    if kind == "csa":
+        _attend_case("csa", 2, 2, H, 200, 900, 4, 128, 256, [4 * 900 + 2, 37, 4 * 500, 130], 151 + H, kv8=True)
+    else:
+        n_cap = 700 if H == 64 else 60
+        _attend_case("hca", 3, 1, H, 0, n_cap, 128, 128, 128, [128 * n_cap + 5, 128 * n_cap // 2 + 127, 0],
+                     153 + n_cap, kv8=True)
+
+
+def test_hca_attend_fp8_kv_running_max_jumps():
+    t = 128 * 700 + 5
+    _attend_case("hca", 2, 1, 64, 0, 700, 128, 128, 128, [t, t], 156, block_scale=(0.02, 1.0), gamma_scale=6.0,
+                 eps=0.0, q_signs=True, rope_offset=-t, kv8=True)
+
+
+def test_kv_quantize_fp8_bit_exact():
+    """The device quantiser of K=V rows against the oracle's (fp32 decisions): codes and scales
+    identical, on Gaussian rows at several magnitudes, an all-zero row, rows with one huge value,
+    and rows that put many values exactly on E4M3FN rounding ties."""
+    rows = synth.normal_bf16((300, 512), 1.0, 160, 1)
+    f = synth.bf16_bits_to_f64(rows)
+    f[:100] *= 37.0
+    f[100:150] *= 1e-3
+    f[150] = 0.0
+    f[151] = 0.0
+    f[151, 7] = -3e4
+    ties = np.array([448.0, 9.0 / 16, 17.0 / 32, 0.75 + 1 / 32, 2.0 ** -9 * 1.5], dtype=np.float64)
+    f[152:160] = np.resize(np.concatenate([ties, -ties]), (8, 512))
+    bits = synth.f32_to_bf16_bits(f.astype(np.float32))
+    codes = torch.empty((300, 512), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((300,), dtype=torch.float32, device=DEV)
+    L.kv_quantize_fp8(from_bits(bits), codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    rc, rs, _ = O.fp8_quantize_rows(synth.bf16_bits_to_f64(bits), kernel_fp32=True)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs.astype(np.float32))
 
 
 def test_hca_attend_single_split_finishes_in_kernel():
