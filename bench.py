@@ -222,6 +222,71 @@ def mhc_row(dev):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def time_stack(layers, steps, warmup, use_graph, ref_y):
+    """Capture one step of every layer into a HIP graph (checked bitwise against the eager outputs
+    ref_y over three replays), then time `steps` replays after `warmup`; eager launches if capture is
+    unavailable.  Returns (graph or None, ms per step)."""
+    import torch
+
+    def step():
+        for layer in layers:
+            layer.step()
+
+    graph = None
+    if use_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(3):
+                for layer in layers:
+                    layer.y.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if not all(torch.equal(layer.y, r) for layer, r in zip(layers, ref_y)):
+                    raise RuntimeError("graph replay differs from eager")
+            graph = g
+        except Exception as e:  # graph capture unavailable: time eager launches
+            log(f"graph capture not used: {e}")
+            graph = None
+    run = graph.replay if graph is not None else step
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return graph, (time.perf_counter() - t0) / steps * 1e3
+
+
+def fp8_kv_stack_row(args, dev):
+    """The same 4-layer decode step with fp8 K=V storage (cache and ring as E4M3FN codes + row scales):
+    tokens/s/layer and the step's algorithmic bytes."""
+    import torch
+    from long_context_sparse_17_amd.pipeline import hybrid_stack
+    layers = hybrid_stack(B=args.batch, ctx=args.ctx, k=1024, device=dev, kv8=True)
+    for _ in range(args.warmup):
+        for layer in layers:
+            layer.step()
+    torch.cuda.synchronize()
+    ref_y = [layer.y.clone() for layer in layers]
+    graph, ms = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
+    nbytes = sum(sum(layer.bytes_per_step().values()) for layer in layers)
+    out = {"what": "hybrid 4-layer decode step, fp8 K=V storage", "tokens_per_s_per_layer":
+           round(args.batch * len(layers) / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "step_bytes": nbytes, "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "graph_replay": graph is not None}
+    del layers, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,10 +297,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--no-fp8kv", action="store_true", help="skip the fp8 K=V variant of the step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU kernel is shown at its "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the per-GPU kernel is shown at its "
               "real shape; sharding is described in the design notes).", file=sys.stderr)
         sys.exit(2)
 
@@ -260,40 +326,8 @@ def main():
     torch.cuda.synchronize()
     ref_y = [layer.y.clone() for layer in layers]
 
-    graph = None
-    if not args.no_graph:
-        try:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                step()
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step()
-            for _ in range(3):
-                for layer in layers:
-                    layer.y.zero_()
-                g.replay()
-                torch.cuda.synchronize()
-                if not all(torch.equal(layer.y, r) for layer, r in zip(layers, ref_y)):
-                    raise RuntimeError("graph replay differs from eager")
-            graph = g
-        except Exception as e:  # graph capture unavailable: time eager launches
-            log(f"graph capture not used: {e}")
-            graph = None
-
-    run = graph.replay if graph is not None else step
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = dt / args.steps * 1e3
+    graph, ms_per_step = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
+    dt = ms_per_step * 1e-3 * args.steps
     B, nl = args.batch, len(layers)
     value = B * nl / (dt / args.steps)
 
@@ -347,6 +381,8 @@ def main():
 
     mfma_tflops = mfma_reference(dev)
     next_rows = {"decode_append": decode_append_rows(dev, B), "mhc_mix": mhc_row(dev)}
+    if not args.no_fp8kv:
+        next_rows["fp8_kv"] = fp8_kv_stack_row(args, dev)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None

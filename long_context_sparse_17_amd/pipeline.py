@@ -23,14 +23,15 @@ import torch
 
 from . import (csa_attend, csa_compress_kv, csa_index_topk, csa_index_topk_workspace, attend_workspace,
                grouped_out_proj, grouped_out_proj_workspace, hca_attend, hca_compress_kv, kv_decode_append,
-               kv_decode_state_bytes, workspace)
+               kv_decode_state_bytes, kv_quantize_fp8, workspace)
 
 RING = 256          # window ring rows (>= the 128-token window)
 
 
 class _Common:
-    def __init__(self, B, ctx, H, W, g, d_g, d, device, weights_std, seed):
+    def __init__(self, B, ctx, H, W, g, d_g, d, device, weights_std, seed, kv8=False):
         self.B, self.ctx, self.H, self.W = B, ctx, H, W
+        self.kv8 = kv8              # fp8 K=V storage (E4M3FN codes + one scale per row) for cache and ring
         self.g, self.d_g, self.d = g, d_g, d
         self.dev = device
         self.t = ctx
@@ -44,7 +45,9 @@ class _Common:
 
         self._nrm = nrm
         self.gamma = torch.ones(512, dtype=torch.bfloat16, device=device)
-        self.ring = torch.zeros((B, RING, 512), dtype=torch.bfloat16, device=device)
+        self.ring = torch.zeros((B, RING, 512), dtype=torch.uint8 if kv8 else torch.bfloat16, device=device)
+        self.ring_sc = torch.zeros((B, RING), dtype=torch.float32, device=device) if kv8 else None
+        self._ring_bf16 = None      # fp8 K=V: the bulk window fill writes bf16 here, then it is quantised
         self.q_pos = torch.full((B, 1), ctx, dtype=torch.int64, device=device)
         self.state = torch.zeros(kv_decode_state_bytes(B), dtype=torch.uint8, device=device)  # empty slots
         self.sink = nrm((H,), 1.0)
@@ -60,7 +63,11 @@ class _Common:
     def fill_ring(self, tok, score, t0):
         """Window tokens [t0, t0 + T) of raw per-token vectors into the ring (m = 1 compression)."""
         T = tok.shape[1]
-        hca_compress_kv(tok, score, tok0=t0, blk_begin=t0, n_blk=T, m=1, gamma_kv=self.gamma, kv_out=self.ring,
+        ring = self.ring
+        if self.kv8:
+            self._ring_bf16 = torch.zeros((self.B, RING, 512), dtype=torch.bfloat16, device=self.dev)
+            ring = self._ring_bf16
+        hca_compress_kv(tok, score, tok0=t0, blk_begin=t0, n_blk=T, m=1, gamma_kv=self.gamma, kv_out=ring,
                         ring_cap=RING)
 
     def prime(self, tok, score, ik=None, iks=None, t0=0):
@@ -78,6 +85,20 @@ class _Common:
         kv_decode_append(self.new_tok.view(self.B, 512), self.new_score.view(self.B), ik, iks, self.q_pos.view(self.B),
                          **self._append_kw())
 
+    def _kv_dtype(self):
+        return torch.uint8 if self.kv8 else torch.bfloat16
+
+    def _to_fp8(self, bf16_cache):
+        """Quantise the bulk-built bf16 cache and window ring into their fp8 stores (once, untimed)."""
+        codes = torch.empty(bf16_cache.shape, dtype=torch.uint8, device=self.dev)
+        kv_quantize_fp8(bf16_cache, codes=codes, scales=self.kv_sc)
+        kv_quantize_fp8(self._ring_bf16, codes=self.ring, scales=self.ring_sc)
+        self._ring_bf16 = None
+        return codes
+
+    def _attend_kw(self):
+        return dict(kv_scale=self.kv_sc, win_scale=self.ring_sc) if self.kv8 else {}
+
     def _window_and_proj_tail(self):
         grouped_out_proj(self.o.view(self.B, self.H * 512), self.w_g, self.w_o, H=self.H, y=self.y,
                          ws=self.ws_proj)
@@ -87,12 +108,13 @@ class CsaDecodeLayer(_Common):
     """One CSA layer (m = 4 with an overlap of 4, fp8 indexer 64 x 128, top-k k)."""
 
     def __init__(self, B, ctx, k=1024, H=64, H_I=64, dI=128, W=128, g=8, d_g=1024, d=4096, m=4, ov=4,
-                 device="cuda", weights_std=0.02, seed=0):
-        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed)
+                 device="cuda", weights_std=0.02, seed=0, kv8=False):
+        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed, kv8)
         self.k, self.H_I, self.dI, self.m, self.ov = k, H_I, dI, m, ov
         self.n_cap = ctx // m
         nrm = self._nrm
-        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
+        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=self._kv_dtype(), device=device)
+        self.kv_sc = torch.empty((B, self.n_cap), dtype=torch.float32, device=device) if kv8 else None
         self.ik_cache = torch.empty((B, self.n_cap, dI), dtype=torch.uint8, device=device)
         self.ik_scale = torch.empty((B, self.n_cap), dtype=torch.float32, device=device)
         self.new_ik = nrm((B, dI), 1.28).to(torch.bfloat16)
@@ -110,6 +132,8 @@ class CsaDecodeLayer(_Common):
         gen = torch.Generator(device=self.dev)
         gen.manual_seed(seed)
         nb_per = block_tokens // m
+        if self.kv8:                     # bulk path in bf16, then one quantisation pass
+            self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=self.dev)
         for blk0 in range(0, self.n_cap, nb_per):
             nb = min(nb_per, self.n_cap - blk0)
             t0 = max(0, blk0 * m - ov)
@@ -123,13 +147,16 @@ class CsaDecodeLayer(_Common):
             if blk0 + nb == self.n_cap:
                 w0 = max(0, self.ctx - self.W + 1)
                 self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
+                if self.kv8:
+                    self.kv_cache = self._to_fp8(self.kv_cache)
                 p0 = self.ctx - ov                # the open block at t = ctx starts ov tokens earlier
                 self.prime(kv[:, p0 - t0:], ks[:, p0 - t0:], ik[:, p0 - t0:], iks[:, p0 - t0:], p0)
             del kv, ks, ik, iks
 
     def _append_kw(self):
         return dict(m=self.m, overlap=self.ov, gamma_kv=self.gamma, state=self.state, kv_out=self.kv_cache,
-                    win=self.ring, ring_cap=RING, ik_out=self.ik_cache, ik_scale=self.ik_scale, ik_fp8=True)
+                    win=self.ring, ring_cap=RING, ik_out=self.ik_cache, ik_scale=self.ik_scale, ik_fp8=True,
+                    kv_scale=self.kv_sc, win_scale=self.ring_sc)
 
     def step(self):
         m = self.m
@@ -137,7 +164,7 @@ class CsaDecodeLayer(_Common):
         csa_index_topk(self.q_idx, self.w_idx, self.ik_cache, self.ik_scale, self.q_pos, n_cap=self.n_cap, m=m,
                        k=self.k, topk_idx=self.topk, ws=self.ws_index)
         csa_attend(self.q, self.gamma, self.kv_cache, self.topk, self.ring, self.sink, self.q_pos, window=self.W,
-                   ring_cap=RING, out=self.o, ws=self.ws_attn)
+                   ring_cap=RING, out=self.o, ws=self.ws_attn, **self._attend_kw())
         self._window_and_proj_tail()
 
     def bytes_per_step(self):
@@ -145,7 +172,8 @@ class CsaDecodeLayer(_Common):
         B, k, W, H = self.B, self.k, self.W, self.H
         n_vis = min(self.t // self.m, self.n_cap)
         index = B * n_vis * (self.dI + 4) + B * self.H_I * (self.dI * 2 + 2)
-        attend = B * (min(k, n_vis) + W) * 1024 + B * H * 512 * 2 * 2 + B * k * 4
+        row = 516 if self.kv8 else 1024
+        attend = B * (min(k, n_vis) + W) * row + B * H * 512 * 2 * 2 + B * k * 4
         proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
         # append: token + key + logits read, ring row written, two pooling-state slots (read + write, write)
         slot = (512 + 128 + 8) * 4
@@ -156,11 +184,13 @@ class CsaDecodeLayer(_Common):
 class HcaDecodeLayer(_Common):
     """One HCA layer (m' = 128, no overlap, dense attention over every visible entry)."""
 
-    def __init__(self, B, ctx, H=64, W=128, g=8, d_g=1024, d=4096, m=128, device="cuda", weights_std=0.02, seed=0):
-        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed)
+    def __init__(self, B, ctx, H=64, W=128, g=8, d_g=1024, d=4096, m=128, device="cuda", weights_std=0.02, seed=0,
+                 kv8=False):
+        super().__init__(B, ctx, H, W, g, d_g, d, device, weights_std, seed, kv8)
         self.m = m
         self.n_cap = ctx // m
-        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=device)
+        self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=self._kv_dtype(), device=device)
+        self.kv_sc = torch.empty((B, self.n_cap), dtype=torch.float32, device=device) if kv8 else None
         self.ws_attn = workspace(attend_workspace(B, 1, H, self.n_cap + W), device)
 
     def build_caches(self, block_tokens=65536, seed=1):
@@ -168,6 +198,8 @@ class HcaDecodeLayer(_Common):
         gen = torch.Generator(device=self.dev)
         gen.manual_seed(seed)
         nb_per = block_tokens // m
+        if self.kv8:                     # bulk path in bf16, then one quantisation pass
+            self.kv_cache = torch.empty((B, self.n_cap, 512), dtype=torch.bfloat16, device=self.dev)
         for blk0 in range(0, self.n_cap, nb_per):
             nb = min(nb_per, self.n_cap - blk0)
             t0 = blk0 * m
@@ -178,34 +210,38 @@ class HcaDecodeLayer(_Common):
             if blk0 + nb == self.n_cap:
                 w0 = max(0, self.ctx - self.W + 1)
                 self.fill_ring(kv[:, w0 - t0:].contiguous(), ks[:, w0 - t0:].contiguous(), w0)
+                if self.kv8:
+                    self.kv_cache = self._to_fp8(self.kv_cache)
             del kv, ks
 
     def _append_kw(self):
         return dict(m=self.m, overlap=0, gamma_kv=self.gamma, state=self.state, kv_out=self.kv_cache, win=self.ring,
-                    ring_cap=RING)
+                    ring_cap=RING, kv_scale=self.kv_sc, win_scale=self.ring_sc)
 
     def step(self):
         m = self.m
         self._append()
         hca_attend(self.q, self.gamma, self.kv_cache, self.ring, self.sink, self.q_pos, n_cap=self.n_cap, m=m,
-                   window=self.W, ring_cap=RING, out=self.o, ws=self.ws_attn)
+                   window=self.W, ring_cap=RING, out=self.o, ws=self.ws_attn, **self._attend_kw())
         self._window_and_proj_tail()
 
     def bytes_per_step(self):
         B, W, H = self.B, self.W, self.H
         n_vis = min(self.t // self.m, self.n_cap)
-        attend = B * (n_vis + W) * 1024 + B * H * 512 * 2 * 2
+        row = 516 if self.kv8 else 1024
+        attend = B * (n_vis + W) * row + B * H * 512 * 2 * 2
         proj = (self.w_g.numel() + self.w_o.numel()) * 2 + B * (H * 512 + self.d) * 2
         compress = B * (512 * 2 + 4 + 512 * 2 + (512 + 8) * 4)   # token + logit, ring row, state slot written
         return {"attend": attend, "proj": proj, "compress": compress}
 
 
-def hybrid_stack(B=8, ctx=1 << 20, k=1024, device="cuda", build=True):
-    """The 4-layer decode stack (CSA, HCA, CSA, HCA) at one GPU's share of the hybrid configuration."""
+def hybrid_stack(B=8, ctx=1 << 20, k=1024, device="cuda", build=True, kv8=False):
+    """The 4-layer decode stack (CSA, HCA, CSA, HCA) at one GPU's share of the hybrid configuration
+    (kv8: fp8 K=V storage)."""
     layers = []
     for i, kind in enumerate(("csa", "hca", "csa", "hca")):
-        L = CsaDecodeLayer(B, ctx, k=k, device=device, seed=100 + i) if kind == "csa" else \
-            HcaDecodeLayer(B, ctx, device=device, seed=100 + i)
+        L = CsaDecodeLayer(B, ctx, k=k, device=device, seed=100 + i, kv8=kv8) if kind == "csa" else \
+            HcaDecodeLayer(B, ctx, device=device, seed=100 + i, kv8=kv8)
         if build:
             L.build_caches(seed=200 + i)
         layers.append(L)

@@ -26,6 +26,17 @@ def host_rows(t, rows):
     return to_np_bf16(t.index_select(0, idx))
 
 
+def kv_rows(Lr, b, rows, ring=False):
+    """Key rows of a decode layer's cache (or ring) as float64: bf16 values, or fp8 codes x row scale."""
+    store = Lr.ring[b] if ring else Lr.kv_cache[b]
+    if not Lr.kv8:
+        return host_rows(store, rows)
+    sc = Lr.ring_sc[b] if ring else Lr.kv_sc[b]
+    idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=store.device)
+    return O.e4m3_decode(store.index_select(0, idx).cpu().numpy()) * \
+        sc.index_select(0, idx).cpu().numpy()[:, None].astype(np.float64)
+
+
 def fp8_rows(codes_dev, scale_dev, n):
     return O.e4m3_decode(codes_dev[:n].cpu().numpy()) * scale_dev[:n].cpu().numpy()[:, None].astype(np.float64)
 
@@ -189,15 +200,22 @@ def test_csa_prefill_2k_full():
     assert_close(got, o_ref, "prefill 2k all queries")
 
 
-def test_hybrid_decode_1m_bench_configuration():
+@pytest.mark.parametrize("kv8", [False, True])
+def test_hybrid_decode_1m_bench_configuration(kv8):
     """The benchmark's 4-layer decode step (same layers, same launches: token append, index, top-k,
     attention, projection) on generator caches; 2 of 8 sequences checked through every layer."""
     from long_context_sparse_17_amd.pipeline import RING, CsaDecodeLayer, hybrid_stack
-    layers = hybrid_stack(B=8, ctx=1 << 20, k=1024, device=DEV, build=False)
+    layers = hybrid_stack(B=8, ctx=1 << 20, k=1024, device=DEV, build=False, kv8=kv8)
     for i, Lr in enumerate(layers):
         s = 5_000_000 + 100 * i
-        Lr.kv_cache.copy_(synth.device_normal_bf16(tuple(Lr.kv_cache.shape), 1.0, s + 1))
-        Lr.ring.copy_(synth.device_normal_bf16(tuple(Lr.ring.shape), 1.0, s + 2))
+        if kv8:       # fp8 K=V: random finite codes and positive row scales for cache and ring
+            Lr.kv_cache.copy_(synth.device_fp8_codes(tuple(Lr.kv_cache.shape), s + 1))
+            Lr.kv_sc.copy_((synth.device_normal_f32(tuple(Lr.kv_sc.shape), 1.0, s + 5).abs() + 0.5) / 448.0)
+            Lr.ring.copy_(synth.device_fp8_codes(tuple(Lr.ring.shape), s + 2))
+            Lr.ring_sc.copy_((synth.device_normal_f32(tuple(Lr.ring_sc.shape), 1.0, s + 6).abs() + 0.5) / 448.0)
+        else:
+            Lr.kv_cache.copy_(synth.device_normal_bf16(tuple(Lr.kv_cache.shape), 1.0, s + 1))
+            Lr.ring.copy_(synth.device_normal_bf16(tuple(Lr.ring.shape), 1.0, s + 2))
         if isinstance(Lr, CsaDecodeLayer):
             Lr.ik_cache.copy_(synth.device_fp8_codes(tuple(Lr.ik_cache.shape), s + 3))
             Lr.ik_scale.copy_((synth.device_normal_f32(tuple(Lr.ik_scale.shape), 1.0, s + 4).abs() + 2.0) / 448.0)
@@ -218,10 +236,18 @@ def test_hybrid_decode_1m_bench_configuration():
                 gsel = Lr.topk[b, 0].cpu().numpy()
                 check_topk_row(gsel, sc, Lr.k, bound)
                 sel = gsel[gsel >= 0]
-                keys = [host_rows(Lr.kv_cache[b], sel)]
+                keys = [kv_rows(Lr, b, sel)]
             else:
-                keys = [host_rows(Lr.kv_cache[b], np.arange(Lr.n_cap))]
-            wrows = host_rows(Lr.ring[b], [j % RING for j in range(t - 127, t)])
+                keys = [kv_rows(Lr, b, np.arange(Lr.n_cap))]
+            wrows = kv_rows(Lr, b, [j % RING for j in range(t - 127, t)], ring=True)
+            if kv8:
+                # the appended row as stored (fp8 of the fp32 row: at most one code from the oracle's)
+                got_row = kv_rows(Lr, b, [t % RING], ring=True)[0]
+                codes, s_ref, deq = O.fp8_quantize_rows(new_win[None])
+                gc = Lr.ring[b, t % RING].cpu().numpy().astype(int)
+                assert np.abs((gc & 0x7F) - (codes[0].astype(int) & 0x7F)).max() <= 1
+                np.testing.assert_allclose(float(Lr.ring_sc[b, t % RING]), s_ref[0], rtol=1e-5)
+                new_win = got_row
             keys = np.concatenate(keys + [wrows, new_win[None]])
             o = O.attend_one(to_np_bf16(Lr.q[b, 0]), ones, keys, Lr.sink.cpu().numpy().astype(np.float64), t, SCALE)
             assert_close(to_np_bf16(Lr.o[b, 0]), o, f"layer o b={b}")
