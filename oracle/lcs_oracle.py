@@ -33,6 +33,10 @@ Readings where the pages are silent (each is listed in the design doc):
       E4M3FN with a per-row absmax/448 scale; top-k ties go to the lower index; ascending, -1 padded.
   R9  grouped projection: group j = heads [j*H/g, (j+1)*H/g); z_j = o_group . W_g[j]^T; y = z . W_o^T
       (weights stored output-major, [out, in]).
+  R11 input projections (upstream of [P1 hybrid] CSA steps 1-3: the query heads, the per-token K=V
+      vector and pooling logit, the indexer's query heads, head weights, key and key logit are linear
+      maps of the token's hidden state h): one output-major matrix per output, concatenated; the
+      layers of a stack chain through the residual h_{l+1} = h_l + y_l.
   R10 mHC: per token the mixing logits are given (their generation from the streams is a projection
       upstream of the kernel); B = Sinkhorn-Knopp of exp(logits), each round dividing every row by
       its sum and then every column by its sum; A = sigmoid, C = sigmoid; the streams update as
@@ -429,3 +433,22 @@ def mhc_mix(X, y, logits, iters=MHC_ITERS):
         Xo[t] = B @ X[t] + C[:, None] * y[t][None, :]
         h[t] = A @ Xo[t]
     return Xo, h
+
+
+# ---------------------------------------------------------------------------------------------
+# Input projections and the residual chain of a stack of layers (R11)
+# ---------------------------------------------------------------------------------------------
+def input_projection(h, w_in, widths):
+    """Outputs of a layer's input projections (R11): out = h . W_in^T (W_in output-major,
+    [sum(widths) + padding, d]), split into consecutive column groups of the given widths."""
+    out = np.asarray(h, dtype=np.float64) @ np.asarray(w_in, dtype=np.float64).T
+    parts, c = [], 0
+    for w in widths:
+        parts.append(out[:, c: c + w])
+        c += w
+    return parts
+
+
+def residual(h, y):
+    """Residual chaining of consecutive layers (R11): h_{l+1} = h_l + y_l."""
+    return np.asarray(h, dtype=np.float64) + np.asarray(y, dtype=np.float64)

@@ -424,3 +424,19 @@ def test_mhc_mix_by_hand_and_stream_sum():
     Lr = randn(6, 24, std=2.0)
     Xo, _ = O.mhc_mix(Xr, np.zeros((6, 8)), Lr, iters=1)
     assert np.allclose(Xo.sum(axis=1), Xr.sum(axis=1), atol=1e-12)
+
+
+# ------------------------------------------------------------------------------- input projections
+def test_input_projection_brute_force_and_split():
+    h = randn(3, 7)
+    w = randn(11, 7)                       # 2 + 1 + 5 columns used, 3 padding rows
+    parts = O.input_projection(h, w, [2, 1, 5])
+    assert [p.shape for p in parts] == [(3, 2), (3, 1), (3, 5)]
+    brute = [[sum(h[m, k] * w[n, k] for k in range(7)) for n in range(8)] for m in range(3)]
+    assert np.allclose(np.concatenate(parts, axis=1), brute, atol=1e-12)
+
+
+def test_residual_chain_closed_forms():
+    h = randn(2, 5)
+    assert np.array_equal(O.residual(h, np.zeros_like(h)), h)
+    assert np.array_equal(O.residual(h, -h), np.zeros_like(h))
