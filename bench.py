@@ -222,15 +222,20 @@ def mhc_row(dev):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def time_stack(layers, steps, warmup, use_graph, ref_y):
-    """Capture one step of every layer into a HIP graph (checked bitwise against the eager outputs
-    ref_y over three replays), then time `steps` replays after `warmup`; eager launches if capture is
-    unavailable.  Returns (graph or None, ms per step)."""
+def time_stack(layers, steps, warmup, use_graph, ref_y, step=None, outputs=None):
+    """Capture one step (default: every layer's step) into a HIP graph (checked bitwise against the
+    eager outputs ref_y over three replays; outputs() gives the tensors to compare, default the layers'
+    y), then time `steps` replays after `warmup`; eager launches if capture is unavailable.
+    Returns (graph or None, ms per step)."""
     import torch
 
-    def step():
-        for layer in layers:
-            layer.step()
+    if step is None:
+        def step():
+            for layer in layers:
+                layer.step()
+    if outputs is None:
+        def outputs():
+            return [layer.y for layer in layers]
 
     graph = None
     if use_graph:
@@ -245,11 +250,11 @@ def time_stack(layers, steps, warmup, use_graph, ref_y):
             with torch.cuda.graph(g):
                 step()
             for _ in range(3):
-                for layer in layers:
-                    layer.y.zero_()
+                for t in outputs():
+                    t.zero_()
                 g.replay()
                 torch.cuda.synchronize()
-                if not all(torch.equal(layer.y, r) for layer, r in zip(layers, ref_y)):
+                if not all(torch.equal(t, r) for t, r in zip(outputs(), ref_y)):
                     raise RuntimeError("graph replay differs from eager")
             graph = g
         except Exception as e:  # graph capture unavailable: time eager launches
@@ -287,6 +292,29 @@ def fp8_kv_stack_row(args, dev):
     return out
 
 
+def chained_stack_row(args, dev):
+    """The 4-layer step as a true stack: input projections of each layer from the hidden state at
+    d = 4096 (one pass over the concatenated weights) and the residual h <- h + y after each layer."""
+    import torch
+    from long_context_sparse_17_amd.pipeline import ChainedStack, hybrid_stack
+    layers = hybrid_stack(B=args.batch, ctx=args.ctx, k=1024, device=dev)
+    stack = ChainedStack(layers)
+    for _ in range(args.warmup):
+        stack.step()
+    torch.cuda.synchronize()
+    ref = [stack.h.clone()]
+    graph, ms = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref, step=stack.step,
+                           outputs=lambda: [stack.h])
+    nbytes = sum(sum(layer.bytes_per_step().values()) for layer in layers) + stack.proj_bytes()
+    out = {"what": "hybrid 4-layer decode step chained: input projections from h (d = 4096) + residual",
+           "tokens_per_s_per_layer": round(args.batch * len(layers) / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "step_bytes": nbytes, "projection_weight_bytes": sum(w.numel() * 2 for w in stack.w_in),
+           "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "graph_replay": graph is not None}
+    del stack, layers, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +326,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-fp8kv", action="store_true", help="skip the fp8 K=V variant of the step")
+    ap.add_argument("--no-chain", action="store_true", help="skip the chained (projections + residual) variant")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -344,7 +373,7 @@ def main():
     kernels = {}
     for name in ("index_score_kernel", "topk_clear_kernel", "topk_filter_kernel", "topk_final_kernel",
                  "attend_kernel", "attend_merge_kernel", "out_proj_group_kernel", "out_proj_out_kernel",
-                 "compress_kernel", "decode_append_kernel"):
+                 "compress_kernel", "decode_append_kernel", "input_proj_kernel"):
         ms, n = L.timing_read(name)
         if n:
             kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}
@@ -383,6 +412,8 @@ def main():
     next_rows = {"decode_append": decode_append_rows(dev, B), "mhc_mix": mhc_row(dev)}
     if not args.no_fp8kv:
         next_rows["fp8_kv"] = fp8_kv_stack_row(args, dev)
+    if not args.no_chain:
+        next_rows["chained_stack"] = chained_stack_row(args, dev)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None

@@ -264,6 +264,29 @@ int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * grouped_out_proj_residual -- grouped_out_proj with the residual stream added: y = z . W_o^T + resid
+ * (summed in fp32, rounded once), so consecutive layers chain as h_{l+1} = h_l + layer_l(h_l).
+ *   resid [M, d] bf16 (16-byte aligned); resid may be y (in place).  Other arguments as above.
+ */
+int grouped_out_proj_residual(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, const uint16_t* resid,
+                              int M, int H, int c, int g, int d_g, int d, uint16_t* y, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * input_proj -- the layer's input projections from the hidden state in one pass over their
+ * concatenated weights (upstream of page 1's CSA steps: the query heads, the per-token K=V vector and
+ * pooling logit, the indexer's query heads, head weights, key and key logit are all linear maps of
+ * the token's hidden state h): out = h . W_in^T, with the output columns split into segments.
+ *   h [M, d] bf16 (M <= 8 rows: decode; d = 4096 or 8192), w_in [n_rows, d] bf16 output-major,
+ *   n_rows % 16 == 0 (pad with rows whose outputs fall past the last segment).
+ *   Segment s (n_seg <= 8) takes the next seg_width[s] columns and writes them to seg_dst[s] as
+ *   row-major [M, seg_ld[s]] (seg_ld[s] >= seg_width[s]), fp32 if seg_fp32[s] else bf16 (RNE).
+ *   seg_* are host arrays; seg_dst[s] are device pointers.
+ */
+int input_proj(const uint16_t* h, int M, int d, const uint16_t* w_in, int n_rows, int n_seg, const int* seg_width,
+               void* const* seg_dst, const int64_t* seg_ld, const int* seg_fp32, void* stream);
+
+/*
  * Kernel timing (measurement facility, off by default).  While enabled, every kernel launch made
  * by the library is bracketed by two hipEvents recorded on the launch stream; lcs_timing_read
  * synchronises those events and returns the summed duration and launch count of the kernels whose

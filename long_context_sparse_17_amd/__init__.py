@@ -44,6 +44,8 @@ SIGNATURES = {
                         _F, _P, _P, _SZ, _P]),
     "grouped_out_proj_workspace": (_SZ, [_I, _I, _I]),
     "grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "grouped_out_proj_residual": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "input_proj": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
     "lcs_timing_enable": (_I, [_I]),
     "lcs_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -292,6 +294,40 @@ def grouped_out_proj(o, w_g, w_o, *, H, y, ws=None, stream=None):
     st = lib().grouped_out_proj(_ptr(o), _ptr(w_g), _ptr(w_o), M, H, HEAD_DIM, g, d_g, d, _ptr(y), _ptr(ws),
                                 ws.numel(), _stream(stream))
     _check("grouped_out_proj", st)
+
+
+def grouped_out_proj_residual(o, w_g, w_o, resid, *, H, y, ws=None, stream=None):
+    """y = grouped projection of o + resid ([M, d] bf16; resid may be y)."""
+    M = o.shape[0]
+    g, d_g, _ = w_g.shape
+    d = w_o.shape[0]
+    _bits(resid, "resid")
+    if ws is None:
+        ws = workspace(grouped_out_proj_workspace(M, g, d_g), o.device)
+    st = lib().grouped_out_proj_residual(_ptr(o), _ptr(w_g), _ptr(w_o), _ptr(resid), M, H, HEAD_DIM, g, d_g, d,
+                                         _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
+    _check("grouped_out_proj_residual", st)
+
+
+def input_proj(h, w_in, segments, *, stream=None):
+    """h [M, d] bf16, w_in [n_rows, d] bf16 (output-major, n_rows % 16 == 0); segments: list of
+    (width, dst tensor) in column order; dst is [M, >= width] (row stride = dst.stride(0)) bf16 or f32,
+    or 1-D [M] for width 1."""
+    import torch
+    M, d = h.shape
+    _bits(h, "h"); _bits(w_in, "w_in")
+    n = len(segments)
+    widths = (ctypes.c_int * n)(*[int(wd) for wd, _ in segments])
+    dsts = (ctypes.c_void_p * n)(*[t.data_ptr() for _, t in segments])
+    lds = (ctypes.c_int64 * n)(*[(t.stride(0) if t.dim() > 1 else 1) for _, t in segments])
+    f32 = (ctypes.c_int * n)(*[int(t.dtype == torch.float32) for _, t in segments])
+    for wd, t in segments:
+        if not t.is_cuda or t.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("segment destinations must be bf16 or f32 GPU tensors")
+        if (t.dim() > 1 and t.stride(-1) != 1) or t.shape[0] != M:
+            raise ValueError("segment destination must be [M, >= width] with unit column stride")
+    st = lib().input_proj(_ptr(h), M, d, _ptr(w_in), w_in.shape[0], n, widths, dsts, lds, f32, _stream(stream))
+    _check("input_proj", st)
 
 
 def timing_enable(on=True):

@@ -213,6 +213,27 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
   return lcs::launch_decode_append(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 
+// ------------------------------------------------------------------------------ input projections
+int input_proj(const uint16_t* h, int M, int d, const uint16_t* w_in, int n_rows, int n_seg, const int* seg_width,
+               void* const* seg_dst, const int64_t* seg_ld, const int* seg_fp32, void* stream) {
+  if (!h || !w_in || !seg_width || !seg_dst || !seg_ld || !seg_fp32) return LCS_ERR_ARG;
+  if (M <= 0 || d <= 0 || n_rows <= 0 || n_seg <= 0) return LCS_ERR_ARG;
+  if (!aligned16(h) || !aligned16(w_in)) return LCS_ERR_ARG;
+  if (M > 8 || (d != 4096 && d != 8192) || n_rows % 16 != 0 || n_seg > lcs::kMaxProjSegments)
+    return LCS_ERR_UNSUPPORTED;
+  lcs::ProjSegments seg{};
+  seg.n = n_seg;
+  int64_t end = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    if (seg_width[i] <= 0 || !seg_dst[i] || seg_ld[i] < seg_width[i]) return LCS_ERR_ARG;
+    if (seg_fp32[i] ? !aligned4(seg_dst[i]) : (reinterpret_cast<uintptr_t>(seg_dst[i]) & 1u)) return LCS_ERR_ARG;
+    end += seg_width[i];
+    if (end > n_rows) return LCS_ERR_ARG;
+    seg.end[i] = (int)end; seg.dst[i] = seg_dst[i]; seg.ld[i] = seg_ld[i]; seg.f32[i] = seg_fp32[i] != 0;
+  }
+  return lcs::launch_input_proj(h, M, d, w_in, n_rows, seg, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
 // ------------------------------------------------------------------------------ fp8 K=V rows
 int kv_quantize_fp8(const uint16_t* kv, int64_t rows, uint8_t* codes, float* scales, void* stream) {
   if (!kv || !codes || !scales || rows <= 0) return LCS_ERR_ARG;
@@ -363,9 +384,11 @@ size_t grouped_out_proj_workspace(int M, int g, int d_g) {
   return lcs::out_proj_workspace(M, g, d_g);
 }
 
-int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
-                     int d_g, int d, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+static int out_proj_common(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
+                           int d_g, int d, const uint16_t* resid, uint16_t* y, void* ws, size_t ws_bytes,
+                           void* stream) {
   if (!o || !w_g || !w_o || !y) return LCS_ERR_ARG;
+  if (resid && !aligned16(resid)) return LCS_ERR_ARG;
   if (M <= 0 || H <= 0 || c <= 0 || g <= 0 || d_g <= 0 || d <= 0) return LCS_ERR_ARG;
   if (!aligned16(o) || !aligned16(w_g) || !aligned16(w_o) || !aligned16(y)) return LCS_ERR_ARG;
   if (H % g != 0 || d_g % 16 != 0 || d % 16 != 0 || ((int64_t)H / g * c) % 32 != 0 || ((int64_t)g * d_g) % 32 != 0)
@@ -375,8 +398,20 @@ int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o
   if (!aligned16(ws)) return LCS_ERR_ARG;
   lcs::OutProjArgs a;
   a.o = o; a.w_g = w_g; a.w_o = w_o; a.M = M; a.H = H; a.c = c; a.g = g; a.d_g = d_g; a.d = d; a.y = y; a.ws = ws;
-  a.ws_bytes = ws_bytes;
+  a.ws_bytes = ws_bytes; a.resid = resid;
   return lcs::launch_out_proj(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
+int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
+                     int d_g, int d, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  return out_proj_common(o, w_g, w_o, M, H, c, g, d_g, d, nullptr, y, ws, ws_bytes, stream);
+}
+
+int grouped_out_proj_residual(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, const uint16_t* resid,
+                              int M, int H, int c, int g, int d_g, int d, uint16_t* y, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!resid) return LCS_ERR_ARG;
+  return out_proj_common(o, w_g, w_o, M, H, c, g, d_g, d, resid, y, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

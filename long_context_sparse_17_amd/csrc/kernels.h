@@ -74,7 +74,21 @@ int launch_attend(const AttendArgs& a, int64_t max_keys, hipStream_t stream);
 struct OutProjArgs {
   const uint16_t* o; const uint16_t* w_g; const uint16_t* w_o;
   int M, H, c, g, d_g, d; uint16_t* y; void* ws; size_t ws_bytes;
+  const uint16_t* resid = nullptr;     // y = z . W_o^T + resid  ([M, d] bf16), nullptr: none
 };
+
+// Output segments of a concatenated projection: columns [end[s-1], end[s]) go to dst[s] (row
+// stride ld[s] elements, fp32 if f32[s] else bf16); columns past end[n-1] are dropped.
+constexpr int kMaxProjSegments = 8;
+struct ProjSegments {
+  int n;
+  int end[kMaxProjSegments];
+  void* dst[kMaxProjSegments];
+  int64_t ld[kMaxProjSegments];
+  int f32[kMaxProjSegments];
+};
+int launch_input_proj(const uint16_t* h, int M, int d, const uint16_t* w, int n_rows, const ProjSegments& seg,
+                      hipStream_t stream);
 size_t out_proj_workspace(int M, int g, int d_g);
 int launch_out_proj(const OutProjArgs& a, hipStream_t stream);
 

@@ -3,7 +3,10 @@
 // projected to an intermediate width d_g, and the concatenation is projected back to d).
 //
 //   z[:, j*d_g:(j+1)*d_g] = o[:, heads of group j] . W_g[j]^T     (z rounded to bf16)
-//   y = z . W_o^T
+//   y = z . W_o^T  (+ the residual stream, optionally)
+//
+// The same weight-streaming kernel also serves the input projections of a layer (one pass over
+// the concatenated projection weights from the hidden state, outputs scattered to their consumers).
 //
 // Both stages are Y[M, N] = X[M, xoff(n) + 0..K) . W[N, K]^T with output-major weights.  At decode
 // M is the batch (<= 16): the kernel streams W once from HBM straight into MFMA A-fragments
@@ -23,7 +26,8 @@ typedef __attribute__((address_space(1))) const u32x4v GU32x4v;   // global addr
 
 __global__ void __launch_bounds__(kWaves * 64)
 rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W,
-                     uint16_t* __restrict__ Y, int64_t y_ld, int M, int N, int K, int n_per_group) {
+                     uint16_t* Y, int64_t y_ld, int M, int N, int K, int n_per_group, const uint16_t* R,
+                     int64_t r_ld) {
   __shared__ float4 red[kWaves][kWave];
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -71,6 +75,10 @@ rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
         y0 += a.x; y1 += a.y; y2 += a.z; y3 += a.w;
       }
       if (mv) {
+        if (R != nullptr) {
+          const uint2 rv = *reinterpret_cast<const uint2*>(R + (int64_t)mrow * r_ld + n0 + 4 * g);
+          y0 += bf2f_lo(rv.x); y1 += bf2f_hi(rv.x); y2 += bf2f_lo(rv.y); y3 += bf2f_hi(rv.y);
+        }
         uint2 o;
         o.x = pack_bf2(y0, y1);
         o.y = pack_bf2(y2, y3);
@@ -84,10 +92,15 @@ rowblock_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
 // Decode shapes (M <= 8, K = 4096 or 8192): the workgroup's slice of X (M x K) is staged once in
 // LDS, and each wave issues all of its W loads (KS k-steps of 16 B per lane) before the first MFMA,
 // so a CU has its whole share of the weights in flight.  X rows >= M are zero in the B fragments.
-template <int K>
+//
+// Epilogue options: R adds a residual (Y = X . W^T + R, summed in fp32); SEG scatters the output
+// columns into the segments of a ProjSegments table (each segment its own destination, row stride and
+// bf16 / fp32 type), so one pass over a concatenated weight matrix feeds several consumers.
+template <int K, bool SEG>
 __global__ void __launch_bounds__(kWaves * 64)
 rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W,
-                     uint16_t* __restrict__ Y, int64_t y_ld, int M, int n_per_group) {
+                     uint16_t* Y, int64_t y_ld, int M, int n_per_group, const uint16_t* R, int64_t r_ld,
+                     ProjSegments seg) {
   constexpr int KS = K / 32 / kWaves;      // k-steps per wave
   constexpr int kXStride = K + 8;          // bf16 per staged X row (16 B pad)
   __shared__ __align__(16) uint16_t sx[8 * kXStride];
@@ -135,11 +148,28 @@ rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
       const float4 a = red[v][lane];
       y0 += a.x; y1 += a.y; y2 += a.z; y3 += a.w;
     }
-    if (mv) {
+    if (mv && R != nullptr) {
+      const uint2 rv = *reinterpret_cast<const uint2*>(R + (int64_t)c16 * r_ld + n0 + 4 * g);
+      y0 += bf2f_lo(rv.x); y1 += bf2f_hi(rv.x); y2 += bf2f_lo(rv.y); y3 += bf2f_hi(rv.y);
+    }
+    if (mv && !SEG) {
       uint2 o;
       o.x = pack_bf2(y0, y1);
       o.y = pack_bf2(y2, y3);
       *reinterpret_cast<uint2*>(Y + (int64_t)c16 * y_ld + n0 + 4 * g) = o;
+    } else if (mv) {
+      const float yv[4] = {y0, y1, y2, y3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 4 * g + i;
+        int sidx = 0;
+        while (sidx < seg.n && n >= seg.end[sidx]) ++sidx;
+        if (sidx == seg.n) continue;                  // padding rows of W
+        const int64_t col = n - (sidx ? seg.end[sidx - 1] : 0);
+        const int64_t at = (int64_t)c16 * seg.ld[sidx] + col;
+        if (seg.f32[sidx]) static_cast<float*>(seg.dst[sidx])[at] = yv[i];
+        else static_cast<uint16_t*>(seg.dst[sidx])[at] = (uint16_t)f2bf(yv[i]);
+      }
     }
   }
 }
@@ -148,16 +178,18 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Y = X . W^T for one stage: the staged-X kernel at the decode shapes, else the general one.
 void launch_stage(const char* name, const uint16_t* X, int64_t x_ld, const uint16_t* W, uint16_t* Y, int64_t y_ld,
-                  int M, int N, int K, int n_per_group, hipStream_t st) {
+                  int M, int N, int K, int n_per_group, hipStream_t st, const uint16_t* R = nullptr,
+                  int64_t r_ld = 0) {
+  const ProjSegments none{};
   if (M <= 8 && K == 4096) {
-    LCS_LAUNCH(name, rowblock_gemv_kernel<4096>, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y,
-               y_ld, M, n_per_group);
+    LCS_LAUNCH(name, (rowblock_gemv_kernel<4096, false>), dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld,
+               W, Y, y_ld, M, n_per_group, R, r_ld, none);
   } else if (M <= 8 && K == 8192) {
-    LCS_LAUNCH(name, rowblock_gemv_kernel<8192>, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y,
-               y_ld, M, n_per_group);
+    LCS_LAUNCH(name, (rowblock_gemv_kernel<8192, false>), dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld,
+               W, Y, y_ld, M, n_per_group, R, r_ld, none);
   } else {
     LCS_LAUNCH(name, rowblock_gemm_kernel, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y, y_ld,
-               M, N, K, n_per_group);
+               M, N, K, n_per_group, R, r_ld);
   }
 }
 
@@ -170,7 +202,20 @@ int launch_out_proj(const OutProjArgs& a, hipStream_t st) {
   const int kg = a.H / a.g * a.c;
   const int nz = a.g * a.d_g;
   launch_stage("out_proj_group_kernel", a.o, (int64_t)a.H * a.c, a.w_g, z, (int64_t)nz, a.M, nz, kg, a.d_g, st);
-  launch_stage("out_proj_out_kernel", z, (int64_t)nz, a.w_o, a.y, (int64_t)a.d, a.M, a.d, nz, a.d, st);
+  launch_stage("out_proj_out_kernel", z, (int64_t)nz, a.w_o, a.y, (int64_t)a.d, a.M, a.d, nz, a.d, st, a.resid,
+               (int64_t)a.d);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int launch_input_proj(const uint16_t* h, int M, int d, const uint16_t* w, int n_rows, const ProjSegments& seg,
+                      hipStream_t st) {
+  if (d == 4096) {
+    LCS_LAUNCH("input_proj_kernel", (rowblock_gemv_kernel<4096, true>), dim3((unsigned)(n_rows / 16)),
+               dim3(kWaves * 64), 0, st, h, (int64_t)d, w, nullptr, 0, M, n_rows, nullptr, 0, seg);
+  } else {
+    LCS_LAUNCH("input_proj_kernel", (rowblock_gemv_kernel<8192, true>), dim3((unsigned)(n_rows / 16)),
+               dim3(kWaves * 64), 0, st, h, (int64_t)d, w, nullptr, 0, M, n_rows, nullptr, 0, seg);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -22,8 +22,8 @@ import math
 import torch
 
 from . import (csa_attend, csa_compress_kv, csa_index_topk, csa_index_topk_workspace, attend_workspace,
-               grouped_out_proj, grouped_out_proj_workspace, hca_attend, hca_compress_kv, kv_decode_append,
-               kv_decode_state_bytes, kv_quantize_fp8, workspace)
+               grouped_out_proj, grouped_out_proj_residual, grouped_out_proj_workspace, hca_attend, hca_compress_kv,
+               input_proj, kv_decode_append, kv_decode_state_bytes, kv_quantize_fp8, workspace)
 
 RING = 256          # window ring rows (>= the 128-token window)
 
@@ -48,6 +48,7 @@ class _Common:
         self.ring = torch.zeros((B, RING, 512), dtype=torch.uint8 if kv8 else torch.bfloat16, device=device)
         self.ring_sc = torch.zeros((B, RING), dtype=torch.float32, device=device) if kv8 else None
         self._ring_bf16 = None      # fp8 K=V: the bulk window fill writes bf16 here, then it is quantised
+        self.stack_h = None         # in a chained stack: the hidden state [B, d] (input, and output in place)
         self.q_pos = torch.full((B, 1), ctx, dtype=torch.int64, device=device)
         self.state = torch.zeros(kv_decode_state_bytes(B), dtype=torch.uint8, device=device)  # empty slots
         self.sink = nrm((H,), 1.0)
@@ -100,8 +101,23 @@ class _Common:
         return dict(kv_scale=self.kv_sc, win_scale=self.ring_sc) if self.kv8 else {}
 
     def _window_and_proj_tail(self):
+        if self.stack_h is not None:   # h <- h + layer(h), in place
+            grouped_out_proj_residual(self.o.view(self.B, self.H * 512), self.w_g, self.w_o, self.stack_h, H=self.H,
+                                      y=self.stack_h, ws=self.ws_proj)
+            return
         grouped_out_proj(self.o.view(self.B, self.H * 512), self.w_g, self.w_o, H=self.H, y=self.y,
                          ws=self.ws_proj)
+
+    def projection_segments(self):
+        """(width, destination) of every input this layer takes from the hidden state, in the column
+        order of its input-projection weights."""
+        B = self.B
+        segs = [(self.H * 512, self.q.view(B, self.H * 512)), (512, self.new_tok.view(B, 512)),
+                (1, self.new_score.view(B))]
+        if isinstance(self, CsaDecodeLayer):
+            segs += [(self.H_I * self.dI, self.q_idx.view(B, self.H_I * self.dI)), (self.H_I, self.w_idx.view(B, self.H_I)),
+                     (self.dI, self.new_ik), (1, self.new_is)]
+        return segs
 
 
 class CsaDecodeLayer(_Common):
@@ -260,5 +276,39 @@ def flops_per_step(layer):
     return {"attend": 4 * 512 * B * H * (n_vis + layer.W), "proj": proj}
 
 
-__all__ = ["CsaDecodeLayer", "HcaDecodeLayer", "hybrid_stack", "flops_per_step", "RING"]
+class ChainedStack:
+    """The decode stack as a chain: each layer's inputs (query heads, K=V token and logit, indexer
+    query, head weights, key and logit) come from one input projection of the hidden state h [B, d],
+    and each layer's grouped projection adds its output to h in place (h <- h + y).  h is reset from
+    h0 at the start of every step, so repeated steps compute the same thing."""
+
+    def __init__(self, layers, d=4096, weights_std=0.02, seed=7):
+        self.layers = layers
+        dev = layers[0].dev
+        B = layers[0].B
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        self.h0 = torch.empty((B, d), device=dev).normal_(0.0, 1.0, generator=gen).to(torch.bfloat16)
+        self.h = self.h0.clone()
+        self.w_in, self.segs = [], []
+        for layer in layers:
+            segs = layer.projection_segments()
+            n = sum(w for w, _ in segs)
+            n_rows = (n + 15) // 16 * 16
+            w = torch.empty((n_rows, d), device=dev).normal_(0.0, weights_std, generator=gen).to(torch.bfloat16)
+            self.w_in.append(w)
+            self.segs.append(segs)
+            layer.stack_h = self.h
+
+    def step(self):
+        self.h.copy_(self.h0)
+        for layer, w, segs in zip(self.layers, self.w_in, self.segs):
+            input_proj(self.h, w, segs)
+            layer.step()
+
+    def proj_bytes(self):
+        return sum(w.numel() * 2 for w in self.w_in) + len(self.layers) * self.h.numel() * 2 * 2
+
+
+__all__ = ["CsaDecodeLayer", "HcaDecodeLayer", "ChainedStack", "hybrid_stack", "flops_per_step", "RING"]
 _ = math
