@@ -206,7 +206,8 @@ attend_kernel(AttnK a) {
       int64_t jr = jm0 + off;                  // j0 < 0: the token itself (< window <= ring_cap)
       if (a.ring_cap > 0 && jr >= a.ring_cap) jr -= a.ring_cap;
       const int32_t wrow = j0 + off < 0 ? -1 : (int32_t)jr;
-      const int32_t crow = LIST ? sel[u] : (int32_t)e;   // a negative list entry is no key
+      // a negative list entry is no key; so is one past the cache (an unfilled slot must not be read)
+      const int32_t crow = LIST ? (sel[u] >= 0 && sel[u] < a.kv_ld ? sel[u] : -1) : (int32_t)e;
       s_rows[i] = i >= nkeys ? -1 : (e < nc ? crow : wrow);
     }
   }

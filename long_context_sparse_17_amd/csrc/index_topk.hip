@@ -717,6 +717,11 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
         ++pos;
       }
     }
+    // every slot is written: with consistent inputs tot == k; the -1 fill is a guard
+    for (int i = (int)tot + tid; i < k; i += kSelThreads) {
+      out[i] = -1;
+      if (out_s) out_s[i] = -INFINITY;
+    }
   } else {
     // winners per chunk, their output offsets, then each wave writes its chunks in order
     for (int c = wave; c < nch; c += kWaves) {
@@ -736,6 +741,10 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
     }
     uint32_t tot;
     uint32_t o2 = block_excl_scan(wsum, s_w, &tot);
+    for (int i = (int)tot + tid; i < k; i += kSelThreads) {   // guard, as in the cached path
+      out[i] = -1;
+      if (out_s) out_s[i] = -INFINITY;
+    }
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) { s_pos[tid * kPerT + u] = o2; o2 += wc[u]; }
     __syncthreads();

@@ -335,6 +335,30 @@ def test_hca_attend_fp8_kv_running_max_jumps():
                  eps=0.0, q_signs=True, rope_offset=-t, kv8=True)
 
 
+def test_csa_attend_list_entries_past_the_cache_are_missing_keys():
+    """A selection slot holding an index past the cache (a slot nobody filled) is no key, exactly
+    like -1: the outputs are bitwise equal (the kernel's own bound, no read past the cache)."""
+    B, H, k, n_cap, W, ring = 1, 64, 64, 300, 128, 256
+    t = 4 * n_cap
+    q = synth.normal_bf16((B, 1, H, 512), 1.28, 161, 1)
+    gq = synth.f32_to_bf16_bits(np.ones(512, np.float32))
+    cache = synth.normal_bf16((B, n_cap, 512), 1.0, 161, 2)
+    win = synth.normal_bf16((B, ring, 512), 1.0, 161, 3)
+    sink = synth.normal_f32((H,), 1.0, 161, 4)
+    sel = np.sort(synth.rng(161, 5).choice(n_cap, k, replace=False)).astype(np.int32)
+    bad, none = sel.copy(), sel.copy()
+    bad[[3, 17, 40]] = [n_cap, n_cap + 12345, 2 ** 30]
+    none[[3, 17, 40]] = -1
+    outs = []
+    for lst in (bad, none):
+        out = torch.zeros((B, 1, H, 512), dtype=torch.bfloat16, device=DEV)
+        L.csa_attend(from_bits(q), from_bits(gq), from_bits(cache), torch.from_numpy(lst.reshape(B, 1, k)).to(DEV),
+                     from_bits(win), dev_f32(sink), dev_i64(np.array([[t]])), window=W, ring_cap=ring, out=out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_kv_quantize_fp8_bit_exact():
     """The device quantiser of K=V rows against the oracle's (fp32 decisions): codes and scales
     identical, on Gaussian rows at several magnitudes, an all-zero row, rows with one huge value,
