@@ -345,10 +345,11 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   const int64_t ngroups = (c1 - c0 + 63) / 64;
 
   Frag cur[4][KS], nxt[4][KS], nx2[4][KS];
-  float cs[4], ns[4], n2[4];
+  float cs, ns, n2;
   // Loads are unconditional (entry index clamped into the chunk) so that the compiler keeps them in
-  // flight; out-of-range entries are zeroed by a select and never stored.
-  auto load_group = [&](int64_t gi, Frag (&fr)[4][KS], float (&sc)[4]) {
+  // flight; out-of-range entries are zeroed by a select and never stored.  One scale load per group:
+  // lane l takes entry 64 gi + l (row-group u of the fragments needs lanes 16u .. 16u+15).
+  auto load_group = [&](int64_t gi, Frag (&fr)[4][KS], float& sc) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       int64_t e = c0 + 64 * gi + 16 * u + c16;
@@ -358,15 +359,19 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
         const uint4 x0 = p[0], x1 = p[1];
         intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         fr[u][0] = *reinterpret_cast<Frag*>(&v);
-        sc[u] = ksc[e];                     // clamped entries are never stored
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           uint4 v = *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g);
           fr[u][ks] = *reinterpret_cast<Frag*>(&v);
         }
-        sc[u] = 1.f;
       }
+    }
+    if (FP8) {
+      int64_t e = c0 + 64 * gi + lane;
+      sc = ksc[e < c1 ? e : c1 - 1];        // clamped entries are never stored
+    } else {
+      sc = 1.f;
     }
   };
 
@@ -375,7 +380,16 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   // one being computed.  Loads past the end re-read the last group (never computed).
   const int64_t nt = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
   auto gidx = [&](int64_t t) -> int64_t { return wave + 4 * (t < nt ? t : nt - 1); };
-  auto compute_group = [&](const Frag (&fr)[4][KS], const float (&sc)[4], int64_t gi) {
+  auto compute_group = [&](const Frag (&fr)[4][KS], float sc_lane, int64_t gi) {
+    // every row group's scales in every lane (same column): rows 0..3 = entries 16u + c16
+    float sc[4];
+    {
+      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sc_lane), __float_as_uint(sc_lane), false, false);
+      const auto lo = __builtin_amdgcn_permlane32_swap(p16[0], p16[0], false, false);   // rows 0, 2
+      const auto hi = __builtin_amdgcn_permlane32_swap(p16[1], p16[1], false, false);   // rows 1, 3
+      sc[0] = __uint_as_float(lo[0]); sc[1] = __uint_as_float(hi[0]);
+      sc[2] = __uint_as_float(lo[1]); sc[3] = __uint_as_float(hi[1]);
+    }
     floatx4 acc[4][HBI];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
