@@ -226,7 +226,7 @@ def time_stack(layers, steps, warmup, use_graph, ref_y, step=None, outputs=None)
     """Capture one step (default: every layer's step) into a HIP graph (checked bitwise against the
     eager outputs ref_y over three replays; outputs() gives the tensors to compare, default the layers'
     y), then time `steps` replays after `warmup`; eager launches if capture is unavailable.
-    Returns (graph or None, ms per step)."""
+    Returns (graph or None, ms per step, per-step p10/p50/p90 in ms from a second set of steps)."""
     import torch
 
     if step is None:
@@ -268,7 +268,18 @@ def time_stack(layers, steps, warmup, use_graph, ref_y, step=None, outputs=None)
     for _ in range(steps):
         run()
     torch.cuda.synchronize()
-    return graph, (time.perf_counter() - t0) / steps * 1e3
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    # per-step spread: events around each of a second set of steps (not part of the timed total)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        run()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    spread = {"p10": round(per[len(per) // 10], 4), "p50": round(per[len(per) // 2], 4),
+              "p90": round(per[(9 * len(per)) // 10], 4)}
+    return graph, ms, spread
 
 
 def fp8_kv_stack_row(args, dev):
@@ -282,7 +293,7 @@ def fp8_kv_stack_row(args, dev):
             layer.step()
     torch.cuda.synchronize()
     ref_y = [layer.y.clone() for layer in layers]
-    graph, ms = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
+    graph, ms, _ = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
     nbytes = sum(sum(layer.bytes_per_step().values()) for layer in layers)
     out = {"what": "hybrid 4-layer decode step, fp8 K=V storage", "tokens_per_s_per_layer":
            round(args.batch * len(layers) / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
@@ -303,7 +314,7 @@ def chained_stack_row(args, dev):
         stack.step()
     torch.cuda.synchronize()
     ref = [stack.h.clone()]
-    graph, ms = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref, step=stack.step,
+    graph, ms, _ = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref, step=stack.step,
                            outputs=lambda: [stack.h])
     nbytes = sum(sum(layer.bytes_per_step().values()) for layer in layers) + stack.proj_bytes()
     out = {"what": "hybrid 4-layer decode step chained: input projections from h (d = 4096) + residual",
@@ -355,7 +366,7 @@ def main():
     torch.cuda.synchronize()
     ref_y = [layer.y.clone() for layer in layers]
 
-    graph, ms_per_step = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
+    graph, ms_per_step, spread = time_stack(layers, args.steps, args.warmup, not args.no_graph, ref_y)
     dt = ms_per_step * 1e-3 * args.steps
     B, nl = args.batch, len(layers)
     value = B * nl / (dt / args.steps)
@@ -431,6 +442,7 @@ def main():
                    "indexer": "64x128 fp8_e4m3", "m_csa": 4, "m_hca": 128, "g": 8, "d_g": 1024, "d": 4096,
                    "graph_replay": graph is not None},
         "roofline": roofline,
+        "step_ms_spread": spread,
         "step_hbm": {"bytes": step_bytes, "achieved_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "flops": step_flops},
