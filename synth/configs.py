@@ -52,20 +52,20 @@ class Workload:
         return [self.ctx + i for i in range(self.Tq)]
 
 
-CONFIGS = {
-    # 1: single CSA layer, causal prefill, ctx 2048, d = 1024, H = 8, indexer 8 x 64 bf16, top-k 128, sink 0.
-    1: Workload("csa_prefill_2k", "csa_prefill", 1, B=1, ctx=2048, Tq=2048, H=8, H_I=8, d_I=64, k=128,
-                ik_fp8=False, d=1024, std_tok=1.0, sink_std=0.0),
-    # 2: single HCA layer decode, B = 64, ctx 65536 -> 512 entries, H = 64.
-    2: Workload("hca_decode_64k", "hca_decode", 2, B=64, ctx=65536, Tq=1),
-    # 3: single CSA layer decode (Flash): B = 32, ctx 131072 -> 32768 entries, fp8 indexer 64 x 128, top-k 512.
-    3: Workload("csa_decode_128k", "csa_decode", 3, B=32, ctx=131072, Tq=1, k=512),
-    # 4: CSA chunked prefill: 4096 queries against a 1,048,576-token cache, top-k 1024, inputs N(0,1).
-    4: Workload("csa_chunked_prefill_1m", "csa_chunked_prefill", 4, B=1, ctx=1 << 20, Tq=4096, k=1024,
-                std_tok=1.0),
-    # 5: hybrid 4-layer decode (CSA, HCA, CSA, HCA) at 1M ctx, B = 8, top-k 1024, g = 8, d_g = 1024, d = 4096.
-    5: Workload("hybrid4_decode_1m", "hybrid_decode", 5, B=8, ctx=1 << 20, Tq=1, k=1024),
-}
+CONFIGS = {w.name: w for w in (
+    # single CSA layer, causal prefill, ctx 2048, d = 1024, H = 8, indexer 8 x 64 bf16, top-k 128, sink 0
+    Workload("csa_prefill_2k", "csa_prefill", 1, B=1, ctx=2048, Tq=2048, H=8, H_I=8, d_I=64, k=128,
+             ik_fp8=False, d=1024, std_tok=1.0, sink_std=0.0),
+    # single HCA layer decode, B = 64, ctx 65536 -> 512 entries, H = 64
+    Workload("hca_decode_64k", "hca_decode", 2, B=64, ctx=65536, Tq=1),
+    # single CSA layer decode (Flash): B = 32, ctx 131072 -> 32768 entries, fp8 indexer 64 x 128, top-k 512
+    Workload("csa_decode_128k", "csa_decode", 3, B=32, ctx=131072, Tq=1, k=512),
+    # CSA chunked prefill: 4096 queries against a 1,048,576-token cache, top-k 1024, inputs N(0,1)
+    Workload("csa_chunked_prefill_1m", "csa_chunked_prefill", 4, B=1, ctx=1 << 20, Tq=4096, k=1024,
+             std_tok=1.0),
+    # hybrid 4-layer decode (CSA, HCA, CSA, HCA) at 1M ctx, B = 8, top-k 1024, g = 8, d_g = 1024, d = 4096
+    Workload("hybrid4_decode_1m", "hybrid_decode", 5, B=8, ctx=1 << 20, Tq=1, k=1024),
+)}
 
 
 def small_workload(kind: str, **kw) -> Workload:

@@ -35,11 +35,11 @@ def test_page_constants_match_workloads():
         name, v = line.split()[:2]
         vals[name] = int(v)
     assert O.C_HEAD == vals["head_dim"] and O.ROPE_DIMS == vals["rope_dims"]
-    w3 = configs.CONFIGS[3]
+    w3 = configs.CONFIGS["csa_decode_128k"]
     assert (w3.m, w3.m_hca, w3.H_I, w3.d_I, w3.k, w3.W) == (
         vals["m_csa"], vals["m_hca"], vals["indexer_heads"], vals["indexer_dim"], vals["topk_flash"],
         vals["window"])
-    assert configs.CONFIGS[5].k == vals["topk_1m"] == configs.CONFIGS[4].k
+    assert configs.CONFIGS["hybrid4_decode_1m"].k == vals["topk_1m"] == configs.CONFIGS["csa_chunked_prefill_1m"].k
 
 
 # ------------------------------------------------------------------------------- RMSNorm
