@@ -599,11 +599,22 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
 
   // ---- stage the list: wave w copies chunks w, w + 4, ...; sixteen chunks' loads in flight ----
   if (cached && heads) {
+    // the 16 chunks' counts and offsets first (all LDS reads in flight together), then the stores
+    int nk[16], pk[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = wave + kWaves * u;
-      if (c < nch && lane < (int)s_keep[c]) s_list[final_slot((int)s_pos[c] + lane)] = vh[u];
+      const int cc = c < nch ? c : nch - 1;
+      nk[u] = c < nch ? (int)s_keep[cc] : 0;
+      pk[u] = (int)s_pos[cc];
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (lane < nk[u]) s_list[final_slot(pk[u] + lane)] = vh[u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)                    // chunks with more than 64 kept entries
+      for (int j = kWave + lane; j < nk[u]; j += kWave)
+        s_list[final_slot(pk[u] + j)] = lrow[(int64_t)(wave + kWaves * u) * kFilterChunk + j];
   }
   if (cached && !heads) {
     for (int cb = wave; cb < nch; cb += kWaves * 16) {
@@ -622,7 +633,7 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
       }
     }
   }
-  if (cached) {
+  if (cached && !heads) {
     for (int c = wave; c < nch; c += kWaves)        // chunks with more than 64 kept entries
       for (int j = kWave + lane; j < (int)s_keep[c]; j += kWave)
         s_list[final_slot((int)s_pos[c] + j)] = lrow[(int64_t)c * kFilterChunk + j];
