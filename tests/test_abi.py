@@ -141,6 +141,30 @@ def test_kv8_entry_points_reject_bad_arguments(lib):
     assert lib.hca_attend_kv8(*hargs) == L.LCS_ERR_ARG  # window keys without their scales
 
 
+def test_projection_and_mhc_entry_points_reject_bad_arguments(lib):
+    widths = (ctypes.c_int * 2)(100, 1)
+    dsts = (ctypes.c_void_p * 2)(1 << 20, 1 << 21)
+    lds = (ctypes.c_int64 * 2)(128, 1)
+    f32 = (ctypes.c_int * 2)(0, 1)
+    args = [FAKE, 8, 4096, FAKE, 112, 2, widths, dsts, lds, f32, None]
+    bad_m = list(args); bad_m[1] = 9
+    assert lib.input_proj(*bad_m) == L.LCS_ERR_UNSUPPORTED       # decode rows only
+    bad_d = list(args); bad_d[2] = 1000
+    assert lib.input_proj(*bad_d) == L.LCS_ERR_UNSUPPORTED
+    bad_rows = list(args); bad_rows[4] = 100
+    assert lib.input_proj(*bad_rows) == L.LCS_ERR_UNSUPPORTED    # weight rows not a multiple of 16
+    short = list(args); short[4] = 96
+    assert lib.input_proj(*short) == L.LCS_ERR_ARG               # segments wider than the weights
+    narrow = (ctypes.c_int64 * 2)(64, 1)
+    bad_ld = list(args); bad_ld[8] = narrow
+    assert lib.input_proj(*bad_ld) == L.LCS_ERR_ARG              # row stride below the width
+    assert lib.grouped_out_proj_residual(FAKE, FAKE, FAKE, None, 8, 64, 512, 8, 1024, 4096, FAKE, FAKE, 1 << 30,
+                                         None) == L.LCS_ERR_ARG
+    assert lib.mhc_sinkhorn(FAKE, 10, 9, 20, FAKE, None) == L.LCS_ERR_UNSUPPORTED      # n > 8
+    assert lib.mhc_sinkhorn(FAKE, 10, 4, 0, FAKE, None) == L.LCS_ERR_ARG               # no rounds
+    assert lib.mhc_mix(FAKE, FAKE, FAKE, 4, 4, 100, 20, FAKE, None, None) == L.LCS_ERR_UNSUPPORTED  # d % 8
+
+
 def test_out_proj_rejects_bad_grouping(lib):
     assert lib.grouped_out_proj(FAKE, FAKE, FAKE, 8, 64, 512, 7, 1024, 4096, FAKE, FAKE, 1 << 30, None) == \
         L.LCS_ERR_UNSUPPORTED

@@ -36,9 +36,10 @@ def _schedule(B, steps, m):
     return pos
 
 
-@pytest.mark.parametrize("mode", ["csa_fp8", "csa_bf16", "hca"])
+@pytest.mark.parametrize("mode", ["csa_fp8", "csa_bf16", "hca", "csa_ov2"])
 def test_decode_append_serving_loop(mode):
-    m, ov, dI, fp8 = {"csa_fp8": (4, 4, 128, True), "csa_bf16": (4, 4, 64, False), "hca": (128, 0, 0, False)}[mode]
+    m, ov, dI, fp8 = {"csa_fp8": (4, 4, 128, True), "csa_bf16": (4, 4, 64, False), "hca": (128, 0, 0, False),
+                      "csa_ov2": (4, 2, 128, True)}[mode]
     B, steps, off = 5, 300, 4321
     cfg = 60 + len(mode)
     kv = synth.normal_bf16((B, steps, 512), 1.28, cfg, 1)

@@ -50,9 +50,10 @@ def test_sinkhorn_one_round_by_hand_on_gpu():
     np.testing.assert_allclose(out.cpu().numpy()[0], [[7 / 16, 7 / 13], [9 / 16, 6 / 13]], rtol=1e-6)
 
 
-@pytest.mark.parametrize("T,n,d,inplace", [(37, 4, 4096, False), (37, 4, 4096, True), (9, 3, 200, False),
-                                           (6, 8, 1024, True), (5, 1, 8, False)])
-def test_mhc_mix_parity(T, n, d, inplace):
+@pytest.mark.parametrize("T,n,d,inplace,iters", [(37, 4, 4096, False, 20), (37, 4, 4096, True, 20),
+                                                 (9, 3, 200, False, 20), (6, 8, 1024, True, 20), (5, 1, 8, False, 20),
+                                                 (11, 4, 512, False, 1)])
+def test_mhc_mix_parity(T, n, d, inplace, iters):
     cfg = 95 + n + d
     X = synth.normal_bf16((T, n, d), 1.0, cfg, 1)
     Y = synth.normal_bf16((T, d), 1.0, cfg, 2)
@@ -60,9 +61,9 @@ def test_mhc_mix_parity(T, n, d, inplace):
     x_dev = from_bits(X)
     x_out = x_dev if inplace else torch.empty_like(x_dev)
     h_out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
-    L.mhc_mix(x_dev, from_bits(Y), torch.from_numpy(Lg).to(DEV), iters=20, x_out=x_out, h_out=h_out)
+    L.mhc_mix(x_dev, from_bits(Y), torch.from_numpy(Lg).to(DEV), iters=iters, x_out=x_out, h_out=h_out)
     torch.cuda.synchronize()
-    Xo, h = O.mhc_mix(synth.bf16_bits_to_f64(X), synth.bf16_bits_to_f64(Y), Lg.astype(np.float64), 20)
+    Xo, h = O.mhc_mix(synth.bf16_bits_to_f64(X), synth.bf16_bits_to_f64(Y), Lg.astype(np.float64), iters)
     assert_bf16_rounding(to_np_bf16(x_out), Xo, f"streams T={T} n={n} d={d}")
     assert_bf16_rounding(to_np_bf16(h_out), h, f"next input T={T} n={n} d={d}")
 
