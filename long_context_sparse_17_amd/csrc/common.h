@@ -82,6 +82,11 @@ __device__ __forceinline__ floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
 __device__ __forceinline__ floatx4 mfma_fp8(intx8 a, intx8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// D(16x16 fp32) = A * B with a power-of-two scale 2^(sa - 127) on each lane's 32 A values (E8M0; lane
+// l holds A row l%16, k = 32 (l/16) .. +31) and unit B scales.
+__device__ __forceinline__ floatx4 mfma_fp8_scale_a(intx8 a, intx8 b, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, sa, 0, 127);
+}
 
 // ----------------------------------------------------------------------------------- wave ops
 // v_permlane16_swap / v_permlane32_swap (VALU, no LDS round trip): every lane receives the values

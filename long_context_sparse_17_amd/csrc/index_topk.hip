@@ -35,6 +35,7 @@ constexpr int kScoreChunk = 1024;           // entries per scoring workgroup
 constexpr int kFilterChunk = 4096;          // entries per filter workgroup
 constexpr int kSelThreads = 256;
 constexpr int kMaxTopk = 2048;
+constexpr int kMaxIndexHeads = 64;         // indexer heads (the entry point rejects more)
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -43,13 +44,21 @@ struct Ws {
   uint32_t* hist;                 // [R, kHistRow]: histograms of the top score-key bits, then of the next 11
   unsigned long long* comb;       // [R, nsp]: kept entries per chunk (decode) / candidates (prefill)
   uint2* counts;                  // [R, nchunk]: per decode chunk (kept, above the threshold bin)
+  uint8_t* qc;                    // [R, HP, 128]: E4M3FN query codes (fp8 prefill)
+  float* qw;                      // [R, HP]: head weights times the query row scales (fp8 prefill)
+  int32_t* qnv;                   // [R]: visible entries per row (fp8 prefill)
+  uint8_t* linc;                  // [B * ceil(Tq / 4), 16, 128]: linear-term parts (fp8 prefill)
+  uint32_t* lins;                 // [B * ceil(Tq / 4), 16, 4]: their scale exponents (E8M0)
   int64_t nsp;
   int nchunk;
 };
 
 inline int64_t n_chunks(int64_t n_cap) { return (n_cap + kFilterChunk - 1) / kFilterChunk; }
 
-Ws carve(void* ws, int R, int64_t n_cap) {
+inline int64_t n_groups4(int B, int Tq) { return (int64_t)B * ((Tq + 3) / 4); }
+
+Ws carve(void* ws, int B, int Tq, int64_t n_cap) {
+  const int R = B * Tq;
   Ws w;
   w.nsp = (n_cap + 63) & ~(int64_t)63;
   w.nchunk = (int)n_chunks(n_cap);
@@ -61,6 +70,16 @@ Ws carve(void* ws, int R, int64_t n_cap) {
   w.comb = reinterpret_cast<unsigned long long*>(p);
   p += al256((size_t)R * w.nsp * 8);
   w.counts = reinterpret_cast<uint2*>(p);
+  p += al256((size_t)R * w.nchunk * 8);
+  w.qc = reinterpret_cast<uint8_t*>(p);
+  p += al256((size_t)R * kMaxIndexHeads * 128);
+  w.qw = reinterpret_cast<float*>(p);
+  p += al256((size_t)R * kMaxIndexHeads * 4);
+  w.qnv = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)R * 4);
+  w.linc = reinterpret_cast<uint8_t*>(p);
+  p += al256((size_t)n_groups4(B, Tq) * 2048);
+  w.lins = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -77,20 +96,46 @@ __global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // ------------------------------------------------------------------------------------ scoring
-// Workgroup: 4 waves.  QW = query rows per wave.  QW == 1: one query per workgroup, the waves split
-// the chunk's entries (decode).  QW == 4: 16 queries per workgroup, every wave scores the whole
-// chunk for its 4 queries (prefill; entries are re-read from L1/L2, not HBM).
-template <bool FP8, int KS, int HBI, int QW>
+// Dims [32g, 32g + 32) of one head row (lane group g = lane / 16, the row's 4 lane groups together
+// hold all 128 dims) quantised to E4M3FN with the row's scale absmax / 448 (RNE, correctly rounded
+// division: the decision rule the selection depends on), packed in MFMA A-fragment order.  Returns
+// the row scale (1 for an all-zero row).  hv == false: zero codes (padding heads).
+__device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg, bool hv, intx8& codes) {
+  uint4 raw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) raw[u] = hv ? *reinterpret_cast<const uint4*>(qseg + 8 * u) : make_uint4(0, 0, 0, 0);
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf2f_lo(wd[j])), fabsf(bf2f_hi(wd[j]))));
+  }
+  amax = max_rows4(amax);
+  const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t b0 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j]), sc));
+      const uint32_t b1 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j]), sc));
+      const uint32_t b2 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j + 1]), sc));
+      const uint32_t b3 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j + 1]), sc));
+      codes[2 * u + j] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+    }
+  }
+  return sc;
+}
+
+// bf16 keys, many query rows (prefill with bf16 indexer keys): 16 queries per workgroup, 4 per wave;
+// every wave scores the workgroup's whole chunk for its 4 queries (entries re-read from L1/L2).
+template <int KS, int HBI>
 __global__ void __launch_bounds__(256)
 index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
-                   const void* __restrict__ ik, const float* __restrict__ ik_scale, int64_t ik_ld,
-                   const int64_t* __restrict__ q_pos, int64_t n_cap, int Tq, int H_I, int dI, int m,
-                   float* __restrict__ scores, uint32_t* __restrict__ hist, int64_t nsp) {
-  constexpr int QWAVES = QW == 1 ? 1 : 4;       // waves that split the queries
-  constexpr int QTILE = QW * QWAVES;
-  constexpr bool HIST = (QW == 1);
-  __shared__ uint32_t lhist[HIST ? kBins : 1];
-
+                   const uint16_t* __restrict__ ik, int64_t ik_ld, const int64_t* __restrict__ q_pos,
+                   int64_t n_cap, int Tq, int H_I, int dI, int m, float* __restrict__ scores, int64_t nsp) {
+  constexpr int QW = 4, QTILE = 16;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int g = lane >> 4, c16 = lane & 15;
@@ -110,23 +155,13 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
   }
   if (c0 >= nv_max) return;                    // uniform across the workgroup
 
-  if (HIST) {
-    for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0u;
-    __syncthreads();
-  }
-
-  // ---- per-query operands: A fragments (head rows) and folded head weights ----
-  const int qgroup = wave % QWAVES;
-  const int kpart = wave / QWAVES;
-  constexpr int KWAVES = 4 / QWAVES;
-  typedef typename std::conditional<FP8, intx8, uint4>::type AFrag;
-  AFrag afr[QW][HBI][KS];
+  uint4 afr[QW][HBI][KS];
   float wq[QW][HBI][4];
   int64_t nvis[QW];
   int64_t rowq[QW];
 #pragma unroll
   for (int qw = 0; qw < QW; ++qw) {
-    const int tq = tq0 + qgroup * QW + qw;
+    const int tq = tq0 + wave * QW + qw;
     const bool qvalid = tq < Tq;
     const int64_t r = (int64_t)b * Tq + (qvalid ? tq : 0);
     rowq[qw] = r;
@@ -136,85 +171,27 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
       const int head = hb * 16 + c16;
       const bool hv = qvalid && head < H_I;
       const uint16_t* qrow = q_idx + (r * H_I + (hv ? head : 0)) * dI;
-      float wh = hv ? bf2f(w_idx[r * H_I + head]) : 0.f;
-      if (FP8) {
-        // dims [32g, 32g+32) of this head row
-        uint4 raw[4];
+      const float wh = hv ? bf2f(w_idx[r * H_I + head]) : 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          raw[u] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * u) : make_uint4(0, 0, 0, 0);
-        float v[32];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[8 * u + 0] = bf2f_lo(raw[u].x); v[8 * u + 1] = bf2f_hi(raw[u].x);
-          v[8 * u + 2] = bf2f_lo(raw[u].y); v[8 * u + 3] = bf2f_hi(raw[u].y);
-          v[8 * u + 4] = bf2f_lo(raw[u].z); v[8 * u + 5] = bf2f_hi(raw[u].z);
-          v[8 * u + 6] = bf2f_lo(raw[u].w); v[8 * u + 7] = bf2f_hi(raw[u].w);
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-        amax = max_rows4(amax);
-        const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-        intx8 codes;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t b0 = f2e4m3(__fdiv_rn(v[4 * j + 0], s));
-          const uint32_t b1 = f2e4m3(__fdiv_rn(v[4 * j + 1], s));
-          const uint32_t b2 = f2e4m3(__fdiv_rn(v[4 * j + 2], s));
-          const uint32_t b3 = f2e4m3(__fdiv_rn(v[4 * j + 3], s));
-          codes[j] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
-        }
-        if (!hv) codes = intx8{0, 0, 0, 0, 0, 0, 0, 0};
-        afr[qw][hb][0] = *reinterpret_cast<AFrag*>(&codes);
-        wh *= s;
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint4 a = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-          afr[qw][hb][ks] = *reinterpret_cast<AFrag*>(&a);
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        afr[qw][hb][ks] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
       // the D fragment of this lane holds heads 16hb + 4g + i: fetch their weights
 #pragma unroll
       for (int i = 0; i < 4; ++i) wq[qw][hb][i] = __shfl(wh, 4 * g + i, kWave);
     }
   }
 
-  // ---- entry loop ----
-  const int64_t span = kScoreChunk / KWAVES;
-  int64_t e_lo = c0 + kpart * span;
-  int64_t e_hi = e_lo + span;
+  int64_t e_hi = c0 + kScoreChunk;
   if (e_hi > nv_max) e_hi = nv_max;
-  const uint8_t* ik8 = static_cast<const uint8_t*>(ik) + (int64_t)b * ik_ld * dI;
-  const uint16_t* ik16 = static_cast<const uint16_t*>(ik) + (int64_t)b * ik_ld * dI;
-  const float* ksc = ik_scale ? ik_scale + (int64_t)b * ik_ld : nullptr;
-
-  for (int64_t e0 = e_lo; e0 < e_hi; e0 += 64) {
-    typedef typename std::conditional<FP8, intx8, uint4>::type BFrag;
-    BFrag bfr[4][KS];
-    float kscale[4];
+  const uint16_t* ik16 = ik + (int64_t)b * ik_ld * dI;
+  for (int64_t e0 = c0; e0 < e_hi; e0 += 64) {
+    uint4 bfr[4][KS];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t e = e0 + 16 * u + c16;
-      const bool ev = e < e_hi;
-      if (FP8) {
-        intx8 v = intx8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (ev) {
-          const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 32 * g);
-          const uint4 x0 = p[0], x1 = p[1];
-          v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
-        bfr[u][0] = *reinterpret_cast<BFrag*>(&v);
-        kscale[u] = ev ? ksc[e] : 0.f;
-      } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint4 v = ev ? *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-          bfr[u][ks] = *reinterpret_cast<BFrag*>(&v);
-        }
-        kscale[u] = 1.f;
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        bfr[u][ks] = e < e_hi ? *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int qw = 0; qw < QW; ++qw) {
@@ -225,34 +202,341 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
         for (int hb = 0; hb < HBI; ++hb) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (FP8)
-              acc = mfma_fp8(*reinterpret_cast<intx8*>(&afr[qw][hb][ks]), *reinterpret_cast<intx8*>(&bfr[u][ks]), acc);
-            else
-              acc = mfma_bf16(*reinterpret_cast<uint4*>(&afr[qw][hb][ks]), *reinterpret_cast<uint4*>(&bfr[u][ks]), acc);
-          }
+          for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(afr[qw][hb][ks], bfr[u][ks], acc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) part += wq[qw][hb][i] * fmaxf(acc[i], 0.f);
         }
         part = sum_rows4(part);
         const int64_t e = e0 + 16 * u + c16;
-        if (g == 0 && e < nvis[qw]) {
-          const float sc = part * kscale[u] + 0.0f;
-          scores[rowq[qw] * nsp + e] = sc;
-          if (HIST) atomicAdd(&lhist[float_key(sc) >> kBinShift], 1u);
-        }
+        if (g == 0 && e < nvis[qw]) scores[rowq[qw] * nsp + e] = part + 0.0f;
       }
     }
   }
+}
 
-  if (HIST) {
+// fp8 keys, many query rows (chunked prefill).  The head sum is evaluated through
+//     sum_h w'_h relu(a_h) = 1/2 sum_h w'_h |a_h|  +  1/2 sum_h w'_h a_h          (w'_h = w_h * s_h)
+// where a_h = q^_h . k is the code dot product of head h: the first half costs one fused multiply-add
+// per head and entry (|a| is a free source modifier), the second is linear in the query,
+// (sum_h w'_h q^_h / 2) . k = u . k, and runs on the matrix cores.  u (128 values per query) is
+// carried as 4 E4M3FN parts with one power-of-two (E8M0) scale each, every part encoding the previous
+// parts' exact residual, so |u - sum of parts| <= 2^-19 max|u| elementwise.  Two
+// kernels:
+//   index_qprep_kernel: every query head row quantised once (codes [R][HP][128] in fragment order,
+//     half weights w'_h / 2 [R][HP], HP = heads padded to 16 with zero codes and weights), each
+//     row's visible entry count (int32), and the parts of u as the rows 4j + p of one MFMA A fragment
+//     per 4 consecutive queries (codes [G][16][128], scale exponents [G][16][4] (all four equal),
+//     G = (b, t / 4)).
+//   index_score_prefill_kernel: one workgroup of 8 waves per chunk of 1024 entries (and a range of
+//     queries).  Each wave keeps the B fragments of its 128 entries (8 blocks of 16) in registers for
+//     the whole launch and streams the queries: stages of 4 queries' codes and weights go through LDS
+//     (double-buffered, one barrier per stage); per stage 8 MFMAs give the 4 queries' u . k (lane
+//     group j holds query j's parts), per query each head block's A fragment feeds 8 MFMAs back to
+//     back, |a| * w'/2 accumulates per entry block onto query j's linear term (lane group j only), and
+//     a reduce-scatter over the 4 lane groups (v_permlane16/32_swap) leaves lane (g, c) with entry
+//     blocks g and 4 + g, so each query's 128 scores leave in two 256-byte row stores.
+constexpr int kPfWaves = 8;
+constexpr int kPfEB = 8;                                // 16-entry blocks per wave
+constexpr int kPfChunk = kPfWaves * kPfEB * 16;         // entries per workgroup
+constexpr int kPfQC = 4;                                // queries per LDS stage
+constexpr int kPfRow = 144;                             // LDS bytes per head row: 128 codes + 16 (conflict-free reads)
+
+constexpr int kLinParts = 4;                            // E4M3FN parts of the linear-term vector u
+
+// E4M3FN code -> value, exact: bias 7, 3 mantissa bits, subnormal quantum 2^-9 (no NaN codes occur).
+__device__ __forceinline__ double e4m3_value(uint32_t c) {
+  const int e = (int)((c >> 3) & 15u), mt = (int)(c & 7u);
+  const double v = e ? ldexp(8.0 + mt, e - 10) : ldexp((double)mt, -9);
+  return (c & 0x80u) ? -v : v;
+}
+
+template <int HBI>
+__global__ void __launch_bounds__(256)
+index_qprep_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx, int H_I,
+                   const int64_t* __restrict__ q_pos, int64_t n_cap, int m, int Tq, uint8_t* __restrict__ qc,
+                   float* __restrict__ qwf, int32_t* __restrict__ qnv, uint8_t* __restrict__ linc,
+                   uint32_t* __restrict__ lins) {
+  constexpr int HP = 16 * HBI;
+  __shared__ uint32_t s_codes[HP][33];                 // a head row's 128 codes as 32 words (+1: no conflicts)
+  __shared__ float s_w[HP];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t r = blockIdx.x;
+  if (wave < HBI) {
+    const int head = 16 * wave + c16;
+    const bool hv = head < H_I;
+    intx8 codes;
+    const float sc = quant_row_e4m3(q_idx + (r * H_I + (hv ? head : 0)) * 128 + 32 * g, hv, codes);
+    uint4* dst = reinterpret_cast<uint4*>(qc + (r * HP + head) * 128 + 32 * g);
+    dst[0] = make_uint4((uint32_t)codes[0], (uint32_t)codes[1], (uint32_t)codes[2], (uint32_t)codes[3]);
+    dst[1] = make_uint4((uint32_t)codes[4], (uint32_t)codes[5], (uint32_t)codes[6], (uint32_t)codes[7]);
+    const float wh = hv ? bf2f(w_idx[r * H_I + head]) * sc * 0.5f : 0.f;
+    if (g == 0) {
+      qwf[r * HP + head] = wh;
+      s_w[head] = wh;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_codes[head][8 * g + i] = (uint32_t)codes[i];
+  }
+  if (threadIdx.x == 0) qnv[r] = (int32_t)n_visible(q_pos, r, m, n_cap);
+  __syncthreads();
+  // u_d = sum_h (w'_h / 2) * value(code_hd) in fp64 (exact products, 64 terms), then split into parts:
+  // part p = RNE_e4m3(res / 2^e_p) with e_p the smallest exponent putting the row's largest |res|
+  // within 448, res -= 2^e_p * part (exact).  One exponent per part and query: the matrix cores'
+  // 32-value scale blocks follow their own k order, so the same exponent goes to all four.
+  // Dims d = threadIdx.x < 128 (waves 0, 1); every thread takes part in the barriers.
+  __shared__ double s_mx[2];
+  const int d = threadIdx.x;
+  double res = 0.0;
+  if (d < 128)
+    for (int h = 0; h < HP; ++h)
+      res += (double)s_w[h] * e4m3_value((s_codes[h][d >> 2] >> (8 * (d & 3))) & 0xFFu);
+  const int64_t b = r / Tq;
+  const int tq = (int)(r % Tq), j = tq & 3;
+  const int64_t G = b * ((Tq + 3) / 4) + tq / 4;
+  uint8_t* crow = linc + G * 2048;
+  uint32_t* srow = lins + G * 64;
+#pragma unroll 1
+  for (int p = 0; p < kLinParts; ++p) {
+    double mx = d < 128 ? fabs(res) : 0.0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, kWave));
+    if (lane == 0 && wave < 2) s_mx[wave] = mx;
     __syncthreads();
-    uint32_t* gh = hist + rowq[0] * kHistRow;
-    for (int i = threadIdx.x; i < kBins; i += 256) {
-      const uint32_t v = lhist[i];
-      if (v) atomicAdd(gh + i, v);
+    mx = fmax(s_mx[0], s_mx[1]);
+    __syncthreads();                                   // s_mx is rewritten by the next part
+    int e = 0;
+    if (mx > 0.0) {
+      int k;
+      const double f = frexp(mx / 448.0, &k);          // mx / 448 = f 2^k, f in [0.5, 1)
+      e = f == 0.5 ? k - 1 : k;
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    if (d < 128) {
+      const uint32_t c = f2e4m3((float)ldexp(res, -e));
+      res -= ldexp(e4m3_value(c), e);
+      crow[(4 * j + p) * 128 + d] = (uint8_t)c;
+    }
+    if (d < 4) srow[(4 * j + p) * 4 + d] = (uint32_t)(e + 127);
+  }
+  // the last query of a partial group clears the rows of the missing ones
+  if (tq == Tq - 1 && d < 128) {
+    for (int jj = j + 1; jj < 4; ++jj)
+      for (int p = 0; p < kLinParts; ++p) {
+        crow[(4 * jj + p) * 128 + d] = 0;
+        if (d < 4) srow[(4 * jj + p) * 4 + d] = 127u;
+      }
+  }
+}
+
+template <int HBI>
+__global__ void __launch_bounds__(kPfWaves * kWave)
+index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restrict__ qwf,
+                           const int32_t* __restrict__ qnv, const uint8_t* __restrict__ linc,
+                           const uint32_t* __restrict__ lins, const uint8_t* __restrict__ ik,
+                           const float* __restrict__ ik_scale, int64_t ik_ld, int64_t n_cap, int Tq, int qsplit,
+                           int qper, float* __restrict__ scores, int64_t nsp) {
+  constexpr int HP = 16 * HBI;
+  constexpr int kCodeBytes = HP * kPfRow;
+  constexpr int kSlot = kCodeBytes + HP * 4 + 16;      // one query in LDS: codes, folded weights, n_vis
+  constexpr int kThreads = kPfWaves * kWave;
+  constexpr int kLd = kPfQC * HP * 8 / kThreads;       // 16-byte code pieces per thread per stage (= HBI)
+  static_assert(kPfQC * HP * 8 == kLd * kThreads, "stage pieces must divide evenly");
+  static_assert(kPfQC * (HP + 1) <= kThreads, "one weight or count per thread");
+  static_assert(kPfQC == 4 && kLinParts == 4, "a stage's linear-term fragment holds 4 queries x 4 parts");
+  __shared__ __align__(16) uint8_t sq[2][kPfQC][kSlot];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int b = blockIdx.y / qsplit;
+  const int q_lo = (blockIdx.y % qsplit) * qper;
+  const int q_hi = q_lo + qper < Tq ? q_lo + qper : Tq;
+  if (q_lo >= q_hi) return;                            // uniform
+  const int64_t c0 = (int64_t)blockIdx.x * kPfChunk;
+  const int64_t ew = c0 + wave * (kPfEB * 16);         // first entry of this wave
+
+  // ---- this wave's keys: B fragments (entry 16 eb + c16, dims [32g, 32g + 32)) and two scales ----
+  intx8 bfr[kPfEB];
+  const uint8_t* ikb = ik + (int64_t)b * ik_ld * 128;
+#pragma unroll
+  for (int eb = 0; eb < kPfEB; ++eb) {
+    const int64_t e = ew + 16 * eb + c16;
+    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+    if (e < n_cap) {
+      const uint4* p = reinterpret_cast<const uint4*>(ikb + e * 128 + 32 * g);
+      x0 = p[0];
+      x1 = p[1];
+    }
+    bfr[eb] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+  const int64_t e_lo = ew + 16 * g + c16;              // entries this lane stores: e_lo, e_lo + 64
+  const float* ksb = ik_scale + (int64_t)b * ik_ld;
+  const float ks0 = e_lo < n_cap ? ksb[e_lo] : 0.f;
+  const float ks1 = e_lo + 64 < n_cap ? ksb[e_lo + 64] : 0.f;
+
+  // ---- query stages: codes, weights and n_vis of kPfQC queries, global -> registers -> LDS.  Slots
+  // past the range load the range's last query (never scored), so every load is unconditional. ----
+  // staging registers as one native vector: an array of uint4 here is not promoted to registers
+  // (it would live in scratch and the prefetch would wait for its loads at once)
+  typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+  static_assert(kLd <= 4, "staging vector holds 4 pieces");
+  u32x16 stg;
+  uint32_t stw = 0u;
+  const int64_t row0 = (int64_t)b * Tq;
+  const int64_t G0 = (int64_t)b * ((Tq + 3) / 4) + q_lo / 4;  // linear-term fragment of stage 0
+  uint4 lx0, lx1;                                      // next stage's fragment: this lane's 32 codes ...
+  uint32_t lxs;                                        // ... and their scale exponent
+#define LCS_PF_FETCH(S)                                                                           \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kLd; ++i) {                                             \
+      const int c = tid + i * kThreads; /* piece index in [kPfQC][HP][8] */                       \
+      const int j = c / (HP * 8), head = (c / 8) % HP, piece = c % 8;                             \
+      int tq = q_lo + (S) * kPfQC + j;                                                            \
+      tq = tq < q_hi ? tq : q_hi - 1;                                                             \
+      const uint4 t = *reinterpret_cast<const uint4*>(qc + ((row0 + tq) * HP + head) * 128 + 16 * piece); \
+      stg[4 * i] = t.x; stg[4 * i + 1] = t.y; stg[4 * i + 2] = t.z; stg[4 * i + 3] = t.w;        \
+    }                                                                                             \
+    {                                                                                             \
+      const uint4* lp = reinterpret_cast<const uint4*>(linc + (G0 + (S)) * 2048 + c16 * 128 + 32 * g); \
+      lx0 = lp[0];                                                                                \
+      lx1 = lp[1];                                                                                \
+      lxs = lins[(G0 + (S)) * 64 + c16 * 4 + g];                                                  \
+    }                                                                                             \
+    if (tid < kPfQC * HP) {                                                                       \
+      int tq = q_lo + (S) * kPfQC + tid / HP;                                                     \
+      tq = tq < q_hi ? tq : q_hi - 1;                                                             \
+      stw = __float_as_uint(qwf[(row0 + tq) * HP + tid % HP]);                                    \
+    } else if (tid < kPfQC * (HP + 1)) {                                                          \
+      int tq = q_lo + (S) * kPfQC + (tid - kPfQC * HP);                                           \
+      tq = tq < q_hi ? tq : q_hi - 1;                                                             \
+      stw = (uint32_t)qnv[row0 + tq];                                                             \
+    }                                                                                             \
+  } while (0)
+#define LCS_PF_COMMIT(BUF)                                                                        \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kLd; ++i) {                                             \
+      const int c = tid + i * kThreads;                                                           \
+      const int j = c / (HP * 8), head = (c / 8) % HP, piece = c % 8;                             \
+      *reinterpret_cast<uint4*>(&sq[BUF][j][head * kPfRow + 16 * piece]) =                       \
+          make_uint4(stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]);                \
+    }                                                                                             \
+    if (tid < kPfQC * HP)                                                                         \
+      *reinterpret_cast<uint32_t*>(&sq[BUF][tid / HP][kCodeBytes + 4 * (tid % HP)]) = stw;        \
+    else if (tid < kPfQC * (HP + 1))                                                              \
+      *reinterpret_cast<uint32_t*>(&sq[BUF][tid - kPfQC * HP][kCodeBytes + 4 * HP]) = stw;        \
+  } while (0)
+
+  const int nst = (q_hi - q_lo + kPfQC - 1) / kPfQC;
+  LCS_PF_FETCH(0);
+  LCS_PF_COMMIT(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const intx8 la = intx8{(int)lx0.x, (int)lx0.y, (int)lx0.z, (int)lx0.w, (int)lx1.x, (int)lx1.y, (int)lx1.z, (int)lx1.w};
+    const int lsc = (int)lxs;
+    if (s + 1 < nst) LCS_PF_FETCH(s + 1);              // in flight while this stage is scored
+    const uint8_t* qb = &sq[s & 1][0][0];
+    int nvq[kPfQC];
+    int nv_hi = 0;
+#pragma unroll
+    for (int j = 0; j < kPfQC; ++j) {
+      const int v = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int32_t*>(qb + j * kSlot + kCodeBytes + 4 * HP));
+      nvq[j] = q_lo + s * kPfQC + j < q_hi ? v : 0;
+      nv_hi = nvq[j] > nv_hi ? nvq[j] : nv_hi;
+    }
+    if (ew < nv_hi) {                                  // wave-uniform: some entry of this wave visible
+      // u . k of the stage's 4 queries: lane group j holds query j's 4 parts; their sum is its term
+      float lin[kPfEB];
+#pragma unroll
+      for (int eb = 0; eb < kPfEB; ++eb) {
+        const floatx4 t = mfma_fp8_scale_a(la, bfr[eb], lsc);
+        lin[eb] = (t[0] + t[1]) + (t[2] + t[3]);
+      }
+      // Straight-line software pipeline over the stage's steps (query j, head block hb): the MFMAs
+      // of step t are issued next to the |a| * w' accumulation of step t - 1, whose results are
+      // long complete, so the in-order issue never waits on a fresh MFMA result.  Invisible
+      // queries of a partly visible stage are computed and not stored.
+      constexpr int NSTEP = kPfQC * HBI;
+      floatx4 acc[2][kPfEB];
+      intx8 av[2];
+      float4 wv[3];                                    // step t's weights are read at t - 1 and used at t + 1
+      float part[kPfEB];
+      float res0[kPfQC], res1[kPfQC];
+      auto read_step = [&](int t) {                    // A fragment and head weights of step t (LDS)
+        const int j = t / HBI, hb = t % HBI;
+        const uint8_t* qs = qb + j * kSlot;
+        const uint4* ap = reinterpret_cast<const uint4*>(qs + (16 * hb + c16) * kPfRow + 32 * g);
+        const uint4 a0 = ap[0], a1 = ap[1];
+        av[t & 1] = intx8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        wv[t % 3] = *reinterpret_cast<const float4*>(qs + kCodeBytes + 4 * (16 * hb + 4 * g));
+      };
+      read_step(0);
+#pragma unroll
+      for (int t = 0; t <= NSTEP; ++t) {
+        if (t + 1 < NSTEP) read_step(t + 1);           // one step ahead
+        if (t < NSTEP) {
+#pragma unroll
+          for (int eb = 0; eb < kPfEB; ++eb) acc[t & 1][eb] = mfma_fp8(av[t & 1], bfr[eb], floatx4{0.f, 0.f, 0.f, 0.f});
+        }
+        if (t > 0) {
+          const int tp = t - 1, jp = tp / HBI, hbp = tp % HBI;
+          const float4 w = wv[tp % 3];
+          if (hbp == 0) {
+#pragma unroll
+            for (int eb = 0; eb < kPfEB; ++eb) part[eb] = g == jp ? lin[eb] : 0.f;
+          }
+#pragma unroll
+          for (int eb = 0; eb < kPfEB; ++eb) {
+            const floatx4 x = acc[tp & 1][eb];
+            part[eb] = fmaf(w.x, fabsf(x[0]), part[eb]);
+            part[eb] = fmaf(w.y, fabsf(x[1]), part[eb]);
+            part[eb] = fmaf(w.z, fabsf(x[2]), part[eb]);
+            part[eb] = fmaf(w.w, fabsf(x[3]), part[eb]);
+          }
+          if (hbp == HBI - 1) {
+            // reduce-scatter over the 4 lane groups: lane group g ends with the totals of entry
+            // blocks g and 4 + g for its column c16
+            float h2[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[2 * p]),
+                                                              __float_as_uint(part[2 * p + 1]), false, false);
+              h2[p] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+            }
+            const auto y0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(h2[0]), __float_as_uint(h2[1]), false, false);
+            const auto y1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(h2[2]), __float_as_uint(h2[3]), false, false);
+            res0[jp] = (__uint_as_float(y0[0]) + __uint_as_float(y0[1])) * ks0 + 0.0f;
+            res1[jp] = (__uint_as_float(y1[0]) + __uint_as_float(y1[1])) * ks1 + 0.0f;
+          }
+        }
+        if (t > 0 && t < NSTEP) {
+          // issue order within the step: the next step's LDS reads first (a whole step ahead of
+          // their use), then one MFMA and four of the previous step's VALU, eight times.  Left
+          // alone, the scheduler clusters the MFMAs (the in-order issue then serialises them with
+          // the VALU work), pairs them with VALU reading their own fresh results, and sinks the
+          // reads to the end of the step, just before their wait.
+          if (t + 1 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+          for (int i = 0; i < kPfEB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);             // steps do not mix
+      }
+#pragma unroll
+      for (int j = 0; j < kPfQC; ++j) {
+        float* srow = scores + (row0 + q_lo + s * kPfQC + j) * nsp;
+        if (e_lo < nvq[j]) srow[e_lo] = res0[j];
+        if (e_lo + 64 < nvq[j]) srow[e_lo + 64] = res1[j];
+      }
+    }
+    if (s + 1 < nst) {
+      LCS_PF_COMMIT((s + 1) & 1);   // that buffer was last read in stage s - 1, before the previous barrier
+      __syncthreads();
     }
   }
+#undef LCS_PF_FETCH
+#undef LCS_PF_COMMIT
 }
 
 // Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  The 4 waves quantise
@@ -289,32 +573,8 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     float wh = bf2f(w_idx[r * H_I + hl]);
     if (!hv) wh = 0.f;
     if (FP8) {
-      uint4 raw[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>(qrow + 32 * g + 8 * u);
-      float amax = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf2f_lo(wd[j])), fabsf(bf2f_hi(wd[j]))));
-      }
-      amax = max_rows4(amax);
-      const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
       intx8 codes;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t b0 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j]), sc));
-          const uint32_t b1 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j]), sc));
-          const uint32_t b2 = f2e4m3(__fdiv_rn(bf2f_lo(wd[2 * j + 1]), sc));
-          const uint32_t b3 = f2e4m3(__fdiv_rn(bf2f_hi(wd[2 * j + 1]), sc));
-          codes[2 * u + j] = (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
-        }
-      }
-      if (!hv) codes = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+      const float sc = quant_row_e4m3(qrow + 32 * g, hv, codes);
       s_afr[wave][0][lane] = *reinterpret_cast<Frag*>(&codes);
       wh *= sc;
     } else {
@@ -1125,36 +1385,75 @@ int64_t decode_chunk(int64_t n_cap, int R) {
   return c;
 }
 
-template <bool FP8, int KS, int HBI, int QW>
-void launch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
-  if constexpr (QW == 1) {
-    const int64_t chunk = decode_chunk(a.n_cap, a.B * a.Tq);
-    dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * a.Tq));
-    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI>), grid, dim3(256), 0, st,
-               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
-               w.scores, w.hist, w.nsp);
-    return;
-  }
-  constexpr int QTILE = QW == 1 ? 1 : 16;
-  const int tiles = (a.Tq + QTILE - 1) / QTILE;
-  dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));
-  LCS_LAUNCH("index_score_kernel", (index_score_kernel<FP8, KS, HBI, QW>), grid, dim3(256), 0, st,
-             a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m,
+template <bool FP8, int KS, int HBI>
+void launch_score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  const int64_t chunk = decode_chunk(a.n_cap, a.B * a.Tq);
+  dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * a.Tq));
+  LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI>), grid, dim3(256), 0, st,
+             a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
              w.scores, w.hist, w.nsp);
 }
 
-template <bool FP8, int KS, int QW>
-void dispatch_hbi(const IndexArgs& a, const Ws& w, hipStream_t st) {
-  if (a.H_I <= 16) launch_score<FP8, KS, 1, QW>(a, w, st);
-  else if (a.H_I <= 32) launch_score<FP8, KS, 2, QW>(a, w, st);
-  else launch_score<FP8, KS, 4, QW>(a, w, st);
+template <int KS, int HBI>
+void launch_score_rows_bf16(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  const int tiles = (a.Tq + 15) / 16;
+  dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));
+  LCS_LAUNCH("index_score_kernel", (index_score_kernel<KS, HBI>), grid, dim3(256), 0, st, a.q_idx, a.w_idx,
+             static_cast<const uint16_t*>(a.ik), a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, w.scores, w.nsp);
 }
 
-template <int QW>
-void dispatch_score(const IndexArgs& a, const Ws& w, hipStream_t st) {
-  if (a.ik_fp8) dispatch_hbi<true, 1, QW>(a, w, st);
-  else if (a.dI == 64) dispatch_hbi<false, 2, QW>(a, w, st);
-  else dispatch_hbi<false, 4, QW>(a, w, st);
+// Query ranges per entry chunk: enough workgroups for two per CU when the chunks alone are fewer.
+template <int HBI>
+void launch_score_rows_fp8(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  constexpr int HP = 16 * HBI;
+  LCS_LAUNCH("index_qprep_kernel", index_qprep_kernel<HBI>, dim3((unsigned)(a.B * a.Tq)), dim3(256), 0, st,
+             a.q_idx, a.w_idx, a.H_I, a.q_pos, a.n_cap, a.m, a.Tq, w.qc, w.qw, w.qnv, w.linc, w.lins);
+  const int64_t nchunk = (a.n_cap + kPfChunk - 1) / kPfChunk;
+  const int nstage = (a.Tq + kPfQC - 1) / kPfQC;
+  const int64_t want = (512 + nchunk * a.B - 1) / (nchunk * a.B);
+  const int qs0 = (int)(want < nstage ? want : nstage);
+  const int qper = (nstage + qs0 - 1) / qs0 * kPfQC;
+  const int qsplit = (a.Tq + qper - 1) / qper;
+  dim3 grid((unsigned)nchunk, (unsigned)(a.B * qsplit));
+  LCS_LAUNCH("index_score_kernel", index_score_prefill_kernel<HBI>, grid, dim3(kPfWaves * kWave), 0, st, w.qc, w.qw,
+             w.qnv, w.linc, w.lins, static_cast<const uint8_t*>(a.ik), a.ik_scale, a.ik_ld, a.n_cap, a.Tq, qsplit, qper, w.scores,
+             w.nsp);
+  (void)HP;
+}
+
+void score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  const int hbi = (a.H_I + 15) / 16;
+  if (a.ik_fp8) {
+    if (hbi == 1) launch_score_decode<true, 1, 1>(a, w, st);
+    else if (hbi == 2) launch_score_decode<true, 1, 2>(a, w, st);
+    else launch_score_decode<true, 1, 4>(a, w, st);
+  } else if (a.dI == 64) {
+    if (hbi == 1) launch_score_decode<false, 2, 1>(a, w, st);
+    else if (hbi == 2) launch_score_decode<false, 2, 2>(a, w, st);
+    else launch_score_decode<false, 2, 4>(a, w, st);
+  } else {
+    if (hbi == 1) launch_score_decode<false, 4, 1>(a, w, st);
+    else if (hbi == 2) launch_score_decode<false, 4, 2>(a, w, st);
+    else launch_score_decode<false, 4, 4>(a, w, st);
+  }
+}
+
+void score_rows(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  const int hbi = (a.H_I + 15) / 16;
+  if (a.ik_fp8) {
+    if (hbi == 1) launch_score_rows_fp8<1>(a, w, st);
+    else if (hbi == 2) launch_score_rows_fp8<2>(a, w, st);
+    else if (hbi == 3) launch_score_rows_fp8<3>(a, w, st);
+    else launch_score_rows_fp8<4>(a, w, st);
+  } else if (a.dI == 64) {
+    if (hbi == 1) launch_score_rows_bf16<2, 1>(a, w, st);
+    else if (hbi == 2) launch_score_rows_bf16<2, 2>(a, w, st);
+    else launch_score_rows_bf16<2, 4>(a, w, st);
+  } else {
+    if (hbi == 1) launch_score_rows_bf16<4, 1>(a, w, st);
+    else if (hbi == 2) launch_score_rows_bf16<4, 2>(a, w, st);
+    else launch_score_rows_bf16<4, 4>(a, w, st);
+  }
 }
 
 }  // namespace
@@ -1164,12 +1463,14 @@ size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   const int64_t R = (int64_t)B * Tq;
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
   return al256((size_t)R * nsp * 4) + al256((size_t)R * kHistRow * 4) + al256((size_t)R * nsp * 8) +
-         al256((size_t)R * n_chunks(n_cap) * 8);
+         al256((size_t)R * n_chunks(n_cap) * 8) + al256((size_t)R * kMaxIndexHeads * 128) +
+         al256((size_t)R * kMaxIndexHeads * 4) + al256((size_t)R * 4) + al256((size_t)n_groups4(B, Tq) * 2048) +
+         al256((size_t)n_groups4(B, Tq) * 256);
 }
 
 int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   const int R = a.B * a.Tq;
-  Ws w = carve(a.ws, R, a.n_cap);
+  Ws w = carve(a.ws, a.B, a.Tq, a.n_cap);
   // Few rows: spread every row over many workgroups (decode).  Many rows, or rows longer than the
   // decode selection stages: row-per-workgroup.
   const bool decode = R < 64 && w.nchunk <= kMaxDecodeChunks;
@@ -1177,14 +1478,14 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
     const int64_t n = (int64_t)R * kHistRow;
     LCS_LAUNCH("topk_clear_kernel", clear_u32_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
                dim3(256), 0, st, w.hist, n);
-    dispatch_score<1>(a, w, st);
+    score_decode(a, w, st);
     dim3 gf((unsigned)w.nchunk, (unsigned)R);
     LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.comb,
                w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k);
     LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
                w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
   } else {
-    dispatch_score<4>(a, w, st);
+    score_rows(a, w, st);
     LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
                w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
   }

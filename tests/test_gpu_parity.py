@@ -192,6 +192,18 @@ def test_index_topk_prefill_fp8_rowwise():
     assert band <= 4
 
 
+@pytest.mark.parametrize("H_I,Tq,n_cap", [(16, 37, 2500), (40, 50, 1100), (64, 35, 5000)])
+def test_index_topk_prefill_fp8_head_blocks_ragged(H_I, Tq, n_cap):
+    # fp8 prefill scoring with 1 / 3 / 4 blocks of 16 heads; Tq not a multiple of 4 (the last group
+    # of 4 queries is partly empty); batch row 0 at the end of the cache, row 1 spread from empty
+    # (t < m) through partial visibility to full; n_cap spanning several 1024-entry chunks + a tail
+    k = 96
+    full = list(range(4 * n_cap - Tq + 1, 4 * n_cap + 1))
+    spread = [int(x) for x in np.linspace(0, 4 * n_cap + 20, Tq)]
+    band = _index_case(2, Tq, n_cap, H_I, 128, k, 4, True, full + spread, 36 + H_I)
+    assert band <= 4
+
+
 def test_index_topk_bf16_small_heads():
     # the prefill-2k shape family: 8 heads x 64 dims, bf16 keys, top-k 128
     Tq, n_cap, k = 70, 512, 128
