@@ -96,14 +96,16 @@ __global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // ------------------------------------------------------------------------------------ scoring
-// Dims [32g, 32g + 32) of one head row (lane group g = lane / 16, the row's 4 lane groups together
-// hold all 128 dims) quantised to E4M3FN with the row's scale absmax / 448 (RNE, correctly rounded
-// division: the decision rule the selection depends on), packed in MFMA A-fragment order.  Returns
-// the row scale (1 for an all-zero row).  hv == false: zero codes (padding heads).
-__device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg, bool hv, intx8& codes) {
+// 32 dims of one head row -- the 16 at qseg0, then the 16 at qseg1 (the row's 4 lane groups together
+// hold all 128 dims) -- quantised to E4M3FN with the row's scale absmax / 448 (RNE, correctly rounded
+// division: the decision rule the selection depends on), packed in that order as an MFMA A fragment.
+// Returns the row scale (1 for an all-zero row).  hv == false: zero codes (padding heads).  The
+// matrix cores only need A and B to share one assignment of dims to (lane group, register, byte).
+__device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg0, const uint16_t* qseg1, bool hv, intx8& codes) {
   uint4 raw[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) raw[u] = hv ? *reinterpret_cast<const uint4*>(qseg + 8 * u) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < 4; ++u)
+    raw[u] = hv ? *reinterpret_cast<const uint4*>((u < 2 ? qseg0 : qseg1) + 8 * (u & 1)) : make_uint4(0, 0, 0, 0);
   float amax = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -266,7 +268,8 @@ index_qprep_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
     const int head = 16 * wave + c16;
     const bool hv = head < H_I;
     intx8 codes;
-    const float sc = quant_row_e4m3(q_idx + (r * H_I + (hv ? head : 0)) * 128 + 32 * g, hv, codes);
+    const uint16_t* qrow = q_idx + (r * H_I + (hv ? head : 0)) * 128;
+    const float sc = quant_row_e4m3(qrow + 32 * g, qrow + 32 * g + 16, hv, codes);
     uint4* dst = reinterpret_cast<uint4*>(qc + (r * HP + head) * 128 + 32 * g);
     dst[0] = make_uint4((uint32_t)codes[0], (uint32_t)codes[1], (uint32_t)codes[2], (uint32_t)codes[3]);
     dst[1] = make_uint4((uint32_t)codes[4], (uint32_t)codes[5], (uint32_t)codes[6], (uint32_t)codes[7]);
@@ -574,7 +577,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     if (!hv) wh = 0.f;
     if (FP8) {
       intx8 codes;
-      const float sc = quant_row_e4m3(qrow + 32 * g, hv, codes);
+      const float sc = quant_row_e4m3(qrow + 16 * g, qrow + 64 + 16 * g, hv, codes);
       s_afr[wave][0][lane] = *reinterpret_cast<Frag*>(&codes);
       wh *= sc;
     } else {
@@ -615,8 +618,10 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       int64_t e = c0 + 64 * gi + 16 * u + c16;
       e = e < c1 ? e : c1 - 1;
       if (FP8) {
-        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 32 * g);
-        const uint4 x0 = p[0], x1 = p[1];
+        // bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16): each load instruction covers 64
+        // contiguous bytes of 16 rows (the query codes use the same dim order)
+        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 16 * g);
+        const uint4 x0 = p[0], x1 = p[4];
         intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         fr[u][0] = *reinterpret_cast<Frag*>(&v);
       } else {
@@ -1128,6 +1133,11 @@ topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __re
 }
 
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
+constexpr int kSampleBlock = 32;            // sampled run of consecutive entries (one 128-byte line)
+constexpr int kSampleBlocks = 512;          // sampled runs per row, at most
+constexpr int kSampleMinStride = 512;       // at least 16x fewer lines than the row
+constexpr int64_t kSampleMinRow = 8192;     // shorter rows take the full path
+constexpr int kSampleMinRatio = 8;          // ... and rows with k above an eighth of them
 constexpr int kBitmapEntries = 1 << 18;     // rows up to this many entries are ordered through an LDS bitmap
 constexpr int kBitmapWords = kBitmapEntries / 32;
 
@@ -1146,10 +1156,11 @@ struct SelShared {
   } u;
 };
 
-// Resolve `need` winners among `ncand` candidate keys (all in the threshold bin) digit by digit and
-// append their entry indices to sel_list.  Keys are read once into LDS when they fit.
+// Resolve `need` winners among `ncand` candidate keys digit by digit and append their entry indices
+// to sel_list.  A key is `key_bits` wide: the score-key bits (all 32, or the 21 below a common bin),
+// then the complemented entry index (32 bits).  Keys are read once into LDS when they fit.
 __device__ __forceinline__ void refine_candidates(const unsigned long long* cand, int ncand, int need, int32_t* sel_list,
-                                  SelShared& s) {
+                                  SelShared& s, int key_bits = 53) {
   const int tid = threadIdx.x;
   const bool cached = ncand <= kCandCache;
   if (cached) {                          // all loads first, then the LDS stores (one round trip)
@@ -1170,22 +1181,24 @@ __device__ __forceinline__ void refine_candidates(const unsigned long long* cand
   __syncthreads();
   // the key source is chosen outside the loops (a per-element select would issue the global load too)
   const unsigned long long* src = cand;
-  int shift = 53;
-  for (int pass = 0; pass < 7; ++pass) {
+  int shift = key_bits;
+  for (int pass = 0; pass < 8 && shift > 0; ++pass) {
     const int width = shift >= 8 ? 8 : shift;
     shift -= width;
     for (int i = tid; i < 256; i += kSelThreads) s.h256[i] = 0u;
     __syncthreads();
     const unsigned long long pre = s.prefix;
+    const int hi = shift + width;                 // 64 on the first pass of 64-bit keys: every key matches
+    auto match = [&](uint64_t key) { return hi >= 64 || (key >> hi) == pre; };
     if (cached) {
       for (int i = tid; i < ncand; i += kSelThreads) {
         const uint64_t key = s.u.ckey[i];
-        if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+        if (match(key)) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
       }
     } else {
       for (int i = tid; i < ncand; i += kSelThreads) {
         const uint64_t key = src[i];
-        if ((key >> (shift + width)) == pre) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
+        if (match(key)) atomicAdd(&s.h256[(key >> shift) & ((1u << width) - 1u)], 1u);
       }
     }
     __syncthreads();
@@ -1355,6 +1368,75 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
     }
     return;
   }
+  unsigned long long* crow = cand + r * nsp;
+  // ---- Sampled threshold (long rows, k a small fraction): a lower bound on the k-th key from a
+  // sample of whole 32-entry blocks, then a single pass keeps every entry at or above it.  Exact
+  // whenever at least k entries pass (the k winners are then all among them); else the full path.
+  if (nv >= kSampleMinRow && nv >= (int64_t)kSampleMinRatio * k) {
+    int64_t stride = (nv + kSampleBlocks - 1) / kSampleBlocks;
+    stride = stride < kSampleMinStride ? kSampleMinStride : (stride + kSampleBlock - 1) / kSampleBlock * kSampleBlock;
+    const int64_t nblk = (nv - kSampleBlock) / stride + 1;     // blocks b * stride + [0, 32), all < nv
+    const int S = (int)(nblk * kSampleBlock);
+    const double expect = (double)k * S / (double)nv;        // sample entries expected above the k-th
+    const int j = (int)ceil(expect + 3.0 * sqrt(expect) + 8.0);
+    if (j <= S / 2) {
+      auto sample_key = [&](int i) { return float_key(srow[(i / kSampleBlock) * stride + i % kSampleBlock]); };
+      for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
+      if (tid == 0) { sT = -1; sAbove = 0; sCand = 0; s.nsel = 0; }
+      __syncthreads();
+      for (int i = tid; i < S; i += kSelThreads) atomicAdd(&h[sample_key(i) >> kBinShift], 1u);
+      __syncthreads();
+      find_threshold(h, j, &sT, &sAbove, s.scan);          // bin of the sample's j-th largest key
+      const int T1 = sT, rem = j - sAbove;
+      for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < S; i += kSelThreads) {
+        const uint32_t key = sample_key(i);
+        if ((int)(key >> kBinShift) == T1) atomicAdd(&h[(key >> (kBinShift - 11)) & (kBins - 1)], 1u);
+      }
+      __syncthreads();
+      find_threshold(h, rem, &sT, &sAbove, s.scan);        // ... refined by its next 11 bits
+      const uint32_t thr = ((uint32_t)T1 << kBinShift) | ((uint32_t)sT << (kBinShift - 11));
+      // one pass: 16 consecutive entries per thread per round, wave-aggregated appends
+      const int lane = lane_id();
+      for (int64_t e0 = 0; e0 < nv; e0 += 16 * kSelThreads) {
+        const int64_t eb = e0 + 16 * tid;
+        uint32_t keys[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                     // eb < nv: eb + 16 <= nsp (a multiple of 64)
+          const float4 x = eb < nv ? *reinterpret_cast<const float4*>(srow + eb + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+          keys[4 * q] = float_key(x.x); keys[4 * q + 1] = float_key(x.y);
+          keys[4 * q + 2] = float_key(x.z); keys[4 * q + 3] = float_key(x.w);
+        }
+        uint32_t keep = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) keep |= (eb + i < nv && keys[i] >= thr ? 1u : 0u) << i;
+        if (__ballot(keep != 0u) == 0ull) continue;           // wave-uniform: nothing kept
+        const uint32_t c = (uint32_t)__popc(keep);
+        uint32_t incl = c;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t t = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += t;
+        }
+        uint32_t base = 0;
+        if (lane == kWave - 1) base = (uint32_t)atomicAdd(&sCand, (int)incl);
+        base = __shfl(base, kWave - 1, kWave) + incl - c;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((keep >> i) & 1u)
+            crow[base++] = ((unsigned long long)keys[i] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(eb + i));
+      }
+      __syncthreads();
+      const int ncand = sCand;
+      if (ncand >= k) {                                    // uniform
+        refine_candidates(crow, ncand, k, list, s, 64);
+        sort_and_write(list, k, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
+        return;
+      }
+      __syncthreads();                                     // the full path reuses h and the counters
+    }
+  }
   for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
   if (tid == 0) { s.nsel = 0; sCand = 0; sT = kBins - 1; sAbove = 0; }
   __syncthreads();
@@ -1362,7 +1444,6 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
   __syncthreads();
   find_threshold(h, k, &sT, &sAbove, s.scan);
   const int T = sT;
-  unsigned long long* crow = cand + r * nsp;
   for (int64_t e = tid; e < nv; e += kSelThreads) {
     const uint32_t key = float_key(srow[e]);
     const int bin = (int)(key >> kBinShift);

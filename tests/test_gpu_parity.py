@@ -137,7 +137,7 @@ def test_hca_compress_and_window_ring_parity():
 
 
 # ----------------------------------------------------------------------------------- indexer + top-k
-def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False):
+def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False, mutate=None):
     q = synth.normal_bf16((B, Tq, H_I, dI), 1.28, cfg, 21)
     w = synth.normal_bf16((B, Tq, H_I), 1.28, cfg, 22)
     ik_ld = n_cap + 5
@@ -147,6 +147,8 @@ def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False):
         if ties:
             codes[:, : n_cap // 2] = codes[:, :1]
             scale[:, : n_cap // 2] = scale[:, :1]
+        if mutate is not None:
+            mutate(codes, scale, w)
         kdeq = O.e4m3_decode(codes) * scale[..., None].astype(np.float64)
         ik = torch.from_numpy(codes).to(DEV)
         iks = dev_f32(scale)
@@ -201,6 +203,30 @@ def test_index_topk_prefill_fp8_head_blocks_ragged(H_I, Tq, n_cap):
     full = list(range(4 * n_cap - Tq + 1, 4 * n_cap + 1))
     spread = [int(x) for x in np.linspace(0, 4 * n_cap + 20, Tq)]
     band = _index_case(2, Tq, n_cap, H_I, 128, k, 4, True, full + spread, 36 + H_I)
+    assert band <= 4
+
+
+def test_index_topk_prefill_long_rows_sampled_threshold():
+    # rows long enough for the sampled threshold (n_vis >= 8192 and >= 8 k) next to shorter ones
+    n_cap, k, Tq = 12000, 128, 64
+    pos = [int(x) for x in np.linspace(4 * 6000, 4 * n_cap + 40, Tq)]
+    band = _index_case(1, Tq, n_cap, 64, 128, k, 4, True, pos, 37)
+    assert band <= 4
+
+
+def test_index_topk_prefill_sampled_threshold_falls_back():
+    # Only the entries a 32-entry-run sample reads score above zero, all distinct: the sample's
+    # threshold then passes fewer than k entries and the row must take the full selection.
+    n_cap, k, Tq = 32768, 256, 64
+    sampled = (np.arange(n_cap) % 512) < 32
+
+    def mutate(codes, scale, w):
+        codes[:, :n_cap][:, ~sampled] = 0
+        codes[:, :n_cap][:, sampled] = codes[:, :1]
+        scale[:, :n_cap] = (np.float32(2.0) + np.arange(n_cap, dtype=np.float32) / np.float32(n_cap)) / np.float32(448.0)
+        w &= np.uint16(0x7FFF)                  # positive head weights: every sampled score > 0
+
+    band = _index_case(1, Tq, n_cap, 64, 128, k, 4, True, [4 * n_cap] * Tq, 38, mutate=mutate)
     assert band <= 4
 
 
