@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA+HCA attention decode tokens/s/layer at 1M ctx; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0      # dense fp8 matrix-core peak (published)
 
 
 def log(*a):
@@ -222,6 +223,61 @@ def mhc_row(dev):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def prefill_row(dev):
+    """CSA chunked prefill at 1M context: 4096 new queries (positions 2^20 - 4096 .. 2^20 - 1) against
+    262144 compressed entries (m = 4), fp8 indexer 64 x 128, top-k 1024, 64 query heads, window 128.
+    Per-kernel times (HIP events on the launch stream, 3 calls after a warm-up call) and the fp8
+    indexer's matrix-core rate: 2 * 64 * 128 flop per visible query-entry pair."""
+    import torch
+    import long_context_sparse_17_amd as L
+    import synth
+    N, Tq, n_cap, k, H, H_I, dI, W, ring = 1 << 20, 4096, 1 << 18, 1024, 64, 64, 128, 128, 8192
+    codes = synth.device_fp8_codes((1, n_cap, dI), 41)
+    scale = (synth.device_normal_f32((1, n_cap), 1.0, 42).abs() + 2.0) / 448.0
+    cache = synth.device_normal_bf16((1, n_cap, 512), 1.0, 43)
+    win = synth.device_normal_bf16((1, ring, 512), 1.0, 44)
+    q = synth.device_normal_bf16((1, Tq, H, 512), 1.0, 45)
+    qi = synth.device_normal_bf16((1, Tq, H_I, dI), 1.0, 46)
+    wi = synth.device_normal_bf16((1, Tq, H_I), 1.0, 47)
+    sink = synth.device_normal_f32((H,), 1.0, 48)
+    gq = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    pos = torch.arange(N - Tq, N, dtype=torch.int64, device=dev).view(1, Tq)
+    topk = torch.empty((1, Tq, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, Tq, H, 512), dtype=torch.bfloat16, device=dev)
+    ws_i = L.workspace(L.csa_index_topk_workspace(1, Tq, n_cap, k))
+    ws_a = L.workspace(L.attend_workspace(1, Tq, H, k + W))
+
+    def call():
+        L.csa_index_topk(qi, wi, codes, scale, pos, n_cap=n_cap, m=4, k=k, topk_idx=topk, ws=ws_i)
+        L.csa_attend(q, gq, cache, topk, win, sink, pos, window=W, ring_cap=ring, out=out, ws=ws_a)
+
+    call()
+    torch.cuda.synchronize()
+    L.timing_enable(True)
+    reps = 3
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("index_qprep_kernel", "index_score_kernel", "topk_rowwise_kernel", "attend_kernel",
+                 "attend_merge_kernel"):
+        ms, n = L.timing_read(name)
+        if n:
+            kern[name] = {"avg_ms": round(ms / n, 4), "launches": n // reps}
+    L.timing_enable(False)
+    pairs = sum((N - Tq + i) // 4 for i in range(Tq))
+    flops = 2.0 * pairs * H_I * dI
+    idx_ms = kern["index_score_kernel"]["avg_ms"]
+    tflops = flops / (idx_ms * 1e-3) / 1e12
+    total = sum(v["avg_ms"] * v["launches"] for v in kern.values())
+    del codes, scale, cache, win, q, qi, wi, topk, out, ws_i, ws_a
+    torch.cuda.empty_cache()
+    return {"what": "CSA chunked prefill, 4096 queries x 262144 entries (1M tokens, m = 4), top-k 1024, 64 heads",
+            "ms_per_call": round(total, 3), "kernels": kern, "indexer_flops": flops,
+            "indexer_tflops": round(tflops, 1), "indexer_bound": "mfma (fp8)", "fp8_peak_tflops": FP8_PEAK_TFLOPS,
+            "indexer_frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+
+
 def time_stack(layers, steps, warmup, use_graph, ref_y, step=None, outputs=None):
     """Capture one step (default: every layer's step) into a HIP graph (checked bitwise against the
     eager outputs ref_y over three replays; outputs() gives the tensors to compare, default the layers'
@@ -338,6 +394,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-fp8kv", action="store_true", help="skip the fp8 K=V variant of the step")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained (projections + residual) variant")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 1M chunked-prefill measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -425,6 +482,7 @@ def main():
         next_rows["fp8_kv"] = fp8_kv_stack_row(args, dev)
     if not args.no_chain:
         next_rows["chained_stack"] = chained_stack_row(args, dev)
+    prefill = None if args.no_prefill else prefill_row(dev)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None
@@ -447,7 +505,7 @@ def main():
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "flops": step_flops},
         "kernels": kernels, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
-        "mfma_gemm_bf16_tflops": round(mfma_tflops, 1), "next": next_rows,
+        "mfma_gemm_bf16_tflops": round(mfma_tflops, 1), "next": next_rows, "prefill_1m": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
