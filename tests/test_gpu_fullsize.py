@@ -129,7 +129,7 @@ def test_csa_chunked_prefill_1m_sampled():
     for i in (0, 1, 2047, 4095):
         t = N - Tq + i
         nv = t // 4
-        ref_sc, bound = index_oracle_row(qi_bits[0, i], wi_bits[0, i], kdeq[:nv], True)
+        ref_sc, bound = index_oracle_row(qi_bits[0, i], wi_bits[0, i], kdeq[:nv], True, split=True)
         check_topk_row(sel_all[i], ref_sc, k, bound)
         sel = sel_all[i][sel_all[i] >= 0]
         keys = np.concatenate([host_rows(cache[0], sel),
