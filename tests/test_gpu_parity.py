@@ -137,7 +137,7 @@ def test_hca_compress_and_window_ring_parity():
 
 
 # ----------------------------------------------------------------------------------- indexer + top-k
-def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False, mutate=None):
+def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False, mutate=None, return_idx=False):
     q = synth.normal_bf16((B, Tq, H_I, dI), 1.28, cfg, 21)
     w = synth.normal_bf16((B, Tq, H_I), 1.28, cfg, 22)
     ik_ld = n_cap + 5
@@ -177,7 +177,7 @@ def _index_case(B, Tq, n_cap, H_I, dI, k, m, fp8, positions, cfg, ties=False, mu
             # scores agree within the fp32 accumulation bound of each selected entry
             assert np.all(np.abs(gs[b, t, : sel.size] - ref[sel]) <= bound[sel] + 1e-30)
             assert np.all(np.isneginf(gs[b, t, sel.size:]))
-    return band
+    return (band, gi) if return_idx else band
 
 
 def test_index_topk_decode_fp8():
@@ -230,6 +230,25 @@ def test_index_topk_prefill_sampled_threshold_falls_back():
 
     band = _index_case(1, Tq, n_cap, 64, 128, k, 4, True, [4 * n_cap] * Tq, 38, mutate=mutate)
     assert band <= 4
+
+
+def test_index_topk_prefill_sampled_threshold_top_ties():
+    # Half of each long row is one repeated key with a scale 64x the others' and positive head
+    # weights, so it scores on top: the sampled threshold keeps ~6000 tied candidates (more than the
+    # LDS cache holds, so the digit passes read them from global memory) and the k winners must be
+    # the lowest indices among the ties.  (The oracle's fp64 matrix products may round equal rows
+    # differently by position, so its own order among the ties is not the reference here: the tie
+    # rule is, and the within-bound check of every row still runs.)
+    n_cap, k, Tq = 12000, 128, 64
+
+    def mutate(codes, scale, w):
+        codes[:, : n_cap // 2] = codes[:, :1]
+        scale[:, : n_cap // 2] = scale[:, :1] * np.float32(64.0)
+        w &= np.uint16(0x7FFF)
+
+    pos = [int(x) for x in np.linspace(4 * 9000, 4 * n_cap, Tq)]
+    _, gi = _index_case(1, Tq, n_cap, 64, 128, k, 4, True, pos, 39, mutate=mutate, return_idx=True)
+    np.testing.assert_array_equal(gi[0], np.broadcast_to(np.arange(k, dtype=np.int32), (Tq, k)))
 
 
 def test_index_topk_bf16_small_heads():
