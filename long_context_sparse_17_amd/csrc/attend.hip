@@ -570,98 +570,79 @@ attend_kernel(AttnK a) {
     *reinterpret_cast<float2*>(a.part_ml + (base + head) * 2) = make_float2(m_ref, l_run);
 }
 
-// Merge split-K partials with the sink; one workgroup of 128 threads per (query, head), 4 dims per
-// thread.  The reference M = max(sink, split maxima) is found first (one split per thread), then the
-// split weights 2^(m_s - M) go through LDS and every thread folds the partial O rows, 32 splits'
-// loads in flight at a time (the first 32 are issued before the weights are known).
-constexpr int kMergeThreads = 128;
-constexpr int kMergeChunk = 32;
-constexpr int kMergeBlock = 1024;          // split weights held in LDS at a time
+// Merge split-K partials with the sink: one wave per (query, head), 8 dims per lane, no LDS and no
+// barrier.  The lanes hold the splits' maxima (split lane + 64 i), the reference M = max(sink, split
+// maxima) is a wave reduction, each split's weight 2^(m_s - M) is formed in the lane that holds it
+// and broadcast with readlane, and the partial rows are read in rounds of kMergeChunk splits with
+// every load of a round issued before the first FMA.
+constexpr int kMergeWaves = 4;             // waves per workgroup
+constexpr int kMergeChunk = 16;            // partial rows in flight per lane
 
-__device__ __forceinline__ float block_max_128(float v, float* red) {
-  v = wave_max(v);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  const float r = fmaxf(red[0], red[1]);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ float block_sum_128(float v, float* red) {
-  v = wave_sum(v);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  const float r = red[0] + red[1];
-  __syncthreads();
-  return r;
-}
-
-__global__ void __launch_bounds__(kMergeThreads)
-merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit, int H,
+__global__ void __launch_bounds__(kMergeWaves * kWave)
+merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int R, int nsplit, int H,
              const float* __restrict__ sink, uint16_t* __restrict__ out) {
-  __shared__ float s_f[kMergeBlock];
-  __shared__ float2 s_ml[kMergeBlock];     // (max, sum) of the first kMergeBlock splits
-  __shared__ float s_red[2];
-  const int64_t r = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  auto o_at = [&](int sp) {                // this thread's 4 dims of split sp's partial
-    return *reinterpret_cast<const uint2*>(part_o + ((r * nsplit + sp) * H + h) * kHeadDim + 4 * tid);
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kMergeWaves + threadIdx.x / kWave;
+  if (gw >= (int64_t)R * H) return;        // wave-uniform
+  const int64_t r = gw / H;
+  const int h = (int)(gw % H);
+  const float z = sink[h] * kLog2e;
+  const int64_t row0 = r * nsplit * H + h;  // split sp's row: row0 + sp * H
+  auto o_at = [&](int sp) {                // this lane's 8 dims of split sp's partial
+    return *reinterpret_cast<const uint4*>(part_o + (row0 + (int64_t)sp * H) * kHeadDim + 8 * lane);
   };
-  auto ml_at = [&](int sp) { return *reinterpret_cast<const float2*>(part_ml + ((r * nsplit + sp) * H + h) * 2); };
+  auto ml_at = [&](int sp) { return *reinterpret_cast<const float2*>(part_ml + (row0 + (int64_t)sp * H) * 2); };
 
-  uint2 v[kMergeChunk];
+  uint4 v[kMergeChunk];
 #pragma unroll
   for (int u = 0; u < kMergeChunk; ++u) v[u] = o_at(u < nsplit ? u : nsplit - 1);   // in flight early
 
-  const float z = sink[h] * kLog2e;
   float mloc = -INFINITY;
-  for (int sp = tid; sp < nsplit; sp += kMergeThreads) {
-    const float2 ml = ml_at(sp);
-    if (sp < kMergeBlock) s_ml[sp] = ml;
-    mloc = fmaxf(mloc, ml.x);
-  }
-  const float M = fmaxf(block_max_128(mloc, s_red), z);
+  for (int sp = lane; sp < nsplit; sp += kWave) mloc = fmaxf(mloc, ml_at(sp).x);
+  const float M = fmaxf(wave_max(mloc), z);
 
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lloc = 0.f;
-  for (int b0 = 0; b0 < nsplit; b0 += kMergeBlock) {
-    const int nb = nsplit - b0 < kMergeBlock ? nsplit - b0 : kMergeBlock;
-    auto weight = [&](int i, float2 ml) {
-      const float f = M == -INFINITY ? 0.f : exp2f(ml.x - M);
-      s_f[i] = f;
-      lloc += f * ml.y;
-    };
-    if (b0 == 0) {                         // s_ml is visible after the max's barriers
-      for (int i = tid; i < nb; i += kMergeThreads) weight(i, s_ml[i]);
-    } else {
-      for (int i = tid; i < nb; i += kMergeThreads) weight(i, ml_at(b0 + i));
+  for (int c0 = 0; c0 < nsplit; c0 += kWave) {
+    // weights of splits c0 .. c0 + 63, one per lane
+    const int sp_l = c0 + lane;
+    float f_l = 0.f;
+    if (sp_l < nsplit) {
+      const float2 ml = ml_at(sp_l);
+      f_l = M == -INFINITY ? 0.f : exp2f(ml.x - M);
+      lloc += f_l * ml.y;
     }
-    __syncthreads();
+    const int nb = nsplit - c0 < kWave ? nsplit - c0 : kWave;
     for (int c = 0; c < nb; c += kMergeChunk) {
-      if (b0 + c > 0) {
+      if (c0 + c > 0) {
 #pragma unroll
         for (int u = 0; u < kMergeChunk; ++u) {
-          const int sp = b0 + c + u;
+          const int sp = c0 + c + u;
           v[u] = o_at(sp < nsplit ? sp : nsplit - 1);
         }
       }
 #pragma unroll
       for (int u = 0; u < kMergeChunk; ++u) {
-        const float f = c + u < nb ? s_f[c + u] : 0.f;
-        acc.x += f * bf2f_lo(v[u].x); acc.y += f * bf2f_hi(v[u].x);
-        acc.z += f * bf2f_lo(v[u].y); acc.w += f * bf2f_hi(v[u].y);
+        // split c0 + c + u's weight, from the lane that formed it (the index is wave-uniform)
+        const float fw = c + u < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), (c + u) & 63)) : 0.f;
+        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += fw * bf2f_lo(wd[q]);
+          acc[2 * q + 1] += fw * bf2f_hi(wd[q]);
+        }
       }
     }
-    __syncthreads();
   }
-  float L = block_sum_128(lloc, s_red);
+  float L = wave_sum(lloc);
   if (z != -INFINITY) L += exp2f(z - M);
   const float inv = L > 0.f ? 1.0f / L : 0.f;      // partials are already rotated
-  uint2 o;
-  o.x = pack_bf2(acc.x * inv, acc.y * inv);
-  o.y = pack_bf2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(out + (r * H + h) * kHeadDim + 4 * tid) = o;
+  uint4 o;
+  o.x = pack_bf2(acc[0] * inv, acc[1] * inv);
+  o.y = pack_bf2(acc[2] * inv, acc[3] * inv);
+  o.z = pack_bf2(acc[4] * inv, acc[5] * inv);
+  o.w = pack_bf2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(out + (r * H + h) * kHeadDim + 8 * lane) = o;
 }
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -715,8 +696,9 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
     else LCS_LAUNCH("attend_kernel", (attend_kernel<false, false>), grid, dim3(256), 0, st, a);
   }
   if (a.nsplit > 1) {
-    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)R, (unsigned)x.H), dim3(kMergeThreads), 0, st,
-               a.part_o, a.part_ml, a.nsplit, x.H, x.sink, x.out);
+    const int64_t waves = (int64_t)R * x.H;
+    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)),
+               dim3(kMergeWaves * kWave), 0, st, a.part_o, a.part_ml, R, a.nsplit, x.H, x.sink, x.out);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
