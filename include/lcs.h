@@ -203,7 +203,9 @@ int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, in
  *   q_pos  [B, Tq] int64 (device)
  *   topk_idx [B, Tq, k] int32; topk_score [B, Tq, k] fp32 (may be NULL; -inf where padded)
  *   ws     device workspace of at least csa_index_topk_workspace(B, Tq, n_cap, k) bytes
- *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1.
+ *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1, B * Tq <= 65535 * 16,
+ *   and launch grids within the device limits (many-row calls: B * ceil(Tq / 16) <= 65535 with bf16
+ *   keys, about B <= 65000 with fp8 keys); otherwise LCS_ERR_UNSUPPORTED before anything runs.
  */
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
 int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx,

@@ -282,6 +282,7 @@ int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_
   if (H_I > LCS_MAX_HEADS || k > LCS_MAX_TOPK) return LCS_ERR_UNSUPPORTED;
   if (n_cap >= ((int64_t)1 << 31)) return LCS_ERR_UNSUPPORTED;
   if ((int64_t)B * Tq > 65535 * 16) return LCS_ERR_UNSUPPORTED;
+  if (!lcs::index_topk_launchable(B, Tq, n_cap, ik_dtype == LCS_IK_FP8)) return LCS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < lcs::index_topk_workspace(B, Tq, n_cap, k)) return LCS_ERR_WORKSPACE;
   if (!aligned16(ws)) return LCS_ERR_ARG;
   lcs::IndexArgs a;

@@ -1483,23 +1483,33 @@ void launch_score_rows_bf16(const IndexArgs& a, const Ws& w, hipStream_t st) {
              static_cast<const uint16_t*>(a.ik), a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, w.scores, w.nsp);
 }
 
-// Query ranges per entry chunk: enough workgroups for two per CU when the chunks alone are fewer.
+// fp8 prefill grid: one workgroup per chunk of kPfChunk entries (x) and per query range of each
+// batch row (y); the query ranges (multiples of kPfQC) are split so that there are enough
+// workgroups for two per CU when the chunks alone are fewer.
+struct PfGrid {
+  int64_t nchunk;
+  int qsplit, qper;
+};
+PfGrid prefill_grid(int B, int Tq, int64_t n_cap) {
+  PfGrid p;
+  p.nchunk = (n_cap + kPfChunk - 1) / kPfChunk;
+  const int nstage = (Tq + kPfQC - 1) / kPfQC;
+  const int64_t want = (512 + p.nchunk * B - 1) / (p.nchunk * B);
+  const int qs0 = (int)(want < nstage ? want : nstage);
+  p.qper = (nstage + qs0 - 1) / qs0 * kPfQC;
+  p.qsplit = (Tq + p.qper - 1) / p.qper;
+  return p;
+}
+
 template <int HBI>
 void launch_score_rows_fp8(const IndexArgs& a, const Ws& w, hipStream_t st) {
-  constexpr int HP = 16 * HBI;
   LCS_LAUNCH("index_qprep_kernel", index_qprep_kernel<HBI>, dim3((unsigned)(a.B * a.Tq)), dim3(256), 0, st,
              a.q_idx, a.w_idx, a.H_I, a.q_pos, a.n_cap, a.m, a.Tq, w.qc, w.qw, w.qnv, w.linc, w.lins);
-  const int64_t nchunk = (a.n_cap + kPfChunk - 1) / kPfChunk;
-  const int nstage = (a.Tq + kPfQC - 1) / kPfQC;
-  const int64_t want = (512 + nchunk * a.B - 1) / (nchunk * a.B);
-  const int qs0 = (int)(want < nstage ? want : nstage);
-  const int qper = (nstage + qs0 - 1) / qs0 * kPfQC;
-  const int qsplit = (a.Tq + qper - 1) / qper;
-  dim3 grid((unsigned)nchunk, (unsigned)(a.B * qsplit));
+  const PfGrid p = prefill_grid(a.B, a.Tq, a.n_cap);
+  dim3 grid((unsigned)p.nchunk, (unsigned)(a.B * p.qsplit));
   LCS_LAUNCH("index_score_kernel", index_score_prefill_kernel<HBI>, grid, dim3(kPfWaves * kWave), 0, st, w.qc, w.qw,
-             w.qnv, w.linc, w.lins, static_cast<const uint8_t*>(a.ik), a.ik_scale, a.ik_ld, a.n_cap, a.Tq, qsplit, qper, w.scores,
-             w.nsp);
-  (void)HP;
+             w.qnv, w.linc, w.lins, static_cast<const uint8_t*>(a.ik), a.ik_scale, a.ik_ld, a.n_cap, a.Tq, p.qsplit,
+             p.qper, w.scores, w.nsp);
 }
 
 void score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
@@ -1538,6 +1548,18 @@ void score_rows(const IndexArgs& a, const Ws& w, hipStream_t st) {
 }
 
 }  // namespace
+
+// Every grid the call would launch fits the HIP limits (x < 2^31, y <= 65535).
+bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
+  const int64_t R = (int64_t)B * Tq;
+  if (R < 64 && n_chunks(n_cap) <= kMaxDecodeChunks) return true;   // decode grids (chunks, R), R < 64
+  if (R >= ((int64_t)1 << 31)) return false;                         // one workgroup per row
+  if (ik_fp8) {
+    const PfGrid p = prefill_grid(B, Tq, n_cap);
+    return p.nchunk < ((int64_t)1 << 31) && (int64_t)B * p.qsplit <= 65535;
+  }
+  return (n_cap + kScoreChunk - 1) / kScoreChunk < ((int64_t)1 << 31) && (int64_t)B * ((Tq + 15) / 16) <= 65535;
+}
 
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   (void)k;

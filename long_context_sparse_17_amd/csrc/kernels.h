@@ -54,6 +54,7 @@ struct IndexArgs {
   void* ws; size_t ws_bytes;
 };
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
+bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8);
 int launch_index_topk(const IndexArgs& a, hipStream_t stream);
 
 struct AttendArgs {

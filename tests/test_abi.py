@@ -82,6 +82,10 @@ def test_index_rejects_bad_arguments(lib):
     assert lib.csa_index_topk(*[a if i != 4 else 999 for i, a in enumerate(base)]) == L.LCS_ERR_ARG
     assert lib.csa_index_topk(*[a if i != 5 else 7 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
     assert lib.csa_index_topk(*[a if i != 3 else None for i, a in enumerate(base)]) == L.LCS_ERR_ARG
+    # many rows of one query each: the row-per-workgroup grids would pass 65535 rows in y
+    assert lib.csa_index_topk(*[a if i != 8 else 70000 for i, a in enumerate(base)]) == L.LCS_ERR_UNSUPPORTED
+    bf16 = [a if i not in (3, 5) else (None if i == 3 else L.LCS_IK_BF16) for i, a in enumerate(base)]
+    assert lib.csa_index_topk(*[a if i != 8 else 70000 for i, a in enumerate(bf16)]) == L.LCS_ERR_UNSUPPORTED
 
 
 def test_compress_rejects_tokens_outside_the_given_columns(lib):
