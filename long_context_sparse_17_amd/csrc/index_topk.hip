@@ -542,10 +542,19 @@ index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restri
 #undef LCS_PF_COMMIT
 }
 
-// Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  The 4 waves quantise
-// one 16-head block each into LDS (codes + folded weights), then stream the chunk in 64-entry groups
-// interleaved across waves, with the next group's loads in flight while the current group's 4*HBI
-// MFMAs run back to back; the epilogue applies relu and the head weights and histograms the scores.
+// 64-entry groups per wave in one decode scoring workgroup (4 waves): chunks of at most 4096 entries.
+constexpr int kDecodeWaveGroups = 16;
+constexpr int64_t kDecodeMaxChunk = 4 * kDecodeWaveGroups * 64;
+
+// Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  The workgroup first
+// issues the loads of the chunk's key scales (staged in LDS) and each wave those of its first two
+// 64-entry groups (they depend only on the chunk), so that the query preparation runs under their
+// latency: the 4 waves quantise one 16-head block each into LDS (codes + folded weights).  The chunk
+// then streams in groups interleaved across waves, two groups in flight while the current group's
+// 4*HBI MFMAs run back to back.  The epilogue applies relu and the head weights, reduce-scatters the
+// 4 entry blocks over the 4 lane groups so that lane l ends with entry 64 gi + l, scales it, counts it
+// in the LDS histogram and keeps it in LDS; the chunk's scores leave in one burst of 16-byte stores at
+// the end.  Only key fragments are then in flight in the loop, so every wait is for a key group.
 template <bool FP8, int KS, int HBI>
 __global__ void __launch_bounds__(256, (FP8 || KS * HBI <= 8) ? 2 : 1)
 index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
@@ -556,18 +565,75 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   __shared__ uint32_t lhist[kBins];
   __shared__ Frag s_afr[HBI][KS][kWave];
   __shared__ float s_w[HBI * 16];
+  __shared__ float s_sc[FP8 ? kDecodeMaxChunk : 1];     // the chunk's key scales
+  __shared__ __align__(16) float s_sco[kDecodeMaxChunk];   // the chunk's scores
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform (readfirstlane): the group loop below is then scalar control flow, and the
+  // compiler tracks the loads in flight exactly across its back edge
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t r = blockIdx.y;
   const int64_t b = r / Tq;
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;       // < n_cap: the grid covers the capacity
+  const uint8_t* ik8 = static_cast<const uint8_t*>(ik) + b * ik_ld * dI;
+  const uint16_t* ik16 = static_cast<const uint16_t*>(ik) + b * ik_ld * dI;
+  const float* ksc = ik_scale ? ik_scale + b * ik_ld : nullptr;
+
+  // Loads are unconditional (entry index clamped below `lim`) so that the compiler keeps them in
+  // flight; the scores of out-of-range entries are never counted or read.
+  auto load_group = [&](int64_t gi, int64_t lim, Frag (&fr)[4][KS]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int64_t e = c0 + 64 * gi + 16 * u + c16;
+      e = e < lim ? e : lim - 1;
+      if (FP8) {
+        // bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16): each load instruction covers 64
+        // contiguous bytes of 16 rows (the query codes use the same dim order)
+        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 16 * g);
+        const uint4 x0 = p[0], x1 = p[4];
+        intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        fr[u][0] = *reinterpret_cast<Frag*>(&v);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 v = *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g);
+          fr[u][ks] = *reinterpret_cast<Frag*>(&v);
+        }
+      }
+    }
+  };
+
+  // The chunk's scales (one 256-entry slice per pass, thread t takes entry t of each) and the first
+  // two groups of this wave (wave and wave + 4), clamped to the cache capacity: the row's visible
+  // count is not known yet.  Entries past it are loaded in bounds and never counted; a wave with
+  // fewer groups never computes the second buffer.
+  constexpr int kScPasses = kDecodeMaxChunk / 256;
+  const int64_t cl = c0 + chunk < n_cap ? c0 + chunk : n_cap;
+  float scv[kScPasses];
+  if (FP8) {
+#pragma unroll
+    for (int j = 0; j < kScPasses; ++j) {
+      if (256 * j < chunk) {                              // uniform
+        const int64_t e = c0 + 256 * j + threadIdx.x;
+        scv[j] = ksc[e < cl ? e : cl - 1];
+      }
+    }
+  }
+  Frag cur[4][KS], nxt[4][KS], nx2[4][KS];
+  load_group(wave, cl, cur);
+  load_group(wave + 4, cl, nxt);
+
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
-  const int64_t c0 = (int64_t)blockIdx.x * chunk;
   if (c0 >= nv) return;                                  // uniform
   const int64_t c1 = c0 + chunk < nv ? c0 + chunk : nv;
 
   for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0u;
+  if (FP8) {
+#pragma unroll
+    for (int j = 0; j < kScPasses; ++j)
+      if (256 * j < chunk) s_sc[256 * j + threadIdx.x] = scv[j];
+  }
   if (wave < HBI) {
     const int head = wave * 16 + c16;
     const bool hv = head < H_I;
@@ -601,63 +667,20 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     for (int i = 0; i < 4; ++i) wq[hb][i] = s_w[hb * 16 + 4 * g + i];
   }
 
-  const uint8_t* ik8 = static_cast<const uint8_t*>(ik) + b * ik_ld * dI;
-  const uint16_t* ik16 = static_cast<const uint16_t*>(ik) + b * ik_ld * dI;
-  const float* ksc = ik_scale ? ik_scale + b * ik_ld : nullptr;
   float* srow = scores + r * nsp;
   const int64_t ngroups = (c1 - c0 + 63) / 64;
-
-  Frag cur[4][KS], nxt[4][KS], nx2[4][KS];
-  float cs, ns, n2;
-  // Loads are unconditional (entry index clamped into the chunk) so that the compiler keeps them in
-  // flight; out-of-range entries are zeroed by a select and never stored.  One scale load per group:
-  // lane l takes entry 64 gi + l (row-group u of the fragments needs lanes 16u .. 16u+15).
-  auto load_group = [&](int64_t gi, Frag (&fr)[4][KS], float& sc) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int64_t e = c0 + 64 * gi + 16 * u + c16;
-      e = e < c1 ? e : c1 - 1;
-      if (FP8) {
-        // bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16): each load instruction covers 64
-        // contiguous bytes of 16 rows (the query codes use the same dim order)
-        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 16 * g);
-        const uint4 x0 = p[0], x1 = p[4];
-        intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        fr[u][0] = *reinterpret_cast<Frag*>(&v);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint4 v = *reinterpret_cast<const uint4*>(ik16 + e * dI + 32 * ks + 8 * g);
-          fr[u][ks] = *reinterpret_cast<Frag*>(&v);
-        }
-      }
-    }
-    if (FP8) {
-      int64_t e = c0 + 64 * gi + lane;
-      sc = ksc[e < c1 ? e : c1 - 1];        // clamped entries are never stored
-    } else {
-      sc = 1.f;
-    }
-  };
 
   // Groups of this wave: wave + 4t, t = 0 .. nt-1.  Three register buffers rotate by unrolling (a
   // copy between buffers would wait for the loads in flight); two groups stay in flight ahead of the
   // one being computed.  Loads past the end re-read the last group (never computed).
   const int64_t nt = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
   auto gidx = [&](int64_t t) -> int64_t { return wave + 4 * (t < nt ? t : nt - 1); };
-  auto compute_group = [&](const Frag (&fr)[4][KS], float sc_lane, int64_t gi) {
-    // every row group's scales in every lane (same column): rows 0..3 = entries 16u + c16
-    float sc[4];
-    {
-      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sc_lane), __float_as_uint(sc_lane), false, false);
-      const auto lo = __builtin_amdgcn_permlane32_swap(p16[0], p16[0], false, false);   // rows 0, 2
-      const auto hi = __builtin_amdgcn_permlane32_swap(p16[1], p16[1], false, false);   // rows 1, 3
-      sc[0] = __uint_as_float(lo[0]); sc[1] = __uint_as_float(hi[0]);
-      sc[2] = __uint_as_float(lo[1]); sc[3] = __uint_as_float(hi[1]);
-    }
-    floatx4 acc[4][HBI];
+  auto compute_group = [&](const Frag (&fr)[4][KS], int64_t gi) {
+    // partial head sums of the lane's 4 heads per head block, entry column c16 of each row group u
+    float p[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
+      floatx4 acc[HBI];
 #pragma unroll
       for (int hb = 0; hb < HBI; ++hb) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
@@ -668,39 +691,49 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
           else
             a = mfma_bf16(*reinterpret_cast<const uint4*>(&afr[hb][ks]), *reinterpret_cast<const uint4*>(&fr[u][ks]), a);
         }
-        acc[u][hb] = a;
+        acc[hb] = a;
       }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float part = 0.f;
+      float s = 0.f;
 #pragma unroll
       for (int hb = 0; hb < HBI; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += wq[hb][i] * fmaxf(acc[u][hb][i], 0.f);
-      part = sum_rows4(part);
-      const int64_t e = c0 + 64 * gi + 16 * u + c16;
-      if (g == 0 && e < c1) {
-        const float v = part * sc[u] + 0.0f;
-        srow[e] = v;
-        atomicAdd(&lhist[float_key(v) >> kBinShift], 1u);
-      }
+        for (int i = 0; i < 4; ++i) s += wq[hb][i] * fmaxf(acc[hb][i], 0.f);
+      p[u] = s;
     }
+    // reduce-scatter over the lane groups: halves first (group g <-> g ^ 2), then rows (g <-> g ^ 1);
+    // lane group g keeps row group u = g, i.e. lane l holds entry 64 gi + l
+    const auto h0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+    const auto h1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+    const float r0 = __uint_as_float(h0[0]) + __uint_as_float(h0[1]);
+    const float r1 = __uint_as_float(h1[0]) + __uint_as_float(h1[1]);
+    const auto q01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(r0), __float_as_uint(r1), false, false);
+    const float tot = __uint_as_float(q01[0]) + __uint_as_float(q01[1]);
+    const int j = (int)(64 * gi) + lane;                  // < chunk
+    const float v = tot * (FP8 ? s_sc[j] : 1.f) + 0.0f;
+    s_sco[j] = v;
+    if (c0 + j < c1) atomicAdd(&lhist[float_key(v) >> kBinShift], 1u);
   };
-  if (nt > 0) {
-    load_group(gidx(0), cur, cs);
-    load_group(gidx(1), nxt, ns);
-    for (int64_t t = 0; t < nt; t += 3) {
-      load_group(gidx(t + 2), nx2, n2);
-      compute_group(cur, cs, gidx(t));
-      if (t + 1 >= nt) break;
-      load_group(gidx(t + 3), cur, cs);
-      compute_group(nxt, ns, gidx(t + 1));
-      if (t + 2 >= nt) break;
-      load_group(gidx(t + 4), nxt, ns);
-      compute_group(nx2, n2, gidx(t + 2));
-    }
+  // Fully unrolled (nt <= kDecodeWaveGroups): straight-line code with forward exits only, so that
+  // every wait for a group's loads leaves the two younger groups in flight (a loop back edge makes
+  // the compiler's count of loads in flight conservative).
+#pragma unroll
+  for (int t = 0; t < kDecodeWaveGroups; t += 3) {
+    if (t >= nt) break;
+    load_group(gidx(t + 2), c1, nx2);
+    compute_group(cur, gidx(t));
+    if (t + 1 >= nt) break;
+    load_group(gidx(t + 3), c1, cur);
+    compute_group(nxt, gidx(t + 1));
+    if (t + 2 >= nt) break;
+    load_group(gidx(t + 4), c1, nxt);
+    compute_group(nx2, gidx(t + 2));
   }
   __syncthreads();
+  // Scores [c0, c1) rounded up to a multiple of 4 entries: the rounding only reaches past the row's
+  // visible end, within the row's stride (a multiple of 64), where readers mask by index.
+  const int n4 = (int)((c1 - c0 + 3) >> 2);
+  float4* dst = reinterpret_cast<float4*>(srow + c0);
+  for (int i = threadIdx.x; i < n4; i += 256) dst[i] = reinterpret_cast<const float4*>(s_sco)[i];
   uint32_t* gh = hist + r * kHistRow;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     const uint32_t v = lhist[i];
@@ -1462,7 +1495,7 @@ int64_t decode_chunk(int64_t n_cap, int R) {
   int64_t c = (n_cap * R + 511) / 512;
   c = (c + 255) & ~(int64_t)255;
   if (c < 256) c = 256;
-  if (c > 65536) c = 65536;
+  if (c > kDecodeMaxChunk) c = kDecodeMaxChunk;
   return c;
 }
 
