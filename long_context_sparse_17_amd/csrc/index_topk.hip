@@ -101,11 +101,15 @@ __global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
 // division: the decision rule the selection depends on), packed in that order as an MFMA A fragment.
 // Returns the row scale (1 for an all-zero row).  hv == false: zero codes (padding heads).  The
 // matrix cores only need A and B to share one assignment of dims to (lane group, register, byte).
-__device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg0, const uint16_t* qseg1, bool hv, intx8& codes) {
+// The two 16-dim segments of a row (unconditional loads; a padding head's values are dropped later).
+__device__ __forceinline__ void load_row_segments(const uint16_t* qseg0, const uint16_t* qseg1, uint4 (&raw)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>((u < 2 ? qseg0 : qseg1) + 8 * (u & 1));
+}
+__device__ __forceinline__ float quant_loaded_e4m3(const uint4 (&loaded)[4], bool hv, intx8& codes) {
   uint4 raw[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    raw[u] = hv ? *reinterpret_cast<const uint4*>((u < 2 ? qseg0 : qseg1) + 8 * (u & 1)) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < 4; ++u) raw[u] = hv ? loaded[u] : make_uint4(0, 0, 0, 0);
   float amax = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -128,6 +132,11 @@ __device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg0, const uin
     }
   }
   return sc;
+}
+__device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg0, const uint16_t* qseg1, bool hv, intx8& codes) {
+  uint4 raw[4];
+  load_row_segments(qseg0, qseg1, raw);                 // callers pass a valid row for padding heads
+  return quant_loaded_e4m3(raw, hv, codes);
 }
 
 // bf16 keys, many query rows (prefill with bf16 indexer keys): 16 queries per workgroup, 4 per wave;
@@ -608,6 +617,22 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   // two groups of this wave (wave and wave + 4), clamped to the cache capacity: the row's visible
   // count is not known yet.  Entries past it are loaded in bounds and never counted; a wave with
   // fewer groups never computes the second buffer.
+  // The query rows of the wave's head block come first (their wait then covers nothing else).
+  const int head = wave * 16 + c16;
+  const bool hv = wave < HBI && head < H_I;
+  const int hl = hv ? head : H_I - 1;
+  const uint16_t* qrow = q_idx + (r * H_I + hl) * dI;
+  uint4 qraw[FP8 ? 4 : KS];
+  uint32_t wraw = 0;
+  if (wave < HBI) {
+    if (FP8) {
+      load_row_segments(qrow + 16 * g, qrow + 64 + 16 * g, *reinterpret_cast<uint4(*)[4]>(&qraw));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+    }
+    wraw = w_idx[r * H_I + hl];
+  }
   constexpr int kScPasses = kDecodeMaxChunk / 256;
   const int64_t cl = c0 + chunk < n_cap ? c0 + chunk : n_cap;
   float scv[kScPasses];
@@ -635,23 +660,20 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       if (256 * j < chunk) s_sc[256 * j + threadIdx.x] = scv[j];
   }
   if (wave < HBI) {
-    const int head = wave * 16 + c16;
-    const bool hv = head < H_I;
-    const int hl = hv ? head : H_I - 1;
-    const uint16_t* qrow = q_idx + (r * H_I + hl) * dI;
-    float wh = bf2f(w_idx[r * H_I + hl]);
-    if (!hv) wh = 0.f;
+    // (an empty statement that takes the weight's bits: keeps their conversion, and so the wait for
+    // them, here instead of right behind the load, ahead of the key loads)
+    asm volatile("" : "+v"(wraw));
+    float wh = hv ? bf2f((uint16_t)wraw) : 0.f;
     if (FP8) {
       intx8 codes;
-      const float sc = quant_row_e4m3(qrow + 16 * g, qrow + 64 + 16 * g, hv, codes);
+      const float sc = quant_loaded_e4m3(*reinterpret_cast<const uint4(*)[4]>(&qraw), hv, codes);
       s_afr[wave][0][lane] = *reinterpret_cast<Frag*>(&codes);
       wh *= sc;
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 a = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
-        if (!hv) a = make_uint4(0, 0, 0, 0);
-        s_afr[wave][ks][lane] = *reinterpret_cast<Frag*>(&a);
+        const uint4 a = hv ? qraw[ks] : make_uint4(0, 0, 0, 0);
+        s_afr[wave][ks][lane] = *reinterpret_cast<const Frag*>(&a);
       }
     }
     if (g == 0) s_w[wave * 16 + c16] = wh;
