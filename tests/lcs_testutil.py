@@ -84,9 +84,11 @@ def index_oracle_row(q_idx_bits, w_idx_bits, k_deq, fp8, split=False):
     q_idx_bits [H_I, dI] bf16 patterns; w_idx_bits [H_I]; k_deq [n, dI] float64 dequantised keys.
     In fp8 mode the query rows are quantised with the kernel's fp32 decision rule.
 
-    Bound of sum_h w_h relu(a_h) evaluated head by head in fp32: (dI + H + 8) 2^-23 mag,
-    mag = sum_h |w_h| sum_d |q_hd k_d|.  split=True: the evaluation the fp8 prefill scorer uses,
-    sum_h (w_h/2)|a_h| + u.k with u = sum_h (w_h/2) q_h carried as 4 E4M3 parts.  Its |a| half has the
+    Bound of sum_h w_h relu(a_h) evaluated head by head in fp32: (2 dI + H + 8) 2^-23 mag,
+    mag = sum_h |w_h| sum_d |q_hd k_d|.  The dI term is twice one fp32 unit in the last place per
+    product: the matrix instructions' internal accumulation (order, width, rounding) is not that of
+    round-to-nearest fp32 additions, and with few heads its error was seen to exceed dI 2^-23 mag.
+    split=True: the evaluation the fp8 prefill scorer uses, sum_h (w_h/2)|a_h| + u.k with u = sum_h (w_h/2) q_h carried as 4 E4M3 parts.  Its |a| half has the
     bound above; its linear half adds an fp32 accumulation over 4 parts of dI products,
     (dI + 12) 2^-23 sum_d |u_d k_d| <= (dI + 12) 2^-23 mag / 2, plus one final addition, and the
     parts' remainder, 2^-19 max_d |u_d| sum_d |k_d|.
@@ -98,7 +100,7 @@ def index_oracle_row(q_idx_bits, w_idx_bits, k_deq, fp8, split=False):
     sc = O.index_scores(q, w, k_deq)
     mag = (np.abs(k_deq) @ np.abs(q).T) @ np.abs(w)
     H, dI = q.shape
-    bound = mag * (dI + H + 8) * 2.0 ** -23
+    bound = mag * (2 * dI + H + 8) * 2.0 ** -23
     if split:
         u = 0.5 * (w[:, None] * q).sum(0)
         bound = bound + mag * ((dI + 12) / 2 + 2) * 2.0 ** -23 + np.abs(u).max() * np.abs(k_deq).sum(1) * 2.0 ** -19

@@ -188,6 +188,16 @@ def test_index_topk_decode_fp8():
     assert band <= 2
 
 
+@pytest.mark.parametrize("fp8,H_I,dI", [(True, 8, 128), (True, 40, 128), (False, 40, 128), (False, 40, 64)])
+def test_index_topk_decode_head_blocks_ragged(fp8, H_I, dI):
+    # decode scoring with padded head blocks (8 -> 16, 40 -> 48 heads) and chunks that end inside a
+    # 64-entry group: rows with n_vis = 0, < k, == k, ragged and at capacity
+    n_cap, k = 3001, 96
+    pos = [0, 5, 4 * 96, 4 * 1023 + 3, 4 * 3001, 4 * 2999 + 1]
+    band = _index_case(6, 1, n_cap, H_I, dI, k, 4, fp8, pos, 41 + H_I + dI)
+    assert band <= 2
+
+
 def test_index_topk_prefill_fp8_rowwise():
     Tq, n_cap, k = 80, 1500, 100
     pos = list(range(4 * 1500 - 79, 4 * 1500 + 1)) + list(range(0, 800, 10))
