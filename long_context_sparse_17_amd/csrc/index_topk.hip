@@ -555,10 +555,11 @@ index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restri
 constexpr int kDecodeWaveGroups = 16;
 constexpr int64_t kDecodeMaxChunk = 4 * kDecodeWaveGroups * 64;
 
-// Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  The workgroup first
-// issues the loads of the chunk's key scales (staged in LDS) and each wave those of its first two
-// 64-entry groups (they depend only on the chunk), so that the query preparation runs under their
-// latency: the 4 waves quantise one 16-head block each into LDS (codes + folded weights).  The chunk
+// Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  Loads return in order,
+// so they are issued in the order they are needed: the query rows, then the chunk's key scales
+// (staged in LDS), then each wave's first two 64-entry groups (they depend only on the chunk), so
+// that the query preparation runs under the keys' latency: the 4 waves quantise one 16-head block
+// each into LDS (codes + folded weights).  The chunk
 // then streams in groups interleaved across waves, two groups in flight while the current group's
 // 4*HBI MFMAs run back to back.  The epilogue applies relu and the head weights, reduce-scatters the
 // 4 entry blocks over the 4 lane groups so that lane l ends with entry 64 gi + l, scales it, counts it
@@ -578,8 +579,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   __shared__ __align__(16) float s_sco[kDecodeMaxChunk];   // the chunk's scores
 
   const int lane = lane_id();
-  // wave-uniform (readfirstlane): the group loop below is then scalar control flow, and the
-  // compiler tracks the loads in flight exactly across its back edge
+  // wave-uniform (readfirstlane): the group schedule below is then scalar control flow
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t r = blockIdx.y;
@@ -613,10 +613,6 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     }
   };
 
-  // The chunk's scales (one 256-entry slice per pass, thread t takes entry t of each) and the first
-  // two groups of this wave (wave and wave + 4), clamped to the cache capacity: the row's visible
-  // count is not known yet.  Entries past it are loaded in bounds and never counted; a wave with
-  // fewer groups never computes the second buffer.
   // The query rows of the wave's head block come first (their wait then covers nothing else).
   const int head = wave * 16 + c16;
   const bool hv = wave < HBI && head < H_I;
@@ -633,6 +629,10 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     }
     wraw = w_idx[r * H_I + hl];
   }
+  // Then the chunk's scales (one 256-entry slice per pass, thread t takes entry t of each) and the
+  // first two groups of this wave (wave and wave + 4), clamped to the cache capacity: the row's
+  // visible count is not known yet.  Entries past it are loaded in bounds and never counted; a wave
+  // with fewer groups never computes the second buffer.
   constexpr int kScPasses = kDecodeMaxChunk / 256;
   const int64_t cl = c0 + chunk < n_cap ? c0 + chunk : n_cap;
   float scv[kScPasses];
@@ -1512,7 +1512,8 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
   sort_and_write(list, n, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
 }
 
-// Entries per decode scoring workgroup: about two workgroups per CU over the whole call.
+// Entries per decode scoring workgroup: about two workgroups per CU over the whole call, at most
+// kDecodeMaxChunk (larger calls take more workgroups).
 int64_t decode_chunk(int64_t n_cap, int R) {
   int64_t c = (n_cap * R + 511) / 512;
   c = (c + 255) & ~(int64_t)255;
