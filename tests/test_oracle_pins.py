@@ -53,6 +53,17 @@ def test_rmsnorm_unit_rms_and_scale_invariance():
     assert np.all(O.rmsnorm(np.zeros(512), g, 1e-6) == 0)
 
 
+def test_rmsnorm_eps_under_the_root_closed_form():
+    """A constant vector c: RMSNorm gives gamma * c / sqrt(c^2 + eps).  At c = 1e-3, eps = 1e-6 this is
+    gamma / sqrt(2): eps added outside the root (0.999), left out (1) or a sum instead of a mean
+    (1/sqrt(512)) all fail."""
+    g = 0.5 + RNG.random(512)
+    for c, eps in ((1e-3, 1e-6), (2.0, 0.5), (-3.0, 1e-6), (0.25, 0.0)):
+        got = O.rmsnorm(np.full(512, c), g, eps)
+        np.testing.assert_allclose(got, g * c / math.sqrt(c * c + eps), rtol=1e-14)
+    np.testing.assert_allclose(O.rmsnorm(np.full(512, 1e-3), np.ones(512), 1e-6), 2 ** -0.5, rtol=1e-12)
+
+
 # ------------------------------------------------------------------------------- RoPE
 def test_rope_matches_complex_rotation():
     x = randn(512)
@@ -176,6 +187,107 @@ def test_fp8_row_quant_scales_absmax_to_448():
     assert (np.abs(c32.astype(int) - codes.astype(int)) <= 1).all()     # fp32 path differs at most one code
     zc, zs, zd = O.fp8_quantize_rows(np.zeros((1, 8)))
     assert zs[0] == 1.0 and (zd == 0).all()
+
+
+def _torch_fp32_route(v):
+    """An independent route to the fp32-decision row quantiser: torch float32 absmax, float32
+    division of it by 448 (1 for an all-zero row), float32 division of every element by that scale,
+    then torch's own E4M3FN cast (round to nearest, ties to even).  torch keeps the sign of a value
+    that rounds to zero (0x80); the quantiser writes +0 there, so 0x80 is compared as 0x00."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
+    amax = t.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / torch.tensor(448.0, dtype=torch.float32), torch.ones_like(amax))
+    codes = (t / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    codes[codes == 0x80] = 0
+    return codes, s.numpy()
+
+
+def _bf16_sweep_rows(amax):
+    """Every finite bf16 value v with |v| <= amax, 127 per row, each row led by the anchor amax (so
+    that every row's scale is amax / 448)."""
+    v = synth.bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    v = v[np.isfinite(v) & (np.abs(v) <= amax)]
+    n = (v.size + 126) // 127
+    rows = np.zeros((n, 128), dtype=np.float32)
+    rows[:, 0] = amax
+    body = rows[:, 1:].reshape(-1)
+    body[: v.size] = v
+    rows[:, 1:] = body.reshape(n, 127)
+    return rows
+
+
+@pytest.mark.parametrize("amax", [448.0, 1.0, 3.0, 0.1015625, 1232.0, 2.0 ** -10, 0.00506591796875,
+                                  37.0, 3.3895313892515355e38])
+def test_fp8_rows_fp32_decisions_bit_exact_exhaustive_bf16(amax):
+    """fp8_quantize_rows(kernel_fp32=True) against the torch route, bit for bit, on every finite bf16
+    value under each anchor (the anchors are bf16 values: scales 1, non-powers of two, tiny, huge)."""
+    rows = _bf16_sweep_rows(np.float32(amax))
+    codes, s, deq = O.fp8_quantize_rows(rows.astype(np.float64), kernel_fp32=True)
+    ref_codes, ref_s = _torch_fp32_route(rows)
+    np.testing.assert_array_equal(s, ref_s.astype(np.float64))
+    np.testing.assert_array_equal(codes, ref_codes)
+    np.testing.assert_array_equal(deq, O.e4m3_decode(ref_codes) * ref_s.astype(np.float64)[:, None])
+
+
+def test_fp8_rows_fp32_decisions_gaussian_zero_and_ties():
+    """Gaussian rows at several scales (bf16 values), all-zero rows, and exact E4M3FN ties: with the
+    scale a power of two, v / s lands exactly on the midpoint of two neighbouring codes and must go to
+    the even one."""
+    r = np.random.default_rng(77)
+    g = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(
+        r.standard_normal((400, 128)).astype(np.float32) * np.repeat([1e-3, 0.02, 1.28, 40.0], 100)[:, None]))
+    g[5] = 0.0
+    c, s, _ = O.fp8_quantize_rows(g.astype(np.float64), kernel_fp32=True)
+    rc, rs = _torch_fp32_route(g)
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(s, rs.astype(np.float64))
+    assert s[5] == 1.0 and (c[5] == 0).all()
+    tab = O.e4m3_table()
+    mids = ((tab[1:] + tab[:-1]) / 2)[:125]                    # ties below 448
+    for k in (0, 3, -7):
+        row = np.concatenate([[448.0], mids, [0.0, -mids[40]]]) * 2.0 ** k   # scale exactly 2^k
+        c, s, _ = O.fp8_quantize_rows(row[None], kernel_fp32=True)
+        assert s[0] == 2.0 ** k
+        lower = np.arange(125)
+        np.testing.assert_array_equal(c[0, 1:126], np.where(lower % 2 == 0, lower, lower + 1))
+        np.testing.assert_array_equal(c[0], _torch_fp32_route(row[None])[0][0])
+
+
+# ------------------------------------------------------------------------------- indexer keys
+def test_compress_ik_brute_force_own_logits_no_norm_no_rope():
+    """Indexer keys: each block's tokens softmax-weighted by the indexer's own logits, then nothing
+    else (no RMSNorm, no rotation), brute force on T <= 16; fp8 mode: the nearest E4M3FN code (ties to
+    even) of key / (absmax / 448), found by searching all finite codes."""
+    for (m, ov, T, dI) in ((4, 4, 15, 16), (4, 0, 16, 128), (3, 2, 14, 64)):
+        r = np.random.default_rng(T + dI)
+        ik, s = r.standard_normal((T, dI)) * 2.0, r.standard_normal(T)
+        got = O.compress_ik(ik, s, m, ov, fp8=False)
+        assert got.shape == (T // m, dI)
+        for i in range(T // m):
+            toks = [j for j in range(T) if i * m - ov <= j < (i + 1) * m]
+            e = [math.exp(s[j] - max(s[u] for u in toks)) for j in toks]
+            for d in range(dI):
+                brute = sum(e[a] * ik[j, d] for a, j in enumerate(toks)) / sum(e)
+                assert abs(got[i, d] - brute) < 1e-12
+        # no norm: the keys scale with the tokens (RMSNorm would undo it); one dominant logit picks
+        # that token's raw vector (a rotation or norm would change it)
+        np.testing.assert_allclose(O.compress_ik(5 * ik, s, m, ov, fp8=False), 5 * got, rtol=1e-13, atol=1e-12)
+        s1 = np.zeros(T)
+        s1[m + 1] = 80.0
+        np.testing.assert_allclose(O.compress_ik(ik, s1, m, ov, fp8=False)[1], ik[m + 1], atol=1e-20)
+        codes, sc, deq = O.compress_ik(ik, s, m, ov, fp8=True)
+        tab = np.array([O.e4m3_value(c) for c in range(127)])
+        for i in range(T // m):
+            assert sc[i] == np.abs(got[i]).max() / 448.0
+            for d in range(dI):
+                x = got[i, d] / sc[i]
+                dist = np.abs(tab - abs(x))
+                best = np.flatnonzero(dist == dist.min())
+                want = best[0] if best.size == 1 else best[best % 2 == 0][0]
+                if x < 0 and want != 0:
+                    want |= 0x80
+                assert codes[i, d] == want
+        np.testing.assert_allclose(deq, O.e4m3_decode(codes) * sc[:, None], rtol=0, atol=0)
 
 
 # ------------------------------------------------------------------------------- indexer + top-k
