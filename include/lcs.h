@@ -52,7 +52,7 @@ extern "C" {
 #define LCS_KV_BF16 0          /* K=V rows (entries, window ring) stored as bf16               */
 #define LCS_KV_FP8 1           /* K=V rows stored as E4M3FN codes + one fp32 scale per row     */
 
-#define LCS_HEAD_DIM 512       /* c, fixed (page 1, CSA step 4: "c set to 512")                */
+#define LCS_HEAD_DIM 512       /* c, fixed (page 1, "hybrid attention", CSA step 4)           */
 #define LCS_MAX_HEADS 64
 #define LCS_MAX_TOPK 2048
 

@@ -327,6 +327,14 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
   a.m = m; a.win = kv8 ? nullptr : win_ring; a.win_ld = win_ld; a.ring_cap = ring_cap; a.window = window; a.sink = sink;
   a.q_pos = q_pos; a.rope_offset = rope_offset; a.B = B; a.Tq = Tq; a.H = H; a.scale = scale; a.eps = eps;
   a.theta = rope_theta; a.out = out; a.ws = ws; a.ws_bytes = ws_bytes;
+  if (!win_ring) {
+    // no window ring (window = 0): the kernels still form addresses for padding slots of a tile, so
+    // point the ring at the cache itself (same row layout, never scored)
+    if (kv8) { a.win8 = a.kv8; a.win_scale = kv_scale; }
+    else a.win = kv_cache;
+    a.win_ld = kv_ld;
+    a.ring_cap = 0;
+  }
   return lcs::launch_attend(a, max_keys, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 

@@ -145,6 +145,20 @@ def test_kv8_entry_points_reject_bad_arguments(lib):
     assert lib.hca_attend_kv8(*hargs) == L.LCS_ERR_ARG  # window keys without their scales
 
 
+def test_kv8_attend_without_window_passes_validation(lib):
+    """window = 0 with no ring (codes and scales NULL) is a valid call on both fp8 entry points: the
+    checks get as far as the workspace (too small here, so nothing launches)."""
+    args = [FAKE, FAKE, FAKE, FAKE, 100, FAKE, 300, None, None, 0, 0, 0, FAKE, FAKE, 0, 1, 1, 64, 512, 0.04,
+            1e-6, 1e4, FAKE, FAKE, 16, None]
+    assert lib.csa_attend_kv8(*args) == L.LCS_ERR_WORKSPACE
+    hargs = [FAKE, FAKE, FAKE, FAKE, 100, 100, 4, None, None, 0, 0, 0, FAKE, FAKE, 0, 1, 1, 64, 512, 0.04,
+             1e-6, 1e4, FAKE, FAKE, 16, None]
+    assert lib.hca_attend_kv8(*hargs) == L.LCS_ERR_WORKSPACE
+    # a window with no ring stays an argument error
+    bad = list(hargs); bad[11] = 128
+    assert lib.hca_attend_kv8(*bad) == L.LCS_ERR_ARG
+
+
 def test_projection_and_mhc_entry_points_reject_bad_arguments(lib):
     widths = (ctypes.c_int * 2)(100, 1)
     dsts = (ctypes.c_void_p * 2)(1 << 20, 1 << 21)

@@ -293,7 +293,7 @@ def test_index_topk_all_equal_scores():
 
 # ----------------------------------------------------------------------------------- attention
 def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_inf=False, rope_offset=0,
-                 block_scale=None, gamma_scale=1.0, eps=1e-6, q_signs=False, kv8=False):
+                 block_scale=None, gamma_scale=1.0, eps=1e-6, q_signs=False, kv8=False, no_ring=False):
     q = synth.normal_bf16((B, Tq, H, 512), 1.28, cfg, 41)
     if q_signs:   # entries +-1: with eps = 0 the normalised query is gamma * q, exact in bf16
         q = synth.f32_to_bf16_bits(np.where(synth.bf16_bits_to_f64(q) >= 0, 1.0, -1.0).astype(np.float32))
@@ -321,6 +321,11 @@ def _attend_case(kind, B, Tq, H, k, n_cap, m, W, ring_cap, positions, cfg, sink_
         wcodes, wsc, win64 = O.fp8_quantize_rows(win64, kernel_fp32=True)
         kv_dev, win_dev = torch.from_numpy(ccodes).to(DEV), torch.from_numpy(wcodes).to(DEV)
         extra = dict(kv_scale=dev_f32(csc), win_scale=dev_f32(wsc))
+    if no_ring:   # window = 0 and no ring at all (NULL codes / rows and scales)
+        assert W == 0
+        win_dev = None
+        if kv8:
+            extra["win_scale"] = None
     if kind == "csa":
         g = synth.rng(cfg, 46)
         topk = -np.ones((B, Tq, k), dtype=np.int32)
@@ -396,6 +401,15 @@ def test_attend_fp8_kv_parity(kind, H):
         n_cap = 700 if H == 64 else 60
         _attend_case("hca", 3, 1, H, 0, n_cap, 128, 128, 128, [128 * n_cap + 5, 128 * n_cap // 2 + 127, 0],
                      153 + n_cap, kv8=True)
+
+
+@pytest.mark.parametrize("kv8", [True, False])
+def test_attend_without_window_ring(kv8):
+    """window = 0 with no ring passed (NULL rows, NULL scales): CSA with k = 300 (a ragged last tile)
+    and rows padded with -1, and HCA with a query at t = 0 and one at t < m', whose key splits are
+    all empty (their outputs are 0: no key, only the sink)."""
+    _attend_case("csa", 2, 1, 64, 300, 900, 4, 0, 0, [4 * 900 + 2, 4 * 200 + 1], 171, kv8=kv8, no_ring=True)
+    _attend_case("hca", 3, 1, 64, 0, 700, 128, 0, 0, [128 * 700 + 5, 0, 100], 172, kv8=kv8, no_ring=True)
 
 
 def test_hca_attend_fp8_kv_running_max_jumps():
