@@ -46,6 +46,7 @@ extern "C" {
 #define LCS_ERR_UNSUPPORTED 2  /* shape or dtype the library does not implement                */
 #define LCS_ERR_WORKSPACE 3    /* workspace NULL or smaller than the *_workspace() query      */
 #define LCS_ERR_HIP 4          /* a HIP launch error                                          */
+#define LCS_ERR_SCRATCH 5      /* the shape needs more than an allocation-free call's scratch */
 
 #define LCS_IK_BF16 0          /* indexer keys stored as bf16, no scale                        */
 #define LCS_IK_FP8 1           /* indexer keys stored as E4M3FN codes + one fp32 scale per key */
@@ -273,6 +274,22 @@ int grouped_out_proj(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o
 int grouped_out_proj_residual(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, const uint16_t* resid,
                               int M, int H, int c, int g, int d_g, int d, uint16_t* y, void* ws, size_t ws_bytes,
                               void* stream);
+
+/*
+ * grouped_out_proj_noalloc -- grouped_out_proj for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same result, bit for bit, but z lives in a static device array of the library
+ * (grouped_out_proj_noalloc_max_bytes() bytes, 4 MiB, held on each GPU the library runs on until the
+ * process ends) instead of a caller workspace.  The call allocates and frees nothing; on its first
+ * call on a device it looks up that array's device address (the device must be current).
+ *   Arguments and requirements as grouped_out_proj (no workspace).  M * g * d_g * 2 bytes, rounded
+ *   up to 256, must fit the array, else LCS_ERR_SCRATCH (e.g. M <= 256 at g * d_g = 8192).
+ *   Every call on one GPU uses the same array: calls that may overlap on one GPU (other streams,
+ *   other threads) race and must be ordered by the caller.
+ */
+size_t grouped_out_proj_noalloc_max_bytes(void);
+int grouped_out_proj_noalloc(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o,
+                             int M, int H, int c, int g, int d_g, int d, uint16_t* y, void* stream);
 
 /*
  * input_proj -- the layer's input projections from the hidden state in one pass over their

@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
 
-LCS_OK, LCS_ERR_ARG, LCS_ERR_UNSUPPORTED, LCS_ERR_WORKSPACE, LCS_ERR_HIP = 0, 1, 2, 3, 4
+LCS_OK, LCS_ERR_ARG, LCS_ERR_UNSUPPORTED, LCS_ERR_WORKSPACE, LCS_ERR_HIP, LCS_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 LCS_IK_BF16, LCS_IK_FP8 = 0, 1
 LCS_KV_BF16, LCS_KV_FP8 = 0, 1
 HEAD_DIM = 512
@@ -45,6 +45,8 @@ SIGNATURES = {
     "grouped_out_proj_workspace": (_SZ, [_I, _I, _I]),
     "grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "grouped_out_proj_residual": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "grouped_out_proj_noalloc_max_bytes": (_SZ, []),
+    "grouped_out_proj_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "input_proj": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]),
     "lcs_timing_enable": (_I, [_I]),
     "lcs_timing_read": (_I, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -307,6 +309,16 @@ def grouped_out_proj_residual(o, w_g, w_o, resid, *, H, y, ws=None, stream=None)
     st = lib().grouped_out_proj_residual(_ptr(o), _ptr(w_g), _ptr(w_o), _ptr(resid), M, H, HEAD_DIM, g, d_g, d,
                                          _ptr(y), _ptr(ws), ws.numel(), _stream(stream))
     _check("grouped_out_proj_residual", st)
+
+
+def grouped_out_proj_noalloc(o, w_g, w_o, *, H, y, stream=None):
+    """grouped_out_proj without a workspace: z in the library's static device scratch (see lcs.h)."""
+    M = o.shape[0]
+    g, d_g, _ = w_g.shape
+    d = w_o.shape[0]
+    st = lib().grouped_out_proj_noalloc(_ptr(o), _ptr(w_g), _ptr(w_o), M, H, HEAD_DIM, g, d_g, d, _ptr(y),
+                                        _stream(stream))
+    _check("grouped_out_proj_noalloc", st)
 
 
 def input_proj(h, w_in, segments, *, stream=None):

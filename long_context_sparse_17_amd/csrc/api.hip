@@ -79,6 +79,7 @@ const char* lcs_status_string(int status) {
     case LCS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case LCS_ERR_WORKSPACE: return "workspace too small";
     case LCS_ERR_HIP: return "HIP launch error";
+    case LCS_ERR_SCRATCH: return "shape needs more than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -393,9 +394,9 @@ size_t grouped_out_proj_workspace(int M, int g, int d_g) {
   return lcs::out_proj_workspace(M, g, d_g);
 }
 
-static int out_proj_common(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
-                           int d_g, int d, const uint16_t* resid, uint16_t* y, void* ws, size_t ws_bytes,
-                           void* stream) {
+// Shape, pointer and alignment checks shared by the grouped-projection entry points.
+static int out_proj_check(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
+                          int d_g, int d, const uint16_t* resid, const uint16_t* y) {
   if (!o || !w_g || !w_o || !y) return LCS_ERR_ARG;
   if (resid && !aligned16(resid)) return LCS_ERR_ARG;
   if (M <= 0 || H <= 0 || c <= 0 || g <= 0 || d_g <= 0 || d <= 0) return LCS_ERR_ARG;
@@ -403,6 +404,14 @@ static int out_proj_common(const uint16_t* o, const uint16_t* w_g, const uint16_
   if (H % g != 0 || d_g % 16 != 0 || d % 16 != 0 || ((int64_t)H / g * c) % 32 != 0 || ((int64_t)g * d_g) % 32 != 0)
     return LCS_ERR_UNSUPPORTED;
   if ((int64_t)g * d_g / 16 > 65535 * 16 || d / 16 > 65535 * 16) return LCS_ERR_UNSUPPORTED;
+  return LCS_OK;
+}
+
+static int out_proj_common(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c, int g,
+                           int d_g, int d, const uint16_t* resid, uint16_t* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  const int chk = out_proj_check(o, w_g, w_o, M, H, c, g, d_g, d, resid, y);
+  if (chk != LCS_OK) return chk;
   if (!ws || ws_bytes < lcs::out_proj_workspace(M, g, d_g)) return LCS_ERR_WORKSPACE;
   if (!aligned16(ws)) return LCS_ERR_ARG;
   lcs::OutProjArgs a;
@@ -421,6 +430,19 @@ int grouped_out_proj_residual(const uint16_t* o, const uint16_t* w_g, const uint
                               void* stream) {
   if (!resid) return LCS_ERR_ARG;
   return out_proj_common(o, w_g, w_o, M, H, c, g, d_g, d, resid, y, ws, ws_bytes, stream);
+}
+
+size_t grouped_out_proj_noalloc_max_bytes(void) { return lcs::kOutProjScratchBytes; }
+
+int grouped_out_proj_noalloc(const uint16_t* o, const uint16_t* w_g, const uint16_t* w_o, int M, int H, int c,
+                             int g, int d_g, int d, uint16_t* y, void* stream) {
+  // every argument check before any HIP call: a rejected call touches no device
+  const int chk = out_proj_check(o, w_g, w_o, M, H, c, g, d_g, d, nullptr, y);
+  if (chk != LCS_OK) return chk;
+  if (lcs::out_proj_workspace(M, g, d_g) > lcs::kOutProjScratchBytes) return LCS_ERR_SCRATCH;
+  void* z = nullptr;
+  if (lcs::out_proj_scratch(&z) != 0) return LCS_ERR_HIP;
+  return out_proj_common(o, w_g, w_o, M, H, c, g, d_g, d, nullptr, y, z, lcs::kOutProjScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -91,6 +91,9 @@ struct ProjSegments {
 int launch_input_proj(const uint16_t* h, int M, int d, const uint16_t* w, int n_rows, const ProjSegments& seg,
                       hipStream_t stream);
 size_t out_proj_workspace(int M, int g, int d_g);
+// Allocation-free variant: z in a static device array of kOutProjScratchBytes (per device).
+constexpr size_t kOutProjScratchBytes = (size_t)4 << 20;
+int out_proj_scratch(void** ptr);
 int launch_out_proj(const OutProjArgs& a, hipStream_t stream);
 
 }  // namespace lcs

@@ -12,6 +12,8 @@
 // M is the batch (<= 16): the kernel streams W once from HBM straight into MFMA A-fragments
 // (16 B per lane, rows contiguous), X fragments come from L2, the waves of a workgroup split K
 // and are summed through LDS.  One workgroup per 16 output features; its 8 waves split K.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -196,6 +198,34 @@ void launch_stage(const char* name, const uint16_t* X, int64_t x_ld, const uint1
 }  // namespace
 
 size_t out_proj_workspace(int M, int g, int d_g) { return al256((size_t)M * g * d_g * 2); }
+
+}  // namespace lcs
+
+// Scratch of the allocation-free grouped projection: the intermediate z lives in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on holds its own copy
+// until the process ends; every call on one GPU shares it, so calls that overlap on one GPU race.
+// z is written in full before it is read, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[lcs::kOutProjScratchBytes];
+
+namespace lcs {
+
+// Device address of `scratch` on the current device, looked up once per device with that device
+// current (the host-side name is only a stand-in, never a device address).
+int out_proj_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 4;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return 4;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return 0;
+}
 
 int launch_out_proj(const OutProjArgs& a, hipStream_t st) {
   uint16_t* z = static_cast<uint16_t*>(a.ws);

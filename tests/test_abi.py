@@ -192,6 +192,19 @@ def test_out_proj_rejects_bad_grouping(lib):
         L.LCS_ERR_WORKSPACE
 
 
+def test_out_proj_noalloc_limits_checked_on_the_host(lib):
+    """The allocation-free projection rejects shapes whose z does not fit its static scratch, and bad
+    shapes, before any HIP call (so on a machine without a GPU these return their codes)."""
+    cap = lib.grouped_out_proj_noalloc_max_bytes()
+    assert cap == 4 << 20
+    assert lib.grouped_out_proj_noalloc(FAKE, FAKE, FAKE, 257, 64, 512, 8, 1024, 4096, FAKE, None) == \
+        L.LCS_ERR_SCRATCH                                              # 257 * 8192 * 2 > 4 MiB
+    assert lib.grouped_out_proj_noalloc(FAKE, FAKE, FAKE, 8, 64, 512, 7, 1024, 4096, FAKE, None) == \
+        L.LCS_ERR_UNSUPPORTED
+    assert lib.grouped_out_proj_noalloc(None, FAKE, FAKE, 8, 64, 512, 8, 1024, 4096, FAKE, None) == L.LCS_ERR_ARG
+    assert lib.lcs_status_string(L.LCS_ERR_SCRATCH).startswith(b"shape needs more")
+
+
 def test_timing_facility_without_launches(lib):
     assert lib.lcs_timing_enable(1) == 0
     ms = ctypes.c_double(-1)
