@@ -8,15 +8,18 @@
 //
 // All query heads share each 1 KiB K=V row, so per key the work is 64 heads x 512 dims twice
 // (QK^T and PV): ~128 flop per byte, above the fp32-vector ridge, hence bf16 MFMA for both.
-// Workgroup = 4 waves = all 64 head slots of one query; keys in tiles of 32.
+// Workgroup = 4 waves covering HB 16-head blocks of one query (HB = 4: all 64 heads; HB = 2: 32
+// heads, the two halves of a (query, split) in two workgroups placed on the same XCD so the second
+// read of each tile comes from its L2, which halves the split partials for the same number of
+// workgroups); one workgroup per CU; keys in tiles of 32.
 //   - wave w loads dims [128w, 128w+128) of each tile key from HBM (16 B per lane) and stores
-//     the slice in LDS, so the tile is read from HBM once;
-//   - QK^T: wave w computes the logits of head block w (heads 16w..16w+15) over all 512 dims,
-//     K fragments from the four LDS slices, qhat fragments held in registers;
-//   - it runs the online softmax of its 16 heads in registers and publishes P (bf16) and the
-//     per-head rescale factors through LDS;
-//   - PV: wave w accumulates O[all heads, its 128 dims] += P V, V read from its own LDS slice
-//     (laid out so the key-major V fragment reads hit distinct banks).
+//     the slice in LDS, so the workgroup reads the tile once;
+//   - QK^T: HB = 4: wave w computes the logits of head block w over both 16-key blocks of the
+//     tile; HB = 2: wave w computes head block w & 1 over key block w >> 1 (all 512 dims, K
+//     fragments from the four LDS slices, qhat fragments held in registers);
+//   - it runs the online softmax of its heads in registers and publishes P (bf16) through LDS;
+//   - PV: wave w accumulates O[the workgroup's heads, its 128 dims] += P V, V read from its own
+//     LDS slice (laid out so the key-major V fragment reads hit distinct banks).
 // The loop is software-pipelined with one barrier per tile: while tile t is scored, tile t-1 is
 // accumulated, tile t+1 is moved from registers to LDS and tiles t+2, t+3 are in flight from HBM.
 // Keys are split across workgroups (split-K); partial (max, sum, O) are merged by merge_kernel,
@@ -29,8 +32,7 @@ namespace lcs {
 namespace {
 
 constexpr int kTile = 32;                 // keys per tile
-constexpr int kWaves = 4;                 // waves per workgroup = 16-head blocks = 128-dim slices
-constexpr int kHeadSlots = 16 * kWaves;   // heads handled by one workgroup (all of them)
+constexpr int kWaves = 4;                 // waves per workgroup = 128-dim slices
 constexpr int kMaxSplitKeys = 2048;       // keys of one split, staged as row indices in LDS
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 GU32x4;   // global address space: global_load, not flat
@@ -56,6 +58,7 @@ struct AttnK {
   RopeFreq rf;
   uint16_t* out; uint16_t* part_o; float* part_ml;
   int nsplit, keys_per_split;
+  int halves;                          // HB = 2: workgroups per (query, split), 1 (H <= 32) or 2
 };
 
 // LDS row of tile key (block kb, row r16 of the 16x16 MFMA block) in a slice: the key itself.  With
@@ -73,25 +76,38 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 // tiles are converted to bf16 (exactly) when staged in LDS, and each key's scale multiplies its
 // logit and, for PV, its probability (o = sum_j p_j s_j code_j), so the MFMAs are those of the bf16
 // path on the codes.
-template <bool LIST, bool F8>
+template <bool LIST, bool F8, int HB>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
+  constexpr int kHeadSlots = 16 * HB;                       // heads of one workgroup
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
-  __shared__ uint4 s_p[2][kWaves * kWave];                  // P fragments [slot][head block][lane]
+  __shared__ uint2 s_p[2][HB * kWave][2];                   // P fragments [slot][head block][lane][key block]
   __shared__ uint4 s_gamma[kHeadDim / 8];                  // gamma_q (bf16)
   __shared__ int s_redo;                                    // some head's running max jumped: second pass
   __shared__ float s_fac[kHeadSlots];
   __shared__ float s_cos[32], s_sin[32];
   __shared__ int32_t s_rows[kMaxSplitKeys];                 // per key of this split: cache/ring row, -1 = none
-  __shared__ float4 s_sc[kWaves][2][kTile / 4];             // F8: each wave's copy of the tile's key scales
+  __shared__ float4 s_sc[F8 ? kWaves : 1][2][kTile / 4];    // F8: each wave's copy of the tile's key scales
+  __shared__ float2 s_ml[2][kHeadSlots];                    // HB = 2: (sum, max) of each key-block wave's head
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t r = blockIdx.y;
   const int64_t b = r / a.Tq;
-  const int split = blockIdx.x;
-  const int head = 16 * w + c16;          // this lane's head in QK^T and the softmax
+  // HB = 2 with two halves: x = 16 j + 8 h + i is split 8 j + i, head half h, so the two halves of a
+  // split are 8 workgroups apart in dispatch order (the same XCD); splits past nsplit are padding
+  int split = blockIdx.x, hh = 0;
+  if (HB == 2 && a.halves == 2) {
+    split = 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7);
+    hh = (int)(blockIdx.x >> 3) & 1;
+  }
+  if (split >= a.nsplit) return;          // uniform
+  const int hq = HB == 4 ? w : (w & 1);   // head block this wave scores
+  const int kbq = HB == 4 ? 0 : (w >> 1); // HB = 2: the key block of each tile it scores
+  const int head0 = 32 * hh;              // first head of the workgroup
+  const int hl = 16 * hq + c16;           // this lane's head slot in QK^T and the softmax
+  const int head = head0 + hl;
   const bool head_ok = head < a.H;
 
   // Key slots of a row: CSA takes the k list slots (entries < 0 are skipped) then the window tokens,
@@ -105,6 +121,8 @@ attend_kernel(AttnK a) {
   // HCA: the first two tiles are loaded speculatively at once, as entries e_begin .. e_begin+63
   // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
+  // Register buffers of tiles in flight (tiles t+2, t+3 while t is scored).
+  constexpr int NB = 2;
   uint4 kb0[2][4], kb1[2][4];
   float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};           // F8: scales of the buffers' keys kb*16 + c16
   uint32_t vb0 = 0, vb1 = 0;
@@ -122,13 +140,15 @@ attend_kernel(AttnK a) {
         const u32x2 x = p0[4 * ks];
         kb0[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
       }
+      if (NB == 2) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x2 x = p1[4 * ks];
-        kb1[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x2 x = p1[4 * ks];
+          kb1[kb][ks] = make_uint4(x.x, x.y, 0u, 0u);
+        }
       }
       sc0[kb] = a.kv_scale[b * a.kv_ld + e0];
-      sc1[kb] = a.kv_scale[b * a.kv_ld + e1];
+      if (NB == 2) sc1[kb] = a.kv_scale[b * a.kv_ld + e1];
     }
   } else if (!LIST) {
 #pragma unroll
@@ -143,10 +163,12 @@ attend_kernel(AttnK a) {
         const u32x4 x = p0[4 * ks];
         kb0[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
       }
+      if (NB == 2) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 x = p1[4 * ks];
-        kb1[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 x = p1[4 * ks];
+          kb1[kb][ks] = make_uint4(x.x, x.y, x.z, x.w);
+        }
       }
     }
   }
@@ -255,18 +277,20 @@ attend_kernel(AttnK a) {
     tile_rows(i0, rr, vmask);
     issue_tile(i0, rr, kf, sf);
   };
-  // Two register buffers; an empty split reads row 0.  A load past the end re-reads the last
+  // The register buffers; an empty split reads row 0.  A load past the end re-reads the last
   // tile, whose copy is never scored.
   auto tile0 = [&](int t) { return (t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0)) * kTile; };
-  if (!LIST && nkeys >= 2 * kTile && nc_local >= 2 * kTile) {
+  if (!LIST && nkeys >= NB * kTile && nc_local >= NB * kTile) {
     vb0 = 0xFFFFFFFFu;                     // the speculative loads are these tiles
     vb1 = 0xFFFFFFFFu;
   } else {
     int32_t r0[2], r1[2];
     tile_rows(tile0(0), r0, vb0);
-    tile_rows(tile0(1), r1, vb1);
     issue_tile(tile0(0), r0, kb0, sc0);
-    issue_tile(tile0(1), r1, kb1, sc1);
+    if (NB == 2) {
+      tile_rows(tile0(1), r1, vb1);
+      issue_tile(tile0(1), r1, kb1, sc1);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -308,7 +332,7 @@ attend_kernel(AttnK a) {
     }
   }
 
-  floatx4 o[kWaves][8];                    // O^T tiles: lane holds head 16hb + c16, dims 128w + 16db + 4g .. +4
+  floatx4 o[HB][8];                        // O^T tiles: lane holds head slot 16hb + c16, dims 128w + 16db + 4g .. +4
   // Softmax state of this lane's head, log2 domain.  m_ref is the reference of the exponentials:
   // the first tile's max (first pass) or the split's max (second pass); it never moves within a
   // pass, so O is only ever touched by MFMA.  A tile whose max exceeds m_ref by more than kJump
@@ -355,56 +379,63 @@ attend_kernel(AttnK a) {
     return vm;
   };
 
-  // Logits of head block w for the tile in `slot`, online softmax, P and rescale factors out.
-  auto score = [&](int slot, uint32_t vm) {
-    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-    // 8 steps of 64 dims (slice h >> 1, ks 2(h & 1) .. +1): the fragments of step h + 1 are read
-    // while the MFMAs of step h run (two sets of 4 fragments, 32 registers)
-    auto kread = [&](int h, uint4 (&f)[2][2]) {
+  // Logits of this wave's head block for the tile in `slot`, online softmax, P out.  HB = 4: both
+  // key blocks of the tile.  HB = 2: the wave's own key block, except on the first tile with a key
+  // of a pass, where both are scored so that the two waves of a head block take the same reference
+  // (the same instructions on the same operands: the same bits).
+  auto qk = [&](int slot, int kb, floatx4& acc) {
+    // 8 steps of 64 dims (slice h >> 1, ks 2(h & 1) .. +1); two accumulation chains (even and odd
+    // 32-dim steps) so that consecutive MFMAs are independent; the fragments of step h + 1 are read
+    // while the MFMAs of step h run
+    floatx4 ae = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+    auto kread = [&](int h, uint4 (&f)[2]) {
       const uint16_t* sl = s_kv[slot][h >> 1];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          f[kb][j] = *reinterpret_cast<const uint4*>(&sl[vt_row(kb, c16) * kVtStride + 32 * (2 * (h & 1) + j) + 8 * g]);
+        f[j] = *reinterpret_cast<const uint4*>(&sl[vt_row(kb, c16) * kVtStride + 32 * (2 * (h & 1) + j) + 8 * g]);
     };
-    uint4 fa[2][2], fb[2][2];
+    uint4 fa[2], fb[2];
     kread(0, fa);
 #pragma unroll
     for (int h = 0; h < 8; h += 2) {
       kread(h + 1, fb);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_bf16(fa[kb][j], qf[2 * h + j], acc[kb]);
-      __builtin_amdgcn_sched_barrier(0);
+      ae = mfma_bf16(fa[0], qf[2 * h], ae);
+      ao = mfma_bf16(fa[1], qf[2 * h + 1], ao);
       if (h + 2 < 8) kread(h + 2, fa);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb] = mfma_bf16(fb[kb][j], qf[2 * h + 2 + j], acc[kb]);
-      __builtin_amdgcn_sched_barrier(0);
+      ae = mfma_bf16(fb[0], qf[2 * h + 2], ae);
+      ao = mfma_bf16(fb[1], qf[2 * h + 3], ao);
+    }
+    acc = ae + ao;
+  };
+  auto score = [&](int slot, uint32_t vm) {
+    floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    const bool both = HB == 4 || m_ref == -INFINITY;       // uniform: -inf only before a tile with a key
+    if (both) {
+      qk(slot, 0, acc[0]);
+      qk(slot, 1, acc[1]);
+    } else {
+      qk(slot, kbq, acc[kbq]);
     }
     float sc[2][4];
     float ksc[2][4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};   // F8: scales of keys kb*16 + 4g + i
     if (F8) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float4 f = s_sc[w][slot][kb * 4 + g];
+        const float4 f = s_sc[F8 ? w : 0][slot][kb * 4 + g];
         ksc[kb][0] = f.x; ksc[kb][1] = f.y; ksc[kb][2] = f.z; ksc[kb][3] = f.w;
       }
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool mine = HB == 4 || kb == kbq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool v = (vm >> (kb * 16 + 4 * g + i)) & 1u;
+        const bool v = (both || mine) && ((vm >> (kb * 16 + 4 * g + i)) & 1u);
         sc[kb][i] = v ? acc[kb][i] * (F8 ? ksc[kb][i] * a.scale_log2 : a.scale_log2) : -INFINITY;
         tmax = fmaxf(tmax, sc[kb][i]);
       }
+    }
     tmax = max_rows4(tmax);
     m_max = fmaxf(m_max, tmax);
     if (m_ref == -INFINITY) {
@@ -413,41 +444,46 @@ attend_kernel(AttnK a) {
       jumped = true;                       // this pass is void (the values below stay finite)
     }
     const float mr = fmaxf(m_ref, tmax - kJump);
-    uint32_t pk[4] = {0u, 0u, 0u, 0u};
     float psum = 0.f;
-    if (mr != -INFINITY) {
-      float pe[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      if (HB == 2 && kb != kbq) continue;  // the other key block is the partner wave's
+      uint32_t pk[2] = {0u, 0u};
+      if (mr != -INFINITY) {
+        float pe[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pe[kb * 4 + i] = exp2f(sc[kb][i] - mr);
-      if (F8) {
-        // PV weights bf16(p_j s_j); the normaliser sums the same rounded weights over s_j, so
-        // numerator and denominator see one rounding of p_j, as in the bf16 path
+        for (int i = 0; i < 4; ++i) pe[i] = exp2f(sc[kb][i] - mr);
+        if (F8) {
+          // PV weights bf16(p_j s_j); the normaliser sums the same rounded weights over s_j, so
+          // numerator and denominator see one rounding of p_j, as in the bf16 path
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s0 = ksc[j >> 1][(2 * j) & 3], s1 = ksc[j >> 1][(2 * j + 1) & 3];
-          pk[j] = pack_bf2(pe[2 * j] * s0, pe[2 * j + 1] * s1);
-          psum += bf2f_lo(pk[j]) * __builtin_amdgcn_rcpf(s0) + bf2f_hi(pk[j]) * __builtin_amdgcn_rcpf(s1);
-        }
-      } else {
+          for (int j = 0; j < 2; ++j) {
+            const float s0 = ksc[kb][2 * j], s1 = ksc[kb][2 * j + 1];
+            pk[j] = pack_bf2(pe[2 * j] * s0, pe[2 * j + 1] * s1);
+            psum += bf2f_lo(pk[j]) * __builtin_amdgcn_rcpf(s0) + bf2f_hi(pk[j]) * __builtin_amdgcn_rcpf(s1);
+          }
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pk[j] = pack_bf2(pe[2 * j], pe[2 * j + 1]);
-          psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+          for (int j = 0; j < 2; ++j) {
+            pk[j] = pack_bf2(pe[2 * j], pe[2 * j + 1]);
+            psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+          }
         }
       }
+      s_p[slot][hq * kWave + lane][kb] = make_uint2(pk[0], pk[1]);
     }
     psum = sum_rows4(psum);
     l_run += psum;
-    s_p[slot][w * kWave + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   };
 
   // O[:, this wave's 128 dims] += P V for the tile in `slot`.
   auto accumulate = [&](int slot) {
-    uint4 pf[kWaves];
+    uint4 pf[HB];
 #pragma unroll
-    for (int hb = 0; hb < kWaves; ++hb) pf[hb] = s_p[slot][hb * kWave + lane];
+    for (int hb = 0; hb < HB; ++hb) {
+      const uint2 lo = s_p[slot][hb * kWave + lane][0], hi = s_p[slot][hb * kWave + lane][1];
+      pf[hb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
     // V fragment (B operand): lane (g, c16) needs k-slots 8g..8g+7 of dim 16db + c16.  Two LDS
     // transpose reads give it: within each 16-lane group, lane j points at 4 consecutive dims
     // (16db + 4(j & 3)) of the key in k-slot 8g + (j >> 2) (then 8g + 4 + (j >> 2)), and lane i
@@ -462,65 +498,75 @@ attend_kernel(AttnK a) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
 #pragma unroll
-      for (int hb = 0; hb < kWaves; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
+      for (int hb = 0; hb < HB; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
     }
   };
 
   // Pipeline: iteration t scores tile t (slot t & 1), accumulates tile t-1 (slot (t-1) & 1), stages
-  // tile t+1 into slot (t+1) & 1 (free: tile t-1's reads are done in this wave, and in every other
-  // wave before the previous barrier) and issues the loads of tile t+3; one barrier.
+  // tile t+1 into slot (t+1) & 1 (free: tile t-1's V reads are done in this wave, which reads only
+  // its own slice, and every wave's K reads of it before the previous barrier) and issues the loads
+  // of tile t+1+NB; one barrier.
   for (int pass = 0;; ++pass) {
-    if (pass > 0) {                        // second pass: the first two tiles again
+    if (pass > 0) {                        // second pass: the first tiles again
       load_tile(tile0(0), kb0, sc0, vb0);
-      load_tile(tile0(1), kb1, sc1, vb1);
-      m_ref = m_max;
+      if (NB == 2) load_tile(tile0(1), kb1, sc1, vb1);
+      m_ref = m_max;                       // the split's max (HB = 2: over both key-block waves)
       l_run = 0.f;
     }
 #pragma unroll
-    for (int hb = 0; hb < kWaves; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
     int32_t rn[2];
     uint32_t vn;
-    tile_rows(tile0(2), rn, vn);
-    uint32_t vm0 = stage(kb0, sc0, vb0, 0, tile0(2), rn, vn);   // tile 0 -> slot 0, buffer 0 <- tile 2
+    tile_rows(tile0(NB), rn, vn);
+    uint32_t vm0 = stage(kb0, sc0, vb0, 0, tile0(NB), rn, vn);  // tile 0 -> slot 0, buffer 0 <- tile NB
     uint32_t vm1 = 0;
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
-      tile_rows(tile0(t + 3), rn, vn);              // row lookups first: their latency hides under QK
+      tile_rows(tile0(t + 1 + NB), rn, vn);         // row lookups first: their latency hides under QK
       score(0, vm0);
       if (t > 0) accumulate(1);
-      vm1 = stage(kb1, sc1, vb1, 1, tile0(t + 3), rn, vn);      // tile t+1 -> slot 1, buffer 1 <- tile t+3
+      // tile t+1 -> slot 1; its buffer <- tile t+1+NB
+      if (NB == 2) vm1 = stage(kb1, sc1, vb1, 1, tile0(t + 3), rn, vn);
+      else vm1 = stage(kb0, sc0, vb0, 1, tile0(t + 2), rn, vn);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 >= ntiles) break;
-      tile_rows(tile0(t + 4), rn, vn);
+      tile_rows(tile0(t + 2 + NB), rn, vn);
       score(1, vm1);
       accumulate(0);
-      vm0 = stage(kb0, sc0, vb0, 0, tile0(t + 4), rn, vn);      // tile t+2 -> slot 0, buffer 0 <- tile t+4
+      vm0 = stage(kb0, sc0, vb0, 0, tile0(t + 2 + NB), rn, vn);  // tile t+2 -> slot 0, buffer 0 <- tile t+2+NB
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
     if (ntiles > 0) accumulate((ntiles - 1) & 1);
     if (jumped) s_redo = 1;
-    {
-      // this pass's output factor per head: one split finishes here (sink, normalisation); with
-      // several, the partials stay unnormalised
-      float f = 1.f;
-      if (a.nsplit == 1) {
-        const float z = head_ok ? a.sink[head] * kLog2e : -INFINITY;
-        const float M = fmaxf(m_ref, z);
-        f = 0.f;
-        if (M != -INFINITY) {
-          const float L = l_run * exp2f(m_ref - M) + exp2f(z - M);
-          f = exp2f(m_ref - M) / L;
-        }
-      }
-      if (g == 0) s_fac[head] = f;
+    if (HB == 2 && g == 0) s_ml[kbq][hl] = make_float2(l_run, m_max);
+    __syncthreads();                       // s_redo, s_ml; every wave is past its last tile reads
+    if (HB == 2) {                         // the partner wave's keys: same reference, its own sum and max
+      const float2 o2 = s_ml[kbq ^ 1][hl];
+      l_run += o2.x;
+      m_max = fmaxf(m_max, o2.y);
     }
-    __syncthreads();                       // s_redo, s_fac; every wave is past its last tile reads
     if (pass > 0 || s_redo == 0) break;
   }
+  {
+    // the output factor per head: one split finishes here (sink, normalisation); with several, the
+    // partials stay unnormalised
+    float f = 1.f;
+    if (a.nsplit == 1) {
+      const float z = head_ok ? a.sink[head] * kLog2e : -INFINITY;
+      const float M = fmaxf(m_ref, z);
+      f = 0.f;
+      if (M != -INFINITY) {
+        const float L = l_run * exp2f(m_ref - M) + exp2f(z - M);
+        f = exp2f(m_ref - M) / L;
+      }
+    }
+    if (g == 0 && kbq == 0) s_fac[hl] = f;
+  }
+  __syncthreads();                         // s_fac
 
   // Epilogue.  One split finishes the output here (factor s_fac: sink, normalisation); with
   // several, the split stores its partial O and (max, sum).  Either way the last 64 dims are rotated
@@ -529,10 +575,10 @@ attend_kernel(AttnK a) {
   // 16 B chunks.
   const bool single = a.nsplit == 1;
   constexpr int kOStride = kHeadDim + 8;   // 520 bf16: the 16 heads of one 8-byte write start 4 banks apart
-  uint16_t* s_o = &s_kv[0][0][0];          // [64 heads][kOStride] bf16
+  uint16_t* s_o = &s_kv[0][0][0];          // [head slots][kOStride] bf16
   static_assert(sizeof(s_kv) >= kHeadSlots * kOStride * 2, "output staging fits the tile buffers");
 #pragma unroll
-  for (int hb = 0; hb < kWaves; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     const int hh = hb * 16 + c16;
     const float fac = single ? s_fac[hh] : 1.f;   // partials: factor 1
 #pragma unroll
@@ -556,18 +602,18 @@ attend_kernel(AttnK a) {
     }
   }
   __syncthreads();
-  const int64_t base = single ? r * a.H : (r * a.nsplit + split) * a.H;
+  const int64_t base = (single ? r * a.H : (r * a.nsplit + split) * a.H) + head0;
   uint16_t* dst = single ? a.out : a.part_o;
 #pragma unroll
-  for (int u = 0; u < kHeadSlots * kHeadDim / 8 / 256; ++u) {   // 16 chunks of 8 dims per thread
-    const int hl = 4 * u + w;              // one head per wave per step: the check is uniform
-    if (hl < a.H) {
-      const uint4 x = *reinterpret_cast<const uint4*>(&s_o[hl * kOStride + 8 * lane]);
-      *reinterpret_cast<uint4*>(dst + (base + hl) * kHeadDim + 8 * lane) = x;
+  for (int u = 0; u < kHeadSlots * kHeadDim / 8 / 256; ++u) {   // HB * 4 chunks of 8 dims per thread
+    const int ho = 4 * u + w;              // one head per wave per step: the check is uniform
+    if (head0 + ho < a.H) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&s_o[ho * kOStride + 8 * lane]);
+      *reinterpret_cast<uint4*>(dst + (base + ho) * kHeadDim + 8 * lane) = x;
     }
   }
-  if (!single && g == 0 && head_ok)
-    *reinterpret_cast<float2*>(a.part_ml + (base + head) * 2) = make_float2(m_ref, l_run);
+  if (!single && g == 0 && kbq == 0 && head_ok)
+    *reinterpret_cast<float2*>(a.part_ml + (base + hl) * 2) = make_float2(m_ref, l_run);
 }
 
 // Merge split-K partials with the sink: one wave per (query, head), 8 dims per lane, no LDS and no
@@ -647,12 +693,15 @@ merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Keys per split: about one workgroup per CU (256) with at least 2 tiles (64 keys) each; every split
-// adds a 64 KiB partial (bf16 O of 64 heads) that the merge reads back, so splits are kept few.
-int keys_per_split(int R, int64_t max_keys) {
+// Keys per split: about one workgroup per CU (256, counting both head halves with HB = 2) with at
+// least 2 tiles (64 keys) each.  Every split adds a 64 KiB partial (bf16 O of 64 heads) that the
+// merge reads back, so splits are kept few.
+template <int HB>
+int keys_per_split(int R, int halves, int64_t max_keys) {
   const int64_t tiles = (max_keys + kTile - 1) / kTile;
   if (tiles <= 0) return kTile;
-  int64_t want_splits = (256 + R - 1) / R;
+  const int64_t slots = 256;
+  int64_t want_splits = (slots + (int64_t)R * halves - 1) / ((int64_t)R * halves);
   if (want_splits < 1) want_splits = 1;
   int64_t tps = (tiles + want_splits - 1) / want_splits;
   if (tps < 2) tps = 2;
@@ -661,14 +710,40 @@ int keys_per_split(int R, int64_t max_keys) {
   return (int)(tps * kTile);
 }
 
+// The layout a call runs with.  Selected entries (CSA): HB = 2, whose halved split partials cut the
+// epilogue and merge that dominate a short key list.  All visible entries (HCA): HB = 4, whose
+// streaming loop keeps twice the unique bytes in flight per CU.
+struct AttendPlan {
+  int hb, halves, keys_per_split, nsplit;
+};
+AttendPlan attend_plan(int R, int H, int64_t max_keys, bool list) {
+  AttendPlan p;
+  p.hb = list ? 2 : 4;
+  p.halves = p.hb == 2 && H > 32 ? 2 : 1;
+  p.keys_per_split = p.hb == 2 ? keys_per_split<2>(R, p.halves, max_keys) : keys_per_split<4>(R, 1, max_keys);
+  p.nsplit = max_keys > 0 ? (int)((max_keys + p.keys_per_split - 1) / p.keys_per_split) : 1;
+  if (p.nsplit < 1) p.nsplit = 1;
+  return p;
+}
+
 }  // namespace
 
 size_t attend_workspace(int B, int Tq, int H, int64_t max_keys) {
+  // one query serves both entry points: the larger of the two layouts' split partials
   const int R = B * Tq;
-  const int kps = keys_per_split(R, max_keys);
-  const int64_t nsplit = max_keys > 0 ? (max_keys + kps - 1) / kps : 1;
+  int nsplit = 1;
+  for (int list = 0; list < 2; ++list) {
+    const AttendPlan p = attend_plan(R, H, max_keys, list != 0);
+    nsplit = p.nsplit > nsplit ? p.nsplit : nsplit;
+  }
   if (nsplit <= 1) return 256;
   return al256((size_t)R * nsplit * H * kHeadDim * 2) + al256((size_t)R * nsplit * H * 2 * 4);
+}
+
+template <bool LIST, bool F8>
+void launch_attend_kernel(const AttnK& a, int hb, dim3 grid, hipStream_t st) {
+  if (hb == 2) LCS_LAUNCH("attend_kernel", (attend_kernel<LIST, F8, 2>), grid, dim3(256), 0, st, a);
+  else LCS_LAUNCH("attend_kernel", (attend_kernel<LIST, F8, 4>), grid, dim3(256), 0, st, a);
 }
 
 int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
@@ -679,21 +754,25 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.window = x.window; a.sink = x.sink; a.q_pos = x.q_pos; a.rope_offset = x.rope_offset;
   a.Tq = x.Tq; a.H = x.H; a.scale_log2 = x.scale * kLog2e; a.eps = x.eps; a.rf = rope_freq(x.theta);
   a.out = x.out;
-  a.keys_per_split = keys_per_split(R, max_keys);
-  a.nsplit = max_keys > 0 ? (int)((max_keys + a.keys_per_split - 1) / a.keys_per_split) : 1;
-  if (a.nsplit < 1) a.nsplit = 1;
+  const AttendPlan p = attend_plan(R, x.H, max_keys, x.topk != nullptr);
+  a.keys_per_split = p.keys_per_split;
+  a.nsplit = p.nsplit;
+  a.halves = p.halves;
   a.part_o = static_cast<uint16_t*>(x.ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
                                        al256((size_t)R * a.nsplit * x.H * kHeadDim * 2));
-  const dim3 grid((unsigned)a.nsplit, (unsigned)R);
+  // HB = 2 with two halves: 16 workgroups per 8 splits (the two halves 8 apart), padded to a multiple
+  // of 16 (the padding returns at once)
+  const unsigned gx = p.hb == 2 && p.halves == 2 ? (unsigned)(16 * ((a.nsplit + 7) / 8)) : (unsigned)a.nsplit;
+  const dim3 grid(gx, (unsigned)R);
   a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
   const bool f8 = x.kv8 != nullptr;
   if (x.topk) {
-    if (f8) LCS_LAUNCH("attend_kernel", (attend_kernel<true, true>), grid, dim3(256), 0, st, a);
-    else LCS_LAUNCH("attend_kernel", (attend_kernel<true, false>), grid, dim3(256), 0, st, a);
+    if (f8) launch_attend_kernel<true, true>(a, p.hb, grid, st);
+    else launch_attend_kernel<true, false>(a, p.hb, grid, st);
   } else {
-    if (f8) LCS_LAUNCH("attend_kernel", (attend_kernel<false, true>), grid, dim3(256), 0, st, a);
-    else LCS_LAUNCH("attend_kernel", (attend_kernel<false, false>), grid, dim3(256), 0, st, a);
+    if (f8) launch_attend_kernel<false, true>(a, p.hb, grid, st);
+    else launch_attend_kernel<false, false>(a, p.hb, grid, st);
   }
   if (a.nsplit > 1) {
     const int64_t waves = (int64_t)R * x.H;
