@@ -244,7 +244,7 @@ def prefill_row(dev):
     pos = torch.arange(N - Tq, N, dtype=torch.int64, device=dev).view(1, Tq)
     topk = torch.empty((1, Tq, k), dtype=torch.int32, device=dev)
     out = torch.empty((1, Tq, H, 512), dtype=torch.bfloat16, device=dev)
-    ws_i = L.workspace(L.csa_index_topk_workspace(1, Tq, n_cap, k))
+    ws_i = L.workspace(L.csa_index_topk_workspace(1, Tq, n_cap, k), zeroed=True)
     ws_a = L.workspace(L.attend_workspace(1, Tq, H, k + W))
 
     def call():
@@ -439,7 +439,7 @@ def main():
         step()
     torch.cuda.synchronize()
     kernels = {}
-    for name in ("index_score_kernel", "topk_clear_kernel", "topk_filter_kernel", "topk_final_kernel",
+    for name in ("index_score_kernel", "topk_filter_kernel", "topk_final_kernel",
                  "attend_kernel", "attend_merge_kernel", "out_proj_group_kernel", "out_proj_out_kernel",
                  "compress_kernel", "decode_append_kernel", "input_proj_kernel"):
         ms, n = L.timing_read(name)

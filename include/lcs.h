@@ -203,12 +203,18 @@ int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, in
  *   ik_cache [B, ik_ld, dI] (codes or bf16), ik_scale [B, ik_ld] fp32 (fp8), n_cap <= ik_ld
  *   q_pos  [B, Tq] int64 (device)
  *   topk_idx [B, Tq, k] int32; topk_score [B, Tq, k] fp32 (may be NULL; -inf where padded)
- *   ws     device workspace of at least csa_index_topk_workspace(B, Tq, n_cap, k) bytes
+ *   ws     device workspace of at least csa_index_topk_workspace(B, Tq, n_cap, k) bytes, zero-filled
+ *          before the first call that uses it.  Every call that returns LCS_OK leaves the workspace's
+ *          leading csa_index_topk_state_bytes() bytes zero-filled again (the decode selection's
+ *          histograms are cleared by the call's last kernel), so one workspace serves any sequence of
+ *          calls, of any shapes, without further clearing; calls that share a workspace must be
+ *          ordered (one stream).
  *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1, B * Tq <= 65535 * 16,
  *   and launch grids within the device limits (many-row calls: B * ceil(Tq / 16) <= 65535 with bf16
  *   keys, about B <= 65000 with fp8 keys); otherwise LCS_ERR_UNSUPPORTED before anything runs.
  */
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
+size_t csa_index_topk_state_bytes(void);
 int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx,
                    const void* ik_cache, const float* ik_scale, int64_t ik_ld, int ik_dtype,
                    const int64_t* q_pos, int64_t n_cap,

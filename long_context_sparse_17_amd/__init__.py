@@ -36,6 +36,7 @@ SIGNATURES = {
     "mhc_sinkhorn": (_I, [_P, _I, _I, _I, _P, _P]),
     "mhc_mix": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
+    "csa_index_topk_state_bytes": (_SZ, []),
     "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "lcs_attend_workspace": (_SZ, [_I, _I, _I, _I64]),
     "csa_attend": (_I, [_P, _P, _P, _I64, _P, _I, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F, _F, _F,
@@ -115,9 +116,12 @@ def _dt(t, dtype, name):
     return t
 
 
-def workspace(nbytes, device="cuda"):
+def workspace(nbytes, device="cuda", zeroed=False):
+    """A device workspace of at least nbytes; zeroed=True zero-fills it (csa_index_topk needs that once,
+    before its first call; every call leaves it ready for the next)."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    alloc = torch.zeros if zeroed else torch.empty
+    return alloc(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 # --------------------------------------------------------------------------------- entry points
@@ -218,13 +222,14 @@ def csa_index_topk_workspace(B, Tq, n_cap, k):
 
 def csa_index_topk(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, topk_score=None,
                    ws=None, stream=None):
-    """q_idx [B,Tq,H_I,dI] bf16, w_idx [B,Tq,H_I] bf16, ik_cache [B,ik_ld,dI] uint8 (fp8) or bf16."""
+    """q_idx [B,Tq,H_I,dI] bf16, w_idx [B,Tq,H_I] bf16, ik_cache [B,ik_ld,dI] uint8 (fp8) or bf16.
+    ws: a workspace(csa_index_topk_workspace(...), zeroed=True), reusable across calls (see lcs.h)."""
     import torch
     B, Tq, H_I, dI = q_idx.shape
     fp8 = ik_cache.dtype == torch.uint8
     _dt(q_pos, torch.int64, "q_pos"); _dt(topk_idx, torch.int32, "topk_idx")
     if ws is None:
-        ws = workspace(csa_index_topk_workspace(B, Tq, n_cap, k), q_idx.device)
+        ws = workspace(csa_index_topk_workspace(B, Tq, n_cap, k), q_idx.device, zeroed=True)
     st = lib().csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(ik_cache), _ptr(ik_scale), ik_cache.shape[1],
                               LCS_IK_FP8 if fp8 else LCS_IK_BF16, _ptr(q_pos), n_cap, B, Tq, H_I, dI, m, k,
                               _ptr(topk_idx), _ptr(topk_score), _ptr(ws), ws.numel(), _stream(stream))

@@ -265,6 +265,8 @@ int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, in
 }
 
 // ------------------------------------------------------------------------------ indexer + top-k
+size_t csa_index_topk_state_bytes(void) { return lcs::index_topk_state_bytes(); }
+
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   if (B <= 0 || Tq <= 0 || n_cap <= 0 || k <= 0) return 0;
   return lcs::index_topk_workspace(B, Tq, n_cap, k);

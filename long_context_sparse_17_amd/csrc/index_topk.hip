@@ -39,9 +39,15 @@ constexpr int kMaxIndexHeads = 64;         // indexer heads (the entry point rej
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Decode selection keeps per-row histograms in a fixed area at the start of the workspace, for up
+// to kDecodeRows rows.  The area is zero between calls: the caller zero-fills the workspace once, the
+// scorer and filter add into the rows a call uses, and the final kernel clears them again, so no call
+// needs a clearing launch of its own.
+constexpr int kDecodeRows = 64;
+
 struct Ws {
+  uint32_t* hist;                 // [kDecodeRows, kHistRow]: histograms of the top score-key bits, then of the next 11
   float* scores;                  // [R, nsp]
-  uint32_t* hist;                 // [R, kHistRow]: histograms of the top score-key bits, then of the next 11
   unsigned long long* comb;       // [R, nsp]: kept entries per chunk (decode) / candidates (prefill)
   uint2* counts;                  // [R, nchunk]: per decode chunk (kept, above the threshold bin)
   uint8_t* qc;                    // [R, HP, 128]: E4M3FN query codes (fp8 prefill)
@@ -63,10 +69,10 @@ Ws carve(void* ws, int B, int Tq, int64_t n_cap) {
   w.nsp = (n_cap + 63) & ~(int64_t)63;
   w.nchunk = (int)n_chunks(n_cap);
   char* p = static_cast<char*>(ws);
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += al256((size_t)kDecodeRows * kHistRow * 4);
   w.scores = reinterpret_cast<float*>(p);
   p += al256((size_t)R * w.nsp * 4);
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += al256((size_t)R * kHistRow * 4);
   w.comb = reinterpret_cast<unsigned long long*>(p);
   p += al256((size_t)R * w.nsp * 8);
   w.counts = reinterpret_cast<uint2*>(p);
@@ -87,12 +93,6 @@ __device__ __forceinline__ int64_t n_visible(const int64_t* q_pos, int64_t r, in
   int64_t t = q_pos[r];
   int64_t n = t >= 0 ? t / m : 0;
   return n < n_cap ? n : n_cap;
-}
-
-// ------------------------------------------------------------------------------------ clear
-__global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
 }
 
 // ------------------------------------------------------------------------------------ scoring
@@ -1174,10 +1174,11 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
   if (tid == 0) counts[r * nchunk + blockIdx.x] = make_uint2(total & 0xFFFFu, total >> 16);
 }
 
-// Decode final: one workgroup per row runs the selection above.
+// Decode final: one workgroup per row runs the selection above, then clears the row's histograms
+// (both levels; nothing reads them after this kernel in the call) for the next call.
 __global__ void __launch_bounds__(kSelThreads)
 topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __restrict__ counts,
-                  const uint32_t* __restrict__ hist, int64_t nsp, int nchunk, const int64_t* __restrict__ q_pos,
+                  uint32_t* __restrict__ hist, int64_t nsp, int nchunk, const int64_t* __restrict__ q_pos,
                   int m, int64_t n_cap, int k, const float* __restrict__ scores, int32_t* __restrict__ topk_idx,
                   float* __restrict__ topk_score) {
   __shared__ FinalShared sh;
@@ -1185,6 +1186,9 @@ topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __re
   const int64_t r = blockIdx.x;
   final_select(sh, s_w, r, n_visible(q_pos, r, m, n_cap), comb, counts, hist, nsp, nchunk, k, scores, topk_idx,
                topk_score);
+  __syncthreads();                                // every read of the level-2 histogram is done
+  uint4* h = reinterpret_cast<uint4*>(hist + r * kHistRow);
+  for (int i = threadIdx.x; i < kHistRow / 4; i += kSelThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
@@ -1608,7 +1612,7 @@ void score_rows(const IndexArgs& a, const Ws& w, hipStream_t st) {
 // Every grid the call would launch fits the HIP limits (x < 2^31, y <= 65535).
 bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
   const int64_t R = (int64_t)B * Tq;
-  if (R < 64 && n_chunks(n_cap) <= kMaxDecodeChunks) return true;   // decode grids (chunks, R), R < 64
+  if (R < kDecodeRows && n_chunks(n_cap) <= kMaxDecodeChunks) return true;   // decode grids (chunks, R)
   if (R >= ((int64_t)1 << 31)) return false;                         // one workgroup per row
   if (ik_fp8) {
     const PfGrid p = prefill_grid(B, Tq, n_cap);
@@ -1617,11 +1621,13 @@ bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
   return (n_cap + kScoreChunk - 1) / kScoreChunk < ((int64_t)1 << 31) && (int64_t)B * ((Tq + 15) / 16) <= 65535;
 }
 
+size_t index_topk_state_bytes() { return al256((size_t)kDecodeRows * kHistRow * 4); }
+
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   (void)k;
   const int64_t R = (int64_t)B * Tq;
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
-  return al256((size_t)R * nsp * 4) + al256((size_t)R * kHistRow * 4) + al256((size_t)R * nsp * 8) +
+  return al256((size_t)kDecodeRows * kHistRow * 4) + al256((size_t)R * nsp * 4) + al256((size_t)R * nsp * 8) +
          al256((size_t)R * n_chunks(n_cap) * 8) + al256((size_t)R * kMaxIndexHeads * 128) +
          al256((size_t)R * kMaxIndexHeads * 4) + al256((size_t)R * 4) + al256((size_t)n_groups4(B, Tq) * 2048) +
          al256((size_t)n_groups4(B, Tq) * 256);
@@ -1632,12 +1638,9 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   Ws w = carve(a.ws, a.B, a.Tq, a.n_cap);
   // Few rows: spread every row over many workgroups (decode).  Many rows, or rows longer than the
   // decode selection stages: row-per-workgroup.
-  const bool decode = R < 64 && w.nchunk <= kMaxDecodeChunks;
+  const bool decode = R < kDecodeRows && w.nchunk <= kMaxDecodeChunks;
   if (decode) {
-    const int64_t n = (int64_t)R * kHistRow;
-    LCS_LAUNCH("topk_clear_kernel", clear_u32_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
-               dim3(256), 0, st, w.hist, n);
-    score_decode(a, w, st);
+    score_decode(a, w, st);                       // the histogram rows start at zero (see kDecodeRows)
     dim3 gf((unsigned)w.nchunk, (unsigned)R);
     LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.comb,
                w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k);

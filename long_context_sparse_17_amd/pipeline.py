@@ -138,7 +138,7 @@ class CsaDecodeLayer(_Common):
         self.q_idx = nrm((B, 1, H_I, dI), 1.28).to(torch.bfloat16)
         self.w_idx = nrm((B, 1, H_I), 1.28).to(torch.bfloat16)
         self.topk = torch.empty((B, 1, k), dtype=torch.int32, device=device)
-        self.ws_index = workspace(csa_index_topk_workspace(B, 1, self.n_cap, k), device)
+        self.ws_index = workspace(csa_index_topk_workspace(B, 1, self.n_cap, k), device, zeroed=True)
         self.ws_attn = workspace(attend_workspace(B, 1, H, k + W), device)
 
     def build_caches(self, block_tokens=65536, seed=1):

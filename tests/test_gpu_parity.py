@@ -188,6 +188,32 @@ def test_index_topk_decode_fp8():
     assert band <= 2
 
 
+def test_index_topk_workspace_left_zeroed_and_reusable():
+    """One zero-filled workspace serves a sequence of calls of different shapes (decode rows, a
+    many-row call, decode again): each call's selection equals a call on a fresh zeroed workspace
+    (bit for bit), and after every call the workspace's leading state bytes are zero again."""
+    shapes = [(8, 1, 20000, 512, 71), (3, 1, 9000, 256, 72), (1, 70, 5000, 128, 73), (5, 1, 30000, 1024, 74)]
+    need = max(L.csa_index_topk_workspace(B, Tq, n, k) for B, Tq, n, k, _ in shapes)
+    shared = L.workspace(need, zeroed=True)
+    state = L.lib().csa_index_topk_state_bytes()
+    assert 0 < state <= need
+    for B, Tq, n_cap, k, cfg in shapes:
+        print(f"shared workspace: B={B} Tq={Tq} n_cap={n_cap} k={k}", flush=True)
+        q = from_bits(synth.normal_bf16((B, Tq, 64, 128), 1.28, cfg, 1))
+        w = from_bits(synth.normal_bf16((B, Tq, 64), 1.28, cfg, 2))
+        codes = torch.from_numpy(synth.fp8_codes((B, n_cap, 128), cfg, 3)).to(DEV)
+        scale = dev_f32(synth.positive_scales((B, n_cap), cfg, 4))
+        pos = 4 * n_cap - 2 * np.arange(B * Tq, dtype=np.int64).reshape(B, Tq) * (n_cap // (B * Tq + 1))
+        outs = []
+        for ws in (shared, None):
+            idx = torch.full((B, Tq, k), -7, dtype=torch.int32, device=DEV)
+            L.csa_index_topk(q, w, codes, scale, dev_i64(pos), n_cap=n_cap, m=4, k=k, topk_idx=idx, ws=ws)
+            outs.append(idx)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        assert int(shared[:state].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("fp8,H_I,dI", [(True, 8, 128), (True, 40, 128), (False, 40, 128), (False, 40, 64)])
 def test_index_topk_decode_head_blocks_ragged(fp8, H_I, dI):
     # decode scoring with padded head blocks (8 -> 16, 40 -> 48 heads) and chunks that end inside a
