@@ -113,7 +113,18 @@ rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
   const int n0 = blockIdx.x * 16;
   const int64_t xoff = (int64_t)(n0 / n_per_group) * K;
 
-  // all of this wave's W fragments in flight (rows n0 + c16, k-steps w*KS ..)
+  // the X slice's loads first (L2 hits; rows >= M are never read), then all of this wave's W
+  // fragments (rows n0 + c16, k-steps w*KS ..): loads return in order, so X is staged while W streams
+  constexpr int kChunks = 8 * K / 8;       // 16 B chunks of the 8-row slice
+  constexpr int kXPer = kChunks / (kWaves * 64);
+  uint4 xs[kXPer];
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int i = threadIdx.x + u * kWaves * 64;
+    const int m = i / (K / 8), kc = i % (K / 8);
+    const int ms = m < M ? m : M - 1;                  // always a readable row
+    xs[u] = *reinterpret_cast<const uint4*>(X + (int64_t)ms * x_ld + xoff + 8 * kc);
+  }
   const GU32x4v* wp = reinterpret_cast<const GU32x4v*>(reinterpret_cast<uintptr_t>(
       W + (int64_t)(n0 + c16) * K + 32 * (w * KS) + 8 * g));
   uint4 wa[KS];
@@ -122,15 +133,11 @@ rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
     const u32x4v x = wp[4 * u];
     wa[u] = make_uint4(x.x, x.y, x.z, x.w);
   }
-  // X slice -> LDS (rows >= M are never read)
-  constexpr int kChunks = 8 * K / 8;       // 16 B chunks of the 8-row slice
 #pragma unroll
-  for (int u = 0; u < kChunks / (kWaves * 64); ++u) {
+  for (int u = 0; u < kXPer; ++u) {
     const int i = threadIdx.x + u * kWaves * 64;
     const int m = i / (K / 8), kc = i % (K / 8);
-    const int ms = m < M ? m : M - 1;                  // always a readable row
-    const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)ms * x_ld + xoff + 8 * kc);
-    *reinterpret_cast<uint4*>(&sx[m * kXStride + 8 * kc]) = x;
+    *reinterpret_cast<uint4*>(&sx[m * kXStride + 8 * kc]) = xs[u];
   }
   __syncthreads();
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
