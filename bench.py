@@ -83,25 +83,29 @@ def cpu_baseline(layers, n_seq, min_s=10.0, max_s=30.0):
             d["m"] = L.m
         host.append(d)
     ones = np.ones(512)
+
+    def unit(b, d):
+        """One layer-token: indexer + top-k (CSA), attention, projection."""
+        t = d["t"]
+        win = np.stack([d["ring"][b][j % RING] for j in range(t - 127, t + 1)])
+        n = O.n_visible(t, d["m"])
+        if d["csa"]:
+            _, _, qI = O.fp8_quantize_rows(d["qI"][b])
+            sc = O.index_scores(qI, d["wI"][b], d["kI"][b][:n])
+            sel = O.topk_select(sc, d["k"])
+            keys = np.concatenate([d["kv"][b][sel[sel >= 0]], win])
+        else:
+            keys = np.concatenate([d["kv"][b][:n], win])
+        o = O.attend_one(d["q"][b], ones, keys, d["sink"], t, 1.0 / np.sqrt(512))
+        O.grouped_out_proj(o.reshape(1, -1), d["wg"], d["wo"])
+
     t0 = time.perf_counter()
     done = 0
     reps = 0
     while True:
         for b in range(n_seq):
             for d in host:
-                t = d["t"]
-                win = np.stack([d["ring"][b][j % RING] for j in range(t - 127, t + 1)])
-                if d["csa"]:
-                    n = O.n_visible(t, d["m"])
-                    _, _, qI = O.fp8_quantize_rows(d["qI"][b])
-                    sc = O.index_scores(qI, d["wI"][b], d["kI"][b][:n])
-                    sel = O.topk_select(sc, d["k"])
-                    keys = np.concatenate([d["kv"][b][sel[sel >= 0]], win])
-                else:
-                    n = O.n_visible(t, d["m"])
-                    keys = np.concatenate([d["kv"][b][:n], win])
-                o = O.attend_one(d["q"][b], ones, keys, d["sink"], t, 1.0 / np.sqrt(512))
-                O.grouped_out_proj(o.reshape(1, -1), d["wg"], d["wo"])
+                unit(b, d)
                 done += 1
             if time.perf_counter() - t0 > max_s:
                 break
@@ -109,6 +113,19 @@ def cpu_baseline(layers, n_seq, min_s=10.0, max_s=30.0):
         if time.perf_counter() - t0 >= min_s:
             break
     dt = time.perf_counter() - t0
+    # one thread: one CSA and one HCA layer-token of sequence 0 (BLAS limited to a single thread)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            for d in host[:2]:
+                unit(0, d)
+            ts = time.perf_counter() - t1
+        single = {"value": round(2 / ts, 3), "unit": "tokens/s/layer", "cores": 1, "seconds": round(ts, 3),
+                  "sample": "sequence 0 through one CSA and one HCA layer (one layer-token each)"}
+    except ImportError:
+        pass
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     try:
         from threadpoolctl import threadpool_info
@@ -119,7 +136,7 @@ def cpu_baseline(layers, n_seq, min_s=10.0, max_s=30.0):
         pass
     return done / dt, dt, threads, f"{n_seq} of {layers[0].B} sequences x {len(layers)} layers, repeated {reps}x " \
                                    f"({done} layer-tokens: indexer + top-k + attention + projection), caches " \
-                                   f"copied from the device"
+                                   f"copied from the device", single
 
 
 def _event_time_us(fn, reps, graph=False):
@@ -259,7 +276,7 @@ def prefill_row(dev):
         call()
     torch.cuda.synchronize()
     kern = {}
-    for name in ("index_qprep_kernel", "index_score_kernel", "topk_rowwise_kernel", "attend_kernel",
+    for name in ("index_qprep_kernel", "index_score_kernel", "topk_rowwise_kernel", "attend_csa_kernel",
                  "attend_merge_kernel"):
         ms, n = L.timing_read(name)
         if n:
@@ -276,6 +293,159 @@ def prefill_row(dev):
             "ms_per_call": round(total, 3), "kernels": kern, "indexer_flops": flops,
             "indexer_tflops": round(tflops, 1), "indexer_bound": "mfma (fp8)", "fp8_peak_tflops": FP8_PEAK_TFLOPS,
             "indexer_frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+
+
+def _graph_time_ms(fn, n_sets, reps=40):
+    """Average time of fn(i) over reps calls captured into one graph (input set i % n_sets), after warm-up."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(reps):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def hca_decode_64k_row(dev, n_sets=20):
+    """HCA decode at 64K context: 64 sequences, 512 visible entries each + the 128-token window, 64 heads,
+    sink.  One step = hca_attend for every sequence.  20 input sets (cache, ring, queries) rotate so that
+    the Infinity Cache does not serve repeats.  Bytes: every visible entry and window row once (1 KiB),
+    q read and o written once."""
+    import torch
+    import long_context_sparse_17_amd as L
+    import synth
+    B, n_cap, H, W, ring, t = 64, 512, 64, 128, 256, 65536
+    sets = [(synth.device_normal_bf16((B, n_cap, 512), 1.0, 3_000_000 + 10 * i),
+             synth.device_normal_bf16((B, ring, 512), 1.0, 3_000_001 + 10 * i),
+             synth.device_normal_bf16((B, 1, H, 512), 1.28, 3_000_002 + 10 * i)) for i in range(n_sets)]
+    sink = synth.device_normal_f32((H,), 1.0, 3_000_003)
+    gq = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    pos = torch.full((B, 1), t, dtype=torch.int64, device=dev)
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=dev)
+    ws = L.workspace(L.attend_workspace(B, 1, H, n_cap + W))
+
+    def fn(i):
+        cache, win, q = sets[i % n_sets]
+        L.hca_attend(q, gq, cache, win, sink, pos, n_cap=n_cap, m=128, window=W, ring_cap=ring, out=out, ws=ws)
+
+    ms = _graph_time_ms(fn, n_sets)
+    nbytes = B * (n_cap + W) * 1024 + B * H * 512 * 2 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del sets, out, ws
+    torch.cuda.empty_cache()
+    return {"what": "HCA decode, 64 sequences at 64K context (512 entries + 128-token window), 64 heads",
+            "ms_per_step": round(ms, 4), "tokens_per_s_per_layer": round(B / (ms * 1e-3), 1),
+            "input_sets": n_sets, "roofline": {"bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+                                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                               "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def csa_decode_128k_row(dev, n_sets=7):
+    """CSA decode at 128K context (the Flash configuration): 32 sequences, 32768 compressed entries each,
+    fp8 indexer 64 x 128, top-k 512, 64 heads, window 128.  One step = csa_index_topk + csa_attend.
+    7 input sets (caches, keys, queries) rotate.  Bytes: every visible indexer key and scale once (132 B),
+    each selected entry and window row once (1 KiB), the queries, head weights, q and o once."""
+    import torch
+    import long_context_sparse_17_amd as L
+    import synth
+    B, n_cap, H, H_I, dI, k, W, ring, t = 32, 32768, 64, 64, 128, 512, 128, 256, 131072
+    sets = []
+    for i in range(n_sets):
+        base = 4_000_000 + 100 * i
+        sets.append(dict(codes=synth.device_fp8_codes((B, n_cap, dI), base + 1),
+                         scale=(synth.device_normal_f32((B, n_cap), 1.0, base + 2).abs() + 2.0) / 448.0,
+                         cache=synth.device_normal_bf16((B, n_cap, 512), 1.0, base + 3),
+                         win=synth.device_normal_bf16((B, ring, 512), 1.0, base + 4),
+                         q=synth.device_normal_bf16((B, 1, H, 512), 1.28, base + 5),
+                         qi=synth.device_normal_bf16((B, 1, H_I, dI), 1.28, base + 6),
+                         wi=synth.device_normal_bf16((B, 1, H_I), 1.28, base + 7)))
+    sink = synth.device_normal_f32((H,), 1.0, 4_000_099)
+    gq = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    pos = torch.full((B, 1), t, dtype=torch.int64, device=dev)
+    topk = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=dev)
+    ws_i = L.workspace(L.csa_index_topk_workspace(B, 1, n_cap, k), zeroed=True)
+    ws_a = L.workspace(L.attend_workspace(B, 1, H, k + W))
+
+    def fn(i):
+        d = sets[i % n_sets]
+        L.csa_index_topk(d["qi"], d["wi"], d["codes"], d["scale"], pos, n_cap=n_cap, m=4, k=k, topk_idx=topk,
+                         ws=ws_i)
+        L.csa_attend(d["q"], gq, d["cache"], topk, d["win"], sink, pos, window=W, ring_cap=ring, out=out, ws=ws_a)
+
+    ms = _graph_time_ms(fn, n_sets)
+    nbytes = B * n_cap * (dI + 4) + B * H_I * (dI * 2 + 2) + B * (k + W) * 1024 + B * H * 512 * 2 * 2 + B * k * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del sets, out, ws_i, ws_a, topk
+    torch.cuda.empty_cache()
+    return {"what": "CSA decode (Flash), 32 sequences at 128K context: fp8 indexer 64x128 over 32768 entries, "
+                    "top-k 512, attention over 512 entries + 128-token window, 64 heads",
+            "ms_per_step": round(ms, 4), "tokens_per_s_per_layer": round(B / (ms * 1e-3), 1),
+            "input_sets": n_sets, "roofline": {"bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+                                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                               "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def csa_prefill_2k_row(dev):
+    """CSA prefill of 2048 tokens (one sequence, 8 heads, indexer 8 x 64 with bf16 keys, top-k 128, sink 0):
+    the whole path from raw per-token vectors: block compression with the indexer keys, the window fill,
+    the indexer + top-k for all 2048 queries and the attention.  Inputs: N(0,1) hidden states (d = 1024)
+    projected by N(0, 0.02^2) weights, drawn on the device.  tokens/s = 2048 / time of the path."""
+    import torch
+    import long_context_sparse_17_amd as L
+    import synth
+    T, d, H, H_I, dI, k, W = 2048, 1024, 8, 8, 64, 128, 128
+    h = synth.device_normal_f32((T, d), 1.0, 5_000_001)
+    proj = lambda n, sd: (h @ synth.device_normal_f32((d, n), 0.02, sd))  # noqa: E731
+    kv = proj(512, 5_000_002).to(torch.bfloat16).view(1, T, 512)
+    ks = proj(1, 5_000_003).view(1, T).contiguous()
+    q = proj(H * 512, 5_000_004).to(torch.bfloat16).view(1, T, H, 512)
+    qi = proj(H_I * dI, 5_000_005).to(torch.bfloat16).view(1, T, H_I, dI)
+    ik = proj(dI, 5_000_006).to(torch.bfloat16).view(1, T, dI)
+    iks = proj(1, 5_000_007).view(1, T).contiguous()
+    wi = proj(H_I, 5_000_008).to(torch.bfloat16).view(1, T, H_I)
+    sink = torch.zeros(H, dtype=torch.float32, device=dev)
+    g = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    n_cap = T // 4
+    kv_cache = torch.zeros((1, n_cap, 512), dtype=torch.bfloat16, device=dev)
+    ik_cache = torch.zeros((1, n_cap, dI), dtype=torch.bfloat16, device=dev)
+    win = torch.zeros((1, T, 512), dtype=torch.bfloat16, device=dev)
+    pos = torch.arange(T, dtype=torch.int64, device=dev).view(1, T)
+    topk = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, T, H, 512), dtype=torch.bfloat16, device=dev)
+    ws_i = L.workspace(L.csa_index_topk_workspace(1, T, n_cap, k), zeroed=True)
+    ws_a = L.workspace(L.attend_workspace(1, T, H, k + W))
+
+    def fn(i):
+        L.csa_compress_kv(kv, ks, ik, iks, tok0=0, blk_begin=0, n_blk=n_cap, m=4, overlap=4, gamma_kv=g,
+                          kv_out=kv_cache, ik_out=ik_cache, ik_fp8=False)
+        L.hca_compress_kv(kv, ks, tok0=0, blk_begin=0, n_blk=T, m=1, gamma_kv=g, kv_out=win)
+        L.csa_index_topk(qi, wi, ik_cache, None, pos, n_cap=n_cap, m=4, k=k, topk_idx=topk, ws=ws_i)
+        L.csa_attend(q, g, kv_cache, topk, win, sink, pos, window=W, ring_cap=0, out=out, ws=ws_a)
+
+    ms = _graph_time_ms(fn, 1, reps=20)
+    pairs = sum(t // 4 for t in range(T))
+    sel = sum(min(k, t // 4) for t in range(T))
+    winkeys = sum(min(W, t + 1) for t in range(T))
+    flops = 2.0 * pairs * H_I * dI + 4.0 * 512 * H * (sel + winkeys)
+    del h, kv, ks, q, qi, ik, iks, wi, kv_cache, ik_cache, win, topk, out, ws_i, ws_a
+    torch.cuda.empty_cache()
+    return {"what": "CSA prefill, 2048 tokens, 8 heads, indexer 8x64 bf16, top-k 128 (compress, window, "
+                    "indexer + top-k, attention)", "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "flops": flops,
+            "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2), "bound": "latency (small)"}
 
 
 def time_stack(layers, steps, warmup, use_graph, ref_y, step=None, outputs=None):
@@ -395,6 +565,7 @@ def main():
     ap.add_argument("--no-fp8kv", action="store_true", help="skip the fp8 K=V variant of the step")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained (projections + residual) variant")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 1M chunked-prefill measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the HCA 64K, CSA 128K and 2K prefill rows")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -440,12 +611,27 @@ def main():
     torch.cuda.synchronize()
     kernels = {}
     for name in ("index_score_kernel", "topk_filter_kernel", "topk_final_kernel",
-                 "attend_kernel", "attend_merge_kernel", "out_proj_group_kernel", "out_proj_out_kernel",
-                 "compress_kernel", "decode_append_kernel", "input_proj_kernel"):
+                 "attend_csa_kernel", "attend_hca_kernel", "attend_merge_kernel", "out_proj_group_kernel",
+                 "out_proj_out_kernel", "compress_kernel", "decode_append_kernel", "input_proj_kernel"):
         ms, n = L.timing_read(name)
         if n:
             kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}
     L.timing_enable(False)
+    # attention against the HBM roofline, per layer type (bytes of one launch: the layer's keys, q, o)
+    attention = {}
+    for layer in layers[:2]:
+        kind = "csa" if isinstance(layer, CsaDecodeLayer) else "hca"
+        name = f"attend_{kind}_kernel"
+        if name in kernels:
+            nb = layer.bytes_per_step()["attend"]
+            us = kernels[name]["avg_us"]
+            gb = nb / (us * 1e-6) / 1e9
+            attention[kind] = {"kernel": name, "bytes_per_launch": nb, "avg_us": us, "achieved": round(gb, 1),
+                               "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBS, 4)}
+            if "attend_merge_kernel" in kernels:
+                usm = us + kernels["attend_merge_kernel"]["avg_us"]
+                attention[kind]["with_merge_us"] = round(usm, 3)
+                attention[kind]["with_merge_frac"] = round(nb / (usm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     csa = [layer for layer in layers if isinstance(layer, CsaDecodeLayer)]
     idx_bytes = csa[0].bytes_per_step()["index"]             # per launch: every visible fp8 key + scale once
@@ -483,13 +669,17 @@ def main():
     if not args.no_chain:
         next_rows["chained_stack"] = chained_stack_row(args, dev)
     prefill = None if args.no_prefill else prefill_row(dev)
+    configs = None
+    if not args.no_configs:
+        configs = {"hca_decode_64k": hca_decode_64k_row(dev), "csa_decode_128k": csa_decode_128k_row(dev),
+                   "csa_prefill_2k": csa_prefill_2k_row(dev)}
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None
     if not args.no_cpu:
-        rate, secs, threads, sample = cpu_baseline(layers, args.cpu_seqs)
+        rate, secs, threads, sample, single = cpu_baseline(layers, args.cpu_seqs)
         cpu = {"value": round(rate, 3), "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
-               "sample": sample, "seconds": round(secs, 2)}
+               "sample": sample, "seconds": round(secs, 2), "single_thread": single}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1, "steps": args.steps,
@@ -504,9 +694,12 @@ def main():
         "step_hbm": {"bytes": step_bytes, "achieved_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "flops": step_flops},
-        "kernels": kernels, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
+        "kernels_event_timed": kernels,
+        "kernels_note": "eager launches, each bracketed by HIP events on its stream (the events add about 2 us "
+                        "per launch): per-kernel durations, not a breakdown of the graph-replayed step",
+        "attention_roofline": attention, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
         "mfma_gemm_bf16_tflops": round(mfma_tflops, 1), "next": next_rows, "prefill_1m": prefill,
-        "cpu_baseline": cpu,
+        "configs": configs, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

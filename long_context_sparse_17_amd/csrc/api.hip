@@ -320,6 +320,7 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
   if (c != LCS_HEAD_DIM || H > LCS_MAX_HEADS) return LCS_ERR_UNSUPPORTED;
   if ((int64_t)B * Tq > 65535) return LCS_ERR_UNSUPPORTED;
   if (max_keys >= ((int64_t)1 << 31)) return LCS_ERR_UNSUPPORTED;
+  if (!lcs::attend_launchable(B, Tq, H, max_keys, topk_idx != nullptr)) return LCS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < lcs::attend_workspace(B, Tq, H, max_keys)) return LCS_ERR_WORKSPACE;
   if (!aligned16(ws)) return LCS_ERR_ARG;
   lcs::AttendArgs a;

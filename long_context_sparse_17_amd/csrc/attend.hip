@@ -59,6 +59,7 @@ struct AttnK {
   uint16_t* out; uint16_t* part_o; float* part_ml;
   int nsplit, keys_per_split;
   int halves;                          // HB = 2: workgroups per (query, split), 1 (H <= 32) or 2
+  int R;                               // query rows
 };
 
 // LDS row of tile key (block kb, row r16 of the 16x16 MFMA block) in a slice: the key itself.  With
@@ -93,16 +94,19 @@ attend_kernel(AttnK a) {
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int g = lane >> 4, c16 = lane & 15;
-  const int64_t r = blockIdx.y;
-  const int64_t b = r / a.Tq;
-  // HB = 2 with two halves: x = 16 j + 8 h + i is split 8 j + i, head half h, so the two halves of a
-  // split are 8 workgroups apart in dispatch order (the same XCD); splits past nsplit are padding
+  // Grid: (split, row) in (x, y); with two head halves a flat x = 16 j + 8 h + i takes (row, split)
+  // number 8 j + i = row * nsplit + split and head half h, so the two halves of a split are 8
+  // workgroups apart in dispatch order (the same XCD); numbers past the last are padding (< 16)
+  int64_t r = blockIdx.y;
   int split = blockIdx.x, hh = 0;
   if (HB == 2 && a.halves == 2) {
-    split = 8 * (int)(blockIdx.x >> 4) + (int)(blockIdx.x & 7);
+    const int64_t u = 8 * (int64_t)(blockIdx.x >> 4) + (blockIdx.x & 7);
+    if (u >= (int64_t)a.R * a.nsplit) return;      // uniform
+    r = u / a.nsplit;
+    split = (int)(u % a.nsplit);
     hh = (int)(blockIdx.x >> 3) & 1;
   }
-  if (split >= a.nsplit) return;          // uniform
+  const int64_t b = r / a.Tq;
   const int hq = HB == 4 ? w : (w & 1);   // head block this wave scores
   const int kbq = HB == 4 ? 0 : (w >> 1); // HB = 2: the key block of each tile it scores
   const int head0 = 32 * hh;              // first head of the workgroup
@@ -710,15 +714,16 @@ int keys_per_split(int R, int halves, int64_t max_keys) {
   return (int)(tps * kTile);
 }
 
-// The layout a call runs with.  Selected entries (CSA): HB = 2, whose halved split partials cut the
-// epilogue and merge that dominate a short key list.  All visible entries (HCA): HB = 4, whose
-// streaming loop keeps twice the unique bytes in flight per CU.
+// The layout a call runs with.  Selected entries (CSA) of few query rows (decode): HB = 2, whose
+// halved split partials cut the epilogue and merge that dominate a short key list.  All visible
+// entries (HCA) and many rows (prefill, one split per row): HB = 4, whose loop keeps twice the unique
+// bytes in flight per CU and reads each tile once.
 struct AttendPlan {
   int hb, halves, keys_per_split, nsplit;
 };
 AttendPlan attend_plan(int R, int H, int64_t max_keys, bool list) {
   AttendPlan p;
-  p.hb = list ? 2 : 4;
+  p.hb = list && R < 128 ? 2 : 4;
   p.halves = p.hb == 2 && H > 32 ? 2 : 1;
   p.keys_per_split = p.hb == 2 ? keys_per_split<2>(R, p.halves, max_keys) : keys_per_split<4>(R, 1, max_keys);
   p.nsplit = max_keys > 0 ? (int)((max_keys + p.keys_per_split - 1) / p.keys_per_split) : 1;
@@ -740,10 +745,20 @@ size_t attend_workspace(int B, int Tq, int H, int64_t max_keys) {
   return al256((size_t)R * nsplit * H * kHeadDim * 2) + al256((size_t)R * nsplit * H * 2 * 4);
 }
 
+// Every grid the call would launch fits the HIP limits (the flat grid of two head halves: x < 2^31).
+bool attend_launchable(int B, int Tq, int H, int64_t max_keys, bool list) {
+  const int R = B * Tq;
+  const AttendPlan p = attend_plan(R, H, max_keys, list);
+  if (p.hb == 2 && p.halves == 2) return 16 * (((int64_t)R * p.nsplit + 7) / 8) < ((int64_t)1 << 31);
+  return p.nsplit < ((int64_t)1 << 31);
+}
+
 template <bool LIST, bool F8>
 void launch_attend_kernel(const AttnK& a, int hb, dim3 grid, hipStream_t st) {
-  if (hb == 2) LCS_LAUNCH("attend_kernel", (attend_kernel<LIST, F8, 2>), grid, dim3(256), 0, st, a);
-  else LCS_LAUNCH("attend_kernel", (attend_kernel<LIST, F8, 4>), grid, dim3(256), 0, st, a);
+  // timing labels: selected-entry lists (CSA) and dense visible ranges (HCA) apart
+  const char* name = LIST ? "attend_csa_kernel" : "attend_hca_kernel";
+  if (hb == 2) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2>), grid, dim3(256), 0, st, a);
+  else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4>), grid, dim3(256), 0, st, a);
 }
 
 int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
@@ -761,10 +776,12 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.part_o = static_cast<uint16_t*>(x.ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(x.ws) +
                                        al256((size_t)R * a.nsplit * x.H * kHeadDim * 2));
-  // HB = 2 with two halves: 16 workgroups per 8 splits (the two halves 8 apart), padded to a multiple
-  // of 16 (the padding returns at once)
-  const unsigned gx = p.hb == 2 && p.halves == 2 ? (unsigned)(16 * ((a.nsplit + 7) / 8)) : (unsigned)a.nsplit;
-  const dim3 grid(gx, (unsigned)R);
+  // HB = 2 with two halves: a flat grid, 16 workgroups per 8 (row, split) numbers (the two halves 8
+  // apart), padded to a multiple of 16 (the padding returns at once)
+  a.R = R;
+  const bool flat = p.hb == 2 && p.halves == 2;
+  const dim3 grid = flat ? dim3((unsigned)(16 * (((int64_t)R * a.nsplit + 7) / 8)), 1u)
+                         : dim3((unsigned)a.nsplit, (unsigned)R);
   a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
   const bool f8 = x.kv8 != nullptr;
   if (x.topk) {

@@ -71,6 +71,7 @@ struct AttendArgs {
   uint16_t* out; void* ws; size_t ws_bytes;
 };
 size_t attend_workspace(int B, int Tq, int H, int64_t max_keys);
+bool attend_launchable(int B, int Tq, int H, int64_t max_keys, bool list);
 int launch_attend(const AttendArgs& a, int64_t max_keys, hipStream_t stream);
 
 struct OutProjArgs {
