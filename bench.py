@@ -139,6 +139,70 @@ def cpu_baseline(layers, n_seq, min_s=10.0, max_s=30.0):
                                    f"copied from the device", single
 
 
+def fp8_indexer_check(dev, B=2, t=4096, k=256, cfg=900):
+    """Part of the oracle leg of the benchmark.  How much the fp8 indexer moves the attention output (the reading that fp8 keys and queries keep
+    the method intact): one CSA decode query per sequence at token t, from raw seeded per-token
+    vectors.  The GPU path (compression with fp8 indexer keys, window fill, indexer + top-k,
+    attention) and the oracle with the fp8 indexer and with an exact one (no quantisation), on the
+    same raw inputs.  Reports the rel-L2 distances and the share of the exact top-k the GPU keeps."""
+    import numpy as np
+    import torch
+    import long_context_sparse_17_amd as L
+    import oracle as O
+    import synth
+    H, H_I, dI, W, m, ov, ring = 64, 64, 128, 128, 4, 4, 256
+    T1 = t + 1
+    s = 1.28
+    kv = synth.normal_bf16((B, T1, 512), s, cfg, 1)
+    ks = synth.normal_f32((B, T1), s, cfg, 2)
+    ik = synth.normal_bf16((B, T1, dI), s, cfg, 3)
+    iks = synth.normal_f32((B, T1), s, cfg, 4)
+    q = synth.normal_bf16((B, 1, H, 512), s, cfg, 5)
+    qi = synth.normal_bf16((B, 1, H_I, dI), s, cfg, 6)
+    wi = synth.normal_bf16((B, 1, H_I), s, cfg, 7)
+    sink = synth.normal_f32((H,), 1.0, cfg, 8)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)  # noqa: E731
+    n_cap = t // m
+    g = torch.ones(512, dtype=torch.bfloat16, device=dev)
+    kv_cache = torch.zeros((B, n_cap, 512), dtype=torch.bfloat16, device=dev)
+    ik_cache = torch.zeros((B, n_cap, dI), dtype=torch.uint8, device=dev)
+    ik_sc = torch.zeros((B, n_cap), dtype=torch.float32, device=dev)
+    L.csa_compress_kv(bf(kv), f32(ks), bf(ik), f32(iks), tok0=0, blk_begin=0, n_blk=n_cap, m=m, overlap=ov, gamma_kv=g,
+                      kv_out=kv_cache, ik_out=ik_cache, ik_scale=ik_sc, ik_fp8=True)
+    win = torch.zeros((B, ring, 512), dtype=torch.bfloat16, device=dev)
+    w0 = t - W + 1
+    L.hca_compress_kv(bf(kv[:, w0:]), f32(ks[:, w0:]), tok0=w0, blk_begin=w0, n_blk=T1 - w0, m=1, gamma_kv=g,
+                      kv_out=win, ring_cap=ring)
+    pos = torch.full((B, 1), t, dtype=torch.int64, device=dev)
+    topk = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    L.csa_index_topk(bf(qi), bf(wi), ik_cache, ik_sc, pos, n_cap=n_cap, m=m, k=k, topk_idx=topk)
+    out = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=dev)
+    L.csa_attend(bf(q), g, kv_cache, topk, win, f32(sink), pos, window=W, ring_cap=ring, out=out)
+    torch.cuda.synchronize()
+    got = synth.bf16_bits_to_f64(out.cpu().view(torch.int16).numpy().view(np.uint16))
+    gsel = topk.cpu().numpy()
+    f = synth.bf16_bits_to_f64
+    rl = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))  # noqa: E731
+    r = {"oracle_fp8_vs_exact": 0.0, "gpu_vs_exact": 0.0, "gpu_vs_oracle_fp8": 0.0, "exact_topk_kept": 1.0}
+    for b in range(B):
+        args = (f(kv[b]), ks[b].astype(np.float64), f(ik[b]), iks[b].astype(np.float64), f(q[b]), f(qi[b]),
+                f(wi[b]), sink.astype(np.float64), [t])
+        o8, _, _ = O.csa_layer(*args, m=m, ov=ov, W=W, k=k, fp8=True)
+        oe, sel_e, _ = O.csa_layer(*args, m=m, ov=ov, W=W, k=k, fp8=False)
+        r["oracle_fp8_vs_exact"] = max(r["oracle_fp8_vs_exact"], rl(o8[0], oe[0]))
+        r["gpu_vs_exact"] = max(r["gpu_vs_exact"], rl(got[b, 0], oe[0]))
+        r["gpu_vs_oracle_fp8"] = max(r["gpu_vs_oracle_fp8"], rl(got[b, 0], o8[0]))
+        se = set(int(x) for x in sel_e[0] if x >= 0)
+        sg = set(int(x) for x in gsel[b, 0] if x >= 0)
+        r["exact_topk_kept"] = min(r["exact_topk_kept"], len(se & sg) / max(1, len(se)))
+    r = {key: round(v, 5) for key, v in r.items()}
+    r["what"] = (f"CSA decode, {B} sequences at t = {t} ({n_cap} entries), top-k {k}, raw seeded tokens: rel-L2 of "
+                 "the attention output; the oracle with the fp8 indexer against the oracle with an exact one, "
+                 "and the GPU against both")
+    return r
+
+
 def _event_time_us(fn, reps, graph=False):
     """Average duration of fn() on the current stream, HIP events around reps back-to-back calls.
     graph=True captures the reps calls into one graph first, so host launch costs do not count."""
@@ -676,10 +740,12 @@ def main():
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None
+    fp8_check = None
     if not args.no_cpu:
         rate, secs, threads, sample, single = cpu_baseline(layers, args.cpu_seqs)
         cpu = {"value": round(rate, 3), "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
                "sample": sample, "seconds": round(secs, 2), "single_thread": single}
+        fp8_check = fp8_indexer_check(dev)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1, "steps": args.steps,
@@ -699,7 +765,7 @@ def main():
                         "per launch): per-kernel durations, not a breakdown of the graph-replayed step",
         "attention_roofline": attention, "kernel_gbs": per_kernel_gbs, "hbm_copy_gbs": round(copy_gbs, 1),
         "mfma_gemm_bf16_tflops": round(mfma_tflops, 1), "next": next_rows, "prefill_1m": prefill,
-        "configs": configs, "cpu_baseline": cpu,
+        "configs": configs, "fp8_indexer_vs_exact": fp8_check, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
