@@ -8,7 +8,8 @@
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers owned by the caller.  The library allocates nothing on the
- *     device and keeps no state between calls (the optional timing facility at the end aside).
+ *     device and keeps no state between calls, with two exceptions: grouped_out_proj_noalloc's
+ *     static scratch array and the optional timing facility at the end.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and runs asynchronously;
  *     faults during execution surface at the caller's next synchronisation.
  *   - bf16 = uint16_t bit pattern; fp8 = uint8_t OCP E4M3FN; positions are int64 token indices.
@@ -316,6 +317,11 @@ int input_proj(const uint16_t* h, int M, int d, const uint16_t* w_in, int n_rows
  * by the library is bracketed by two hipEvents recorded on the launch stream; lcs_timing_read
  * synchronises those events and returns the summed duration and launch count of the kernels whose
  * name contains `name`.  Not for use under stream capture.  lcs_timing_enable(0) drops the events.
+ * This is the part of the ABI that keeps process-wide state (the recorded events, under a mutex)
+ * and synchronises with the device (lcs_timing_read waits for the events it reads); it exists so a
+ * benchmark can time each kernel on the stream it was launched on.  The events are created with
+ * hipEventDisableSystemFence, so recording one adds no cache write-back or invalidation between
+ * the launches it brackets.  While disabled, a launch pays one relaxed atomic load.
  */
 int lcs_timing_enable(int on);
 int lcs_timing_read(const char* name, double* total_ms, int64_t* launches);

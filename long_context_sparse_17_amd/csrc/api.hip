@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -22,15 +23,17 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // ------------------------------------------------------------------------------ timing facility
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
   struct Rec { std::string name; hipEvent_t a, b; };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
   hipEvent_t pending = nullptr;
   hipEvent_t get() {
     if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    // Timing-only events: no system-scope fence when one is recorded, so recording it neither
+    // writes back nor invalidates the caches between the launches it brackets.
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
 };
@@ -50,14 +53,14 @@ RopeFreq rope_freq(float theta) {
 
 void timing_before(const char*, hipStream_t s) {
   Timing& t = timing();
-  if (!t.on) return;
+  if (!t.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(t.mu);
   t.pending = t.get();
   if (t.pending) hipEventRecord(t.pending, s);
 }
 void timing_after(const char* name, hipStream_t s) {
   Timing& t = timing();
-  if (!t.on) return;
+  if (!t.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(t.mu);
   if (!t.pending) return;
   hipEvent_t b = t.get();
