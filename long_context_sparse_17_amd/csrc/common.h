@@ -126,6 +126,21 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Inclusive prefix sum over the 64 lanes of a fully active wave: DPP row_shr steps of 1, 2, 4, 8
+// inside each row of 16 lanes (lanes shifted in from outside the row read 0), then the totals of
+// the lower rows, read with readlane, added per row.  No LDS round trip.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row > 0 ? t0 : 0u) + (row > 1 ? t1 : 0u) + (row > 2 ? t2 : 0u);
+}
+
 }  // namespace lcs
 
 // ----------------------------------------------------------------------------------- host side

@@ -767,12 +767,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
 // Block-wide exclusive prefix sum over the 256 threads; *total receives the sum.  s_w: 4 words.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_w, uint32_t* total) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) s_w[wave] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -847,9 +842,9 @@ struct FinalShared {
   int remaining, done, shift, T2, above2;
 };
 
-// Row r's selection (nv visible entries).
-__device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int64_t r, int64_t nv,
-                                             const unsigned long long* __restrict__ comb,
+// Row r's selection (the row's visible entries: n_visible of its query position).
+__device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int64_t r, const int64_t* q_pos, int m,
+                                             int64_t n_cap, const unsigned long long* __restrict__ comb,
                                              const uint2* __restrict__ counts, const uint32_t* __restrict__ hist,
                                              int64_t nsp, int nchunk, int k, const float* __restrict__ scores,
                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
@@ -870,6 +865,30 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
   int32_t* out = topk_idx + r * k;
   float* out_s = topk_score ? topk_score + r * k : nullptr;
   const float* srow = scores + r * nsp;
+  const unsigned long long* lrow = comb + r * nsp;
+
+  // ---- one round trip, issued with the query position's load rather than after it (every
+  //      address is clamped into the row's regions, not to its visible part): the per-chunk counts
+  //      and, speculatively, the first 64 list entries of each of the first 64 chunks (wave w:
+  //      chunks w, w + 4, ...), which usually hold the whole list ----
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  constexpr int kHeadChunks = kWaves * 16;
+  unsigned long long vh[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = min(wave + kWaves * u, nchunk - 1);
+    vh[u] = lrow[min((int64_t)c * kFilterChunk + lane, nsp - 1)];
+  }
+  const uint32_t* h2 = hist + r * kHistRow + kBins;
+  const uint4 h2a = *reinterpret_cast<const uint4*>(h2 + tid * 8);
+  const uint4 h2b = *reinterpret_cast<const uint4*>(h2 + tid * 8 + 4);
+  constexpr int kPerT = kMaxDecodeChunks / kSelThreads;   // 8
+  uint2 ccv[kPerT];
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int c = tid * kPerT + u;
+    ccv[u] = counts[r * nchunk + (c < nchunk ? c : 0)];
+  }
   if (nv <= k) {                                    // every visible entry, ascending
     for (int64_t i = tid; i < k; i += kSelThreads) {
       out[i] = i < nv ? (int32_t)i : -1;
@@ -878,31 +897,15 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
     return;
   }
   const int nch = (int)((nv + kFilterChunk - 1) / kFilterChunk);
-  const unsigned long long* lrow = comb + r * nsp;
-
-  // ---- one round trip: the per-chunk counts and, speculatively, the first 64 list entries of each
-  //      of the first 64 chunks (wave w: chunks w, w + 4, ...), which usually hold the whole list ----
-  constexpr int kHeadChunks = kWaves * 16;
   const bool heads = nch <= kHeadChunks;
-  unsigned long long vh[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int c = min(wave + kWaves * u, nch - 1);
-    vh[u] = lrow[min((int64_t)c * kFilterChunk + lane, nv - 1)];
-  }
-  const uint32_t* h2 = hist + r * kHistRow + kBins;
-  const uint4 h2a = *reinterpret_cast<const uint4*>(h2 + tid * 8);
-  const uint4 h2b = *reinterpret_cast<const uint4*>(h2 + tid * 8 + 4);
-  constexpr int kPerT = kMaxDecodeChunks / kSelThreads;   // 8
   uint32_t kc[kPerT];
   uint32_t ksum = 0, asum = 0;
 #pragma unroll
   for (int u = 0; u < kPerT; ++u) {
     const int c = tid * kPerT + u;
-    const uint2 cc = counts[r * nchunk + (c < nch ? c : 0)];
-    kc[u] = c < nch ? cc.x : 0u;
+    kc[u] = c < nch ? ccv[u].x : 0u;
     ksum += kc[u];
-    asum += c < nch ? cc.y : 0u;
+    asum += c < nch ? ccv[u].y : 0u;
   }
   uint32_t total_keep, total_above;
   uint32_t off = block_excl_scan(ksum, s_w, &total_keep);
@@ -1008,12 +1011,7 @@ __device__ __forceinline__ void final_select(FinalShared& sh, uint32_t* s_w, int
         uint32_t lsum = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) { c[u] = s_h[255 - 4 * tid - u]; lsum += c[u]; }
-        uint32_t incl = lsum;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t v = __shfl_up(incl, o, kWave);
-          if (tid >= o) incl += v;
-        }
+        const uint32_t incl = wave_incl_scan(lsum);
         const uint32_t rem = (uint32_t)s_remaining;
         const uint64_t hit = __ballot(incl >= rem);
         const int first = __ffsll((unsigned long long)hit) - 1;
@@ -1127,13 +1125,17 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
   __shared__ int sT, sAbove;
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.y;
-  const int64_t nv = n_visible(q_pos, r, m, n_cap);
   const int64_t c0 = (int64_t)blockIdx.x * kFilterChunk;
-  if (c0 >= nv) return;                                      // uniform
   constexpr int kPer = kFilterChunk / kSelThreads;           // 16 consecutive entries per thread
   const int64_t e0 = c0 + (int64_t)kPer * tid;
   const float* srow = scores + r * nsp;
-  const int64_t q4max = (nv - 1) >> 2;                       // last readable float4 (nsp is a multiple of 64)
+  // the score loads go out with the query position's load, not after it: they are clamped into the
+  // row's region (nsp is a multiple of 64), and entries past the visible ones are masked below
+  const int64_t q4max = (nsp >> 2) - 1;
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const uint32_t* hrow = hist + r * kHistRow;               // the row histogram, first back
+  const uint4 ha = *reinterpret_cast<const uint4*>(hrow + tid * 8);
+  const uint4 hb = *reinterpret_cast<const uint4*>(hrow + tid * 8 + 4);
   uint32_t keys[kPer];
 #pragma unroll
   for (int q = 0; q < kPer / 4; ++q) {                       // clamped, unconditional loads
@@ -1144,9 +1146,13 @@ topk_filter_kernel(const float* __restrict__ scores, uint32_t* __restrict__ hist
     keys[4 * q + 2] = float_key(x.z);
     keys[4 * q + 3] = float_key(x.w);
   }
+  if (c0 >= nv) return;                                      // uniform
   if (tid == 0) { sT = -1; sAbove = 0; }
   __syncthreads();
-  if (nv > k) find_threshold(hist + r * kHistRow, k, &sT, &sAbove, s_w);
+  if (nv > k) {
+    const uint32_t loc[8] = {ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
+    find_threshold_bins(loc, k, &sT, &sAbove, s_w);
+  }
   const int T = sT;
   uint32_t keep = 0, above = 0;
 #pragma unroll
@@ -1184,8 +1190,7 @@ topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __re
   __shared__ FinalShared sh;
   __shared__ uint32_t s_w[kSelThreads / kWave];
   const int64_t r = blockIdx.x;
-  final_select(sh, s_w, r, n_visible(q_pos, r, m, n_cap), comb, counts, hist, nsp, nchunk, k, scores, topk_idx,
-               topk_score);
+  final_select(sh, s_w, r, q_pos, m, n_cap, comb, counts, hist, nsp, nchunk, k, scores, topk_idx, topk_score);
   __syncthreads();                                // every read of the level-2 histogram is done
   uint4* h = reinterpret_cast<uint4*>(hist + r * kHistRow);
   for (int i = threadIdx.x; i < kHistRow / 4; i += kSelThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -1267,12 +1272,7 @@ __device__ __forceinline__ void refine_candidates(const unsigned long long* cand
       uint32_t lsum = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) { c[u] = s.h256[255 - 4 * tid - u]; lsum += c[u]; }
-      uint32_t incl = lsum;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += v;
-      }
+      const uint32_t incl = wave_incl_scan(lsum);
       const uint32_t rem = (uint32_t)s.remaining;
       const uint64_t hit = __ballot(incl >= rem);
       const int first = __ffsll((unsigned long long)hit) - 1;
@@ -1346,12 +1346,7 @@ __device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv,
     uint32_t cnt = 0;
 #pragma unroll
     for (int q = 0; q < kWordsPerThread; ++q) cnt += (uint32_t)__popc(bits[q]);
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t v = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += v;
-    }
+    const uint32_t incl = wave_incl_scan(cnt);
     if (lane == kWave - 1) s.wtot[wave] = incl;
     __syncthreads();
     uint32_t pos = incl - cnt;
@@ -1472,12 +1467,7 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
         for (int i = 0; i < 16; ++i) keep |= (eb + i < nv && keys[i] >= thr ? 1u : 0u) << i;
         if (__ballot(keep != 0u) == 0ull) continue;           // wave-uniform: nothing kept
         const uint32_t c = (uint32_t)__popc(keep);
-        uint32_t incl = c;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t t = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += t;
-        }
+        const uint32_t incl = wave_incl_scan(c);
         uint32_t base = 0;
         if (lane == kWave - 1) base = (uint32_t)atomicAdd(&sCand, (int)incl);
         base = __shfl(base, kWave - 1, kWave) + incl - c;
