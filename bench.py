@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA+HCA attention decode tokens/s/layer at 1M ctx; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0      # dense fp8 matrix-core peak (published)
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak (published)
 
 
 def log(*a):
@@ -327,10 +328,16 @@ def prefill_row(dev):
     out = torch.empty((1, Tq, H, 512), dtype=torch.bfloat16, device=dev)
     ws_i = L.workspace(L.csa_index_topk_workspace(1, Tq, n_cap, k), zeroed=True)
     ws_a = L.workspace(L.attend_workspace(1, Tq, H, k + W))
+    g, d_g, d = 8, 1024, 4096
+    w_g = synth.device_normal_bf16((g, d_g, H * 512 // g), 0.02, 49)
+    w_o = synth.device_normal_bf16((d, g * d_g), 0.02, 50)
+    y = torch.empty((Tq, d), dtype=torch.bfloat16, device=dev)
+    ws_p = L.workspace(L.grouped_out_proj_workspace(Tq, g, d_g))
 
     def call():
         L.csa_index_topk(qi, wi, codes, scale, pos, n_cap=n_cap, m=4, k=k, topk_idx=topk, ws=ws_i)
         L.csa_attend(q, gq, cache, topk, win, sink, pos, window=W, ring_cap=ring, out=out, ws=ws_a)
+        L.grouped_out_proj(out.view(Tq, H * 512), w_g, w_o, H=H, y=y, ws=ws_p)
 
     call()
     torch.cuda.synchronize()
@@ -341,7 +348,7 @@ def prefill_row(dev):
     torch.cuda.synchronize()
     kern = {}
     for name in ("index_qprep_kernel", "index_score_kernel", "topk_rowwise_kernel", "attend_csa_kernel",
-                 "attend_merge_kernel"):
+                 "attend_merge_kernel", "out_proj_group_kernel", "out_proj_out_kernel"):
         ms, n = L.timing_read(name)
         if n:
             kern[name] = {"avg_ms": round(ms / n, 4), "launches": n // reps}
@@ -351,12 +358,23 @@ def prefill_row(dev):
     idx_ms = kern["index_score_kernel"]["avg_ms"]
     tflops = flops / (idx_ms * 1e-3) / 1e12
     total = sum(v["avg_ms"] * v["launches"] for v in kern.values())
-    del codes, scale, cache, win, q, qi, wi, topk, out, ws_i, ws_a
+    # attention: 4 * 512 flop per head and key (QK^T and PV), keys = the k selected + the 128-token window
+    att_flops = 4.0 * 512 * H * Tq * (k + W)
+    att_ms = kern["attend_csa_kernel"]["avg_ms"]
+    # grouped projection: 2 flop per weight and row, both stages
+    proj_flops = 2.0 * Tq * (g * d_g * (H * 512 // g) + d * g * d_g)
+    proj_ms = kern["out_proj_group_kernel"]["avg_ms"] + kern["out_proj_out_kernel"]["avg_ms"]
+    del codes, scale, cache, win, q, qi, wi, topk, out, ws_i, ws_a, w_g, w_o, y, ws_p
     torch.cuda.empty_cache()
-    return {"what": "CSA chunked prefill, 4096 queries x 262144 entries (1M tokens, m = 4), top-k 1024, 64 heads",
+    return {"what": "CSA chunked prefill, 4096 queries x 262144 entries (1M tokens, m = 4), top-k 1024, 64 heads, "
+                    "then the grouped output projection of the 4096 rows (8 x 1024 -> 4096)",
             "ms_per_call": round(total, 3), "kernels": kern, "indexer_flops": flops,
             "indexer_tflops": round(tflops, 1), "indexer_bound": "mfma (fp8)", "fp8_peak_tflops": FP8_PEAK_TFLOPS,
-            "indexer_frac": round(tflops / FP8_PEAK_TFLOPS, 4)}
+            "indexer_frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "attention_tflops": round(att_flops / (att_ms * 1e-3) / 1e12, 1),
+            "attention_frac": round(att_flops / (att_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "out_proj_ms": round(proj_ms, 4), "out_proj_tflops": round(proj_flops / (proj_ms * 1e-3) / 1e12, 1),
+            "out_proj_frac": round(proj_flops / (proj_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
 
 def _graph_time_ms(fn, n_sets, reps=40):

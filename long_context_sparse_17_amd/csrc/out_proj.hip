@@ -183,6 +183,111 @@ rowblock_gemv_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_
   }
 }
 
+// Prefill shapes (M >= 64): a tiled GEMM.  A workgroup computes a 128 x 128 block of Y (output
+// features n0 .., rows m0 ..), stepping through K in slices of 64: the W and X slices (128 rows x
+// 128 B each) go global -> registers -> LDS, double-buffered so the next slice's loads are in flight
+// while the current one feeds the matrix cores; one barrier per slice.  Four waves in a 2 x 2
+// arrangement each own a 64 x 64 sub-block (4 x 4 MFMA tiles, W fragments as A, X fragments as B,
+// so a lane ends with 4 consecutive features of one row).  Each W and X element is read from
+// global memory once per 128-row / 128-feature block instead of once per 16 rows.
+constexpr int kTgM = 128, kTgN = 128, kTgK = 64;
+constexpr int kTgStride = kTgK + 8;       // bf16 per LDS row (144 B: 16 rows of a fragment read start 36 words apart)
+constexpr int kTgThreads = 256;
+
+__global__ void __launch_bounds__(kTgThreads, 2)
+tile_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W, uint16_t* Y,
+                 int64_t y_ld, int M, int K, int n_per_group, const uint16_t* R, int64_t r_ld) {
+  __shared__ __align__(16) uint16_t sw[2][kTgN * kTgStride];
+  __shared__ __align__(16) uint16_t sxm[2][kTgM * kTgStride];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wn = w & 1, wm = w >> 1;       // this wave's 64 x 64 sub-block
+  const int n0 = blockIdx.x * kTgN;
+  const int m0 = blockIdx.y * kTgM;
+  const int64_t xoff = (int64_t)(n0 / n_per_group) * K;
+
+  // global -> register staging: 16 B chunks, chunk q = tid + 256 j (j = 0..3) is row q / 8, k-chunk
+  // q % 8 of the slice; rows past M read row M - 1 (never stored)
+  const uint16_t* wsrc[4];
+  const uint16_t* xsrc[4];
+  int lds_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = threadIdx.x + kTgThreads * j;
+    const int row = q >> 3, kc = q & 7;
+    const int m = m0 + row < M ? m0 + row : M - 1;
+    wsrc[j] = W + (int64_t)(n0 + row) * K + 8 * kc;
+    xsrc[j] = X + (int64_t)m * x_ld + xoff + 8 * kc;
+    lds_off[j] = row * kTgStride + 8 * kc;
+  }
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / kTgK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint4*>(&sw[0][lds_off[j]]) = *reinterpret_cast<const uint4*>(wsrc[j]);
+    *reinterpret_cast<uint4*>(&sxm[0][lds_off[j]]) = *reinterpret_cast<const uint4*>(xsrc[j]);
+  }
+  __syncthreads();
+  // one 64-deep slice from LDS slot `slot` into the accumulators
+  auto multiply = [&](int slot) {
+#pragma unroll
+    for (int ks = 0; ks < kTgK / 32; ++ks) {
+      uint4 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)                     // W rows (features) wn*64 + 16i + c16
+        fa[i] = *reinterpret_cast<const uint4*>(&sw[slot][(wn * 64 + 16 * i + c16) * kTgStride + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)                     // X rows wm*64 + 16j + c16
+        fb[j] = *reinterpret_cast<const uint4*>(&sxm[slot][(wm * 64 + 16 * j + c16) * kTgStride + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    }
+  };
+  for (int t = 0; t + 1 < nk; ++t) {
+    const int slot = t & 1;
+    const int k0 = (t + 1) * kTgK;                  // slice t + 1 in flight while slice t is multiplied
+    uint4 nw0 = *reinterpret_cast<const uint4*>(wsrc[0] + k0), nx0 = *reinterpret_cast<const uint4*>(xsrc[0] + k0);
+    uint4 nw1 = *reinterpret_cast<const uint4*>(wsrc[1] + k0), nx1 = *reinterpret_cast<const uint4*>(xsrc[1] + k0);
+    uint4 nw2 = *reinterpret_cast<const uint4*>(wsrc[2] + k0), nx2 = *reinterpret_cast<const uint4*>(xsrc[2] + k0);
+    uint4 nw3 = *reinterpret_cast<const uint4*>(wsrc[3] + k0), nx3 = *reinterpret_cast<const uint4*>(xsrc[3] + k0);
+    multiply(slot);
+    // the other slot was last read before the previous barrier
+    uint16_t* dw = sw[slot ^ 1];
+    uint16_t* dx = sxm[slot ^ 1];
+    *reinterpret_cast<uint4*>(&dw[lds_off[0]]) = nw0; *reinterpret_cast<uint4*>(&dx[lds_off[0]]) = nx0;
+    *reinterpret_cast<uint4*>(&dw[lds_off[1]]) = nw1; *reinterpret_cast<uint4*>(&dx[lds_off[1]]) = nx1;
+    *reinterpret_cast<uint4*>(&dw[lds_off[2]]) = nw2; *reinterpret_cast<uint4*>(&dx[lds_off[2]]) = nx2;
+    *reinterpret_cast<uint4*>(&dw[lds_off[3]]) = nw3; *reinterpret_cast<uint4*>(&dx[lds_off[3]]) = nx3;
+    __syncthreads();
+  }
+  multiply((nk - 1) & 1);
+
+  // acc[i][j]: lane holds row m0 + wm*64 + 16j + c16, features n0 + wn*64 + 16i + 4g .. +3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 64 + 16 * j + c16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + wn * 64 + 16 * i + 4 * g;
+      float y0 = acc[i][j][0], y1 = acc[i][j][1], y2 = acc[i][j][2], y3 = acc[i][j][3];
+      if (R != nullptr) {
+        const uint2 rv = *reinterpret_cast<const uint2*>(R + (int64_t)m * r_ld + n);
+        y0 += bf2f_lo(rv.x); y1 += bf2f_hi(rv.x); y2 += bf2f_lo(rv.y); y3 += bf2f_hi(rv.y);
+      }
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * y_ld + n) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+    }
+  }
+}
+
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Y = X . W^T for one stage: the staged-X kernel at the decode shapes, else the general one.
@@ -196,6 +301,9 @@ void launch_stage(const char* name, const uint16_t* X, int64_t x_ld, const uint1
   } else if (M <= 8 && K == 8192) {
     LCS_LAUNCH(name, (rowblock_gemv_kernel<8192, false>), dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld,
                W, Y, y_ld, M, n_per_group, R, r_ld, none);
+  } else if (M >= 64 && N % kTgN == 0 && n_per_group % kTgN == 0 && K % kTgK == 0) {
+    LCS_LAUNCH(name, tile_gemm_kernel, dim3((unsigned)(N / kTgN), (unsigned)((M + kTgM - 1) / kTgM)), dim3(kTgThreads),
+               0, st, X, x_ld, W, Y, y_ld, M, K, n_per_group, R, r_ld);
   } else {
     LCS_LAUNCH(name, rowblock_gemm_kernel, dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld, W, Y, y_ld,
                M, N, K, n_per_group, R, r_ld);

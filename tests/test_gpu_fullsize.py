@@ -148,6 +148,29 @@ def test_csa_chunked_prefill_1m_sampled():
     assert band <= 2 * len(picks)
 
 
+def test_grouped_out_proj_prefill_4096_sampled():
+    """Grouped output projection of a 4096-token prefill chunk (64 heads x 512 -> 8 groups x 1024 -> 4096,
+    plus a residual): the tiled GEMM path; 48 rows (block edges and seeded picks) against the oracle,
+    which computes each output row from that row alone."""
+    M, H, g, d_g, d = 4096, 64, 8, 1024, 4096
+    o = synth.device_normal_bf16((M, H * 512), 0.3, 7_000_001)
+    wg = synth.device_normal_bf16((g, d_g, H * 512 // g), 0.02, 7_000_002)
+    wo = synth.device_normal_bf16((d, g * d_g), 0.02, 7_000_003)
+    r = synth.device_normal_bf16((M, d), 1.0, 7_000_004)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    yr = torch.empty((M, d), dtype=torch.bfloat16, device=DEV)
+    L.grouped_out_proj(o, wg, wo, H=H, y=y)
+    L.grouped_out_proj_residual(o, wg, wo, r, H=H, y=yr)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 127, 128, 2047, 4095] + synth.rng(9, 98).choice(M, 42, replace=False).tolist()))
+    idx = torch.as_tensor(rows, device=DEV)
+    wg_h, wo_h = to_np_bf16(wg), to_np_bf16(wo)
+    _, ref = O.grouped_out_proj(to_np_bf16(o.index_select(0, idx)), wg_h, wo_h)
+    assert_close(to_np_bf16(y.index_select(0, idx)), ref, "prefill grouped out-proj, sampled rows")
+    assert_close(to_np_bf16(yr.index_select(0, idx)), O.residual(to_np_bf16(r.index_select(0, idx)), ref),
+                 "prefill grouped out-proj + residual, sampled rows")
+
+
 def test_csa_prefill_2k_full():
     """Single CSA layer prefill, 2048 tokens, d = 1024 hidden states projected on the host, 8 heads,
     indexer 8 x 64 bf16, top-k 128, sink 0: every query checked end to end."""

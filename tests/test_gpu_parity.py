@@ -503,7 +503,10 @@ def test_hca_attend_prefill_rows_with_rope_offset():
 
 
 # ----------------------------------------------------------------------------------- projection
-@pytest.mark.parametrize("M,H,g,d_g,d", [(8, 64, 8, 1024, 4096), (3, 16, 2, 64, 96), (37, 8, 1, 32, 48)])
+# M = 8: the decode GEMV; 3 and 37: the row-block kernel; 64, 130 and 300 rows: the tiled prefill GEMM
+# (one and several 128-row blocks, ragged last block, one group and eight)
+@pytest.mark.parametrize("M,H,g,d_g,d", [(8, 64, 8, 1024, 4096), (3, 16, 2, 64, 96), (37, 8, 1, 32, 48),
+                                         (64, 16, 2, 128, 256), (130, 8, 1, 128, 384), (300, 64, 8, 1024, 4096)])
 def test_grouped_out_proj_parity(M, H, g, d_g, d):
     cfg = 60 + M
     o = synth.normal_bf16((M, H * 512), 0.3, cfg, 1)
