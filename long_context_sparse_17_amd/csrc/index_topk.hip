@@ -44,11 +44,12 @@ inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // scorer and filter add into the rows a call uses, and the final kernel clears them again, so no call
 // needs a clearing launch of its own.
 constexpr int kDecodeRows = 64;
+constexpr int kMaxDecodeChunks = 2048;       // decode selection: rows up to 8M entries
 
 struct Ws {
   uint32_t* hist;                 // [kDecodeRows, kHistRow]: histograms of the top score-key bits, then of the next 11
-  float* scores;                  // [R, nsp]
-  unsigned long long* comb;       // [R, nsp]: kept entries per chunk (decode) / candidates (prefill)
+  float* scores;                  // [RS, nsp] (RS: every row at decode, one batch of queries in prefill)
+  unsigned long long* comb;       // [RS, nsp]: kept entries per chunk (decode) / candidates (prefill)
   uint2* counts;                  // [R, nchunk]: per decode chunk (kept, above the threshold bin)
   uint8_t* qc;                    // [R, HP, 128]: E4M3FN query codes (fp8 prefill)
   float* qw;                      // [R, HP]: head weights times the query row scales (fp8 prefill)
@@ -61,10 +62,32 @@ struct Ws {
 
 inline int64_t n_chunks(int64_t n_cap) { return (n_cap + kFilterChunk - 1) / kFilterChunk; }
 
+// Rows of many queries (prefill) are scored and selected in batches of queries: each batch takes
+// query positions [t0, t0 + tb) of every batch row, so the score and candidate buffers hold B * tb
+// rows whatever Tq is.  tb is a multiple of 16 (the bf16 scorer's query tile, and a multiple of the
+// fp8 scorer's 4-query stage) unless one batch covers all of Tq.  768 rows are one round of the
+// selection kernel (3 workgroups per CU on 256 CUs): a batch that leaves a partial second round
+// costs more than the extra launches.
+constexpr int kPfBatchRows = 768;
+inline int prefill_batch(int B, int Tq) {
+  const int want = kPfBatchRows / B;
+  if (Tq <= want || Tq <= 16) return Tq;
+  const int tb = want / 16 * 16;
+  return tb < 16 ? 16 : tb;
+}
+inline bool decode_rows(int B, int Tq, int64_t n_cap) {
+  return (int64_t)B * Tq < kDecodeRows && n_chunks(n_cap) <= kMaxDecodeChunks;
+}
+// rows of the score and candidate buffers: every row at decode, one batch of queries otherwise
+inline int64_t buffer_rows(int B, int Tq, int64_t n_cap) {
+  return decode_rows(B, Tq, n_cap) ? (int64_t)B * Tq : (int64_t)B * prefill_batch(B, Tq);
+}
+
 inline int64_t n_groups4(int B, int Tq) { return (int64_t)B * ((Tq + 3) / 4); }
 
 Ws carve(void* ws, int B, int Tq, int64_t n_cap) {
   const int R = B * Tq;
+  const int64_t RS = buffer_rows(B, Tq, n_cap);
   Ws w;
   w.nsp = (n_cap + 63) & ~(int64_t)63;
   w.nchunk = (int)n_chunks(n_cap);
@@ -72,9 +95,9 @@ Ws carve(void* ws, int B, int Tq, int64_t n_cap) {
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += al256((size_t)kDecodeRows * kHistRow * 4);
   w.scores = reinterpret_cast<float*>(p);
-  p += al256((size_t)R * w.nsp * 4);
+  p += al256((size_t)RS * w.nsp * 4);
   w.comb = reinterpret_cast<unsigned long long*>(p);
-  p += al256((size_t)R * w.nsp * 8);
+  p += al256((size_t)RS * w.nsp * 8);
   w.counts = reinterpret_cast<uint2*>(p);
   p += al256((size_t)R * w.nchunk * 8);
   w.qc = reinterpret_cast<uint8_t*>(p);
@@ -145,21 +168,24 @@ template <int KS, int HBI>
 __global__ void __launch_bounds__(256)
 index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
                    const uint16_t* __restrict__ ik, int64_t ik_ld, const int64_t* __restrict__ q_pos,
-                   int64_t n_cap, int Tq, int H_I, int dI, int m, float* __restrict__ scores, int64_t nsp) {
+                   int64_t n_cap, int Tq, int t0, int tcur, int tb, int H_I, int dI, int m,
+                   float* __restrict__ scores, int64_t nsp) {
   constexpr int QW = 4, QTILE = 16;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int g = lane >> 4, c16 = lane & 15;
-  const int tiles_per_b = (Tq + QTILE - 1) / QTILE;
+  // query positions [t0, t0 + tcur) of every batch row; scores to buffer rows b * tb + (t - t0)
+  const int tiles_per_b = (tcur + QTILE - 1) / QTILE;
   const int b = blockIdx.y / tiles_per_b;
-  const int tq0 = (blockIdx.y % tiles_per_b) * QTILE;
+  const int tq0 = t0 + (blockIdx.y % tiles_per_b) * QTILE;
+  const int tq_end = t0 + tcur < Tq ? t0 + tcur : Tq;
   const int64_t c0 = (int64_t)blockIdx.x * kScoreChunk;
 
   // entry limit of this workgroup = max n_vis over its queries
   int64_t nv_max = 0;
   for (int i = 0; i < QTILE; ++i) {
     const int tq = tq0 + i;
-    if (tq < Tq) {
+    if (tq < tq_end) {
       const int64_t nv = n_visible(q_pos, (int64_t)b * Tq + tq, m, n_cap);
       nv_max = nv > nv_max ? nv : nv_max;
     }
@@ -169,13 +195,13 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
   uint4 afr[QW][HBI][KS];
   float wq[QW][HBI][4];
   int64_t nvis[QW];
-  int64_t rowq[QW];
+  int64_t rowq[QW];                            // buffer row of each query
 #pragma unroll
   for (int qw = 0; qw < QW; ++qw) {
     const int tq = tq0 + wave * QW + qw;
-    const bool qvalid = tq < Tq;
-    const int64_t r = (int64_t)b * Tq + (qvalid ? tq : 0);
-    rowq[qw] = r;
+    const bool qvalid = tq < tq_end;
+    const int64_t r = (int64_t)b * Tq + (qvalid ? tq : t0);
+    rowq[qw] = (int64_t)b * tb + ((qvalid ? tq : t0) - t0);
     nvis[qw] = qvalid ? n_visible(q_pos, r, m, n_cap) : 0;
 #pragma unroll
     for (int hb = 0; hb < HBI; ++hb) {
@@ -346,8 +372,8 @@ __global__ void __launch_bounds__(kPfWaves * kWave)
 index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restrict__ qwf,
                            const int32_t* __restrict__ qnv, const uint8_t* __restrict__ linc,
                            const uint32_t* __restrict__ lins, const uint8_t* __restrict__ ik,
-                           const float* __restrict__ ik_scale, int64_t ik_ld, int64_t n_cap, int Tq, int qsplit,
-                           int qper, float* __restrict__ scores, int64_t nsp) {
+                           const float* __restrict__ ik_scale, int64_t ik_ld, int64_t n_cap, int Tq, int t0,
+                           int tcur, int tb, int qsplit, int qper, float* __restrict__ scores, int64_t nsp) {
   constexpr int HP = 16 * HBI;
   constexpr int kCodeBytes = HP * kPfRow;
   constexpr int kSlot = kCodeBytes + HP * 4 + 16;      // one query in LDS: codes, folded weights, n_vis
@@ -360,9 +386,12 @@ index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restri
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int g = lane >> 4, c16 = lane & 15;
+  // this launch scores query positions [t0, t0 + tcur) of every batch row; their scores go to buffer
+  // rows b * tb + (t - t0)
   const int b = blockIdx.y / qsplit;
-  const int q_lo = (blockIdx.y % qsplit) * qper;
-  const int q_hi = q_lo + qper < Tq ? q_lo + qper : Tq;
+  const int q_lo = t0 + (blockIdx.y % qsplit) * qper;
+  const int q_end = t0 + tcur < Tq ? t0 + tcur : Tq;
+  const int q_hi = q_lo + qper < q_end ? q_lo + qper : q_end;
   if (q_lo >= q_hi) return;                            // uniform
   const int64_t c0 = (int64_t)blockIdx.x * kPfChunk;
   const int64_t ew = c0 + wave * (kPfEB * 16);         // first entry of this wave
@@ -537,7 +566,7 @@ index_score_prefill_kernel(const uint8_t* __restrict__ qc, const float* __restri
       }
 #pragma unroll
       for (int j = 0; j < kPfQC; ++j) {
-        float* srow = scores + (row0 + q_lo + s * kPfQC + j) * nsp;
+        float* srow = scores + ((int64_t)b * tb + (q_lo - t0) + s * kPfQC + j) * nsp;
         if (e_lo < nvq[j]) srow[e_lo] = res0[j];
         if (e_lo + 64 < nvq[j]) srow[e_lo + 64] = res1[j];
       }
@@ -829,7 +858,6 @@ constexpr unsigned long long kAbove = 1ull << 63;   // kept entry from a bin abo
 constexpr int kFinalCache = 4096;
 constexpr int kFinalSeg = kFinalCache / kSelThreads;        // 16 list positions per thread
 constexpr int kFinalStride = kSelThreads + 1;               // LDS row stride of the transposed list
-constexpr int kMaxDecodeChunks = 2048;                      // rows up to 8M entries take this path
 
 __device__ __forceinline__ int final_slot(int i) { return (i % kFinalSeg) * kFinalStride + i / kFinalSeg; }
 
@@ -1405,16 +1433,19 @@ __device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv,
 // Prefill: one workgroup per row does histogram, filter, refine, sort.
 __global__ void __launch_bounds__(kSelThreads)
 topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __restrict__ cand, int64_t nsp,
-                    const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k,
-                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+                    const int64_t* __restrict__ q_pos, int m, int64_t n_cap, int k, int Tq, int t0, int tcur,
+                    int tb, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelShared s;
   __shared__ int32_t list[kMaxTopk];
   __shared__ __align__(16) uint32_t h[kBins];
   __shared__ int sT, sAbove, sCand;
   const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
+  // workgroup x: query position t0 + x % tcur of batch row x / tcur (buffer row b * tb + x % tcur)
+  const int64_t bq = blockIdx.x / tcur, tq = t0 + blockIdx.x % tcur;
+  const int64_t r = bq * Tq + tq;
+  const int64_t rb = bq * tb + (tq - t0);
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
-  const float* srow = scores + r * nsp;
+  const float* srow = scores + rb * nsp;
   if (nv <= k) {
     for (int64_t i = tid; i < k; i += kSelThreads) {
       topk_idx[r * k + i] = i < nv ? (int32_t)i : -1;
@@ -1422,7 +1453,7 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
     }
     return;
   }
-  unsigned long long* crow = cand + r * nsp;
+  unsigned long long* crow = cand + rb * nsp;
   // ---- Sampled threshold (long rows, k a small fraction): a lower bound on the k-th key from a
   // sample of whole 32-entry blocks, then a single pass keeps every entry at or above it.  Exact
   // whenever at least k entries pass (the k winners are then all among them); else the full path.
@@ -1526,11 +1557,12 @@ void launch_score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
 }
 
 template <int KS, int HBI>
-void launch_score_rows_bf16(const IndexArgs& a, const Ws& w, hipStream_t st) {
-  const int tiles = (a.Tq + 15) / 16;
+void launch_score_rows_bf16(const IndexArgs& a, const Ws& w, int t0, int tcur, int tb, hipStream_t st) {
+  const int tiles = (tcur + 15) / 16;
   dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));
   LCS_LAUNCH("index_score_kernel", (index_score_kernel<KS, HBI>), grid, dim3(256), 0, st, a.q_idx, a.w_idx,
-             static_cast<const uint16_t*>(a.ik), a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, w.scores, w.nsp);
+             static_cast<const uint16_t*>(a.ik), a.ik_ld, a.q_pos, a.n_cap, a.Tq, t0, tcur, tb, a.H_I, a.dI, a.m,
+             w.scores, w.nsp);
 }
 
 // fp8 prefill grid: one workgroup per chunk of kPfChunk entries (x) and per query range of each
@@ -1552,14 +1584,17 @@ PfGrid prefill_grid(int B, int Tq, int64_t n_cap) {
 }
 
 template <int HBI>
-void launch_score_rows_fp8(const IndexArgs& a, const Ws& w, hipStream_t st) {
+void launch_qprep_fp8(const IndexArgs& a, const Ws& w, hipStream_t st) {
   LCS_LAUNCH("index_qprep_kernel", index_qprep_kernel<HBI>, dim3((unsigned)(a.B * a.Tq)), dim3(256), 0, st,
              a.q_idx, a.w_idx, a.H_I, a.q_pos, a.n_cap, a.m, a.Tq, w.qc, w.qw, w.qnv, w.linc, w.lins);
-  const PfGrid p = prefill_grid(a.B, a.Tq, a.n_cap);
+}
+template <int HBI>
+void launch_score_rows_fp8(const IndexArgs& a, const Ws& w, int t0, int tcur, int tb, hipStream_t st) {
+  const PfGrid p = prefill_grid(a.B, tcur, a.n_cap);
   dim3 grid((unsigned)p.nchunk, (unsigned)(a.B * p.qsplit));
   LCS_LAUNCH("index_score_kernel", index_score_prefill_kernel<HBI>, grid, dim3(kPfWaves * kWave), 0, st, w.qc, w.qw,
-             w.qnv, w.linc, w.lins, static_cast<const uint8_t*>(a.ik), a.ik_scale, a.ik_ld, a.n_cap, a.Tq, p.qsplit,
-             p.qper, w.scores, w.nsp);
+             w.qnv, w.linc, w.lins, static_cast<const uint8_t*>(a.ik), a.ik_scale, a.ik_ld, a.n_cap, a.Tq, t0, tcur,
+             tb, p.qsplit, p.qper, w.scores, w.nsp);
 }
 
 void score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
@@ -1579,21 +1614,32 @@ void score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
   }
 }
 
-void score_rows(const IndexArgs& a, const Ws& w, hipStream_t st) {
+// fp8: the query rows' codes, weights and linear terms, once for all rows
+void prep_rows(const IndexArgs& a, const Ws& w, hipStream_t st) {
+  if (!a.ik_fp8) return;
+  const int hbi = (a.H_I + 15) / 16;
+  if (hbi == 1) launch_qprep_fp8<1>(a, w, st);
+  else if (hbi == 2) launch_qprep_fp8<2>(a, w, st);
+  else if (hbi == 3) launch_qprep_fp8<3>(a, w, st);
+  else launch_qprep_fp8<4>(a, w, st);
+}
+
+// scores of query positions [t0, t0 + tcur) of every batch row into buffer rows b * tb + (t - t0)
+void score_rows(const IndexArgs& a, const Ws& w, int t0, int tcur, int tb, hipStream_t st) {
   const int hbi = (a.H_I + 15) / 16;
   if (a.ik_fp8) {
-    if (hbi == 1) launch_score_rows_fp8<1>(a, w, st);
-    else if (hbi == 2) launch_score_rows_fp8<2>(a, w, st);
-    else if (hbi == 3) launch_score_rows_fp8<3>(a, w, st);
-    else launch_score_rows_fp8<4>(a, w, st);
+    if (hbi == 1) launch_score_rows_fp8<1>(a, w, t0, tcur, tb, st);
+    else if (hbi == 2) launch_score_rows_fp8<2>(a, w, t0, tcur, tb, st);
+    else if (hbi == 3) launch_score_rows_fp8<3>(a, w, t0, tcur, tb, st);
+    else launch_score_rows_fp8<4>(a, w, t0, tcur, tb, st);
   } else if (a.dI == 64) {
-    if (hbi == 1) launch_score_rows_bf16<2, 1>(a, w, st);
-    else if (hbi == 2) launch_score_rows_bf16<2, 2>(a, w, st);
-    else launch_score_rows_bf16<2, 4>(a, w, st);
+    if (hbi == 1) launch_score_rows_bf16<2, 1>(a, w, t0, tcur, tb, st);
+    else if (hbi == 2) launch_score_rows_bf16<2, 2>(a, w, t0, tcur, tb, st);
+    else launch_score_rows_bf16<2, 4>(a, w, t0, tcur, tb, st);
   } else {
-    if (hbi == 1) launch_score_rows_bf16<4, 1>(a, w, st);
-    else if (hbi == 2) launch_score_rows_bf16<4, 2>(a, w, st);
-    else launch_score_rows_bf16<4, 4>(a, w, st);
+    if (hbi == 1) launch_score_rows_bf16<4, 1>(a, w, t0, tcur, tb, st);
+    else if (hbi == 2) launch_score_rows_bf16<4, 2>(a, w, t0, tcur, tb, st);
+    else launch_score_rows_bf16<4, 4>(a, w, t0, tcur, tb, st);
   }
 }
 
@@ -1604,11 +1650,13 @@ bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
   const int64_t R = (int64_t)B * Tq;
   if (R < kDecodeRows && n_chunks(n_cap) <= kMaxDecodeChunks) return true;   // decode grids (chunks, R)
   if (R >= ((int64_t)1 << 31)) return false;                         // one workgroup per row
+  const int tb = prefill_batch(B, Tq);                 // query positions per batch launch
+  if ((int64_t)B * tb >= ((int64_t)1 << 31)) return false;
   if (ik_fp8) {
-    const PfGrid p = prefill_grid(B, Tq, n_cap);
+    const PfGrid p = prefill_grid(B, tb, n_cap);
     return p.nchunk < ((int64_t)1 << 31) && (int64_t)B * p.qsplit <= 65535;
   }
-  return (n_cap + kScoreChunk - 1) / kScoreChunk < ((int64_t)1 << 31) && (int64_t)B * ((Tq + 15) / 16) <= 65535;
+  return (n_cap + kScoreChunk - 1) / kScoreChunk < ((int64_t)1 << 31) && (int64_t)B * ((tb + 15) / 16) <= 65535;
 }
 
 size_t index_topk_state_bytes() { return al256((size_t)kDecodeRows * kHistRow * 4); }
@@ -1616,8 +1664,9 @@ size_t index_topk_state_bytes() { return al256((size_t)kDecodeRows * kHistRow * 
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   (void)k;
   const int64_t R = (int64_t)B * Tq;
+  const int64_t RS = buffer_rows(B, Tq, n_cap);
   const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
-  return al256((size_t)kDecodeRows * kHistRow * 4) + al256((size_t)R * nsp * 4) + al256((size_t)R * nsp * 8) +
+  return al256((size_t)kDecodeRows * kHistRow * 4) + al256((size_t)RS * nsp * 4) + al256((size_t)RS * nsp * 8) +
          al256((size_t)R * n_chunks(n_cap) * 8) + al256((size_t)R * kMaxIndexHeads * 128) +
          al256((size_t)R * kMaxIndexHeads * 4) + al256((size_t)R * 4) + al256((size_t)n_groups4(B, Tq) * 2048) +
          al256((size_t)n_groups4(B, Tq) * 256);
@@ -1628,7 +1677,7 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   Ws w = carve(a.ws, a.B, a.Tq, a.n_cap);
   // Few rows: spread every row over many workgroups (decode).  Many rows, or rows longer than the
   // decode selection stages: row-per-workgroup.
-  const bool decode = R < kDecodeRows && w.nchunk <= kMaxDecodeChunks;
+  const bool decode = decode_rows(a.B, a.Tq, a.n_cap);
   if (decode) {
     score_decode(a, w, st);                       // the histogram rows start at zero (see kDecodeRows)
     dim3 gf((unsigned)w.nchunk, (unsigned)R);
@@ -1637,9 +1686,15 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
     LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
                w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
   } else {
-    score_rows(a, w, st);
-    LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.scores,
-               w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.topk_idx, a.topk_score);
+    // batches of query positions: score, then select, reusing the score and candidate buffers
+    prep_rows(a, w, st);
+    const int tb = prefill_batch(a.B, a.Tq);
+    for (int t0 = 0; t0 < a.Tq; t0 += tb) {
+      const int tcur = a.Tq - t0 < tb ? a.Tq - t0 : tb;
+      score_rows(a, w, t0, tcur, tb, st);
+      LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)(a.B * tcur)), dim3(kSelThreads), 0, st,
+                 w.scores, w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.Tq, t0, tcur, tb, a.topk_idx, a.topk_score);
+    }
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -244,6 +244,22 @@ def test_index_topk_prefill_fp8_head_blocks_ragged(H_I, Tq, n_cap):
     assert band <= 4
 
 
+@pytest.mark.parametrize("B,Tq,H_I,dI,fp8", [(3, 700, 16, 128, True), (2, 1100, 8, 64, False)])
+def test_index_topk_prefill_query_batches(B, Tq, H_I, dI, fp8):
+    # many rows are scored and selected in batches of query positions (B * batch <= 768 rows of
+    # buffers): 3 x 700 runs batches of 256, 256 and 188 positions, 2 x 1100 of 384, 384 and 332, so
+    # batch edges, a short last batch and every batch row are covered, with rows from empty to full
+    n_cap, k = 900, 64
+    pos = []
+    for b in range(B):
+        if b % 2 == 0:
+            pos += [int(x) for x in np.linspace(0, 4 * n_cap + 30, Tq)]
+        else:
+            pos += list(range(4 * n_cap - Tq + 1, 4 * n_cap + 1))
+    band = _index_case(B, Tq, n_cap, H_I, dI, k, 4, fp8, pos, 45 + B)
+    assert band <= 2 * B * Tq // 100 + 4
+
+
 def test_index_topk_prefill_long_rows_sampled_threshold():
     # rows long enough for the sampled threshold (n_vis >= 8192 and >= 8 k) next to shorter ones
     n_cap, k, Tq = 12000, 128, 64
