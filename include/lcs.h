@@ -210,8 +210,11 @@ int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, in
  *          histograms are cleared by the call's last kernel), so one workspace serves any sequence of
  *          calls, of any shapes, without further clearing; calls that share a workspace must be
  *          ordered (one stream).
+ *   Many-row calls (prefill) score and select batches of query positions, tb = min(Tq, max(16,
+ *   768 / B rounded down to a multiple of 16)) of every batch row at a time, so the workspace holds
+ *   B * tb score and candidate rows, not B * Tq.
  *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1, B * Tq <= 65535 * 16,
- *   and launch grids within the device limits (many-row calls: B * ceil(Tq / 16) <= 65535 with bf16
+ *   and launch grids within the device limits (many-row calls: B * ceil(tb / 16) <= 65535 with bf16
  *   keys, about B <= 65000 with fp8 keys); otherwise LCS_ERR_UNSUPPORTED before anything runs.
  */
 size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
@@ -222,6 +225,37 @@ int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx,
                    int B, int Tq, int H_I, int dI, int m, int k,
                    int32_t* topk_idx, float* topk_score,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_index_topk_append -- csa_index_topk and kv_decode_append in one call, for a CSA decode step
+ * (page 1, CSA steps 1 and 2: the step's new token is pooled into the compressed state while the
+ * query selects among the entries visible to it).  The first 18 arguments are csa_index_topk's, the
+ * next 29 kv_decode_append's (B_app, m_app, dI_app: its B, m, dI; ik_out, ik_out_scale, ik_out_ld,
+ * ik_out_dtype: its ik_out, ik_scale, ik_ld, ik_dtype), then the stream.  Every argument is checked as
+ * the two entry points check it, all before anything is enqueued.  The result is that of
+ * csa_index_topk followed by kv_decode_append: the append runs beside the selection's last kernel
+ * (decode: B * Tq < 64 rows; one launch fewer) or after it (otherwise), once the indexer keys have
+ * been scored.  When each sequence's appended token is its query token (pos[b] = q_pos[b, Tq - 1]),
+ * the entry a token finishes lies past the entries visible to that query, so the result is also that
+ * of the two calls in the other order (the usual decode step: append, then select).  The append's
+ * buffers must not overlap the selection's workspace or outputs; ik_out may be ik_cache and pos may
+ * be q_pos.
+ */
+int csa_index_topk_append(const uint16_t* q_idx, const uint16_t* w_idx,
+                          const void* ik_cache, const float* ik_scale, int64_t ik_ld, int ik_dtype,
+                          const int64_t* q_pos, int64_t n_cap,
+                          int B, int Tq, int H_I, int dI, int m, int k,
+                          int32_t* topk_idx, float* topk_score,
+                          void* ws, size_t ws_bytes,
+                          const uint16_t* kv_tok, const float* kv_score,
+                          const uint16_t* ik_tok, const float* ik_score,
+                          const int64_t* pos, int B_app, int m_app, int overlap, int c, int dI_app,
+                          const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
+                          float* state, size_t state_bytes, int kv_dtype,
+                          void* win, float* win_scale, int64_t win_ld, int64_t ring_cap,
+                          void* kv_out, float* kv_scale, int64_t kv_ld, int64_t kv_ring,
+                          void* ik_out, float* ik_out_scale, int64_t ik_out_ld, int ik_out_dtype,
+                          void* stream);
 
 /*
  * csa_attend -- CSA step 3 (page 1, CSA step 3: multi-query attention over the selected entries;

@@ -38,6 +38,9 @@ SIGNATURES = {
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk_state_bytes": (_SZ, []),
     "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "csa_index_topk_append": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ,
+                                   _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _I, _P, _P,
+                                   _I64, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _I, _P]),
     "lcs_attend_workspace": (_SZ, [_I, _I, _I, _I64]),
     "csa_attend": (_I, [_P, _P, _P, _I64, _P, _I, _P, _I64, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F, _F, _F,
                         _P, _P, _SZ, _P]),
@@ -158,12 +161,10 @@ def kv_decode_state_bytes(B):
     return lib().kv_decode_state_bytes(B)
 
 
-def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gamma_kv, state, kv_out, kv_ring=0,
-                     win=None, ring_cap=0, ik_out=None, ik_scale=None, ik_fp8=True, eps=1e-6, rope_theta=10000.0,
-                     rope_offset=0, kv_scale=None, win_scale=None, stream=None):
-    """Append token pos[b] of every sequence b (pos < 0: skip).  kv_tok [B,512] bf16, kv_score [B] f32,
-    ik_tok [B,dI] bf16 | None, pos [B] int64, state: uint8 buffer of kv_decode_state_bytes(B) bytes.
-    kv_out / win bf16, or uint8 E4M3FN codes with kv_scale / win_scale [B, ld] f32 (fp8 K=V)."""
+def _append_argv(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gamma_kv, state, kv_out, kv_ring=0,
+                 win=None, ring_cap=0, ik_out=None, ik_scale=None, ik_fp8=True, eps=1e-6, rope_theta=10000.0,
+                 rope_offset=0, kv_scale=None, win_scale=None):
+    """The C arguments of kv_decode_append (without the stream)."""
     import torch
     B, c = kv_tok.shape
     kv8 = kv_out.dtype == torch.uint8
@@ -175,13 +176,21 @@ def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, m, overlap, gam
     _dt(kv_score, torch.float32, "kv_score"); _dt(ik_score, torch.float32, "ik_score"); _dt(pos, torch.int64, "pos")
     dI = ik_tok.shape[-1] if ik_tok is not None else 0
     ik_ld = ik_out.shape[1] if ik_out is not None else 0
-    st = lib().kv_decode_append(_ptr(kv_tok), _ptr(kv_score), _ptr(ik_tok), _ptr(ik_score), _ptr(pos), B, m, overlap,
-                                c, dI, _ptr(gamma_kv), eps, rope_theta, rope_offset, _ptr(state),
-                                state.numel() * state.element_size(), LCS_KV_FP8 if kv8 else LCS_KV_BF16, _ptr(win),
-                                _ptr(win_scale), win.shape[1] if win is not None else 0, ring_cap, _ptr(kv_out),
-                                _ptr(kv_scale), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
-                                LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16, _stream(stream))
-    _check("kv_decode_append", st)
+    return (_ptr(kv_tok), _ptr(kv_score), _ptr(ik_tok), _ptr(ik_score), _ptr(pos), B, m, overlap, c, dI,
+            _ptr(gamma_kv), eps, rope_theta, rope_offset, _ptr(state), state.numel() * state.element_size(),
+            LCS_KV_FP8 if kv8 else LCS_KV_BF16, _ptr(win), _ptr(win_scale), win.shape[1] if win is not None else 0,
+            ring_cap, _ptr(kv_out), _ptr(kv_scale), kv_out.shape[1], kv_ring, _ptr(ik_out), _ptr(ik_scale), ik_ld,
+            LCS_IK_FP8 if ik_fp8 else LCS_IK_BF16)
+
+
+def kv_decode_append(kv_tok, kv_score, ik_tok, ik_score, pos, *, stream=None, **kw):
+    """Append token pos[b] of every sequence b (pos < 0: skip).  kv_tok [B,512] bf16, kv_score [B] f32,
+    ik_tok [B,dI] bf16 | None, pos [B] int64, state: uint8 buffer of kv_decode_state_bytes(B) bytes.
+    kv_out / win bf16, or uint8 E4M3FN codes with kv_scale / win_scale [B, ld] f32 (fp8 K=V).
+    Keywords: m, overlap, gamma_kv, state, kv_out (required); kv_ring, win, ring_cap, ik_out, ik_scale,
+    ik_fp8, eps, rope_theta, rope_offset, kv_scale, win_scale."""
+    argv = _append_argv(kv_tok, kv_score, ik_tok, ik_score, pos, **kw)
+    _check("kv_decode_append", lib().kv_decode_append(*argv, _stream(stream)))
 
 
 def kv_quantize_fp8(kv, *, codes, scales, stream=None):
@@ -220,20 +229,38 @@ def csa_index_topk_workspace(B, Tq, n_cap, k):
     return lib().csa_index_topk_workspace(B, Tq, n_cap, k)
 
 
-def csa_index_topk(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, topk_score=None,
-                   ws=None, stream=None):
-    """q_idx [B,Tq,H_I,dI] bf16, w_idx [B,Tq,H_I] bf16, ik_cache [B,ik_ld,dI] uint8 (fp8) or bf16.
-    ws: a workspace(csa_index_topk_workspace(...), zeroed=True), reusable across calls (see lcs.h)."""
+def _index_argv(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, topk_score=None, ws=None):
+    """The C arguments of csa_index_topk (without the stream) and the workspace they reference."""
     import torch
     B, Tq, H_I, dI = q_idx.shape
     fp8 = ik_cache.dtype == torch.uint8
     _dt(q_pos, torch.int64, "q_pos"); _dt(topk_idx, torch.int32, "topk_idx")
     if ws is None:
         ws = workspace(csa_index_topk_workspace(B, Tq, n_cap, k), q_idx.device, zeroed=True)
-    st = lib().csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(ik_cache), _ptr(ik_scale), ik_cache.shape[1],
-                              LCS_IK_FP8 if fp8 else LCS_IK_BF16, _ptr(q_pos), n_cap, B, Tq, H_I, dI, m, k,
-                              _ptr(topk_idx), _ptr(topk_score), _ptr(ws), ws.numel(), _stream(stream))
-    _check("csa_index_topk", st)
+    return (_ptr(q_idx), _ptr(w_idx), _ptr(ik_cache), _ptr(ik_scale), ik_cache.shape[1],
+            LCS_IK_FP8 if fp8 else LCS_IK_BF16, _ptr(q_pos), n_cap, B, Tq, H_I, dI, m, k, _ptr(topk_idx),
+            _ptr(topk_score), _ptr(ws), ws.numel()), ws
+
+
+def csa_index_topk(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, topk_score=None,
+                   ws=None, stream=None):
+    """q_idx [B,Tq,H_I,dI] bf16, w_idx [B,Tq,H_I] bf16, ik_cache [B,ik_ld,dI] uint8 (fp8) or bf16.
+    ws: a workspace(csa_index_topk_workspace(...), zeroed=True), reusable across calls (see lcs.h)."""
+    argv, ws = _index_argv(q_idx, w_idx, ik_cache, ik_scale, q_pos, n_cap=n_cap, m=m, k=k, topk_idx=topk_idx,
+                           topk_score=topk_score, ws=ws)
+    _check("csa_index_topk", lib().csa_index_topk(*argv, _stream(stream)))
+
+
+def csa_index_topk_append(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, append,
+                          topk_score=None, ws=None, stream=None):
+    """csa_index_topk, and in the same call the decode token append described by `append`: a dict of
+    kv_decode_append's arguments (kv_tok, kv_score, ik_tok, ik_score, pos and its keywords)."""
+    argv, ws = _index_argv(q_idx, w_idx, ik_cache, ik_scale, q_pos, n_cap=n_cap, m=m, k=k, topk_idx=topk_idx,
+                           topk_score=topk_score, ws=ws)
+    ap = dict(append)
+    aargv = _append_argv(ap.pop("kv_tok"), ap.pop("kv_score"), ap.pop("ik_tok"), ap.pop("ik_score"), ap.pop("pos"),
+                         **ap)
+    _check("csa_index_topk_append", lib().csa_index_topk_append(*argv, *aargv, _stream(stream)))
 
 
 def attend_workspace(B, Tq, H, max_keys):

@@ -56,7 +56,10 @@ void timing_before(const char*, hipStream_t s) {
   if (!t.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(t.mu);
   t.pending = t.get();
-  if (t.pending) hipEventRecord(t.pending, s);
+  if (t.pending && hipEventRecord(t.pending, s) != hipSuccess) {   // this launch goes untimed
+    t.pool.push_back(t.pending);
+    t.pending = nullptr;
+  }
 }
 void timing_after(const char* name, hipStream_t s) {
   Timing& t = timing();
@@ -64,8 +67,12 @@ void timing_after(const char* name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(t.mu);
   if (!t.pending) return;
   hipEvent_t b = t.get();
-  if (!b) return;
-  hipEventRecord(b, s);
+  if (!b || hipEventRecord(b, s) != hipSuccess) {                  // this launch goes untimed
+    if (b) t.pool.push_back(b);
+    t.pool.push_back(t.pending);
+    t.pending = nullptr;
+    return;
+  }
   t.recs.push_back({name, t.pending, b});
   t.pending = nullptr;
 }
@@ -91,8 +98,8 @@ int lcs_timing_enable(int on) {
   Timing& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
   if (!on) {
-    for (auto& r : t.recs) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
-    for (auto e : t.pool) hipEventDestroy(e);
+    for (auto& r : t.recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+    for (auto e : t.pool) (void)hipEventDestroy(e);
     t.recs.clear();
     t.pool.clear();
   }
@@ -179,12 +186,15 @@ int hca_compress_kv(const uint16_t* kv_tok, const float* kv_score, int B, int T,
 // ------------------------------------------------------------------------------ decode append
 size_t kv_decode_state_bytes(int B) { return B > 0 ? lcs::decode_state_bytes(B) : 0; }
 
-int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
-                     const int64_t* pos, int B, int m, int overlap, int c, int dI, const uint16_t* gamma_kv,
-                     float eps, float rope_theta, int64_t rope_offset, float* state, size_t state_bytes,
-                     int kv_dtype, void* win, float* win_scale, int64_t win_ld, int64_t ring_cap, void* kv_out,
-                     float* kv_scale, int64_t kv_ld, int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld,
-                     int ik_dtype, void* stream) {
+}  // extern "C"
+
+// Checks of kv_decode_append's arguments; fills the launch arguments when they pass.
+static int append_args(const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
+                       const int64_t* pos, int B, int m, int overlap, int c, int dI, const uint16_t* gamma_kv,
+                       float eps, float rope_theta, int64_t rope_offset, float* state, size_t state_bytes,
+                       int kv_dtype, void* win, float* win_scale, int64_t win_ld, int64_t ring_cap, void* kv_out,
+                       float* kv_scale, int64_t kv_ld, int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld,
+                       int ik_dtype, lcs::DecodeAppendArgs* out) {
   if (!kv_tok || !kv_score || !pos || !gamma_kv || !state || !kv_out) return LCS_ERR_ARG;
   if (B <= 0 || m <= 0 || overlap < 0 || kv_ld <= 0 || kv_ring < 0) return LCS_ERR_ARG;
   if (!(eps >= 0.f) || !(rope_theta > 0.f)) return LCS_ERR_ARG;
@@ -206,7 +216,7 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
     if (dI != 64 && dI != 128) return LCS_ERR_UNSUPPORTED;
     if (ik_dtype == LCS_IK_FP8 && !ik_scale) return LCS_ERR_ARG;
   }
-  lcs::DecodeAppendArgs a;
+  lcs::DecodeAppendArgs& a = *out;
   a.kv_tok = kv_tok; a.kv_score = kv_score; a.ik_tok = has_ik ? ik_tok : nullptr; a.ik_score = ik_score;
   a.pos = pos; a.B = B; a.m = m; a.ov = overlap; a.dI = has_ik ? dI : 0;
   a.gamma = gamma_kv; a.eps = eps; a.theta = rope_theta; a.rope_offset = rope_offset;
@@ -214,6 +224,22 @@ int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16
   a.kv_out = kv_out; a.kv_ld = kv_ld; a.kv_ring = kv_ring;
   a.kv8 = kv8; a.win_scale = win_scale; a.kv_scale = kv_scale;
   a.ik_out = ik_out; a.ik_scale = ik_scale; a.ik_ld = ik_ld; a.ik_fp8 = ik_dtype == LCS_IK_FP8;
+  return LCS_OK;
+}
+
+extern "C" {
+
+int kv_decode_append(const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
+                     const int64_t* pos, int B, int m, int overlap, int c, int dI, const uint16_t* gamma_kv,
+                     float eps, float rope_theta, int64_t rope_offset, float* state, size_t state_bytes,
+                     int kv_dtype, void* win, float* win_scale, int64_t win_ld, int64_t ring_cap, void* kv_out,
+                     float* kv_scale, int64_t kv_ld, int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld,
+                     int ik_dtype, void* stream) {
+  lcs::DecodeAppendArgs a;
+  const int st = append_args(kv_tok, kv_score, ik_tok, ik_score, pos, B, m, overlap, c, dI, gamma_kv, eps, rope_theta,
+                             rope_offset, state, state_bytes, kv_dtype, win, win_scale, win_ld, ring_cap, kv_out,
+                             kv_scale, kv_ld, kv_ring, ik_out, ik_scale, ik_ld, ik_dtype, &a);
+  if (st != LCS_OK) return st;
   return lcs::launch_decode_append(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 
@@ -275,10 +301,13 @@ size_t csa_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
   return lcs::index_topk_workspace(B, Tq, n_cap, k);
 }
 
-int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_cache, const float* ik_scale,
-                   int64_t ik_ld, int ik_dtype, const int64_t* q_pos, int64_t n_cap, int B, int Tq, int H_I,
-                   int dI, int m, int k, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
-                   void* stream) {
+}  // extern "C"
+
+// Checks of csa_index_topk's arguments; fills the launch arguments when they pass.
+static int index_args(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_cache, const float* ik_scale,
+                      int64_t ik_ld, int ik_dtype, const int64_t* q_pos, int64_t n_cap, int B, int Tq, int H_I,
+                      int dI, int m, int k, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                      lcs::IndexArgs* out) {
   if (!q_idx || !w_idx || !ik_cache || !q_pos || !topk_idx) return LCS_ERR_ARG;
   if (B <= 0 || Tq <= 0 || H_I <= 0 || m <= 0 || k <= 0 || n_cap <= 0 || ik_ld < n_cap) return LCS_ERR_ARG;
   if (!aligned16(q_idx) || !aligned16(ik_cache) || !aligned4(topk_idx)) return LCS_ERR_ARG;
@@ -291,10 +320,47 @@ int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_
   if (!lcs::index_topk_launchable(B, Tq, n_cap, ik_dtype == LCS_IK_FP8)) return LCS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < lcs::index_topk_workspace(B, Tq, n_cap, k)) return LCS_ERR_WORKSPACE;
   if (!aligned16(ws)) return LCS_ERR_ARG;
-  lcs::IndexArgs a;
+  lcs::IndexArgs& a = *out;
   a.q_idx = q_idx; a.w_idx = w_idx; a.ik = ik_cache; a.ik_scale = ik_scale; a.ik_ld = ik_ld;
   a.ik_fp8 = ik_dtype == LCS_IK_FP8; a.q_pos = q_pos; a.n_cap = n_cap; a.B = B; a.Tq = Tq; a.H_I = H_I;
   a.dI = dI; a.m = m; a.k = k; a.topk_idx = topk_idx; a.topk_score = topk_score; a.ws = ws; a.ws_bytes = ws_bytes;
+  a.append = nullptr;
+  return LCS_OK;
+}
+
+extern "C" {
+
+int csa_index_topk(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_cache, const float* ik_scale,
+                   int64_t ik_ld, int ik_dtype, const int64_t* q_pos, int64_t n_cap, int B, int Tq, int H_I,
+                   int dI, int m, int k, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                   void* stream) {
+  lcs::IndexArgs a;
+  const int st = index_args(q_idx, w_idx, ik_cache, ik_scale, ik_ld, ik_dtype, q_pos, n_cap, B, Tq, H_I, dI, m, k,
+                            topk_idx, topk_score, ws, ws_bytes, &a);
+  if (st != LCS_OK) return st;
+  return lcs::launch_index_topk(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
+}
+
+int csa_index_topk_append(const uint16_t* q_idx, const uint16_t* w_idx, const void* ik_cache, const float* ik_scale,
+                          int64_t ik_ld, int ik_dtype, const int64_t* q_pos, int64_t n_cap, int B, int Tq, int H_I,
+                          int dI, int m, int k, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                          const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok,
+                          const float* ik_score, const int64_t* pos, int B_app, int m_app, int overlap, int c,
+                          int dI_app, const uint16_t* gamma_kv, float eps, float rope_theta, int64_t rope_offset,
+                          float* state, size_t state_bytes, int kv_dtype, void* win, float* win_scale,
+                          int64_t win_ld, int64_t ring_cap, void* kv_out, float* kv_scale, int64_t kv_ld,
+                          int64_t kv_ring, void* ik_out, float* ik_out_scale, int64_t ik_out_ld, int ik_out_dtype,
+                          void* stream) {
+  lcs::IndexArgs a;
+  int st = index_args(q_idx, w_idx, ik_cache, ik_scale, ik_ld, ik_dtype, q_pos, n_cap, B, Tq, H_I, dI, m, k, topk_idx,
+                      topk_score, ws, ws_bytes, &a);
+  if (st != LCS_OK) return st;
+  lcs::DecodeAppendArgs ap;
+  st = append_args(kv_tok, kv_score, ik_tok, ik_score, pos, B_app, m_app, overlap, c, dI_app, gamma_kv, eps,
+                   rope_theta, rope_offset, state, state_bytes, kv_dtype, win, win_scale, win_ld, ring_cap, kv_out,
+                   kv_scale, kv_ld, kv_ring, ik_out, ik_out_scale, ik_out_ld, ik_out_dtype, &ap);
+  if (st != LCS_OK) return st;
+  a.append = &ap;
   return lcs::launch_index_topk(a, static_cast<hipStream_t>(stream)) ? LCS_ERR_HIP : LCS_OK;
 }
 

@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "decode_append.h"
 #include "kernels.h"
 
 namespace lcs {
@@ -1224,6 +1225,31 @@ topk_final_kernel(const unsigned long long* __restrict__ comb, const uint2* __re
   for (int i = threadIdx.x; i < kHistRow / 4; i += kSelThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// The final selection with a decode token append beside it: workgroups x < R select row x, the
+// next B run the append of sequence x - R on their first 128 threads.  The two touch disjoint
+// buffers (the selection's workspace and output; the append's state, ring and caches), and nothing
+// the append writes is read by this call's selection: the entry a token finishes lies past the
+// visible range of a query at that token.  One launch fewer per CSA decode layer.
+__global__ void __launch_bounds__(kSelThreads)
+topk_final_append_kernel(const unsigned long long* __restrict__ comb, const uint2* __restrict__ counts,
+                         uint32_t* __restrict__ hist, int64_t nsp, int nchunk, const int64_t* __restrict__ q_pos,
+                         int m, int64_t n_cap, int k, const float* __restrict__ scores, int32_t* __restrict__ topk_idx,
+                         float* __restrict__ topk_score, int R, DecodeAppendArgs ap, RopeFreq rf) {
+  __shared__ FinalShared sh;
+  __shared__ uint32_t s_w[kSelThreads / kWave];
+  __shared__ float red[2];
+  if ((int)blockIdx.x >= R) {
+    if (threadIdx.x >= dapp::kThreads) return;       // whole waves: the append's barriers count the rest
+    dapp::decode_append_seq(ap, rf, (int)blockIdx.x - R, red);
+    return;
+  }
+  const int64_t r = blockIdx.x;
+  final_select(sh, s_w, r, q_pos, m, n_cap, comb, counts, hist, nsp, nchunk, k, scores, topk_idx, topk_score);
+  __syncthreads();                                // every read of the level-2 histogram is done
+  uint4* h = reinterpret_cast<uint4*>(hist + r * kHistRow);
+  for (int i = threadIdx.x; i < kHistRow / 4; i += kSelThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 constexpr int kCandCache = 4096;            // candidate keys kept in LDS during the digit passes
 constexpr int kSampleBlock = 32;            // sampled run of consecutive entries (one 128-byte line)
 constexpr int kSampleBlocks = 512;          // sampled runs per row, at most
@@ -1683,8 +1709,14 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
     dim3 gf((unsigned)w.nchunk, (unsigned)R);
     LCS_LAUNCH("topk_filter_kernel", topk_filter_kernel, gf, dim3(kSelThreads), 0, st, w.scores, w.hist, w.comb,
                w.counts, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k);
-    LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
-               w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
+    if (a.append) {
+      LCS_LAUNCH("topk_final_kernel", topk_final_append_kernel, dim3((unsigned)(R + a.append->B)), dim3(kSelThreads),
+                 0, st, w.comb, w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx,
+                 a.topk_score, R, *a.append, rope_freq(a.append->theta));
+    } else {
+      LCS_LAUNCH("topk_final_kernel", topk_final_kernel, dim3((unsigned)R), dim3(kSelThreads), 0, st, w.comb,
+                 w.counts, w.hist, w.nsp, w.nchunk, a.q_pos, a.m, a.n_cap, a.k, w.scores, a.topk_idx, a.topk_score);
+    }
   } else {
     // batches of query positions: score, then select, reusing the score and candidate buffers
     prep_rows(a, w, st);
@@ -1695,6 +1727,7 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
       LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)(a.B * tcur)), dim3(kSelThreads), 0, st,
                  w.scores, w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.Tq, t0, tcur, tb, a.topk_idx, a.topk_score);
     }
+    if (a.append && launch_decode_append(*a.append, st)) return 4;
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -52,6 +52,7 @@ struct IndexArgs {
   int B, Tq, H_I, dI, m, k;
   int32_t* topk_idx; float* topk_score;
   void* ws; size_t ws_bytes;
+  const DecodeAppendArgs* append = nullptr;   // also run this token append (decode: beside the final selection)
 };
 size_t index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
 size_t index_topk_state_bytes();   // leading workspace bytes that stay zero between calls

@@ -21,7 +21,8 @@ import math
 
 import torch
 
-from . import (csa_attend, csa_compress_kv, csa_index_topk, csa_index_topk_workspace, attend_workspace,
+from . import (csa_attend, csa_compress_kv, csa_index_topk_append, csa_index_topk_workspace,
+               attend_workspace,
                grouped_out_proj, grouped_out_proj_residual, grouped_out_proj_workspace, hca_attend, hca_compress_kv,
                input_proj, kv_decode_append, kv_decode_state_bytes, kv_quantize_fp8, workspace)
 
@@ -175,10 +176,12 @@ class CsaDecodeLayer(_Common):
                     kv_scale=self.kv_sc, win_scale=self.ring_sc)
 
     def step(self):
-        m = self.m
-        self._append()
-        csa_index_topk(self.q_idx, self.w_idx, self.ik_cache, self.ik_scale, self.q_pos, n_cap=self.n_cap, m=m,
-                       k=self.k, topk_idx=self.topk, ws=self.ws_index)
+        # the token append runs inside the selection call (beside its final kernel): nothing the append
+        # writes is read by this step's selection, and the attention after it sees the new ring row
+        append = dict(kv_tok=self.new_tok.view(self.B, 512), kv_score=self.new_score.view(self.B), ik_tok=self.new_ik,
+                      ik_score=self.new_is, pos=self.q_pos.view(self.B), **self._append_kw())
+        csa_index_topk_append(self.q_idx, self.w_idx, self.ik_cache, self.ik_scale, self.q_pos, n_cap=self.n_cap,
+                              m=self.m, k=self.k, topk_idx=self.topk, ws=self.ws_index, append=append)
         csa_attend(self.q, self.gamma, self.kv_cache, self.topk, self.ring, self.sink, self.q_pos, window=self.W,
                    ring_cap=RING, out=self.o, ws=self.ws_attn, **self._attend_kw())
         self._window_and_proj_tail()

@@ -133,6 +133,28 @@ def test_decode_append_rejects_bad_arguments(lib):
     assert call(a6=0) == L.LCS_ERR_ARG
 
 
+def test_index_topk_append_checks_both_argument_sets(lib):
+    """The fused selection + append call applies each entry point's checks, all on the host."""
+    ws_need = lib.csa_index_topk_workspace(8, 1, 1000, 64)
+    need = lib.kv_decode_state_bytes(8)
+    index = [FAKE, FAKE, FAKE, FAKE, 1000, L.LCS_IK_FP8, FAKE, 1000, 8, 1, 64, 128, 4, 64, FAKE, None, FAKE, ws_need]
+    append = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 4, 512, 128, FAKE, 1e-6, 1e4, 0, FAKE, need, L.LCS_KV_BF16, FAKE,
+              None, 256, 256, FAKE, None, 1000, 0, FAKE, FAKE, 1000, L.LCS_IK_FP8]
+    def call(i=None, a=None):
+        ix, ap = list(index), list(append)
+        for k, v in (i or {}).items():
+            ix[k] = v
+        for k, v in (a or {}).items():
+            ap[k] = v
+        return lib.csa_index_topk_append(*ix, *ap, None)
+    assert call(i={17: 16}) == L.LCS_ERR_WORKSPACE          # selection workspace too small
+    assert call(i={13: 4096}) == L.LCS_ERR_UNSUPPORTED      # k
+    assert call(a={15: need - 1}) == L.LCS_ERR_WORKSPACE    # decode state too small
+    assert call(a={7: 5}) == L.LCS_ERR_UNSUPPORTED          # overlap > m
+    assert call(a={4: None}) == L.LCS_ERR_ARG               # append positions
+    assert call(a={26: None}) == L.LCS_ERR_ARG              # fp8 keys of the append need scales
+
+
 def test_kv8_entry_points_reject_bad_arguments(lib):
     assert lib.kv_quantize_fp8(FAKE, 0, FAKE, FAKE, None) == L.LCS_ERR_ARG
     assert lib.kv_quantize_fp8(ctypes.c_void_p((1 << 20) + 8), 4, FAKE, FAKE, None) == L.LCS_ERR_ARG   # alignment

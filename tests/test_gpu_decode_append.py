@@ -227,3 +227,69 @@ def test_decode_append_inactive_batch_touches_nothing():
                        kv_out=out, win=ring, ring_cap=8)
     torch.cuda.synchronize()
     assert torch.all(state == 7.0) and torch.all(ring == 3.0) and torch.all(out == 5.0)
+
+
+@pytest.mark.parametrize("kv8", [False, True])
+def test_index_topk_append_matches_separate_calls(kv8):
+    """csa_index_topk_append (the append run beside the decode selection's final kernel) leaves every
+    buffer bit for bit as kv_decode_append followed by csa_index_topk: selections, pooling state, ring
+    rows, finished entries and indexer keys.  Sequences at a block-ending token, mid-block, at a block
+    start, inactive (position -1), with the open blocks primed by earlier appends."""
+    B, m, ov, dI, H_I, k, n_cap, ring = 6, 4, 4, 128, 64, 64, 600, 256
+    t_step = np.array([2399, 2397, -1, 1203, 2000, 1204], dtype=np.int64)
+    cfg = 71
+    gamma = from_bits(synth.normal_bf16((512,), 1.0, cfg, 1))
+    kv8_dt = torch.uint8 if kv8 else torch.bfloat16
+    kv_out = torch.zeros((B, n_cap, 512), dtype=kv8_dt, device=DEV)
+    win = torch.zeros((B, ring, 512), dtype=kv8_dt, device=DEV)
+    kv_sc = torch.zeros((B, n_cap), dtype=torch.float32, device=DEV) if kv8 else None
+    win_sc = torch.zeros((B, ring), dtype=torch.float32, device=DEV) if kv8 else None
+    ik = torch.from_numpy(synth.fp8_codes((B, n_cap, dI), cfg, 2)).to(DEV)
+    iks = torch.from_numpy(synth.positive_scales((B, n_cap), cfg, 3)).to(DEV)
+    state = torch.zeros(L.kv_decode_state_bytes(B), dtype=torch.uint8, device=DEV)
+    akw = dict(m=m, overlap=ov, gamma_kv=gamma, state=state, kv_out=kv_out, win=win, ring_cap=ring, ik_out=ik,
+               ik_scale=iks, ik_fp8=True, kv_scale=kv_sc, win_scale=win_sc)
+
+    def tokens(seed):
+        return (from_bits(synth.normal_bf16((B, 512), 1.28, cfg, seed)), torch.from_numpy(
+                synth.normal_f32((B,), 1.28, cfg, seed + 1)).to(DEV),
+                from_bits(synth.normal_bf16((B, dI), 1.28, cfg, seed + 2)), torch.from_numpy(
+                synth.normal_f32((B,), 1.28, cfg, seed + 3)).to(DEV))
+
+    # prime the open blocks: the 7 tokens before each position, one append per token
+    for j in range(7, 0, -1):
+        pos = torch.from_numpy(np.where(t_step >= j, t_step - j, -1)).to(DEV)
+        L.kv_decode_append(*tokens(10 + 4 * j), pos, **akw)
+    pos = torch.from_numpy(t_step).to(DEV)
+    q_pos = pos.view(B, 1).clone()
+    q_idx = from_bits(synth.normal_bf16((B, 1, H_I, dI), 1.28, cfg, 60))
+    w_idx = from_bits(synth.normal_bf16((B, 1, H_I), 1.28, cfg, 61))
+    tok = tokens(70)
+    ws = L.workspace(L.csa_index_topk_workspace(B, 1, n_cap, k), zeroed=True)
+    bufs = [state, kv_out, win, ik, iks] + ([kv_sc, win_sc] if kv8 else [])
+    start = [t.clone() for t in bufs]
+
+    sel_a = torch.full((B, 1, k), -7, dtype=torch.int32, device=DEV)
+    L.kv_decode_append(*tok, pos, **akw)
+    L.csa_index_topk(q_idx, w_idx, ik, iks, q_pos, n_cap=n_cap, m=m, k=k, topk_idx=sel_a, ws=ws)
+    torch.cuda.synchronize()
+    after_a = [t.clone() for t in bufs]
+
+    for t, s0 in zip(bufs, start):
+        t.copy_(s0)
+    sel_b = torch.full((B, 1, k), -7, dtype=torch.int32, device=DEV)
+    L.csa_index_topk_append(q_idx, w_idx, ik, iks, q_pos, n_cap=n_cap, m=m, k=k, topk_idx=sel_b, ws=ws,
+                            append=dict(kv_tok=tok[0], kv_score=tok[1], ik_tok=tok[2], ik_score=tok[3], pos=pos, **akw))
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b)
+    for name, a, b in zip(["state", "kv_out", "win", "ik", "iks", "kv_sc", "win_sc"], after_a, bufs):
+        assert torch.equal(a, b), f"{name} differs between the fused and the separate calls"
+    # the step wrote what it should: the ring rows of the active sequences, and the entries of the
+    # blocks that end at their token (t = 2399 -> entry 599, t = 1203 -> entry 300)
+    for b in range(B):
+        t = int(t_step[b])
+        changed = not torch.equal(win[b, t % ring], start[2][b, t % ring]) if t >= 0 else False
+        assert changed == (t >= 0), f"ring row of sequence {b}"
+    assert not torch.equal(kv_out[0, 599], start[1][0, 599]) and not torch.equal(kv_out[3, 300], start[1][3, 300])
+    assert torch.equal(kv_out[1], start[1][1]) and torch.equal(kv_out[4], start[1][4])
+    assert int(ws[:L.lib().csa_index_topk_state_bytes()].count_nonzero()) == 0   # zero state kept
