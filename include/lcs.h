@@ -169,6 +169,30 @@ int hca_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv
                    uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hca_attend_append -- an HCA decode step's append and attention in one call (page 1, HCA paragraph:
+ * the token is pooled into the compressed state and attends over every visible entry and its window):
+ * kv_decode_append with the 29 arguments after ws_bytes (m and overlap: the HCA block size and 0;
+ * ik_tok may be NULL), and hca_attend (bf16) or hca_attend_kv8 (kv_dtype = LCS_KV_FP8) over the
+ * stores that append writes: cache kv_out / kv_scale with kv_ld, ring win / win_scale with win_ld and
+ * ring_cap, block size m.  The result is bit for bit that of kv_decode_append followed by the
+ * attention.  The append's workgroups run in the attention's launch; the split holding a query's own
+ * token (the window's last key) forms that row as the append does, instead of reading the ring row
+ * the append is writing.  Requirements: Tq = 1, B_app = B, kv_ring = 0, and pos[b] equal to
+ * q_pos[b, 0] or negative (inactive: the query then reads its window from the ring as stored);
+ * otherwise as the two entry points.  Every argument is checked before anything is enqueued.
+ */
+int hca_attend_append(const uint16_t* q, const uint16_t* gamma_q, int64_t n_cap, int window, const float* sink,
+                      const int64_t* q_pos, int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps,
+                      float rope_theta, uint16_t* out, void* ws, size_t ws_bytes,
+                      const uint16_t* kv_tok, const float* kv_score, const uint16_t* ik_tok, const float* ik_score,
+                      const int64_t* pos, int B_app, int m, int overlap, int c_app, int dI,
+                      const uint16_t* gamma_kv, float eps_kv, float rope_theta_kv, int64_t rope_offset_kv,
+                      float* state, size_t state_bytes, int kv_dtype,
+                      void* win, float* win_scale, int64_t win_ld, int64_t ring_cap,
+                      void* kv_out, float* kv_scale, int64_t kv_ld, int64_t kv_ring,
+                      void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype, void* stream);
+
+/*
  * mhc_sinkhorn -- the doubly stochastic projection of mHC (page 1, section on mHC: the mixing
  * matrix of the residual streams is held on the doubly stochastic matrices by Sinkhorn-Knopp,
  * alternating row and column normalisation, 20 rounds per layer; page 4 section 3.2).  For each of

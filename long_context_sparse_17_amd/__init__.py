@@ -38,6 +38,9 @@ SIGNATURES = {
     "csa_index_topk_workspace": (_SZ, [_I, _I, _I64, _I]),
     "csa_index_topk_state_bytes": (_SZ, []),
     "csa_index_topk": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_append": (_I, [_P, _P, _I64, _I, _P, _P, _I64, _I, _I, _I, _I, _F, _F, _F, _P, _P, _SZ,
+                               _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _I, _P, _P,
+                               _I64, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _I, _P]),
     "csa_index_topk_append": (_I, [_P, _P, _P, _P, _I64, _I, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ,
                                    _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _F, _I64, _P, _SZ, _I, _P, _P,
                                    _I64, _I64, _P, _P, _I64, _I64, _P, _P, _I64, _I, _P]),
@@ -249,6 +252,24 @@ def csa_index_topk(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk
     argv, ws = _index_argv(q_idx, w_idx, ik_cache, ik_scale, q_pos, n_cap=n_cap, m=m, k=k, topk_idx=topk_idx,
                            topk_score=topk_score, ws=ws)
     _check("csa_index_topk", lib().csa_index_topk(*argv, _stream(stream)))
+
+
+def hca_attend_append(q, gamma_q, sink, q_pos, *, n_cap, window, out, append, scale=None, eps=1e-6,
+                      rope_theta=10000.0, rope_offset=0, ws=None, stream=None):
+    """An HCA decode step's token append and attention in one call.  q [B,1,H,512] bf16 raw; `append`: a dict
+    of kv_decode_append's arguments (kv_tok, kv_score, ik_tok, ik_score, pos and its keywords); the
+    attention reads the cache (kv_out, kv_scale) and ring (win, win_scale) the append writes."""
+    B, Tq, H, c = q.shape
+    scale = 1.0 / (c ** 0.5) if scale is None else scale
+    if ws is None:
+        ws = workspace(attend_workspace(B, Tq, H, n_cap + window), q.device)
+    ap = dict(append)
+    aargv = _append_argv(ap.pop("kv_tok"), ap.pop("kv_score"), ap.pop("ik_tok"), ap.pop("ik_score"), ap.pop("pos"),
+                         **ap)
+    st = lib().hca_attend_append(_ptr(q), _ptr(gamma_q), n_cap, window, _ptr(sink), _ptr(q_pos), rope_offset, B, Tq,
+                                 H, c, scale, eps, rope_theta, _ptr(out), _ptr(ws), ws.numel(), *aargv,
+                                 _stream(stream))
+    _check("hca_attend_append", st)
 
 
 def csa_index_topk_append(q_idx, w_idx, ik_cache, ik_scale, q_pos, *, n_cap, m, k, topk_idx, append,

@@ -375,7 +375,8 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
                          int64_t win_ld, int64_t ring_cap, int window, const float* sink, const int64_t* q_pos,
                          int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps, float rope_theta,
                          uint16_t* out, void* ws, size_t ws_bytes, void* stream, int64_t max_keys,
-                         const float* kv_scale = nullptr, const float* win_scale = nullptr, bool kv8 = false) {
+                         const float* kv_scale = nullptr, const float* win_scale = nullptr, bool kv8 = false,
+                         const lcs::DecodeAppendArgs* append = nullptr) {
   if (!q || !gamma_q || !kv_cache || !sink || !q_pos || !out) return LCS_ERR_ARG;
   if (kv8 && (!kv_scale || !aligned4(kv_scale) || (window > 0 && (!win_scale || !aligned4(win_scale)))))
     return LCS_ERR_ARG;
@@ -400,6 +401,7 @@ static int attend_common(const uint16_t* q, const uint16_t* gamma_q, const uint1
   a.m = m; a.win = kv8 ? nullptr : win_ring; a.win_ld = win_ld; a.ring_cap = ring_cap; a.window = window; a.sink = sink;
   a.q_pos = q_pos; a.rope_offset = rope_offset; a.B = B; a.Tq = Tq; a.H = H; a.scale = scale; a.eps = eps;
   a.theta = rope_theta; a.out = out; a.ws = ws; a.ws_bytes = ws_bytes;
+  a.append = append;
   if (!win_ring) {
     // no window ring (window = 0): the kernels still form addresses for padding slots of a tile, so
     // point the ring at the cache itself (same row layout, never scored)
@@ -458,6 +460,31 @@ int hca_attend_kv8(const uint16_t* q, const uint16_t* gamma_q, const uint8_t* kv
                        reinterpret_cast<const uint16_t*>(win_codes), win_ld, ring_cap, window, sink, q_pos,
                        rope_offset, B, Tq, H, c, scale, eps, rope_theta, out, ws, ws_bytes, stream, n_cap + window,
                        kv_scale, win_scale, true);
+}
+
+int hca_attend_append(const uint16_t* q, const uint16_t* gamma_q, int64_t n_cap, int window, const float* sink,
+                      const int64_t* q_pos, int64_t rope_offset, int B, int Tq, int H, int c, float scale, float eps,
+                      float rope_theta, uint16_t* out, void* ws, size_t ws_bytes, const uint16_t* kv_tok,
+                      const float* kv_score, const uint16_t* ik_tok, const float* ik_score, const int64_t* pos,
+                      int B_app, int m, int overlap, int c_app, int dI, const uint16_t* gamma_kv, float eps_kv,
+                      float rope_theta_kv, int64_t rope_offset_kv, float* state, size_t state_bytes, int kv_dtype,
+                      void* win, float* win_scale, int64_t win_ld, int64_t ring_cap, void* kv_out, float* kv_scale,
+                      int64_t kv_ld, int64_t kv_ring, void* ik_out, float* ik_scale, int64_t ik_ld, int ik_dtype,
+                      void* stream) {
+  lcs::DecodeAppendArgs ap;
+  const int st = append_args(kv_tok, kv_score, ik_tok, ik_score, pos, B_app, m, overlap, c_app, dI, gamma_kv, eps_kv,
+                             rope_theta_kv, rope_offset_kv, state, state_bytes, kv_dtype, win, win_scale, win_ld,
+                             ring_cap, kv_out, kv_scale, kv_ld, kv_ring, ik_out, ik_scale, ik_ld, ik_dtype, &ap);
+  if (st != LCS_OK) return st;
+  // one query per sequence, the append's batch; the attention reads the stores the append writes
+  if (Tq != 1 || B_app != B || kv_ring != 0) return LCS_ERR_UNSUPPORTED;
+  if (n_cap < 0 || n_cap > kv_ld) return LCS_ERR_ARG;
+  if (window > 0 && !win) return LCS_ERR_ARG;
+  const bool kv8 = kv_dtype == LCS_KV_FP8;
+  return attend_common(q, gamma_q, static_cast<const uint16_t*>(kv_out), kv_ld, nullptr, 0, n_cap, m,
+                       static_cast<const uint16_t*>(win), win_ld, ring_cap, window, sink, q_pos, rope_offset, B, Tq,
+                       H, c, scale, eps, rope_theta, out, ws, ws_bytes, stream, n_cap + window, kv_scale, win_scale,
+                       kv8, &ap);
 }
 
 // ------------------------------------------------------------------------------ grouped projection

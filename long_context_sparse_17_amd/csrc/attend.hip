@@ -25,6 +25,7 @@
 // Keys are split across workgroups (split-K); partial (max, sum, O) are merged by merge_kernel,
 // which adds the sink once.  With one split the workgroup finishes the output itself.
 #include "common.h"
+#include "decode_append.h"
 #include "kernels.h"
 
 namespace lcs {
@@ -60,6 +61,11 @@ struct AttnK {
   int nsplit, keys_per_split;
   int halves;                          // HB = 2: workgroups per (query, split), 1 (H <= 32) or 2
   int R;                               // query rows
+  // HCA with a token append in the same launch (app_rows > 0 extra grid rows of append workgroups):
+  // a query whose token the append stores forms that window row itself (see the prologue)
+  int app_rows;
+  DecodeAppendArgs ap;
+  RopeFreq rf_ap;
 };
 
 // LDS row of tile key (block kb, row r16 of the 16x16 MFMA block) in a slice: the key itself.  With
@@ -90,6 +96,18 @@ attend_kernel(AttnK a) {
   __shared__ int32_t s_rows[kMaxSplitKeys];                 // per key of this split: cache/ring row, -1 = none
   __shared__ float4 s_sc[F8 ? kWaves : 1][2][kTile / 4];    // F8: each wave's copy of the tile's key scales
   __shared__ float2 s_ml[2][kHeadSlots];                    // HB = 2: (sum, max) of each key-block wave's head
+
+  __shared__ __align__(16) uint16_t s_self[kHeadDim];     // the query's own window row (bf16, or kv8 codes)
+  __shared__ float s_self_sc;
+
+  if (!LIST && a.app_rows > 0 && (int)blockIdx.y >= a.R) {
+    // an append workgroup: sequence (y - R) * nsplit + x on its first 128 threads
+    __shared__ float s_red2[2];
+    const int ab = ((int)blockIdx.y - a.R) * (int)gridDim.x + (int)blockIdx.x;
+    if (ab >= a.ap.B || threadIdx.x >= dapp::kThreads) return;     // whole waves
+    dapp::decode_append_seq(a.ap, a.rf_ap, ab, s_red2);
+    return;
+  }
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -130,6 +148,7 @@ attend_kernel(AttnK a) {
   uint4 kb0[2][4], kb1[2][4];
   float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};           // F8: scales of the buffers' keys kb*16 + c16
   uint32_t vb0 = 0, vb1 = 0;
+  int ib0 = 0, ib1 = kTile;                                  // first key (split index) of each buffer's tile
   if (!LIST && F8) {
     const uint8_t* kv8_b = a.kv8 + b * a.kv_ld * kHeadDim;
 #pragma unroll
@@ -217,6 +236,16 @@ attend_kernel(AttnK a) {
   if (e_end > nk) e_end = nk;
   const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
   const int nkeys = e_end > e_begin ? (int)(e_end - e_begin) : 0;
+  // The query's own token, when this launch's append stores it (HCA with an append, pos[b] = t): its
+  // window row (the last key, slot nk - 1) is being written to the ring by the append workgroups, so
+  // the split that holds it forms the row here, the way the append does, and the staging puts it in
+  // place of whatever the ring row read returns.  sk: its index in this split, or -1.
+  int sk = -1;
+  if (!LIST && a.app_rows > 0 && a.window > 0 && t_q >= 0 && a.ap.pos[b] == t_q) {
+    const int64_t s0 = nk - 1 - e_begin;
+    if (s0 >= 0 && s0 < nkeys) sk = (int)s0;
+  }
+  if (sk >= 0 && w == 0) dapp::ring_row_wave(a.ap, a.rf_ap, (int)b, t_q, s_self, &s_self_sc);   // before the barrier below
 
   // ---- the split's key rows: list entry or entry number, then window tokens (ring row); -1 where a
   //      key does not exist ----
@@ -289,6 +318,8 @@ attend_kernel(AttnK a) {
     vb1 = 0xFFFFFFFFu;
   } else {
     int32_t r0[2], r1[2];
+    ib0 = tile0(0);
+    ib1 = tile0(1);
     tile_rows(tile0(0), r0, vb0);
     issue_tile(tile0(0), r0, kb0, sc0);
     if (NB == 2) {
@@ -349,9 +380,27 @@ attend_kernel(AttnK a) {
   // Tile registers -> this wave's LDS slice of `slot` (invalid keys zeroed), then the buffer is
   // refilled with the tile at next_i0, whose rows rn and mask vn were looked up earlier.  Returns
   // the staged tile's key mask.
-  auto stage = [&](uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, int slot, int next_i0,
+  auto stage = [&](uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, int& bi0, int slot, int next_i0,
                    const int32_t (&rn)[2], uint32_t vn) -> uint32_t {
     const uint32_t vm = vmask;
+    if (sk >= bi0 && sk < bi0 + kTile) {   // uniform: this tile holds the query's own window row
+      const int j = sk - bi0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb * 16 + c16 != j) continue;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int d = 128 * w + 32 * ks + 8 * g;
+          if (F8) {
+            const uint2 cw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(s_self) + d);
+            kf[kb][ks] = make_uint4(cw.x, cw.y, 0u, 0u);
+          } else {
+            kf[kb][ks] = *reinterpret_cast<const uint4*>(&s_self[d]);
+          }
+        }
+        if (F8) sf[kb] = s_self_sc;
+      }
+    }
     if (F8) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -379,6 +428,7 @@ attend_kernel(AttnK a) {
       for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(&sl[vr * kVtStride + 32 * ks + 8 * g]) = kf[kb][ks];
     }
     issue_tile(next_i0, rn, kf, sf);
+    bi0 = next_i0;
     vmask = vn;
     return vm;
   };
@@ -513,7 +563,8 @@ attend_kernel(AttnK a) {
   for (int pass = 0;; ++pass) {
     if (pass > 0) {                        // second pass: the first tiles again
       load_tile(tile0(0), kb0, sc0, vb0);
-      if (NB == 2) load_tile(tile0(1), kb1, sc1, vb1);
+      ib0 = tile0(0);
+      if (NB == 2) { load_tile(tile0(1), kb1, sc1, vb1); ib1 = tile0(1); }
       m_ref = m_max;                       // the split's max (HB = 2: over both key-block waves)
       l_run = 0.f;
     }
@@ -524,7 +575,7 @@ attend_kernel(AttnK a) {
     int32_t rn[2];
     uint32_t vn;
     tile_rows(tile0(NB), rn, vn);
-    uint32_t vm0 = stage(kb0, sc0, vb0, 0, tile0(NB), rn, vn);  // tile 0 -> slot 0, buffer 0 <- tile NB
+    uint32_t vm0 = stage(kb0, sc0, vb0, ib0, 0, tile0(NB), rn, vn);  // tile 0 -> slot 0, buffer 0 <- tile NB
     uint32_t vm1 = 0;
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
@@ -532,15 +583,15 @@ attend_kernel(AttnK a) {
       score(0, vm0);
       if (t > 0) accumulate(1);
       // tile t+1 -> slot 1; its buffer <- tile t+1+NB
-      if (NB == 2) vm1 = stage(kb1, sc1, vb1, 1, tile0(t + 3), rn, vn);
-      else vm1 = stage(kb0, sc0, vb0, 1, tile0(t + 2), rn, vn);
+      if (NB == 2) vm1 = stage(kb1, sc1, vb1, ib1, 1, tile0(t + 3), rn, vn);
+      else vm1 = stage(kb0, sc0, vb0, ib0, 1, tile0(t + 2), rn, vn);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 >= ntiles) break;
       tile_rows(tile0(t + 2 + NB), rn, vn);
       score(1, vm1);
       accumulate(0);
-      vm0 = stage(kb0, sc0, vb0, 0, tile0(t + 2 + NB), rn, vn);  // tile t+2 -> slot 0, buffer 0 <- tile t+2+NB
+      vm0 = stage(kb0, sc0, vb0, ib0, 0, tile0(t + 2 + NB), rn, vn);  // tile t+2 -> slot 0, buffer 0 <- tile t+2+NB
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -784,12 +835,21 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
                          : dim3((unsigned)a.nsplit, (unsigned)R);
   a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
   const bool f8 = x.kv8 != nullptr;
+  a.app_rows = 0;
+  dim3 grid_k = grid;
+  if (x.append && !x.topk && !flat) {           // the append's workgroups in extra rows of the grid
+    a.ap = *x.append;
+    a.rf_ap = rope_freq(x.append->theta);
+    a.app_rows = (x.append->B + a.nsplit - 1) / a.nsplit;
+    grid_k.y += (unsigned)a.app_rows;
+  }
+  if (x.append && a.app_rows == 0 && launch_decode_append(*x.append, st)) return 4;   // other shapes: first
   if (x.topk) {
-    if (f8) launch_attend_kernel<true, true>(a, p.hb, grid, st);
-    else launch_attend_kernel<true, false>(a, p.hb, grid, st);
+    if (f8) launch_attend_kernel<true, true>(a, p.hb, grid_k, st);
+    else launch_attend_kernel<true, false>(a, p.hb, grid_k, st);
   } else {
-    if (f8) launch_attend_kernel<false, true>(a, p.hb, grid, st);
-    else launch_attend_kernel<false, false>(a, p.hb, grid, st);
+    if (f8) launch_attend_kernel<false, true>(a, p.hb, grid_k, st);
+    else launch_attend_kernel<false, false>(a, p.hb, grid_k, st);
   }
   if (a.nsplit > 1) {
     const int64_t waves = (int64_t)R * x.H;

@@ -43,6 +43,27 @@ __device__ __forceinline__ void rope4(float (&y)[4], int d0, double pos, const R
   }
 }
 
+// The window row of a token, shared by the append (128 threads, thread x: dims 4x .. 4x+3) and by
+// ring_row_wave below (one wave doing the work of threads x and x + 64), so both give the same bits.
+__device__ __forceinline__ float sq4(const float (&v)[4]) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
+__device__ __forceinline__ void norm_rope4(const float (&v)[4], const float (&g4)[4], float ss, float eps, int d0,
+                                           double pos, const RopeFreq& rf, float (&y)[4]) {
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = v[i] * rstd * g4[i];
+  rope4(y, d0, pos, rf);
+}
+__device__ __forceinline__ float absmax4(const float (&y)[4]) {
+  return fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+}
+__device__ __forceinline__ float row_scale(float amax) { return amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f; }
+__device__ __forceinline__ uint32_t codes4(const float (&y)[4], float sc) {
+  uint32_t c = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c |= f2e4m3(__fdiv_rn(y[k], sc)) << (8 * k);
+  return c;
+}
+
 // Row (b, row) of a [B, ld, 512] K=V store from this thread's 4 dims: bf16, or (kv8) E4M3FN codes with
 // the row's scale absmax / 448 (block-wide max; every thread must call it).  ok = false: not stored.
 __device__ __forceinline__ void store_kv_row(const DecodeAppendArgs& a, void* base, float* scale, int64_t b,
@@ -50,17 +71,45 @@ __device__ __forceinline__ void store_kv_row(const DecodeAppendArgs& a, void* ba
   const int x = threadIdx.x;
   const int64_t off = (b * ld + row) * kHeadDim + 4 * x;
   if (a.kv8) {
-    const float amax = block_max(fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))), red);
-    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-    uint32_t c = 0u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) c |= f2e4m3(__fdiv_rn(y[k], sc)) << (8 * k);
+    const float sc = row_scale(block_max(absmax4(y), red));
+    const uint32_t c = codes4(y, sc);
     if (ok) {
       *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + off) = c;
       if (x == 0) scale[b * ld + row] = sc;
     }
   } else if (ok) {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+  }
+}
+
+// Token t's window row of sequence b, RoPE_t(RMSNorm(kv_tok[b])), computed by one wave exactly as the
+// append computes and stores it (the reduction in the same order: two 64-lane sums added), into LDS:
+// 512 bf16 values, or (kv8) 512 E4M3FN codes and the row scale.
+__device__ __forceinline__ void ring_row_wave(const DecodeAppendArgs& a, const RopeFreq& rf, int b, int64_t t,
+                                              void* s_row, float* s_scale) {
+  const int l = lane_id();
+  float v[2][4], g4[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int x = l + 64 * h;
+    const uint2 raw = *reinterpret_cast<const uint2*>(a.kv_tok + (int64_t)b * kHeadDim + 4 * x);
+    const uint2 gm = *reinterpret_cast<const uint2*>(a.gamma + 4 * x);
+    v[h][0] = bf2f_lo(raw.x); v[h][1] = bf2f_hi(raw.x); v[h][2] = bf2f_lo(raw.y); v[h][3] = bf2f_hi(raw.y);
+    g4[h][0] = bf2f_lo(gm.x); g4[h][1] = bf2f_hi(gm.x); g4[h][2] = bf2f_lo(gm.y); g4[h][3] = bf2f_hi(gm.y);
+  }
+  const float ss = wave_sum(sq4(v[0])) + wave_sum(sq4(v[1]));
+  float y[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) norm_rope4(v[h], g4[h], ss, a.eps, 4 * (l + 64 * h), (double)(t + a.rope_offset), rf, y[h]);
+  if (a.kv8) {
+    const float sc = row_scale(wave_max(fmaxf(absmax4(y[0]), absmax4(y[1]))));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) static_cast<uint32_t*>(s_row)[l + 64 * h] = codes4(y[h], sc);
+    if (l == 0) *s_scale = sc;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      static_cast<uint2*>(s_row)[l + 64 * h] = make_uint2(pack_bf2(y[h][0], y[h][1]), pack_bf2(y[h][2], y[h][3]));
   }
 }
 
@@ -85,12 +134,9 @@ __device__ __forceinline__ void decode_append_seq(const DecodeAppendArgs& a, con
 
   // ---- window ring row t % ring_cap: RoPE_t(RMSNorm(x)) ----
   if (a.win != nullptr) {
-    const float ss = block_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3], red);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+    const float ss = block_sum(sq4(v), red);
     float y[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = v[i] * rstd * g4[i];
-    rope4(y, 4 * x, (double)(t + a.rope_offset), rf);
+    norm_rope4(v, g4, ss, a.eps, 4 * x, (double)(t + a.rope_offset), rf, y);
     store_kv_row(a, a.win, a.win_scale, b, a.win_ld, t % a.ring_cap, true, y, red);
   }
 

@@ -70,6 +70,9 @@ struct AttendArgs {
   const float* sink; const int64_t* q_pos; int64_t rope_offset;
   int B, Tq, H; float scale, eps, theta;
   uint16_t* out; void* ws; size_t ws_bytes;
+  // dense visible ranges (HCA) with one query per sequence: also run this token append (pos[b] = the
+  // query position or negative), its workgroups in the same launch
+  const DecodeAppendArgs* append = nullptr;
 };
 size_t attend_workspace(int B, int Tq, int H, int64_t max_keys);
 bool attend_launchable(int B, int Tq, int H, int64_t max_keys, bool list);

@@ -23,7 +23,8 @@ import torch
 
 from . import (csa_attend, csa_compress_kv, csa_index_topk_append, csa_index_topk_workspace,
                attend_workspace,
-               grouped_out_proj, grouped_out_proj_residual, grouped_out_proj_workspace, hca_attend, hca_compress_kv,
+               grouped_out_proj, grouped_out_proj_residual, grouped_out_proj_workspace, hca_attend_append,
+               hca_compress_kv,
                input_proj, kv_decode_append, kv_decode_state_bytes, kv_quantize_fp8, workspace)
 
 RING = 256          # window ring rows (>= the 128-token window)
@@ -80,12 +81,6 @@ class _Common:
             kv_decode_append(tok[:, j].contiguous(), score[:, j].contiguous(),
                              None if ik is None else ik[:, j].contiguous(),
                              None if iks is None else iks[:, j].contiguous(), pos, **self._append_kw())
-
-    def _append(self):
-        ik = getattr(self, "new_ik", None)
-        iks = getattr(self, "new_is", None)
-        kv_decode_append(self.new_tok.view(self.B, 512), self.new_score.view(self.B), ik, iks, self.q_pos.view(self.B),
-                         **self._append_kw())
 
     def _kv_dtype(self):
         return torch.uint8 if self.kv8 else torch.bfloat16
@@ -238,10 +233,12 @@ class HcaDecodeLayer(_Common):
                     ring_cap=RING, kv_scale=self.kv_sc, win_scale=self.ring_sc)
 
     def step(self):
-        m = self.m
-        self._append()
-        hca_attend(self.q, self.gamma, self.kv_cache, self.ring, self.sink, self.q_pos, n_cap=self.n_cap, m=m,
-                   window=self.W, ring_cap=RING, out=self.o, ws=self.ws_attn, **self._attend_kw())
+        # the token append runs in the attention's launch; the query's own window row is formed by the
+        # split that holds it, so nothing waits for the ring row the append writes
+        append = dict(kv_tok=self.new_tok.view(self.B, 512), kv_score=self.new_score.view(self.B), ik_tok=None,
+                      ik_score=None, pos=self.q_pos.view(self.B), **self._append_kw())
+        hca_attend_append(self.q, self.gamma, self.sink, self.q_pos, n_cap=self.n_cap, window=self.W, out=self.o,
+                          ws=self.ws_attn, append=append)
         self._window_and_proj_tail()
 
     def bytes_per_step(self):

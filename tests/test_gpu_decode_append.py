@@ -293,3 +293,72 @@ def test_index_topk_append_matches_separate_calls(kv8):
     assert not torch.equal(kv_out[0, 599], start[1][0, 599]) and not torch.equal(kv_out[3, 300], start[1][3, 300])
     assert torch.equal(kv_out[1], start[1][1]) and torch.equal(kv_out[4], start[1][4])
     assert int(ws[:L.lib().csa_index_topk_state_bytes()].count_nonzero()) == 0   # zero state kept
+
+
+@pytest.mark.parametrize("kv8", [False, True])
+def test_hca_attend_append_matches_separate_calls(kv8):
+    """hca_attend_append (the append's workgroups in the attention's launch, the query's own window
+    row formed by the split that holds it) gives bit for bit kv_decode_append followed by hca_attend:
+    outputs, pooling state, ring rows and entries.  Sequences at a block-ending token, mid-block and
+    inactive (position -1: the query then reads its window row as stored), many splits."""
+    B, m, H, n_cap, ring, W = 5, 128, 64, 64, 256, 128
+    t_step = np.array([64 * 128 - 1, 5000, -1, 2 * 128 - 1, 7000], dtype=np.int64)
+    cfg = 72
+    gamma = from_bits(synth.normal_bf16((512,), 1.0, cfg, 1))
+    kv8_dt = torch.uint8 if kv8 else torch.bfloat16
+    kv_out = torch.zeros((B, n_cap, 512), dtype=kv8_dt, device=DEV)
+    win = torch.zeros((B, ring, 512), dtype=kv8_dt, device=DEV)
+    kv_sc = torch.ones((B, n_cap), dtype=torch.float32, device=DEV) if kv8 else None
+    win_sc = torch.ones((B, ring), dtype=torch.float32, device=DEV) if kv8 else None
+    state = torch.zeros(L.kv_decode_state_bytes(B), dtype=torch.uint8, device=DEV)
+    akw = dict(m=m, overlap=0, gamma_kv=gamma, state=state, kv_out=kv_out, win=win, ring_cap=ring, kv_scale=kv_sc,
+               win_scale=win_sc)
+
+    def tokens(seed):
+        return (from_bits(synth.normal_bf16((B, 512), 1.28, cfg, seed)),
+                torch.from_numpy(synth.normal_f32((B,), 1.28, cfg, seed + 1)).to(DEV))
+
+    # fill the caches and rings with earlier tokens: the last 150 tokens before each position one by
+    # one (the window and the open block), the older entries drawn directly
+    if kv8:
+        kv_out.copy_(torch.from_numpy(synth.fp8_codes((B, n_cap, 512), cfg, 3)))
+        kv_sc.copy_(torch.from_numpy(synth.positive_scales((B, n_cap), cfg, 4)))
+    else:
+        kv_out.copy_(from_bits(synth.normal_bf16((B, n_cap, 512), 1.0, cfg, 3)))
+    for j in range(150, 0, -1):
+        pos = torch.from_numpy(np.where(t_step >= j, t_step - j, -1)).to(DEV)
+        kt, ks = tokens(100 + 2 * j)
+        L.kv_decode_append(kt, ks, None, None, pos, **akw)
+    pos = torch.from_numpy(t_step).to(DEV)
+    q_pos = pos.view(B, 1).clone()
+    q = from_bits(synth.normal_bf16((B, 1, H, 512), 1.28, cfg, 60))
+    sink = torch.from_numpy(synth.normal_f32((H,), 1.0, cfg, 61)).to(DEV)
+    kt, ks = tokens(70)
+    ws = L.workspace(L.attend_workspace(B, 1, H, n_cap + W))
+    bufs = [state, kv_out, win] + ([kv_sc, win_sc] if kv8 else [])
+    start = [t.clone() for t in bufs]
+    extra = dict(kv_scale=kv_sc, win_scale=win_sc) if kv8 else {}
+
+    out_a = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=DEV)
+    L.kv_decode_append(kt, ks, None, None, pos, **akw)
+    L.hca_attend(q, gamma, kv_out, win, sink, q_pos, n_cap=n_cap, m=m, window=W, ring_cap=ring, out=out_a, ws=ws,
+                 **extra)
+    torch.cuda.synchronize()
+    after_a = [t.clone() for t in bufs]
+
+    for t, s0 in zip(bufs, start):
+        t.copy_(s0)
+    out_b = torch.empty((B, 1, H, 512), dtype=torch.bfloat16, device=DEV)
+    L.hca_attend_append(q, gamma, sink, q_pos, n_cap=n_cap, window=W, out=out_b, ws=ws,
+                        append=dict(kv_tok=kt, kv_score=ks, ik_tok=None, ik_score=None, pos=pos, **akw))
+    torch.cuda.synchronize()
+    active = t_step >= 0
+    assert torch.equal(out_a[torch.from_numpy(active)], out_b[torch.from_numpy(active)])
+    for name, a, b in zip(["state", "kv_out", "win", "kv_sc", "win_sc"], after_a, bufs):
+        assert torch.equal(a, b), f"{name} differs between the fused and the separate calls"
+    # the query's own row is the last window key: the ring row the append wrote is the one scored
+    for b in range(B):
+        t = int(t_step[b])
+        if t >= 0:
+            assert not torch.equal(win[b, t % ring], start[2][b, t % ring])
+    assert not torch.equal(kv_out[0, 63], start[1][0, 63]) and not torch.equal(kv_out[3, 1], start[1][3, 1])
