@@ -139,7 +139,13 @@ attend_kernel(AttnK a) {
   if (threadIdx.x == 0) s_redo = 0;          // read after the first pass's last barrier
 
   const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
-  const int64_t t_q = a.q_pos[r];                         // first load: the RoPE table waits for it alone
+  const int64_t t_q = a.q_pos[r];                         // uniform: a scalar load
+  // this thread's RoPE frequency (threads < 32).  A selected-entry list: picked from the table with
+  // constant indices (scalar loads of the kernel arguments), so the RoPE table and the row list ahead of
+  // the first tile loads do not wait behind the q loads, as an indexed vector load would (vector loads
+  // complete in order).  Dense ranges issue their first tiles before anything else; there the indexed
+  // load, placed at its use, measured faster (the scalar table loads delay the tile loads' issue).
+  const double rinv = LIST ? rope_inv(a.rf, (int)(threadIdx.x & 31)) : a.rf.inv[threadIdx.x & 31];
   // HCA: the first two tiles are loaded speculatively at once, as entries e_begin .. e_begin+63
   // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
@@ -205,6 +211,9 @@ attend_kernel(AttnK a) {
     const bool in = e < a.k && threadIdx.x + 256 * u < a.keys_per_split;
     sel[u] = LIST ? a.topk[r * a.k + (in ? e : 0)] : 0;
   }
+  // gamma before q: loads complete in order, and the barrier below (which the first tile loads of a
+  // selected-entry list wait for) needs gamma, the list and the position, not q
+  const uint4 gam = *reinterpret_cast<const uint4*>(a.gamma_q + 8 * (threadIdx.x % (kHeadDim / 8)));
   // qhat B fragments: lane holds head c16 of block w, dims 32kk + 8g .. +8 for kk = 0..15
   uint4 qf[16];
   {
@@ -212,14 +221,13 @@ attend_kernel(AttnK a) {
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
-  const uint4 gam = *reinterpret_cast<const uint4*>(a.gamma_q + 8 * (threadIdx.x % (kHeadDim / 8)));
   __builtin_amdgcn_sched_barrier(0);
 
   // rope table for this query position (same angles for every head), while the rest is in flight
   const double pos = (double)(t_q + a.rope_offset);
   if (threadIdx.x < 32) {
     float cs, sn;
-    rope_cs(pos, a.rf.inv[threadIdx.x], &cs, &sn);
+    rope_cs(pos, rinv, &cs, &sn);
     s_cos[threadIdx.x] = cs;
     s_sin[threadIdx.x] = sn;
   }
@@ -836,6 +844,8 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
   const bool f8 = x.kv8 != nullptr;
   a.app_rows = 0;
+  a.ap = DecodeAppendArgs{};                    // no append: never read (app_rows = 0)
+  a.rf_ap = a.rf;
   dim3 grid_k = grid;
   if (x.append && !x.topk && !flat) {           // the append's workgroups in extra rows of the grid
     a.ap = *x.append;

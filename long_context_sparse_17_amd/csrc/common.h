@@ -146,6 +146,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // ----------------------------------------------------------------------------------- host side
 namespace lcs {
 RopeFreq rope_freq(float theta);
+// inv[j] for a per-thread j, picked with constant indices: when the table is a kernel argument these
+// are scalar loads, issued at once, instead of an indexed vector load that the compiler places at its
+// use, behind every vector load in flight (vector loads complete in order)
+__device__ __forceinline__ double rope_inv(const RopeFreq& rf, int j) {
+  double v = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRopeDims / 2; ++i) v = j == i ? rf.inv[i] : v;
+  return v;
+}
 // Launch timing hooks (no-ops unless lcs_timing_enable(1)).
 void timing_before(const char* name, hipStream_t s);
 void timing_after(const char* name, hipStream_t s);

@@ -36,7 +36,7 @@ __device__ __forceinline__ void rope4(float (&y)[4], int d0, double pos, const R
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     float c, s;
-    rope_cs(pos, rf.inv[(d0 - kRopeStart) / 2 + p], &c, &s);
+    rope_cs(pos, rope_inv(rf, (d0 - kRopeStart) / 2 + p), &c, &s);
     const float a0 = y[2 * p], a1 = y[2 * p + 1];
     y[2 * p] = a0 * c - a1 * s;
     y[2 * p + 1] = a0 * s + a1 * c;
