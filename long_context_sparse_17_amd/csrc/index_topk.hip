@@ -587,10 +587,10 @@ constexpr int64_t kDecodeMaxChunk = 4 * kDecodeWaveGroups * 64;
 
 // Decode scoring: one query row per workgroup, `chunk` entries per workgroup.  Loads return in order,
 // so they are issued in the order they are needed: the query rows, then the chunk's key scales
-// (staged in LDS), then each wave's first two 64-entry groups (they depend only on the chunk), so
+// (staged in LDS), then each wave's first three 64-entry groups (they depend only on the chunk), so
 // that the query preparation runs under the keys' latency: the 4 waves quantise one 16-head block
 // each into LDS (codes + folded weights).  The chunk
-// then streams in groups interleaved across waves, two groups in flight while the current group's
+// then streams in groups interleaved across waves, three groups in flight while the current group's
 // 4*HBI MFMAs run back to back.  The epilogue applies relu and the head weights, reduce-scatters the
 // 4 entry blocks over the 4 lane groups so that lane l ends with entry 64 gi + l, scales it, counts it
 // in the LDS histogram and keeps it in LDS; the chunk's scores leave in one burst of 16-byte stores at
@@ -660,7 +660,7 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     wraw = w_idx[r * H_I + hl];
   }
   // Then the chunk's scales (one 256-entry slice per pass, thread t takes entry t of each) and the
-  // first two groups of this wave (wave and wave + 4), clamped to the cache capacity: the row's
+  // first three groups of this wave (wave, wave + 4, wave + 8), clamped to the cache capacity: the row's
   // visible count is not known yet.  Entries past it are loaded in bounds and never counted; a wave
   // with fewer groups never computes the second buffer.
   constexpr int kScPasses = kDecodeMaxChunk / 256;
@@ -675,9 +675,13 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       }
     }
   }
-  Frag cur[4][KS], nxt[4][KS], nx2[4][KS];
+  // key groups in flight ahead of the one computed: 3 (four buffers) where the registers allow
+  // (fp8 keys, bf16 with dI = 64), else 2 (bf16 with dI = 128 would spill)
+  constexpr int kAhead = (FP8 || KS <= 2) ? 3 : 2;
+  Frag cur[4][KS], nxt[4][KS], nx2[4][KS], nx3[4][KS];
   load_group(wave, cl, cur);
   load_group(wave + 4, cl, nxt);
+  if (kAhead == 3) load_group(wave + 8, cl, nx2);
 
   const int64_t nv = n_visible(q_pos, r, m, n_cap);
   if (c0 >= nv) return;                                  // uniform
@@ -722,9 +726,10 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   float* srow = scores + r * nsp;
   const int64_t ngroups = (c1 - c0 + 63) / 64;
 
-  // Groups of this wave: wave + 4t, t = 0 .. nt-1.  Three register buffers rotate by unrolling (a
-  // copy between buffers would wait for the loads in flight); two groups stay in flight ahead of the
-  // one being computed.  Loads past the end re-read the last group (never computed).
+  // Groups of this wave: wave + 4t, t = 0 .. nt-1.  kAhead + 1 register buffers rotate by unrolling
+  // (a copy between buffers would wait for the loads in flight); kAhead groups stay in flight ahead of
+  // the one being computed (fp8: two in flight measured 1.5-2 us slower per launch than three).
+  // Loads past the end re-read the last group (never computed).
   const int64_t nt = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
   auto gidx = [&](int64_t t) -> int64_t { return wave + 4 * (t < nt ? t : nt - 1); };
   auto compute_group = [&](const Frag (&fr)[4][KS], int64_t gi) {
@@ -766,19 +771,37 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
     if (c0 + j < c1) atomicAdd(&lhist[float_key(v) >> kBinShift], 1u);
   };
   // Fully unrolled (nt <= kDecodeWaveGroups): straight-line code with forward exits only, so that
-  // every wait for a group's loads leaves the two younger groups in flight (a loop back edge makes
+  // every wait for a group's loads leaves the three younger groups in flight (a loop back edge makes
   // the compiler's count of loads in flight conservative).
+  if constexpr (kAhead == 3) {
 #pragma unroll
-  for (int t = 0; t < kDecodeWaveGroups; t += 3) {
-    if (t >= nt) break;
-    load_group(gidx(t + 2), c1, nx2);
-    compute_group(cur, gidx(t));
-    if (t + 1 >= nt) break;
-    load_group(gidx(t + 3), c1, cur);
-    compute_group(nxt, gidx(t + 1));
-    if (t + 2 >= nt) break;
-    load_group(gidx(t + 4), c1, nxt);
-    compute_group(nx2, gidx(t + 2));
+    for (int t = 0; t < kDecodeWaveGroups; t += 4) {
+      if (t >= nt) break;
+      load_group(gidx(t + 3), c1, nx3);
+      compute_group(cur, gidx(t));
+      if (t + 1 >= nt) break;
+      load_group(gidx(t + 4), c1, cur);
+      compute_group(nxt, gidx(t + 1));
+      if (t + 2 >= nt) break;
+      load_group(gidx(t + 5), c1, nxt);
+      compute_group(nx2, gidx(t + 2));
+      if (t + 3 >= nt) break;
+      load_group(gidx(t + 6), c1, nx2);
+      compute_group(nx3, gidx(t + 3));
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kDecodeWaveGroups; t += 3) {
+      if (t >= nt) break;
+      load_group(gidx(t + 2), c1, nx2);
+      compute_group(cur, gidx(t));
+      if (t + 1 >= nt) break;
+      load_group(gidx(t + 3), c1, cur);
+      compute_group(nxt, gidx(t + 1));
+      if (t + 2 >= nt) break;
+      load_group(gidx(t + 4), c1, nxt);
+      compute_group(nx2, gidx(t + 2));
+    }
   }
   __syncthreads();
   // Scores [c0, c1) rounded up to a multiple of 4 entries: the rounding only reaches past the row's
