@@ -140,6 +140,10 @@ attend_kernel(AttnK a) {
 
   const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
   const int64_t t_q = a.q_pos[r];                         // uniform: a scalar load
+  // with an append in this launch: wave 0 loads the query's raw token first, in case this split
+  // holds the query's own window row (known once t is; see below), ahead of every other load
+  dapp::RingRowIn self_in;
+  if (!LIST && a.app_rows > 0 && w == 0) dapp::ring_row_load(a.ap, (int)(r / a.Tq), self_in);
   // this thread's RoPE frequency (threads < 32).  A selected-entry list: picked from the table with
   // constant indices (scalar loads of the kernel arguments), so the RoPE table and the row list ahead of
   // the first tile loads do not wait behind the q loads, as an indexed vector load would (vector loads
@@ -253,7 +257,7 @@ attend_kernel(AttnK a) {
     const int64_t s0 = nk - 1 - e_begin;
     if (s0 >= 0 && s0 < nkeys) sk = (int)s0;
   }
-  if (sk >= 0 && w == 0) dapp::ring_row_wave(a.ap, a.rf_ap, (int)b, t_q, s_self, &s_self_sc);   // before the barrier below
+  if (sk >= 0 && w == 0) dapp::ring_row_compute(a.ap, a.rf_ap, t_q, self_in, s_self, &s_self_sc);   // before the barrier below
 
   // ---- the split's key rows: list entry or entry number, then window tokens (ring row); -1 where a
   //      key does not exist ----

@@ -84,18 +84,30 @@ __device__ __forceinline__ void store_kv_row(const DecodeAppendArgs& a, void* ba
 
 // Token t's window row of sequence b, RoPE_t(RMSNorm(kv_tok[b])), computed by one wave exactly as the
 // append computes and stores it (the reduction in the same order: two 64-lane sums added), into LDS:
-// 512 bf16 values, or (kv8) 512 E4M3FN codes and the row scale.
-__device__ __forceinline__ void ring_row_wave(const DecodeAppendArgs& a, const RopeFreq& rf, int b, int64_t t,
-                                              void* s_row, float* s_scale) {
+// 512 bf16 values, or (kv8) 512 E4M3FN codes and the row scale.  The loads (ring_row_load) are apart
+// so that a caller can issue them ahead of its other loads.
+struct RingRowIn {
+  uint2 raw[2], gm[2];
+};
+__device__ __forceinline__ void ring_row_load(const DecodeAppendArgs& a, int b, RingRowIn& in) {
+  const int l = lane_id();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int x = l + 64 * h;
+    in.raw[h] = *reinterpret_cast<const uint2*>(a.kv_tok + (int64_t)b * kHeadDim + 4 * x);
+    in.gm[h] = *reinterpret_cast<const uint2*>(a.gamma + 4 * x);
+  }
+}
+__device__ __forceinline__ void ring_row_compute(const DecodeAppendArgs& a, const RopeFreq& rf, int64_t t,
+                                                 const RingRowIn& in, void* s_row, float* s_scale) {
   const int l = lane_id();
   float v[2][4], g4[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int x = l + 64 * h;
-    const uint2 raw = *reinterpret_cast<const uint2*>(a.kv_tok + (int64_t)b * kHeadDim + 4 * x);
-    const uint2 gm = *reinterpret_cast<const uint2*>(a.gamma + 4 * x);
-    v[h][0] = bf2f_lo(raw.x); v[h][1] = bf2f_hi(raw.x); v[h][2] = bf2f_lo(raw.y); v[h][3] = bf2f_hi(raw.y);
-    g4[h][0] = bf2f_lo(gm.x); g4[h][1] = bf2f_hi(gm.x); g4[h][2] = bf2f_lo(gm.y); g4[h][3] = bf2f_hi(gm.y);
+    v[h][0] = bf2f_lo(in.raw[h].x); v[h][1] = bf2f_hi(in.raw[h].x);
+    v[h][2] = bf2f_lo(in.raw[h].y); v[h][3] = bf2f_hi(in.raw[h].y);
+    g4[h][0] = bf2f_lo(in.gm[h].x); g4[h][1] = bf2f_hi(in.gm[h].x);
+    g4[h][2] = bf2f_lo(in.gm[h].y); g4[h][3] = bf2f_hi(in.gm[h].y);
   }
   const float ss = wave_sum(sq4(v[0])) + wave_sum(sq4(v[1]));
   float y[2][4];
