@@ -234,9 +234,10 @@ int mhc_mix(const uint16_t* x, const uint16_t* y, const float* logits, int T, in
  *          histograms are cleared by the call's last kernel), so one workspace serves any sequence of
  *          calls, of any shapes, without further clearing; calls that share a workspace must be
  *          ordered (one stream).
- *   Many-row calls (prefill) score and select batches of query positions, tb = min(Tq, max(16,
- *   768 / B rounded down to a multiple of 16)) of every batch row at a time, so the workspace holds
- *   B * tb score and candidate rows, not B * Tq.
+ *   Many-row calls (prefill) whose score and candidate rows would exceed 64 MiB for all queries
+ *   (B * Tq * n_cap' * 12 bytes, n_cap' = n_cap rounded up to a multiple of 64) score and select
+ *   batches of query positions, tb = min(Tq, max(16, 768 / B rounded down to a multiple of 16)) of
+ *   every batch row at a time, so the workspace holds B * tb score and candidate rows, not B * Tq.
  *   Requirements: H_I <= 64, dI in {64, 128} (fp8: 128), 1 <= k <= 2048, m >= 1, B * Tq <= 65535 * 16,
  *   and launch grids within the device limits (many-row calls: B * ceil(tb / 16) <= 65535 with bf16
  *   keys, about B <= 65000 with fp8 keys); otherwise LCS_ERR_UNSUPPORTED before anything runs.

@@ -68,11 +68,15 @@ inline int64_t n_chunks(int64_t n_cap) { return (n_cap + kFilterChunk - 1) / kFi
 // rows whatever Tq is.  tb is a multiple of 16 (the bf16 scorer's query tile, and a multiple of the
 // fp8 scorer's 4-query stage) unless one batch covers all of Tq.  768 rows are one round of the
 // selection kernel (3 workgroups per CU on 256 CUs): a batch that leaves a partial second round
-// costs more than the extra launches.
+// costs more than the extra launches.  Calls whose buffers for all rows (12 bytes per row and
+// entry) stay within kPfOneBatchBytes run as one batch: there the launches of more batches cost more
+// than the buffers save.
 constexpr int kPfBatchRows = 768;
-inline int prefill_batch(int B, int Tq) {
+constexpr int64_t kPfOneBatchBytes = (int64_t)64 << 20;
+inline int prefill_batch(int B, int Tq, int64_t n_cap) {
   const int want = kPfBatchRows / B;
-  if (Tq <= want || Tq <= 16) return Tq;
+  const int64_t nsp = (n_cap + 63) & ~(int64_t)63;
+  if (Tq <= want || Tq <= 16 || (int64_t)B * Tq * nsp * 12 <= kPfOneBatchBytes) return Tq;
   const int tb = want / 16 * 16;
   return tb < 16 ? 16 : tb;
 }
@@ -81,7 +85,7 @@ inline bool decode_rows(int B, int Tq, int64_t n_cap) {
 }
 // rows of the score and candidate buffers: every row at decode, one batch of queries otherwise
 inline int64_t buffer_rows(int B, int Tq, int64_t n_cap) {
-  return decode_rows(B, Tq, n_cap) ? (int64_t)B * Tq : (int64_t)B * prefill_batch(B, Tq);
+  return decode_rows(B, Tq, n_cap) ? (int64_t)B * Tq : (int64_t)B * prefill_batch(B, Tq, n_cap);
 }
 
 inline int64_t n_groups4(int B, int Tq) { return (int64_t)B * ((Tq + 3) / 4); }
@@ -1699,7 +1703,7 @@ bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
   const int64_t R = (int64_t)B * Tq;
   if (R < kDecodeRows && n_chunks(n_cap) <= kMaxDecodeChunks) return true;   // decode grids (chunks, R)
   if (R >= ((int64_t)1 << 31)) return false;                         // one workgroup per row
-  const int tb = prefill_batch(B, Tq);                 // query positions per batch launch
+  const int tb = prefill_batch(B, Tq, n_cap);          // query positions per batch launch
   if ((int64_t)B * tb >= ((int64_t)1 << 31)) return false;
   if (ik_fp8) {
     const PfGrid p = prefill_grid(B, tb, n_cap);
@@ -1743,7 +1747,7 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
   } else {
     // batches of query positions: score, then select, reusing the score and candidate buffers
     prep_rows(a, w, st);
-    const int tb = prefill_batch(a.B, a.Tq);
+    const int tb = prefill_batch(a.B, a.Tq, a.n_cap);
     for (int t0 = 0; t0 < a.Tq; t0 += tb) {
       const int tcur = a.Tq - t0 < tb ? a.Tq - t0 : tb;
       score_rows(a, w, t0, tcur, tb, st);

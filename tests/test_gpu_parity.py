@@ -246,10 +246,12 @@ def test_index_topk_prefill_fp8_head_blocks_ragged(H_I, Tq, n_cap):
 
 @pytest.mark.parametrize("B,Tq,H_I,dI,fp8", [(3, 700, 16, 128, True), (2, 1100, 8, 64, False)])
 def test_index_topk_prefill_query_batches(B, Tq, H_I, dI, fp8):
-    # many rows are scored and selected in batches of query positions (B * batch <= 768 rows of
-    # buffers): 3 x 700 runs batches of 256, 256 and 188 positions, 2 x 1100 of 384, 384 and 332, so
-    # batch edges, a short last batch and every batch row are covered, with rows from empty to full
-    n_cap, k = 900, 64
+    # many rows whose buffers exceed 64 MiB are scored and selected in batches of query positions
+    # (B * batch <= 768 rows of buffers): 3 x 700 rows of 3008 entries runs batches of 256, 256 and
+    # 188 positions, 2 x 1100 of 384, 384 and 332, so batch edges, a short last batch and every batch
+    # row are covered, with rows from empty to full
+    n_cap, k = 3000, 64
+    assert L.csa_index_topk_workspace(B, Tq, n_cap, k) < B * Tq * 3008 * 12   # less than one batch would need
     pos = []
     for b in range(B):
         if b % 2 == 0:
