@@ -42,6 +42,7 @@ typedef __attribute__((address_space(1))) const u32x2 GU32x2;
 typedef __bf16 bf16x2_cv __attribute__((ext_vector_type(2)));
 constexpr int kVtStride = 136;            // bf16 per LDS row of a 128-dim slice (128 + 8 pad: rows 4 banks apart)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr bf16x2_cv kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 LdsV4i16;   // LDS operand of the transpose read
 typedef __attribute__((address_space(3))) const uint16_t LdsU16;
@@ -89,7 +90,7 @@ attend_kernel(AttnK a) {
   constexpr int kHeadSlots = 16 * HB;                       // heads of one workgroup
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
   __shared__ uint2 s_p[2][HB * kWave][2];                   // P fragments [slot][head block][lane][key block]
-  __shared__ uint4 s_gamma[kHeadDim / 8];                  // gamma_q (bf16)
+  __shared__ float4 s_gamma[kHeadDim / 4];                 // gamma_q (fp32)
   __shared__ int s_redo;                                    // some head's running max jumped: second pass
   __shared__ float s_fac[kHeadSlots];
   __shared__ float s_cos[32], s_sin[32];
@@ -278,7 +279,10 @@ attend_kernel(AttnK a) {
       s_rows[i] = i >= nkeys ? -1 : (e < nc ? crow : wrow);
     }
   }
-  if (threadIdx.x < kHeadDim / 8) s_gamma[threadIdx.x] = gam;   // gamma: 1 KiB, staged once in LDS
+  if (threadIdx.x < kHeadDim / 8) {          // gamma: staged once in LDS, as fp32
+    s_gamma[2 * threadIdx.x] = make_float4(bf2f_lo(gam.x), bf2f_hi(gam.x), bf2f_lo(gam.y), bf2f_hi(gam.y));
+    s_gamma[2 * threadIdx.x + 1] = make_float4(bf2f_lo(gam.z), bf2f_hi(gam.z), bf2f_lo(gam.w), bf2f_hi(gam.w));
+  }
   __syncthreads();
   const uint16_t* win_b = a.win ? a.win + b * a.win_ld * kHeadDim : a.kv;
   const int nc_local = nc > e_begin ? (int)(nc - e_begin) : 0;   // split keys that are compressed
@@ -341,30 +345,33 @@ attend_kernel(AttnK a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- qhat = RoPE(RMSNorm(q) * gamma) for head c16 of block w (zero for a padding head) ----
+  // ---- qhat = RoPE(RMSNorm(q) * gamma) for head c16 of block w (zero for a padding head).  The
+  //      fragments hold RoPE(q * gamma); the head's 1 / rms, a scalar, multiplies its logits instead
+  //      (the rotation is linear), which saves a multiply per element here and costs none there ----
+  float lsc;                               // this lane's head: logit scale (log2 domain) / rms
   {
     float acc = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const uint4 x = qf[kk];
-      const float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
-                          bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += v[j] * v[j];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_cv, x.x), __builtin_bit_cast(bf16x2_cv, x.x), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_cv, x.y), __builtin_bit_cast(bf16x2_cv, x.y), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_cv, x.z), __builtin_bit_cast(bf16x2_cv, x.z), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_cv, x.w), __builtin_bit_cast(bf16x2_cv, x.w), acc, false);
     }
     acc = sum_rows4(acc);
     const float rstd = head_ok ? 1.0f / sqrtf(acc * (1.0f / kHeadDim) + a.eps) : 0.f;
+    lsc = a.scale_log2 * rstd;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int d = 32 * kk + 8 * g;
       const uint4 x = qf[kk];
-      const uint4 gm = s_gamma[4 * kk + g];   // dims 32kk + 8g .. +8
+      const float4 g0 = s_gamma[8 * kk + 2 * g], g1 = s_gamma[8 * kk + 2 * g + 1];   // dims 32kk + 8g .. +8
       float v[8] = {bf2f_lo(x.x), bf2f_hi(x.x), bf2f_lo(x.y), bf2f_hi(x.y),
                     bf2f_lo(x.z), bf2f_hi(x.z), bf2f_lo(x.w), bf2f_hi(x.w)};
-      const float gv[8] = {bf2f_lo(gm.x), bf2f_hi(gm.x), bf2f_lo(gm.y), bf2f_hi(gm.y),
-                           bf2f_lo(gm.z), bf2f_hi(gm.z), bf2f_lo(gm.w), bf2f_hi(gm.w)};
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] * rstd * gv[j];
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * gv[j];
       if (d >= kRopeStart) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -491,17 +498,26 @@ attend_kernel(AttnK a) {
         ksc[kb][0] = f.x; ksc[kb][1] = f.y; ksc[kb][2] = f.z; ksc[kb][3] = f.w;
       }
     }
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bool mine = HB == 4 || kb == kbq;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool v = (both || mine) && ((vm >> (kb * 16 + 4 * g + i)) & 1u);
-        sc[kb][i] = v ? acc[kb][i] * (F8 ? ksc[kb][i] * a.scale_log2 : a.scale_log2) : -INFINITY;
-        tmax = fmaxf(tmax, sc[kb][i]);
+      for (int i = 0; i < 4; ++i) sc[kb][i] = acc[kb][i] * (F8 ? ksc[kb][i] * lsc : lsc);
+    if (vm != 0xFFFFFFFFu || HB == 2) {    // uniform: missing keys, or key blocks not scored here
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool mine = HB == 4 || kb == kbq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool v = (both || mine) && ((vm >> (kb * 16 + 4 * g + i)) & 1u);
+          sc[kb][i] = v ? sc[kb][i] : -INFINITY;
+        }
       }
     }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
     tmax = max_rows4(tmax);
     m_max = fmaxf(m_max, tmax);
     if (m_ref == -INFINITY) {
@@ -518,7 +534,7 @@ attend_kernel(AttnK a) {
       if (mr != -INFINITY) {
         float pe[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pe[i] = exp2f(sc[kb][i] - mr);
+        for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[kb][i] - mr);   // arguments <= kJump
         if (F8) {
           // PV weights bf16(p_j s_j); the normaliser sums the same rounded weights over s_j, so
           // numerator and denominator see one rounding of p_j, as in the bf16 path
@@ -532,7 +548,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             pk[j] = pack_bf2(pe[2 * j], pe[2 * j + 1]);
-            psum += bf2f_lo(pk[j]) + bf2f_hi(pk[j]);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_cv, pk[j]), kOnes2, psum, false);
           }
         }
       }
@@ -647,13 +663,13 @@ attend_kernel(AttnK a) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int hh = hb * 16 + c16;
-    const float fac = single ? s_fac[hh] : 1.f;   // partials: factor 1
+    const float fac = single ? s_fac[hh] : 1.f;   // partials: factor 1 (exact)
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int d = 128 * w + 16 * db + 4 * g;     // dims d .. d + 3 of head hh
       float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = single ? o[hb][db][i] * fac : o[hb][db][i];
+      for (int i = 0; i < 4; ++i) v[i] = o[hb][db][i] * fac;
       if (w == kWaves - 1 && 16 * db >= kRopeStart - 128 * (kWaves - 1)) {
         // dims >= 448 (last wave, db >= 4): rotate the pairs (d, d + 1), (d + 2, d + 3) by -(t + offset)
 #pragma unroll
