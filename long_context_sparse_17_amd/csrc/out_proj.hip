@@ -288,6 +288,118 @@ tile_gemm_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* _
   }
 }
 
+// Large prefill shapes (M >= 512): 256 x 256 blocks, one workgroup of 8 waves per CU (two per SIMD),
+// each wave owning 128 rows x 64 features (4 x 8 MFMA tiles, 128 accumulators).  A wave reads 0.375
+// KiB of fragments from LDS per MFMA instead of 0.5 (128 x 128 blocks of 64 x 64 waves).  Same slice
+// pipeline as tile_gemm_kernel: K in slices of 64 through double-buffered LDS (global -> registers ->
+// LDS, rows 144 B apart), one barrier per slice.
+constexpr int kTg2 = 256;                  // block rows and features
+constexpr int kTg2Threads = 512;
+constexpr int kTg2Chunks = kTg2 * kTgK / 8 / kTg2Threads;   // 16 B chunks per thread per operand slice (4)
+
+__global__ void __launch_bounds__(kTg2Threads, 1)
+tile_gemm256_kernel(const uint16_t* __restrict__ X, int64_t x_ld, const uint16_t* __restrict__ W, uint16_t* Y,
+                    int64_t y_ld, int M, int K, int n_per_group, const uint16_t* R, int64_t r_ld) {
+  __shared__ __align__(16) uint16_t sw[2][kTg2 * kTgStride];
+  __shared__ __align__(16) uint16_t sxm[2][kTg2 * kTgStride];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wn = w & 3, wm = w >> 2;       // this wave's features n0 + 64 wn .., rows m0 + 128 wm ..
+  const int n0 = blockIdx.x * kTg2;
+  const int m0 = blockIdx.y * kTg2;
+  const int64_t xoff = (int64_t)(n0 / n_per_group) * K;
+
+  // global -> register staging: chunk q = tid + 512 j is row q / 8, k-chunk q % 8 of the slice; rows
+  // past M read row M - 1 (never stored)
+  const int kc = threadIdx.x & 7, row0 = threadIdx.x >> 3;   // rows row0 + 64 j
+  const uint16_t* wbase = W + (int64_t)(n0 + row0) * K + 8 * kc;
+  const uint16_t* xbase = X + xoff + 8 * kc;
+  const bool xfull = m0 + kTg2 <= M;                          // uniform: every block row exists
+  const int lds0 = row0 * kTgStride + 8 * kc;                // + 64 j rows
+  floatx4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  static_assert(kTg2Chunks == 4, "four staging chunks per operand");
+  // X row offsets of the thread's 4 chunks (rows past M: row M - 1)
+  int64_t xr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = xfull || m0 + row0 + 64 * j < M ? m0 + row0 + 64 * j : M - 1;
+    xr[j] = (int64_t)m * x_ld;
+  }
+  const int64_t wr = (int64_t)64 * K;
+#define LCS_TG2_FETCH(k0)                                                             \
+  const uint4 nw0 = *reinterpret_cast<const uint4*>(wbase + (k0));                    \
+  const uint4 nw1 = *reinterpret_cast<const uint4*>(wbase + wr + (k0));               \
+  const uint4 nw2 = *reinterpret_cast<const uint4*>(wbase + 2 * wr + (k0));           \
+  const uint4 nw3 = *reinterpret_cast<const uint4*>(wbase + 3 * wr + (k0));           \
+  const uint4 nx0 = *reinterpret_cast<const uint4*>(xbase + xr[0] + (k0));            \
+  const uint4 nx1 = *reinterpret_cast<const uint4*>(xbase + xr[1] + (k0));            \
+  const uint4 nx2 = *reinterpret_cast<const uint4*>(xbase + xr[2] + (k0));            \
+  const uint4 nx3 = *reinterpret_cast<const uint4*>(xbase + xr[3] + (k0));
+#define LCS_TG2_COMMIT(slot)                                                          \
+  *reinterpret_cast<uint4*>(&sw[slot][lds0]) = nw0;                                   \
+  *reinterpret_cast<uint4*>(&sw[slot][lds0 + 64 * kTgStride]) = nw1;                  \
+  *reinterpret_cast<uint4*>(&sw[slot][lds0 + 128 * kTgStride]) = nw2;                 \
+  *reinterpret_cast<uint4*>(&sw[slot][lds0 + 192 * kTgStride]) = nw3;                 \
+  *reinterpret_cast<uint4*>(&sxm[slot][lds0]) = nx0;                                  \
+  *reinterpret_cast<uint4*>(&sxm[slot][lds0 + 64 * kTgStride]) = nx1;                 \
+  *reinterpret_cast<uint4*>(&sxm[slot][lds0 + 128 * kTgStride]) = nx2;                \
+  *reinterpret_cast<uint4*>(&sxm[slot][lds0 + 192 * kTgStride]) = nx3;
+  // one 64-deep slice: per 32-deep step, the wave's 4 W fragments, then each X fragment against all 4
+  auto multiply = [&](int slot) {
+#pragma unroll
+    for (int ks = 0; ks < kTgK / 32; ++ks) {
+      uint4 fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)                     // W rows (features) wn*64 + 16i + c16
+        fa[i] = *reinterpret_cast<const uint4*>(&sw[slot][(wn * 64 + 16 * i + c16) * kTgStride + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {                   // X rows wm*128 + 16j + c16
+        const uint4 fb = *reinterpret_cast<const uint4*>(&sxm[slot][(wm * 128 + 16 * j + c16) * kTgStride + 32 * ks + 8 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma_bf16(fa[i], fb, acc[i][j]);
+      }
+    }
+  };
+  const int nk = K / kTgK;
+  {
+    LCS_TG2_FETCH(0)
+    LCS_TG2_COMMIT(0)
+  }
+  __syncthreads();
+  for (int t = 0; t + 1 < nk; ++t) {
+    LCS_TG2_FETCH((t + 1) * kTgK)                     // slice t + 1 in flight while slice t is multiplied
+    multiply(t & 1);
+    LCS_TG2_COMMIT((t + 1) & 1)                       // that slot was last read before the previous barrier
+    __syncthreads();
+  }
+  multiply((nk - 1) & 1);
+#undef LCS_TG2_FETCH
+#undef LCS_TG2_COMMIT
+
+  // acc[i][j]: lane holds row m0 + wm*128 + 16j + c16, features n0 + wn*64 + 16i + 4g .. +3
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + wm * 128 + 16 * j + c16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + wn * 64 + 16 * i + 4 * g;
+      float y0 = acc[i][j][0], y1 = acc[i][j][1], y2 = acc[i][j][2], y3 = acc[i][j][3];
+      if (R != nullptr) {
+        const uint2 rv = *reinterpret_cast<const uint2*>(R + (int64_t)m * r_ld + n);
+        y0 += bf2f_lo(rv.x); y1 += bf2f_hi(rv.x); y2 += bf2f_lo(rv.y); y3 += bf2f_hi(rv.y);
+      }
+      *reinterpret_cast<uint2*>(Y + (int64_t)m * y_ld + n) = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+    }
+  }
+}
+
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Y = X . W^T for one stage: the staged-X kernel at the decode shapes, else the general one.
@@ -301,6 +413,9 @@ void launch_stage(const char* name, const uint16_t* X, int64_t x_ld, const uint1
   } else if (M <= 8 && K == 8192) {
     LCS_LAUNCH(name, (rowblock_gemv_kernel<8192, false>), dim3((unsigned)(N / 16)), dim3(kWaves * 64), 0, st, X, x_ld,
                W, Y, y_ld, M, n_per_group, R, r_ld, none);
+  } else if (M >= 512 && N % kTg2 == 0 && n_per_group % kTg2 == 0 && K % kTgK == 0) {
+    LCS_LAUNCH(name, tile_gemm256_kernel, dim3((unsigned)(N / kTg2), (unsigned)((M + kTg2 - 1) / kTg2)),
+               dim3(kTg2Threads), 0, st, X, x_ld, W, Y, y_ld, M, K, n_per_group, R, r_ld);
   } else if (M >= 64 && N % kTgN == 0 && n_per_group % kTgN == 0 && K % kTgK == 0) {
     LCS_LAUNCH(name, tile_gemm_kernel, dim3((unsigned)(N / kTgN), (unsigned)((M + kTgM - 1) / kTgM)), dim3(kTgThreads),
                0, st, X, x_ld, W, Y, y_ld, M, K, n_per_group, R, r_ld);
