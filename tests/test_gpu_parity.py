@@ -522,9 +522,11 @@ def test_hca_attend_prefill_rows_with_rope_offset():
 
 # ----------------------------------------------------------------------------------- projection
 # M = 8: the decode GEMV; 3 and 37: the row-block kernel; 64, 130 and 300 rows: the tiled prefill GEMM
-# (one and several 128-row blocks, ragged last block, one group and eight)
+# (one and several 128-row blocks, ragged last block, one group and eight); 600 rows: the 256 x 256
+# blocks (two whole row blocks and a ragged one, two groups of 256 features, then one group)
 @pytest.mark.parametrize("M,H,g,d_g,d", [(8, 64, 8, 1024, 4096), (3, 16, 2, 64, 96), (37, 8, 1, 32, 48),
-                                         (64, 16, 2, 128, 256), (130, 8, 1, 128, 384), (300, 64, 8, 1024, 4096)])
+                                         (64, 16, 2, 128, 256), (130, 8, 1, 128, 384), (300, 64, 8, 1024, 4096),
+                                         (600, 16, 2, 256, 512)])
 def test_grouped_out_proj_parity(M, H, g, d_g, d):
     cfg = 60 + M
     o = synth.normal_bf16((M, H * 512), 0.3, cfg, 1)

@@ -43,7 +43,8 @@ def test_input_proj_segments(M, d):
 
 @pytest.mark.parametrize("M,H,g,d_g,d,inplace", [(8, 64, 8, 1024, 4096, False), (8, 64, 8, 1024, 4096, True),
                                                   (37, 8, 2, 64, 96, False), (200, 16, 2, 128, 256, True),
-                                                  (200, 16, 2, 128, 256, False)])
+                                                  (200, 16, 2, 128, 256, False), (600, 16, 2, 256, 512, True),
+                                                  (600, 16, 2, 256, 512, False)])
 def test_grouped_out_proj_residual(M, H, g, d_g, d, inplace):
     o = synth.normal_bf16((M, H * 512), 1.0, 190 + M, 1)
     wg = synth.normal_bf16((g, d_g, H // g * 512), 0.02, 190 + M, 2)
