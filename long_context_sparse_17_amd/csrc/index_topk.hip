@@ -1518,38 +1518,58 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
     const double expect = (double)k * S / (double)nv;        // sample entries expected above the k-th
     const int j = (int)ceil(expect + 3.0 * sqrt(expect) + 8.0);
     if (j <= S / 2) {
-      auto sample_key = [&](int i) { return float_key(srow[(i / kSampleBlock) * stride + i % kSampleBlock]); };
+      // the thread's sample keys (entries tid + 256 u), all loads in flight at once, kept in registers
+      // for both histogram levels
+      constexpr int kSampPer = kSampleBlocks * kSampleBlock / kSelThreads;   // 64
+      uint32_t sk[kSampPer];
+#pragma unroll
+      for (int u = 0; u < kSampPer; ++u) {
+        const int i = tid + kSelThreads * u;
+        const int ic = i < S ? i : 0;                         // a readable entry
+        sk[u] = float_key(srow[(ic / kSampleBlock) * stride + ic % kSampleBlock]);
+      }
       for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
       if (tid == 0) { sT = -1; sAbove = 0; sCand = 0; s.nsel = 0; }
       __syncthreads();
-      for (int i = tid; i < S; i += kSelThreads) atomicAdd(&h[sample_key(i) >> kBinShift], 1u);
+#pragma unroll
+      for (int u = 0; u < kSampPer; ++u)
+        if (tid + kSelThreads * u < S) atomicAdd(&h[sk[u] >> kBinShift], 1u);
       __syncthreads();
       find_threshold(h, j, &sT, &sAbove, s.scan);          // bin of the sample's j-th largest key
       const int T1 = sT, rem = j - sAbove;
       for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < S; i += kSelThreads) {
-        const uint32_t key = sample_key(i);
-        if ((int)(key >> kBinShift) == T1) atomicAdd(&h[(key >> (kBinShift - 11)) & (kBins - 1)], 1u);
-      }
+#pragma unroll
+      for (int u = 0; u < kSampPer; ++u)
+        if (tid + kSelThreads * u < S && (int)(sk[u] >> kBinShift) == T1)
+          atomicAdd(&h[(sk[u] >> (kBinShift - 11)) & (kBins - 1)], 1u);
       __syncthreads();
       find_threshold(h, rem, &sT, &sAbove, s.scan);        // ... refined by its next 11 bits
       const uint32_t thr = ((uint32_t)T1 << kBinShift) | ((uint32_t)sT << (kBinShift - 11));
-      // one pass: 16 consecutive entries per thread per round, wave-aggregated appends
+      // one pass: 16 consecutive entries per thread per round, wave-aggregated appends.  The loads
+      // are unconditional (clamped into the row's buffer, entries past nv masked after) and the
+      // next round's are in flight while a round is filtered (two register sets, alternating).
       const int lane = lane_id();
-      for (int64_t e0 = 0; e0 < nv; e0 += 16 * kSelThreads) {
+      constexpr int64_t kRound = 16 * kSelThreads;
+      auto load16 = [&](int64_t e0, float4& x0, float4& x1, float4& x2, float4& x3) {
+        int64_t eb = e0 + 16 * tid;
+        eb = eb < nsp - 16 ? eb : nsp - 16;                // readable: nsp is a multiple of 64
+        const float4* p = reinterpret_cast<const float4*>(srow + eb);
+        x0 = p[0]; x1 = p[1]; x2 = p[2]; x3 = p[3];
+      };
+      auto filter16 = [&](int64_t e0, const float4& x0, const float4& x1, const float4& x2, const float4& x3) {
         const int64_t eb = e0 + 16 * tid;
+        const float4 xs[4] = {x0, x1, x2, x3};
         uint32_t keys[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {                     // eb < nv: eb + 16 <= nsp (a multiple of 64)
-          const float4 x = eb < nv ? *reinterpret_cast<const float4*>(srow + eb + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-          keys[4 * q] = float_key(x.x); keys[4 * q + 1] = float_key(x.y);
-          keys[4 * q + 2] = float_key(x.z); keys[4 * q + 3] = float_key(x.w);
+        for (int q = 0; q < 4; ++q) {
+          keys[4 * q] = float_key(xs[q].x); keys[4 * q + 1] = float_key(xs[q].y);
+          keys[4 * q + 2] = float_key(xs[q].z); keys[4 * q + 3] = float_key(xs[q].w);
         }
         uint32_t keep = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) keep |= (eb + i < nv && keys[i] >= thr ? 1u : 0u) << i;
-        if (__ballot(keep != 0u) == 0ull) continue;           // wave-uniform: nothing kept
+        if (__ballot(keep != 0u) == 0ull) return;             // wave-uniform: nothing kept
         const uint32_t c = (uint32_t)__popc(keep);
         const uint32_t incl = wave_incl_scan(c);
         uint32_t base = 0;
@@ -1559,6 +1579,15 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
         for (int i = 0; i < 16; ++i)
           if ((keep >> i) & 1u)
             crow[base++] = ((unsigned long long)keys[i] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(eb + i));
+      };
+      float4 a0, a1, a2, a3, b0, b1, b2, b3;
+      load16(0, a0, a1, a2, a3);
+      for (int64_t e0 = 0; e0 < nv; e0 += 2 * kRound) {
+        load16(e0 + kRound, b0, b1, b2, b3);
+        filter16(e0, a0, a1, a2, a3);
+        if (e0 + kRound >= nv) break;                       // uniform
+        load16(e0 + 2 * kRound, a0, a1, a2, a3);
+        filter16(e0 + kRound, b0, b1, b2, b3);
       }
       __syncthreads();
       const int ncand = sCand;
