@@ -1304,11 +1304,12 @@ struct SelShared {
 // Resolve `need` winners among `ncand` candidate keys digit by digit and append their entry indices
 // to sel_list.  A key is `key_bits` wide: the score-key bits (all 32, or the 21 below a common bin),
 // then the complemented entry index (32 bits).  Keys are read once into LDS when they fit.
+// in_lds: the candidates are already in s.u.ckey (ncand <= kCandCache), cand is not read.
 __device__ __forceinline__ void refine_candidates(const unsigned long long* cand, int ncand, int need, int32_t* sel_list,
-                                  SelShared& s, int key_bits = 53) {
+                                  SelShared& s, int key_bits = 53, bool in_lds = false) {
   const int tid = threadIdx.x;
   const bool cached = ncand <= kCandCache;
-  if (cached) {                          // all loads first, then the LDS stores (one round trip)
+  if (cached && !in_lds) {               // all loads first, then the LDS stores (one round trip)
     constexpr int kPer = kCandCache / kSelThreads;
     unsigned long long v[kPer];
 #pragma unroll
@@ -1557,7 +1558,11 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
         const float4* p = reinterpret_cast<const float4*>(srow + eb);
         x0 = p[0]; x1 = p[1]; x2 = p[2]; x3 = p[3];
       };
-      auto filter16 = [&](int64_t e0, const float4& x0, const float4& x1, const float4& x2, const float4& x3) {
+      // TO_LDS: candidates go to the refine phase's LDS key array (positions past it are counted, not
+      // stored), so the pass's memory counter holds only its loads; else to the row's global list
+      auto filter16 = [&](auto to_lds_c, int64_t e0, const float4& x0, const float4& x1, const float4& x2,
+                          const float4& x3) {
+        constexpr bool kToLds = decltype(to_lds_c)::value;
         const int64_t eb = e0 + 16 * tid;
         const float4 xs[4] = {x0, x1, x2, x3};
         uint32_t keys[16];
@@ -1577,22 +1582,44 @@ topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __rest
         base = __shfl(base, kWave - 1, kWave) + incl - c;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if ((keep >> i) & 1u)
-            crow[base++] = ((unsigned long long)keys[i] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(eb + i));
+          if ((keep >> i) & 1u) {
+            const unsigned long long v = ((unsigned long long)keys[i] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)(eb + i));
+            if (kToLds) {
+              if (base < (uint32_t)kCandCache) s.u.ckey[base] = v;
+            } else {
+              crow[base] = v;
+            }
+            ++base;
+          }
       };
-      float4 a0, a1, a2, a3, b0, b1, b2, b3;
-      load16(0, a0, a1, a2, a3);
-      for (int64_t e0 = 0; e0 < nv; e0 += 2 * kRound) {
-        load16(e0 + kRound, b0, b1, b2, b3);
-        filter16(e0, a0, a1, a2, a3);
-        if (e0 + kRound >= nv) break;                       // uniform
-        load16(e0 + 2 * kRound, a0, a1, a2, a3);
-        filter16(e0 + kRound, b0, b1, b2, b3);
-      }
+      auto run_pass = [&](auto to_lds_c) {
+        float4 a0, a1, a2, a3, b0, b1, b2, b3;
+        load16(0, a0, a1, a2, a3);
+        for (int64_t e0 = 0; e0 < nv; e0 += 2 * kRound) {
+          load16(e0 + kRound, b0, b1, b2, b3);
+          __builtin_amdgcn_sched_barrier(0);               // the next round's loads go out first
+          filter16(to_lds_c, e0, a0, a1, a2, a3);
+          if (e0 + kRound >= nv) break;                     // uniform
+          load16(e0 + 2 * kRound, a0, a1, a2, a3);
+          __builtin_amdgcn_sched_barrier(0);
+          filter16(to_lds_c, e0 + kRound, b0, b1, b2, b3);
+        }
+      };
+      run_pass(std::true_type{});
       __syncthreads();
-      const int ncand = sCand;
+      int ncand = sCand;
+      bool in_lds = true;
+      if (ncand > kCandCache) {                             // uniform, rare: the pass again, to HBM
+        __syncthreads();                                    // every thread has read sCand
+        if (tid == 0) sCand = 0;
+        __syncthreads();
+        run_pass(std::false_type{});
+        __syncthreads();
+        ncand = sCand;
+        in_lds = false;
+      }
       if (ncand >= k) {                                    // uniform
-        refine_candidates(crow, ncand, k, list, s, 64);
+        refine_candidates(crow, ncand, k, list, s, 64, in_lds);
         sort_and_write(list, k, nv, k, srow, topk_idx + r * k, topk_score ? topk_score + r * k : nullptr, s);
         return;
       }
