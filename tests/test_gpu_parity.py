@@ -289,7 +289,8 @@ def test_index_topk_prefill_sampled_threshold_falls_back():
 def test_index_topk_prefill_sampled_threshold_top_ties():
     # Half of each long row is one repeated key with a scale 64x the others' and positive head
     # weights, so it scores on top: the sampled threshold keeps ~6000 tied candidates (more than the
-    # LDS cache holds, so the digit passes read them from global memory) and the k winners must be
+    # LDS array holds, so the candidate pass runs again into global memory and the digit passes read
+    # them from there) and the k winners must be
     # the lowest indices among the ties.  (The oracle's fp64 matrix products may round equal rows
     # differently by position, so its own order among the ties is not the reference here: the tie
     # rule is, and the within-bound check of every row still runs.)
