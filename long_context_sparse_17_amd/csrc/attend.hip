@@ -24,6 +24,8 @@
 // accumulated, tile t+1 is moved from registers to LDS and tiles t+2, t+3 are in flight from HBM.
 // Keys are split across workgroups (split-K); partial (max, sum, O) are merged by merge_kernel,
 // which adds the sink once.  With one split the workgroup finishes the output itself.
+#include <type_traits>
+
 #include "common.h"
 #include "decode_append.h"
 #include "kernels.h"
@@ -84,7 +86,9 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 // tiles are converted to bf16 (exactly) when staged in LDS, and each key's scale multiplies its
 // logit and, for PV, its probability (o = sum_j p_j s_j code_j), so the MFMAs are those of the bf16
 // path on the codes.
-template <bool LIST, bool F8, int HB>
+// PAD: some head blocks of a workgroup may hold padding heads only (H < 16 HB per workgroup); they are
+// neither scored nor accumulated.  Without PAD every head block holds a real head.
+template <bool LIST, bool F8, int HB, bool PAD>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
   constexpr int kHeadSlots = 16 * HB;                       // heads of one workgroup
@@ -132,6 +136,9 @@ attend_kernel(AttnK a) {
   const int hl = 16 * hq + c16;           // this lane's head slot in QK^T and the softmax
   const int head = head0 + hl;
   const bool head_ok = head < a.H;
+  // head blocks of the workgroup that hold a real head (fewer than HB when H < 16 HB): the others are
+  // neither scored nor accumulated
+  const int nvb = !PAD || a.H - head0 >= 16 * HB ? HB : (a.H - head0 + 15) / 16;
 
   // Key slots of a row: CSA takes the k list slots (entries < 0 are skipped) then the window tokens,
   // at fixed positions, so a split's range needs no scan of the list; HCA takes the n_vis visible
@@ -481,6 +488,7 @@ attend_kernel(AttnK a) {
     acc = ae + ao;
   };
   auto score = [&](int slot, uint32_t vm) {
+    if (PAD && hq >= nvb) return;          // wave-uniform: a head block of padding heads only
     floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     const bool both = HB == 4 || m_ref == -INFINITY;       // uniform: -inf only before a tile with a key
     if (both) {
@@ -559,10 +567,12 @@ attend_kernel(AttnK a) {
   };
 
   // O[:, this wave's 128 dims] += P V for the tile in `slot`.
-  auto accumulate = [&](int slot) {
+  // NV: the head blocks accumulated (a compile-time count, so the full case has no per-block test)
+  auto accumulate_nv = [&](int slot, auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
     uint4 pf[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+    for (int hb = 0; hb < NV; ++hb) {
       const uint2 lo = s_p[slot][hb * kWave + lane][0], hi = s_p[slot][hb * kWave + lane][1];
       pf[hb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
@@ -580,8 +590,14 @@ attend_kernel(AttnK a) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       const uint4 vf = make_uint4(l2.x, l2.y, h2.x, h2.y);
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
+      for (int hb = 0; hb < NV; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
     }
+  };
+  auto accumulate = [&](int slot) {
+    if (PAD && nvb == 1) accumulate_nv(slot, std::integral_constant<int, 1>{});
+    else if (PAD && HB == 4 && nvb == 2) accumulate_nv(slot, std::integral_constant<int, (HB == 4 ? 2 : 1)>{});
+    else if (PAD && HB == 4 && nvb == 3) accumulate_nv(slot, std::integral_constant<int, (HB == 4 ? 3 : 1)>{});
+    else accumulate_nv(slot, std::integral_constant<int, HB>{});
   };
 
   // Pipeline: iteration t scores tile t (slot t & 1), accumulates tile t-1 (slot (t-1) & 1), stages
@@ -662,6 +678,7 @@ attend_kernel(AttnK a) {
   static_assert(sizeof(s_kv) >= kHeadSlots * kOStride * 2, "output staging fits the tile buffers");
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
+    if (PAD && hb >= nvb) break;           // uniform: padding heads are not stored
     const int hh = hb * 16 + c16;
     const float fac = single ? s_fac[hh] : 1.f;   // partials: factor 1 (exact)
 #pragma unroll
@@ -794,15 +811,16 @@ int keys_per_split(int R, int halves, int64_t max_keys) {
 }
 
 // The layout a call runs with.  Selected entries (CSA) of few query rows (decode): HB = 2, whose
-// halved split partials cut the epilogue and merge that dominate a short key list.  All visible
-// entries (HCA) and many rows (prefill, one split per row): HB = 4, whose loop keeps twice the unique
-// bytes in flight per CU and reads each tile once.
+// halved split partials cut the epilogue and merge that dominate a short key list.  At most 32 heads:
+// HB = 2 too (32 head slots hold every head; 64 would be half padding or more).  All visible entries
+// (HCA) and many rows (prefill, one split per row) of more heads: HB = 4, whose loop keeps twice the
+// unique bytes in flight per CU and reads each tile once.
 struct AttendPlan {
   int hb, halves, keys_per_split, nsplit;
 };
 AttendPlan attend_plan(int R, int H, int64_t max_keys, bool list) {
   AttendPlan p;
-  p.hb = list && R < 128 ? 2 : 4;
+  p.hb = (list && R < 128) || H <= 32 ? 2 : 4;   // H <= 32: 32 head slots are enough
   p.halves = p.hb == 2 && H > 32 ? 2 : 1;
   p.keys_per_split = p.hb == 2 ? keys_per_split<2>(R, p.halves, max_keys) : keys_per_split<4>(R, 1, max_keys);
   p.nsplit = max_keys > 0 ? (int)((max_keys + p.keys_per_split - 1) / p.keys_per_split) : 1;
@@ -836,8 +854,11 @@ template <bool LIST, bool F8>
 void launch_attend_kernel(const AttnK& a, int hb, dim3 grid, hipStream_t st) {
   // timing labels: selected-entry lists (CSA) and dense visible ranges (HCA) apart
   const char* name = LIST ? "attend_csa_kernel" : "attend_hca_kernel";
-  if (hb == 2) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2>), grid, dim3(256), 0, st, a);
-  else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4>), grid, dim3(256), 0, st, a);
+  const bool pad = a.H < 16 * hb * (hb == 2 ? a.halves : 1);   // some workgroup has padding-only head blocks
+  if (hb == 2 && pad) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2, true>), grid, dim3(256), 0, st, a);
+  else if (hb == 2) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2, false>), grid, dim3(256), 0, st, a);
+  else if (pad) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true>), grid, dim3(256), 0, st, a);
+  else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, false>), grid, dim3(256), 0, st, a);
 }
 
 int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {

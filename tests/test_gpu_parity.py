@@ -521,6 +521,25 @@ def test_hca_attend_prefill_rows_with_rope_offset():
     _attend_case("hca", 1, 40, 64, 0, 40, 128, 128, 0, pos, 54, rope_offset=12345)
 
 
+@pytest.mark.parametrize("kind,H", [("csa", 40), ("hca", 40), ("hca", 24)])
+def test_attend_head_blocks_of_padding_only(kind, H):
+    # head counts that leave a workgroup's last block(s) of 16 head slots without a real head: CSA
+    # decode with 40 heads in two halves of 32 slots (heads 32..39 in the second), HCA with 40 heads
+    # in 64 slots (blocks 0..2 hold heads) and 24 heads in 32 slots
+    if kind == "csa":
+        _attend_case("csa", 2, 2, H, 200, 900, 4, 128, 256, [4 * 900 + 2, 37, 4 * 500, 130], 181 + H)
+    else:
+        _attend_case("hca", 3, 1, H, 0, 700, 128, 128, 128, [128 * 700 + 5, 128 * 350 + 127, 0], 183 + H)
+
+
+@pytest.mark.parametrize("H", [40, 8])
+def test_csa_attend_many_rows_padding_head_blocks(H):
+    # 130 query rows (the many-row layout, one split per row) with 40 heads (64 slots, one block of
+    # padding) and 8 heads (32 slots, one block holds all of them)
+    pos = [1000 + 3 * i for i in range(130)]
+    _attend_case("csa", 1, 130, H, 64, 300, 4, 64, 0, pos, 185 + H)
+
+
 # ----------------------------------------------------------------------------------- projection
 # M = 8: the decode GEMV; 3 and 37: the row-block kernel; 64, 130 and 300 rows: the tiled prefill GEMM
 # (one and several 128-row blocks, ragged last block, one group and eight); 600 rows: the 256 x 256
