@@ -37,6 +37,7 @@ namespace {
 constexpr int kTile = 32;                 // keys per tile
 constexpr int kWaves = 4;                 // waves per workgroup = 128-dim slices
 constexpr int kMaxSplitKeys = 2048;       // keys of one split, staged as row indices in LDS
+constexpr int kMaxBlockEntries = 2048;    // row blocks (QB > 1): cache entries a bitmap covers
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 GU32x4;   // global address space: global_load, not flat
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -88,22 +89,30 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 // path on the codes.
 // PAD: some head blocks of a workgroup may hold padding heads only (H < 16 HB per workgroup); they are
 // neither scored nor accumulated.  Without PAD every head block holds a real head.
-template <bool LIST, bool F8, int HB, bool PAD>
+// QB > 1 (selected-entry lists of many query rows with H = 64 / QB heads): a workgroup takes QB
+// consecutive rows of one sequence, head slot s holding head s % H of row s / H, so all 64 slots
+// hold real heads.  Its keys are the union of the rows' list entries (one bitmap per row over the
+// cache, at most kMaxBlockEntries entries), ascending, then the union of the rows' windows; each
+// slot keeps only the logits of its own row's keys (a per-row mask of every tile).  One split.
+template <bool LIST, bool F8, int HB, bool PAD, int QB = 1>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
+  static_assert(QB == 1 || (LIST && HB == 4 && PAD), "row blocks: selected-entry lists, 64 head slots");
   constexpr int kHeadSlots = 16 * HB;                       // heads of one workgroup
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
   __shared__ uint2 s_p[2][HB * kWave][2];                   // P fragments [slot][head block][lane][key block]
   __shared__ float4 s_gamma[kHeadDim / 4];                 // gamma_q (fp32)
   __shared__ int s_redo;                                    // some head's running max jumped: second pass
   __shared__ float s_fac[kHeadSlots];
-  __shared__ float s_cos[32], s_sin[32];
+  __shared__ float s_cos[QB][32], s_sin[QB][32];           // RoPE table of each row's position
   __shared__ int32_t s_rows[kMaxSplitKeys];                 // per key of this split: cache/ring row, -1 = none
   __shared__ float4 s_sc[F8 ? kWaves : 1][2][kTile / 4];    // F8: each wave's copy of the tile's key scales
   __shared__ float2 s_ml[2][kHeadSlots];                    // HB = 2: (sum, max) of each key-block wave's head
 
   __shared__ __align__(16) uint16_t s_self[kHeadDim];     // the query's own window row (bf16, or kv8 codes)
   __shared__ float s_self_sc;
+  __shared__ uint32_t s_bits[QB][QB > 1 ? kMaxBlockEntries / 32 : 1];   // QB > 1: each row's entries
+  __shared__ int s_nu;                                      // QB > 1: entries in the union
 
   if (!LIST && a.app_rows > 0 && (int)blockIdx.y >= a.R) {
     // an append workgroup: sequence (y - R) * nsplit + x on its first 128 threads
@@ -129,16 +138,26 @@ attend_kernel(AttnK a) {
     split = (int)(u % a.nsplit);
     hh = (int)(blockIdx.x >> 3) & 1;
   }
+  int nrows = 1;                          // QB > 1: rows of the block (fewer in a sequence's last block)
+  if (QB > 1) {
+    const int nblk = (a.Tq + QB - 1) / QB;
+    const int q0 = (int)(blockIdx.y % nblk) * QB;
+    r = (int64_t)(blockIdx.y / nblk) * a.Tq + q0;
+    nrows = a.Tq - q0 < QB ? a.Tq - q0 : QB;
+  }
   const int64_t b = r / a.Tq;
   const int hq = HB == 4 ? w : (w & 1);   // head block this wave scores
   const int kbq = HB == 4 ? 0 : (w >> 1); // HB = 2: the key block of each tile it scores
   const int head0 = 32 * hh;              // first head of the workgroup
   const int hl = 16 * hq + c16;           // this lane's head slot in QK^T and the softmax
-  const int head = head0 + hl;
-  const bool head_ok = head < a.H;
+  constexpr int kH = 64 / QB;             // QB > 1: the heads of every row
+  const int qi = QB > 1 ? hl / kH : 0;    // QB > 1: this lane's row in the block
+  const int head = QB > 1 ? hl % kH : head0 + hl;
+  const bool head_ok = QB > 1 ? qi < nrows : head < a.H;
   // head blocks of the workgroup that hold a real head (fewer than HB when H < 16 HB): the others are
   // neither scored nor accumulated
-  const int nvb = !PAD || a.H - head0 >= 16 * HB ? HB : (a.H - head0 + 15) / 16;
+  const int nvb = QB > 1 ? (nrows * kH + 15) / 16
+                         : !PAD || a.H - head0 >= 16 * HB ? HB : (a.H - head0 + 15) / 16;
 
   // Key slots of a row: CSA takes the k list slots (entries < 0 are skipped) then the window tokens,
   // at fixed positions, so a split's range needs no scan of the list; HCA takes the n_vis visible
@@ -147,7 +166,24 @@ attend_kernel(AttnK a) {
   if (threadIdx.x == 0) s_redo = 0;          // read after the first pass's last barrier
 
   const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
-  const int64_t t_q = a.q_pos[r];                         // uniform: a scalar load
+  int64_t t_q = a.q_pos[r];                               // uniform: a scalar load (QB > 1: the last)
+  int64_t t_lo = t_q;                                     // QB > 1: the block's first position
+  int64_t t_r[QB > 4 ? 2 : 1] = {0};                      // QB > 1: positions of rows g (and g + 4)
+  if (QB > 1) {
+#pragma unroll
+    for (int i = 1; i < QB; ++i) {
+      if (i < nrows) {
+        const int64_t t = a.q_pos[r + i];
+        t_q = t > t_q ? t : t_q;
+        t_lo = t < t_lo ? t : t_lo;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < (QB > 4 ? 2 : 1); ++h) {
+      const int qr = g + 4 * h < nrows ? g + 4 * h : nrows - 1;
+      t_r[h] = a.q_pos[r + qr];
+    }
+  }
   // with an append in this launch: wave 0 loads the query's raw token first, in case this split
   // holds the query's own window row (known once t is; see below), ahead of every other load
   dapp::RingRowIn self_in;
@@ -166,6 +202,7 @@ attend_kernel(AttnK a) {
   uint4 kb0[2][4], kb1[2][4];
   float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};           // F8: scales of the buffers' keys kb*16 + c16
   uint32_t vb0 = 0, vb1 = 0;
+  uint32_t lb0 = 0, lb1 = 0;                                 // QB > 1: the buffers' per-row key masks
   int ib0 = 0, ib1 = kTile;                                  // first key (split index) of each buffer's tile
   if (!LIST && F8) {
     const uint8_t* kv8_b = a.kv8 + b * a.kv_ld * kHeadDim;
@@ -221,7 +258,7 @@ attend_kernel(AttnK a) {
   for (int u = 0; u < kPer; ++u) {                        // unconditional (clamped) loads
     const int64_t e = e_begin + threadIdx.x + 256 * u;
     const bool in = e < a.k && threadIdx.x + 256 * u < a.keys_per_split;
-    sel[u] = LIST ? a.topk[r * a.k + (in ? e : 0)] : 0;
+    sel[u] = LIST && QB == 1 ? a.topk[r * a.k + (in ? e : 0)] : 0;
   }
   // gamma before q: loads complete in order, and the barrier below (which the first tile loads of a
   // selected-entry list wait for) needs gamma, the list and the position, not q
@@ -229,29 +266,81 @@ attend_kernel(AttnK a) {
   // qhat B fragments: lane holds head c16 of block w, dims 32kk + 8g .. +8 for kk = 0..15
   uint4 qf[16];
   {
-    const uint16_t* qrow = a.q + (r * a.H + (head_ok ? head : a.H - 1)) * kHeadDim + 8 * g;
+    const int64_t qrw = QB > 1 ? (r + (head_ok ? qi : 0)) * a.H + head : r * a.H + (head_ok ? head : a.H - 1);
+    const uint16_t* qrow = a.q + qrw * kHeadDim + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qf[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // rope table for this query position (same angles for every head), while the rest is in flight
-  const double pos = (double)(t_q + a.rope_offset);
-  if (threadIdx.x < 32) {
+  // (QB > 1: one table per row, threads 32 qr .. 32 qr + 31 for row qr)
+  if (threadIdx.x < 32 * QB) {
+    const int qr = QB > 1 ? (int)(threadIdx.x >> 5) : 0;
+    const int64_t tq = QB > 1 ? a.q_pos[r + (qr < nrows ? qr : nrows - 1)] : t_q;
+    const double pos = (double)(tq + a.rope_offset);
     float cs, sn;
     rope_cs(pos, rinv, &cs, &sn);
-    s_cos[threadIdx.x] = cs;
-    s_sin[threadIdx.x] = sn;
+    s_cos[qr][threadIdx.x & 31] = cs;
+    s_sin[qr][threadIdx.x & 31] = sn;
+  }
+
+  // QB > 1: one bitmap per row of its list entries (entries < 0 or past the cache are no key), their
+  // union compacted into s_rows in ascending order by wave 0 (lane l: entries 32 l .. 32 l + 31)
+  if (QB > 1) {
+    constexpr int kWords = kMaxBlockEntries / 32;
+    for (int i = threadIdx.x; i < QB * kWords; i += 256) s_bits[i / kWords][i % kWords] = 0u;
+    __syncthreads();
+    const int n_list = nrows * a.k;
+    for (int i0 = 0; i0 < n_list; i0 += 4 * 256) {
+      int32_t ev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {                       // unconditional (clamped) loads
+        const int i = i0 + 256 * u + (int)threadIdx.x;
+        ev[u] = a.topk[r * a.k + (i < n_list ? i : 0)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 256 * u + (int)threadIdx.x;
+        const int32_t e = ev[u];
+        if (i < n_list && e >= 0 && e < a.kv_ld) atomicOr(&s_bits[i / a.k][e >> 5], 1u << (e & 31));
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      uint32_t un = 0u;
+#pragma unroll
+      for (int q = 0; q < QB; ++q) un |= s_bits[q][lane];
+      const int cnt = __popc(un);
+      int incl = cnt;                                     // inclusive prefix over the lanes
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      int at = incl - cnt;
+      while (un != 0u) {
+        s_rows[at++] = 32 * lane + __ffs(un) - 1;
+        un &= un - 1u;
+      }
+      if (lane == kWave - 1) s_nu = incl;
+    }
+    __syncthreads();
   }
 
   int64_t nc;                                             // compressed key slots of the row
-  if (LIST) {
+  if (QB > 1) {
+    nc = s_nu;
+  } else if (LIST) {
     nc = a.k;
   } else {
     const int64_t nv = t_q >= 0 ? t_q / a.m : 0;
     nc = nv < a.n_cap ? nv : a.n_cap;
   }
-  const int64_t nk = nc + a.window;
+  // QB > 1: the rows' windows as one range of tokens j_lo .. t_q (a token no row uses is no key)
+  const int64_t j_lo = QB > 1 ? (t_lo - a.window + 1 > 0 ? t_lo - a.window + 1 : 0) : 0;
+  const int64_t nwin = QB > 1 ? (a.window > 0 && t_q >= j_lo ? t_q - j_lo + 1 : 0) : a.window;
+  const int64_t nk = nc + nwin;
   int64_t e_end = e_begin + a.keys_per_split;
   if (e_end > nk) e_end = nk;
   const int ntiles = e_end > e_begin ? (int)((e_end - e_begin + kTile - 1) / kTile) : 0;
@@ -268,8 +357,8 @@ attend_kernel(AttnK a) {
   if (sk >= 0 && w == 0) dapp::ring_row_compute(a.ap, a.rf_ap, t_q, self_in, s_self, &s_self_sc);   // before the barrier below
 
   // ---- the split's key rows: list entry or entry number, then window tokens (ring row); -1 where a
-  //      key does not exist ----
-  {
+  //      key does not exist (QB > 1: s_rows holds the union's entries; window rows are formed per tile) ----
+  if (QB == 1) {
     const int64_t j0 = t_q - a.window + 1;                // first window token
     // ring row of token j0 + off (0 <= off < window <= ring_cap): one modulo per row
     const int64_t jm0 = a.ring_cap > 0 && j0 > 0 ? j0 % a.ring_cap : j0;
@@ -295,12 +384,70 @@ attend_kernel(AttnK a) {
   const int nc_local = nc > e_begin ? (int)(nc - e_begin) : 0;   // split keys that are compressed
 
   // ---- tile loads: lane (g, c16) fetches dims 128w + 32ks + 8g of keys kb*16 + c16 ----
-  // rows of keys kb*16 + c16 (s_rows is -1 past the split's keys; i0 + 32 <= kMaxSplitKeys)
-  auto tile_rows = [&](int i0, int32_t (&rr)[2], uint32_t& vmask) {
+  // QB > 1: ring row of window token j_lo + off (off < nwin); one wrap when nwin <= ring_cap
+  const int64_t jm_lo = QB > 1 && a.ring_cap > 0 ? j_lo % a.ring_cap : j_lo;
+  const bool wrap_once = a.ring_cap <= 0 || nwin <= a.ring_cap;
+  // rows of keys kb*16 + c16 (s_rows is -1 past the split's keys; i0 + 32 <= kMaxSplitKeys).  lmask
+  // (QB > 1): bit j is set where key j of the tile is a key of this lane's row; vmask then marks the
+  // keys of any row of the block (the others are not keys)
+  auto tile_rows = [&](int i0, int32_t (&rr)[2], uint32_t& vmask, uint32_t& lmask) {
+    if (QB == 1) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) rr[kb] = s_rows[i0 + kb * 16 + c16];
-    const uint32_t b0 = (uint32_t)__ballot(rr[0] >= 0), b1 = (uint32_t)__ballot(rr[1] >= 0);
-    vmask = (b0 & 0xFFFFu) | (b1 << 16);   // bit j: key j of the tile exists (lanes 0..15 hold keys c16)
+      for (int kb = 0; kb < 2; ++kb) rr[kb] = s_rows[i0 + kb * 16 + c16];
+      const uint32_t b0 = (uint32_t)__ballot(rr[0] >= 0), b1 = (uint32_t)__ballot(rr[1] >= 0);
+      vmask = (b0 & 0xFFFFu) | (b1 << 16);   // bit j: key j of the tile exists (lanes 0..15 hold keys c16)
+      lmask = vmask;
+      return;
+    }
+    // QB > 1: lane (g, c16) decides key kb*16 + c16 for rows g and g + 4
+    constexpr int NH = QB > 4 ? 2 : 1;
+    uint64_t bal[2][NH];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int i = i0 + kb * 16 + c16;
+      int32_t row = -1;
+      int64_t j = -1;                                     // window token, or -1 for an entry
+      if (i < nc_local) {
+        row = s_rows[i];
+      } else if (i < nkeys) {
+        const int64_t off = (int64_t)(i - nc_local);
+        j = j_lo + off;
+        int64_t jr = jm_lo + off;
+        if (a.ring_cap > 0) {
+          if (wrap_once) jr = jr >= a.ring_cap ? jr - a.ring_cap : jr;
+          else jr %= a.ring_cap;
+        }
+        row = (int32_t)jr;
+      }
+      rr[kb] = row;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int qr = g + 4 * h;
+        bool in = false;
+        if (qr < nrows && row >= 0) {
+          if (j < 0) in = (s_bits[qr][row >> 5] >> (row & 31)) & 1u;
+          else in = j > t_r[h] - a.window && j <= t_r[h];
+        }
+        bal[kb][h] = __ballot(in);
+      }
+    }
+    // row q's bits of key block kb: bits 16 (q & 3) .. +15 of bal[kb][q >> 2]
+    uint32_t any[2] = {0u, 0u};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint64_t x = bal[kb][h];
+        any[kb] |= (uint32_t)(x | (x >> 16) | (x >> 32) | (x >> 48)) & 0xFFFFu;
+      }
+    vmask = any[0] | (any[1] << 16);
+    const int hsel = qi >> 2, csel = 16 * (qi & 3);
+    const uint64_t x0 = NH == 2 && hsel ? bal[0][NH - 1] : bal[0][0];
+    const uint64_t x1 = NH == 2 && hsel ? bal[1][NH - 1] : bal[1][0];
+    lmask = ((uint32_t)(x0 >> csel) & 0xFFFFu) | (((uint32_t)(x1 >> csel) & 0xFFFFu) << 16);
+    // a key of no row is not loaded
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) rr[kb] = (vmask >> (kb * 16 + c16)) & 1u ? rr[kb] : -1;
   };
   auto issue_tile = [&](int i0, const int32_t (&rr)[2], uint4 (&kf)[2][4], float (&sf)[2]) {
 #pragma unroll
@@ -328,9 +475,9 @@ attend_kernel(AttnK a) {
       }
     }
   };
-  auto load_tile = [&](int i0, uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask) {
+  auto load_tile = [&](int i0, uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, uint32_t& lmask) {
     int32_t rr[2];
-    tile_rows(i0, rr, vmask);
+    tile_rows(i0, rr, vmask, lmask);
     issue_tile(i0, rr, kf, sf);
   };
   // The register buffers; an empty split reads row 0.  A load past the end re-reads the last
@@ -343,10 +490,10 @@ attend_kernel(AttnK a) {
     int32_t r0[2], r1[2];
     ib0 = tile0(0);
     ib1 = tile0(1);
-    tile_rows(tile0(0), r0, vb0);
+    tile_rows(tile0(0), r0, vb0, lb0);
     issue_tile(tile0(0), r0, kb0, sc0);
     if (NB == 2) {
-      tile_rows(tile0(1), r1, vb1);
+      tile_rows(tile0(1), r1, vb1, lb1);
       issue_tile(tile0(1), r1, kb1, sc1);
     }
   }
@@ -383,7 +530,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int jr = (d + 2 * p - kRopeStart) >> 1;
-          const float cs = s_cos[jr], sn = s_sin[jr];
+          const float cs = s_cos[qi][jr], sn = s_sin[qi][jr];
           const float a0 = v[2 * p], a1 = v[2 * p + 1];
           v[2 * p] = a0 * cs - a1 * sn;
           v[2 * p + 1] = a0 * sn + a1 * cs;
@@ -406,9 +553,10 @@ attend_kernel(AttnK a) {
   // Tile registers -> this wave's LDS slice of `slot` (invalid keys zeroed), then the buffer is
   // refilled with the tile at next_i0, whose rows rn and mask vn were looked up earlier.  Returns
   // the staged tile's key mask.
-  auto stage = [&](uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, int& bi0, int slot, int next_i0,
-                   const int32_t (&rn)[2], uint32_t vn) -> uint32_t {
+  auto stage = [&](uint4 (&kf)[2][4], float (&sf)[2], uint32_t& vmask, uint32_t& lmask, int& bi0, int slot,
+                   int next_i0, const int32_t (&rn)[2], uint32_t vn, uint32_t ln, uint32_t& lm) -> uint32_t {
     const uint32_t vm = vmask;
+    lm = lmask;
     if (sk >= bi0 && sk < bi0 + kTile) {   // uniform: this tile holds the query's own window row
       const int j = sk - bi0;
 #pragma unroll
@@ -456,6 +604,7 @@ attend_kernel(AttnK a) {
     issue_tile(next_i0, rn, kf, sf);
     bi0 = next_i0;
     vmask = vn;
+    lmask = ln;
     return vm;
   };
 
@@ -487,7 +636,7 @@ attend_kernel(AttnK a) {
     }
     acc = ae + ao;
   };
-  auto score = [&](int slot, uint32_t vm) {
+  auto score = [&](int slot, uint32_t vm, uint32_t lm) {
     if (PAD && hq >= nvb) return;          // wave-uniform: a head block of padding heads only
     floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
     const bool both = HB == 4 || m_ref == -INFINITY;       // uniform: -inf only before a tile with a key
@@ -510,13 +659,14 @@ attend_kernel(AttnK a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[kb][i] = acc[kb][i] * (F8 ? ksc[kb][i] * lsc : lsc);
-    if (vm != 0xFFFFFFFFu || HB == 2) {    // uniform: missing keys, or key blocks not scored here
+    if (QB > 1 || vm != 0xFFFFFFFFu || HB == 2) {   // uniform: missing keys, or key blocks not scored here
+      const uint32_t mk = QB > 1 ? lm : vm;            // QB > 1: the keys of this lane's row
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bool mine = HB == 4 || kb == kbq;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool v = (both || mine) && ((vm >> (kb * 16 + 4 * g + i)) & 1u);
+          const bool v = (both || mine) && ((mk >> (kb * 16 + 4 * g + i)) & 1u);
           sc[kb][i] = v ? sc[kb][i] : -INFINITY;
         }
       }
@@ -606,9 +756,9 @@ attend_kernel(AttnK a) {
   // of tile t+1+NB; one barrier.
   for (int pass = 0;; ++pass) {
     if (pass > 0) {                        // second pass: the first tiles again
-      load_tile(tile0(0), kb0, sc0, vb0);
+      load_tile(tile0(0), kb0, sc0, vb0, lb0);
       ib0 = tile0(0);
-      if (NB == 2) { load_tile(tile0(1), kb1, sc1, vb1); ib1 = tile0(1); }
+      if (NB == 2) { load_tile(tile0(1), kb1, sc1, vb1, lb1); ib1 = tile0(1); }
       m_ref = m_max;                       // the split's max (HB = 2: over both key-block waves)
       l_run = 0.f;
     }
@@ -617,25 +767,25 @@ attend_kernel(AttnK a) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) o[hb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
     int32_t rn[2];
-    uint32_t vn;
-    tile_rows(tile0(NB), rn, vn);
-    uint32_t vm0 = stage(kb0, sc0, vb0, ib0, 0, tile0(NB), rn, vn);  // tile 0 -> slot 0, buffer 0 <- tile NB
+    uint32_t vn, ln, lm0, lm1 = 0;
+    tile_rows(tile0(NB), rn, vn, ln);
+    uint32_t vm0 = stage(kb0, sc0, vb0, lb0, ib0, 0, tile0(NB), rn, vn, ln, lm0);  // tile 0 -> slot 0, buffer 0 <- tile NB
     uint32_t vm1 = 0;
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
-      tile_rows(tile0(t + 1 + NB), rn, vn);         // row lookups first: their latency hides under QK
-      score(0, vm0);
+      tile_rows(tile0(t + 1 + NB), rn, vn, ln);     // row lookups first: their latency hides under QK
+      score(0, vm0, lm0);
       if (t > 0) accumulate(1);
       // tile t+1 -> slot 1; its buffer <- tile t+1+NB
-      if (NB == 2) vm1 = stage(kb1, sc1, vb1, ib1, 1, tile0(t + 3), rn, vn);
-      else vm1 = stage(kb0, sc0, vb0, ib0, 1, tile0(t + 2), rn, vn);
+      if (NB == 2) vm1 = stage(kb1, sc1, vb1, lb1, ib1, 1, tile0(t + 3), rn, vn, ln, lm1);
+      else vm1 = stage(kb0, sc0, vb0, lb0, ib0, 1, tile0(t + 2), rn, vn, ln, lm1);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 >= ntiles) break;
-      tile_rows(tile0(t + 2 + NB), rn, vn);
-      score(1, vm1);
+      tile_rows(tile0(t + 2 + NB), rn, vn, ln);
+      score(1, vm1, lm1);
       accumulate(0);
-      vm0 = stage(kb0, sc0, vb0, ib0, 0, tile0(t + 2 + NB), rn, vn);  // tile t+2 -> slot 0, buffer 0 <- tile t+2+NB
+      vm0 = stage(kb0, sc0, vb0, lb0, ib0, 0, tile0(t + 2 + NB), rn, vn, ln, lm0);  // tile t+2 -> slot 0, buffer 0 <- tile t+2+NB
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -692,7 +842,8 @@ attend_kernel(AttnK a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int jr = ((d - kRopeStart) >> 1) + p;
-          const float cs = s_cos[jr], sn = s_sin[jr];
+          const int qo = QB > 1 ? hh / kH : 0;
+          const float cs = s_cos[qo][jr], sn = s_sin[qo][jr];
           const float x = v[2 * p], y = v[2 * p + 1];
           v[2 * p] = x * cs + y * sn;
           v[2 * p + 1] = y * cs - x * sn;
@@ -707,7 +858,7 @@ attend_kernel(AttnK a) {
 #pragma unroll
   for (int u = 0; u < kHeadSlots * kHeadDim / 8 / 256; ++u) {   // HB * 4 chunks of 8 dims per thread
     const int ho = 4 * u + w;              // one head per wave per step: the check is uniform
-    if (head0 + ho < a.H) {
+    if (QB > 1 ? ho < nrows * kH : head0 + ho < a.H) {
       const uint4 x = *reinterpret_cast<const uint4*>(&s_o[ho * kOStride + 8 * lane]);
       *reinterpret_cast<uint4*>(dst + (base + ho) * kHeadDim + 8 * lane) = x;
     }
@@ -850,10 +1001,26 @@ bool attend_launchable(int B, int Tq, int H, int64_t max_keys, bool list) {
   return p.nsplit < ((int64_t)1 << 31);
 }
 
+// Rows per workgroup: QB > 1 for selected-entry lists of many rows (prefill) with few heads (H = 64 /
+// QB, QB = 2, 4 or 8) over a cache of at most kMaxBlockEntries entries, whose rows' lists overlap
+// enough that their union is far shorter than QB lists.  Else 1.
+int attend_rows_per_block(int B, int Tq, int H, int64_t kv_ld, bool list, bool append) {
+  if (!list || append || (int64_t)B * Tq < 128 || kv_ld > kMaxBlockEntries) return 1;
+  if (H != 8 && H != 16 && H != 32) return 1;
+  const int qb = 64 / H;
+  return Tq >= qb ? qb : 1;
+}
+
 template <bool LIST, bool F8>
-void launch_attend_kernel(const AttnK& a, int hb, dim3 grid, hipStream_t st) {
+void launch_attend_kernel(const AttnK& a, int hb, int qb, dim3 grid, hipStream_t st) {
   // timing labels: selected-entry lists (CSA) and dense visible ranges (HCA) apart
   const char* name = LIST ? "attend_csa_kernel" : "attend_hca_kernel";
+  if (LIST && qb > 1) {
+    if (qb == 8) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 8 : 1)>), grid, dim3(256), 0, st, a);
+    else if (qb == 4) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 4 : 1)>), grid, dim3(256), 0, st, a);
+    else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 2 : 1)>), grid, dim3(256), 0, st, a);
+    return;
+  }
   const bool pad = a.H < 16 * hb * (hb == 2 ? a.halves : 1);   // some workgroup has padding-only head blocks
   if (hb == 2 && pad) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2, true>), grid, dim3(256), 0, st, a);
   else if (hb == 2) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 2, false>), grid, dim3(256), 0, st, a);
@@ -869,7 +1036,14 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   a.window = x.window; a.sink = x.sink; a.q_pos = x.q_pos; a.rope_offset = x.rope_offset;
   a.Tq = x.Tq; a.H = x.H; a.scale_log2 = x.scale * kLog2e; a.eps = x.eps; a.rf = rope_freq(x.theta);
   a.out = x.out;
-  const AttendPlan p = attend_plan(R, x.H, max_keys, x.topk != nullptr);
+  AttendPlan p = attend_plan(R, x.H, max_keys, x.topk != nullptr);
+  const int qb = attend_rows_per_block(x.B, x.Tq, x.H, x.kv_ld, x.topk != nullptr, x.append != nullptr);
+  if (qb > 1) {                                  // row blocks: one split, every key of the block's rows
+    p.hb = 4;
+    p.halves = 1;
+    p.nsplit = 1;
+    p.keys_per_split = 1 << 30;
+  }
   a.keys_per_split = p.keys_per_split;
   a.nsplit = p.nsplit;
   a.halves = p.halves;
@@ -880,8 +1054,9 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   // apart), padded to a multiple of 16 (the padding returns at once)
   a.R = R;
   const bool flat = p.hb == 2 && p.halves == 2;
-  const dim3 grid = flat ? dim3((unsigned)(16 * (((int64_t)R * a.nsplit + 7) / 8)), 1u)
-                         : dim3((unsigned)a.nsplit, (unsigned)R);
+  const dim3 grid = flat   ? dim3((unsigned)(16 * (((int64_t)R * a.nsplit + 7) / 8)), 1u)
+                    : qb > 1 ? dim3(1u, (unsigned)(x.B * ((x.Tq + qb - 1) / qb)))
+                             : dim3((unsigned)a.nsplit, (unsigned)R);
   a.kv8 = x.kv8; a.kv_scale = x.kv_scale; a.win8 = x.win8; a.win_scale = x.win_scale;
   const bool f8 = x.kv8 != nullptr;
   a.app_rows = 0;
@@ -896,11 +1071,11 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   }
   if (x.append && a.app_rows == 0 && launch_decode_append(*x.append, st)) return 4;   // other shapes: first
   if (x.topk) {
-    if (f8) launch_attend_kernel<true, true>(a, p.hb, grid_k, st);
-    else launch_attend_kernel<true, false>(a, p.hb, grid_k, st);
+    if (f8) launch_attend_kernel<true, true>(a, p.hb, qb, grid_k, st);
+    else launch_attend_kernel<true, false>(a, p.hb, qb, grid_k, st);
   } else {
-    if (f8) launch_attend_kernel<false, true>(a, p.hb, grid_k, st);
-    else launch_attend_kernel<false, false>(a, p.hb, grid_k, st);
+    if (f8) launch_attend_kernel<false, true>(a, p.hb, 1, grid_k, st);
+    else launch_attend_kernel<false, false>(a, p.hb, 1, grid_k, st);
   }
   if (a.nsplit > 1) {
     const int64_t waves = (int64_t)R * x.H;

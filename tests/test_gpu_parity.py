@@ -487,6 +487,45 @@ def test_csa_attend_list_entries_past_the_cache_are_missing_keys():
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("H,B,Tq,kv8,ring", [(8, 1, 130, False, 0), (16, 2, 67, False, 512), (32, 1, 129, True, 0),
+                                         (8, 2, 70, True, 512), (8, 1, 128, False, 64)])
+def test_csa_attend_row_blocks(H, B, Tq, kv8, ring):
+    # many query rows over a small cache (at most 2048 entries) with 8, 16 or 32 heads: a workgroup
+    # takes 64 / H consecutive rows of one sequence (ragged last blocks) and attends to the union of
+    # their lists and windows, each row keeping only its own keys.  Positions are spread (sorted
+    # random), so the block's window range holds tokens no row uses; with the 64-token ring that
+    # range is longer than the ring.  Early rows have fewer visible entries than k (-1 slots).
+    n_cap, k, W = 300, 64, 64
+    pos = np.sort(synth.rng(190 + H, 7).integers(20, 4 * n_cap + 50, size=(B, Tq)), axis=1)
+    if ring == 64:
+        pos = np.arange(Tq).reshape(1, Tq) * 9 + 40
+    _attend_case("csa", B, Tq, H, k, n_cap, 4, W, ring, pos.ravel().tolist(), 191 + H, kv8=kv8)
+
+
+def test_csa_attend_row_blocks_entries_past_the_cache_are_missing_keys():
+    """Row blocks: list slots holding an index past the cache are no key, exactly like -1."""
+    B, Tq, H, k, n_cap, W, ring = 1, 128, 8, 64, 300, 128, 512
+    q = synth.normal_bf16((B, Tq, H, 512), 1.28, 171, 1)
+    gq = synth.f32_to_bf16_bits(np.ones(512, np.float32))
+    cache = synth.normal_bf16((B, n_cap, 512), 1.0, 171, 2)
+    win = synth.normal_bf16((B, ring, 512), 1.0, 171, 3)
+    sink = synth.normal_f32((H,), 1.0, 171, 4)
+    g = synth.rng(171, 5)
+    sel = np.stack([np.sort(g.choice(n_cap, k, replace=False)) for _ in range(Tq)]).astype(np.int32)
+    bad, none = sel.copy(), sel.copy()
+    bad[::3, [3, 17, 40]] = [n_cap, n_cap + 12345, 2 ** 30]
+    none[::3, [3, 17, 40]] = -1
+    pos = np.arange(4 * n_cap, 4 * n_cap + Tq).reshape(B, Tq)
+    outs = []
+    for lst in (bad, none):
+        out = torch.zeros((B, Tq, H, 512), dtype=torch.bfloat16, device=DEV)
+        L.csa_attend(from_bits(q), from_bits(gq), from_bits(cache), torch.from_numpy(lst.reshape(B, Tq, k)).to(DEV),
+                     from_bits(win), dev_f32(sink), dev_i64(pos), window=W, ring_cap=ring, out=out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_kv_quantize_fp8_bit_exact():
     """The device quantiser of K=V rows against the oracle's (fp32 decisions): codes and scales
     identical, on Gaussian rows at several magnitudes, an all-zero row, rows with one huge value,
