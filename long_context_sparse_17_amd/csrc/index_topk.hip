@@ -1484,6 +1484,122 @@ __device__ __forceinline__ void sort_and_write(int32_t* list, int n, int64_t nv,
   }
 }
 
+// Prefill rows of at most kWaveRowMax visible entries: one wave per row, no workgroup barrier.  The
+// wave holds the row's order-preserving keys in registers (lane l: entries 16 l .. 16 l + 15; past the
+// row: key 0, below every finite score's key), finds the k-th largest key by four 8-bit radix passes
+// (a 256-bin LDS histogram of its own, scanned from the top by the lanes four bins each), and writes
+// the keys above it plus the lowest-index keys equal to it, in index order.
+constexpr int kWaveRowMax = 1024;
+constexpr int kWaveRowPer = kWaveRowMax / kWave;    // 16 keys per lane
+constexpr int kWaveRowWaves = 4;                    // rows per workgroup
+
+// The wave's earlier LDS accesses are complete before its later ones (the histogram is the wave's own).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ void __launch_bounds__(kWaveRowWaves * kWave)
+topk_wave_kernel(const float* __restrict__ scores, int64_t nsp, const int64_t* __restrict__ q_pos, int m,
+                 int64_t n_cap, int k, int Tq, int t0, int tcur, int tb, int nrows, int32_t* __restrict__ topk_idx,
+                 float* __restrict__ topk_score) {
+  __shared__ __align__(16) uint32_t hist[kWaveRowWaves][256];
+  const int lane = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int x = blockIdx.x * kWaveRowWaves + wv;      // row x of this batch: (x / tcur, t0 + x % tcur)
+  if (x >= nrows) return;                              // wave-uniform
+  const int64_t bq = x / tcur, tq = t0 + x % tcur;
+  const int64_t r = bq * Tq + tq;
+  const int64_t rb = bq * tb + (tq - t0);
+  const int64_t nv = n_visible(q_pos, r, m, n_cap);
+  const float* srow = scores + rb * nsp;
+  int32_t* oi = topk_idx + r * k;
+  float* os = topk_score ? topk_score + r * k : nullptr;
+  if (nv <= k) {
+    for (int i = lane; i < k; i += kWave) {
+      oi[i] = i < nv ? i : -1;
+      if (os) os[i] = i < nv ? srow[i] : -INFINITY;
+    }
+    return;
+  }
+  // entries 16 lane + j, read inside the row (nsp >= 64 is a multiple of 64)
+  const int64_t e0 = 16 * lane;
+  const float4* src = reinterpret_cast<const float4*>(srow + (e0 + 16 <= nsp ? e0 : nsp - 16));
+  float val[kWaveRowPer];
+#pragma unroll
+  for (int q = 0; q < kWaveRowPer / 4; ++q) {
+    const float4 v = src[q];
+    val[4 * q] = v.x; val[4 * q + 1] = v.y; val[4 * q + 2] = v.z; val[4 * q + 3] = v.w;
+  }
+  uint32_t key[kWaveRowPer];
+#pragma unroll
+  for (int j = 0; j < kWaveRowPer; ++j) key[j] = e0 + j < nv ? float_key(val[j]) : 0u;
+
+  uint32_t* hw = hist[wv];
+  uint32_t prefix = 0u, pmask = 0u;
+  uint32_t kk = (uint32_t)k;               // rank, from the top, of the k-th key among those matching prefix
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int sh = 24 - 8 * pass;
+    reinterpret_cast<uint4*>(hw)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_order();
+#pragma unroll
+    for (int j = 0; j < kWaveRowPer; ++j)
+      if ((key[j] & pmask) == prefix) atomicAdd(&hw[(key[j] >> sh) & 255u], 1u);
+    wave_lds_order();
+    uint32_t c[4];                         // bins 255 - 4 lane - q, descending
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = hw[255 - 4 * lane - q];
+    wave_lds_order();
+    const uint32_t s4 = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(s4);
+    const uint32_t excl = incl - s4;
+    const bool here = excl < kk && kk <= incl;
+    const uint64_t bl = __ballot(here);
+    const int srcl = bl ? __ffsll((unsigned long long)bl) - 1 : 0;
+    int bin = 0;
+    uint32_t above = excl;
+    if (here) {
+      bin = 252 - 4 * lane;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!found && above + c[q] >= kk) { bin = 255 - 4 * lane - q; found = true; }
+        else if (!found) above += c[q];
+      }
+    }
+    bin = __builtin_amdgcn_readlane(bin, srcl);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)above, srcl);
+    prefix |= (uint32_t)bin << sh;
+    pmask |= 255u << sh;
+    kk -= above;
+  }
+  // prefix is the k-th largest key; every key above it and the kk lowest-index keys equal to it win
+  uint32_t eq = 0u, gt = 0u;
+#pragma unroll
+  for (int j = 0; j < kWaveRowPer; ++j) {
+    eq += key[j] == prefix ? 1u : 0u;
+    gt += key[j] > prefix ? 1u : 0u;
+  }
+  const uint32_t eq_before = wave_incl_scan(eq) - eq;
+  const uint32_t take_eq = kk > eq_before ? (kk - eq_before < eq ? kk - eq_before : eq) : 0u;
+  const uint32_t cnt = gt + take_eq;
+  uint32_t pos = wave_incl_scan(cnt) - cnt;
+  uint32_t er = eq_before;
+#pragma unroll
+  for (int j = 0; j < kWaveRowPer; ++j) {
+    const bool tie = key[j] == prefix;
+    const bool win = key[j] > prefix || (tie && er < kk);
+    er += tie ? 1u : 0u;
+    if (win && pos < (uint32_t)k) {        // exactly k win; the bound keeps every store in the row
+      oi[pos] = (int32_t)(e0 + j);
+      if (os) os[pos] = val[j];
+      ++pos;
+    }
+  }
+}
+
 // Prefill: one workgroup per row does histogram, filter, refine, sort.
 __global__ void __launch_bounds__(kSelThreads)
 topk_rowwise_kernel(const float* __restrict__ scores, unsigned long long* __restrict__ cand, int64_t nsp,
@@ -1807,8 +1923,16 @@ int launch_index_topk(const IndexArgs& a, hipStream_t st) {
     for (int t0 = 0; t0 < a.Tq; t0 += tb) {
       const int tcur = a.Tq - t0 < tb ? a.Tq - t0 : tb;
       score_rows(a, w, t0, tcur, tb, st);
-      LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)(a.B * tcur)), dim3(kSelThreads), 0, st,
-                 w.scores, w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.Tq, t0, tcur, tb, a.topk_idx, a.topk_score);
+      if (a.n_cap <= kWaveRowMax) {            // short rows: one wave each
+        const int nrows = a.B * tcur;
+        LCS_LAUNCH("topk_wave_kernel", topk_wave_kernel, dim3((unsigned)((nrows + kWaveRowWaves - 1) / kWaveRowWaves)),
+                   dim3(kWaveRowWaves * kWave), 0, st, w.scores, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.Tq, t0, tcur, tb,
+                   nrows, a.topk_idx, a.topk_score);
+      } else {
+        LCS_LAUNCH("topk_rowwise_kernel", topk_rowwise_kernel, dim3((unsigned)(a.B * tcur)), dim3(kSelThreads), 0,
+                   st, w.scores, w.comb, w.nsp, a.q_pos, a.m, a.n_cap, a.k, a.Tq, t0, tcur, tb, a.topk_idx,
+                   a.topk_score);
+      }
     }
     if (a.append && launch_decode_append(*a.append, st)) return 4;
   }

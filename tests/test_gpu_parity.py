@@ -313,6 +313,60 @@ def test_index_topk_bf16_small_heads():
     _index_case(1, Tq, n_cap, 8, 64, k, 4, False, pos, 33)
 
 
+def _short_row_positions(Tq, n_cap, k):
+    # n_vis = 0, 1, k - 1, k, k + 1, k + 2, capacity - 1 and capacity, the rest spread between
+    nvs = [0, 1, k - 1, k, k + 1, k + 2, n_cap - 1, n_cap]
+    nvs += [int(x) for x in np.linspace(0, n_cap, Tq - len(nvs))]
+    return [4 * v + (i % 4) for i, v in enumerate(nvs)]
+
+
+@pytest.mark.parametrize("fp8,n_cap,k,ties", [(True, 1024, 100, False), (False, 1000, 256, False),
+                                              (True, 700, 512, True), (False, 1024, 1000, True)])
+def test_index_topk_prefill_short_rows(fp8, n_cap, k, ties):
+    # rows of at most 1024 visible entries take one wave each: trivial rows (n_vis <= k), one entry
+    # over k, and full rows whose last lanes lie past the row; with half the keys tied, the ties at
+    # the k-th key go to the lower index
+    Tq = 72
+    H_I, dI = (64, 128) if fp8 else (8, 64)
+    band = _index_case(1, Tq, n_cap, H_I, dI, k, 4, fp8, _short_row_positions(Tq, n_cap, k), 57 + k, ties=ties)
+    assert band <= 4
+
+
+@pytest.mark.parametrize("fp8,k", [(True, 100), (False, 256), (True, 1000)])
+def test_index_topk_short_rows_wave_path_matches_workgroup_path(fp8, k):
+    """The same rows (n_vis <= 1024) selected by the one-wave path (capacity 1024) and by the
+    workgroup path (capacity 1088): the same scores and the same tie rule give identical indices
+    and scores, with and without a tied half of the keys."""
+    Tq, cfg = 72, 58 + k
+    H_I, dI = (64, 128) if fp8 else (8, 64)
+    ik_ld = 1088 + 5
+    q = from_bits(synth.normal_bf16((1, Tq, H_I, dI), 1.28, cfg, 1))
+    w = from_bits(synth.normal_bf16((1, Tq, H_I), 1.28, cfg, 2))
+    pos = dev_i64(np.array(_short_row_positions(Tq, 1024, k), dtype=np.int64).reshape(1, Tq))
+    for ties in (False, True):
+        if fp8:
+            codes = synth.fp8_codes((1, ik_ld, dI), cfg, 3)
+            scale = synth.positive_scales((1, ik_ld), cfg, 4)
+            if ties:
+                codes[:, :512] = codes[:, :1]
+                scale[:, :512] = scale[:, :1]
+            ik, iks = torch.from_numpy(codes).to(DEV), dev_f32(scale)
+        else:
+            kb = synth.normal_bf16((1, ik_ld, dI), 1.28, cfg, 3)
+            if ties:
+                kb[:, :512] = kb[:, :1]
+            ik, iks = from_bits(kb), None
+        res = []
+        for n_cap in (1024, 1088):
+            idx = torch.full((1, Tq, k), -7, dtype=torch.int32, device=DEV)
+            sc = torch.zeros((1, Tq, k), dtype=torch.float32, device=DEV)
+            L.csa_index_topk(q, w, ik, iks, pos, n_cap=n_cap, m=4, k=k, topk_idx=idx, topk_score=sc)
+            res.append((idx, sc))
+        torch.cuda.synchronize()
+        assert torch.equal(res[0][0], res[1][0]), f"ties={ties}: indices differ"
+        assert torch.equal(res[0][1], res[1][1]), f"ties={ties}: scores differ"
+
+
 @pytest.mark.parametrize("fp8,n_cap", [(True, 3000), (False, 3000), (True, 12000)])
 def test_index_topk_exact_ties_go_to_lower_index(fp8, n_cap):
     # half the keys identical: the tied block fills the threshold bin (12000: more candidates than
