@@ -168,13 +168,14 @@ __device__ __forceinline__ float quant_row_e4m3(const uint16_t* qseg0, const uin
 }
 
 // bf16 keys, many query rows (prefill with bf16 indexer keys): 16 queries per workgroup, 4 per wave;
-// every wave scores the workgroup's whole chunk for its 4 queries (entries re-read from L1/L2).
+// every wave scores the workgroup's whole chunk (`chunk` entries, a multiple of 64) for its 4 queries
+// (entries re-read from L1/L2).
 template <int KS, int HBI>
 __global__ void __launch_bounds__(256)
 index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
                    const uint16_t* __restrict__ ik, int64_t ik_ld, const int64_t* __restrict__ q_pos,
                    int64_t n_cap, int Tq, int t0, int tcur, int tb, int H_I, int dI, int m,
-                   float* __restrict__ scores, int64_t nsp) {
+                   float* __restrict__ scores, int64_t nsp, int chunk) {
   constexpr int QW = 4, QTILE = 16;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -184,7 +185,7 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
   const int b = blockIdx.y / tiles_per_b;
   const int tq0 = t0 + (blockIdx.y % tiles_per_b) * QTILE;
   const int tq_end = t0 + tcur < Tq ? t0 + tcur : Tq;
-  const int64_t c0 = (int64_t)blockIdx.x * kScoreChunk;
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
 
   // entry limit of this workgroup = max n_vis over its queries
   int64_t nv_max = 0;
@@ -223,7 +224,7 @@ index_score_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restric
     }
   }
 
-  int64_t e_hi = c0 + kScoreChunk;
+  int64_t e_hi = c0 + chunk;
   if (e_hi > nv_max) e_hi = nv_max;
   const uint16_t* ik16 = ik + (int64_t)b * ik_ld * dI;
   for (int64_t e0 = c0; e0 < e_hi; e0 += 64) {
@@ -1784,10 +1785,14 @@ void launch_score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
 template <int KS, int HBI>
 void launch_score_rows_bf16(const IndexArgs& a, const Ws& w, int t0, int tcur, int tb, hipStream_t st) {
   const int tiles = (tcur + 15) / 16;
-  dim3 grid((unsigned)((a.n_cap + kScoreChunk - 1) / kScoreChunk), (unsigned)(a.B * tiles));
+  // entries per workgroup: kScoreChunk, halved (down to 64) while the grid has fewer than about 1024
+  // workgroups (short caches: a 1024-entry chunk per 16 queries leaves most CUs idle)
+  int chunk = kScoreChunk;
+  while (chunk > 64 && ((a.n_cap + chunk - 1) / chunk) * a.B * tiles < 1024) chunk /= 2;
+  dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * tiles));
   LCS_LAUNCH("index_score_kernel", (index_score_kernel<KS, HBI>), grid, dim3(256), 0, st, a.q_idx, a.w_idx,
              static_cast<const uint16_t*>(a.ik), a.ik_ld, a.q_pos, a.n_cap, a.Tq, t0, tcur, tb, a.H_I, a.dI, a.m,
-             w.scores, w.nsp);
+             w.scores, w.nsp, chunk);
 }
 
 // fp8 prefill grid: one workgroup per chunk of kPfChunk entries (x) and per query range of each
@@ -1881,7 +1886,7 @@ bool index_topk_launchable(int B, int Tq, int64_t n_cap, int ik_fp8) {
     const PfGrid p = prefill_grid(B, tb, n_cap);
     return p.nchunk < ((int64_t)1 << 31) && (int64_t)B * p.qsplit <= 65535;
   }
-  return (n_cap + kScoreChunk - 1) / kScoreChunk < ((int64_t)1 << 31) && (int64_t)B * ((tb + 15) / 16) <= 65535;
+  return (n_cap + 63) / 64 < ((int64_t)1 << 31) && (int64_t)B * ((tb + 15) / 16) <= 65535;
 }
 
 size_t index_topk_state_bytes() { return al256((size_t)kDecodeRows * kHistRow * 4); }
