@@ -97,7 +97,7 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 template <bool LIST, bool F8, int HB, bool PAD, int QB = 1>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
-  static_assert(QB == 1 || (LIST && HB == 4 && PAD), "row blocks: selected-entry lists, 64 head slots");
+  static_assert(QB == 1 || (LIST && HB == 4 && !PAD), "row blocks: selected-entry lists, 64 head slots");
   constexpr int kHeadSlots = 16 * HB;                       // heads of one workgroup
   __shared__ uint16_t s_kv[2][kWaves][kTile * kVtStride];  // tile slices [slot][slice]
   __shared__ uint2 s_p[2][HB * kWave][2];                   // P fragments [slot][head block][lane][key block]
@@ -156,8 +156,9 @@ attend_kernel(AttnK a) {
   const bool head_ok = QB > 1 ? qi < nrows : head < a.H;
   // head blocks of the workgroup that hold a real head (fewer than HB when H < 16 HB): the others are
   // neither scored nor accumulated
-  const int nvb = QB > 1 ? (nrows * kH + 15) / 16
-                         : !PAD || a.H - head0 >= 16 * HB ? HB : (a.H - head0 + 15) / 16;
+  // (QB > 1: every block is scored and accumulated; the slots of rows past a sequence's last row have
+  // no key, and are not stored)
+  const int nvb = !PAD || a.H - head0 >= 16 * HB ? HB : (a.H - head0 + 15) / 16;
 
   // Key slots of a row: CSA takes the k list slots (entries < 0 are skipped) then the window tokens,
   // at fixed positions, so a split's range needs no scan of the list; HCA takes the n_vis visible
@@ -1016,9 +1017,9 @@ void launch_attend_kernel(const AttnK& a, int hb, int qb, dim3 grid, hipStream_t
   // timing labels: selected-entry lists (CSA) and dense visible ranges (HCA) apart
   const char* name = LIST ? "attend_csa_kernel" : "attend_hca_kernel";
   if (LIST && qb > 1) {
-    if (qb == 8) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 8 : 1)>), grid, dim3(256), 0, st, a);
-    else if (qb == 4) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 4 : 1)>), grid, dim3(256), 0, st, a);
-    else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, true, (LIST ? 2 : 1)>), grid, dim3(256), 0, st, a);
+    if (qb == 8) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, false, (LIST ? 8 : 1)>), grid, dim3(256), 0, st, a);
+    else if (qb == 4) LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, false, (LIST ? 4 : 1)>), grid, dim3(256), 0, st, a);
+    else LCS_LAUNCH(name, (attend_kernel<LIST, F8, 4, false, (LIST ? 2 : 1)>), grid, dim3(256), 0, st, a);
     return;
   }
   const bool pad = a.H < 16 * hb * (hb == 2 ? a.halves : 1);   // some workgroup has padding-only head blocks
