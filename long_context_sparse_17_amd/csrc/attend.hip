@@ -88,7 +88,7 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 // logit and, for PV, its probability (o = sum_j p_j s_j code_j), so the MFMAs are those of the bf16
 // path on the codes.
 // PAD: some head blocks of a workgroup may hold padding heads only (H < 16 HB per workgroup); they are
-// neither scored nor accumulated.  Without PAD every head block holds a real head.
+// not scored (their P stays zero) and not stored.  Without PAD every head block holds a real head.
 // QB > 1 (selected-entry lists of many query rows with H = 64 / QB heads): a workgroup takes QB
 // consecutive rows of one sequence, head slot s holding head s % H of row s / H, so all 64 slots
 // hold real heads.  Its keys are the union of the rows' list entries (one bitmap per row over the
@@ -165,6 +165,13 @@ attend_kernel(AttnK a) {
   // entries then the window tokens.
   const int64_t e_begin = (int64_t)split * a.keys_per_split;
   if (threadIdx.x == 0) s_redo = 0;          // read after the first pass's last barrier
+  if (PAD && hq >= nvb) {                     // a padding block's P: zero in both slots, never written again
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      s_p[sl][hq * kWave + lane][0] = make_uint2(0u, 0u);
+      s_p[sl][hq * kWave + lane][1] = make_uint2(0u, 0u);
+    }
+  }
 
   const uint16_t* kv_b = a.kv + b * a.kv_ld * kHeadDim;
   int64_t t_q = a.q_pos[r];                               // uniform: a scalar load (QB > 1: the last)
@@ -744,12 +751,9 @@ attend_kernel(AttnK a) {
       for (int hb = 0; hb < NV; ++hb) o[hb][db] = mfma_bf16(vf, pf[hb], o[hb][db]);
     }
   };
-  auto accumulate = [&](int slot) {
-    if (PAD && nvb == 1) accumulate_nv(slot, std::integral_constant<int, 1>{});
-    else if (PAD && HB == 4 && nvb == 2) accumulate_nv(slot, std::integral_constant<int, (HB == 4 ? 2 : 1)>{});
-    else if (PAD && HB == 4 && nvb == 3) accumulate_nv(slot, std::integral_constant<int, (HB == 4 ? 3 : 1)>{});
-    else accumulate_nv(slot, std::integral_constant<int, HB>{});
-  };
+  // Every head block is accumulated (the padding blocks' P is zero): choosing the block count per call
+  // would make the compiler move the accumulators between register assignments in the loop.
+  auto accumulate = [&](int slot) { accumulate_nv(slot, std::integral_constant<int, HB>{}); };
 
   // Pipeline: iteration t scores tile t (slot t & 1), accumulates tile t-1 (slot (t-1) & 1), stages
   // tile t+1 into slot (t+1) & 1 (free: tile t-1's V reads are done in this wave, which reads only
