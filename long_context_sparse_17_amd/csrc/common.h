@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }

@@ -634,9 +634,11 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       if (FP8) {
         // bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16): each load instruction covers 64
         // contiguous bytes of 16 rows (the query codes use the same dim order)
-        const uint4* p = reinterpret_cast<const uint4*>(ik8 + e * 128 + 16 * g);
-        const uint4 x0 = p[0], x1 = p[4];
-        intx8 v = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        // (non-temporal: each key is read once per step, and keeping the 277 MB stream of a 1M-token
+        // cache out of the caches' retention leaves them to the data the later launches reuse)
+        const intx4 x0 = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(ik8 + e * 128 + 16 * g));
+        const intx4 x1 = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(ik8 + e * 128 + 64 + 16 * g));
+        intx8 v = intx8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         fr[u][0] = *reinterpret_cast<Frag*>(&v);
       } else {
 #pragma unroll
@@ -813,7 +815,9 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
   // visible end, within the row's stride (a multiple of 64), where readers mask by index.
   const int n4 = (int)((c1 - c0 + 3) >> 2);
   float4* dst = reinterpret_cast<float4*>(srow + c0);
-  for (int i = threadIdx.x; i < n4; i += 256) dst[i] = reinterpret_cast<const float4*>(s_sco)[i];
+  // (non-temporal: the scores are read once, by the selection launch)
+  for (int i = threadIdx.x; i < n4; i += 256)
+    __builtin_nontemporal_store(reinterpret_cast<const floatx4*>(s_sco)[i], reinterpret_cast<floatx4*>(dst) + i);
   uint32_t* gh = hist + r * kHistRow;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     const uint32_t v = lhist[i];
