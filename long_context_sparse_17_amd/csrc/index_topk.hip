@@ -600,7 +600,13 @@ constexpr int64_t kDecodeMaxChunk = 4 * kDecodeWaveGroups * 64;
 // 4 entry blocks over the 4 lane groups so that lane l ends with entry 64 gi + l, scales it, counts it
 // in the LDS histogram and keeps it in LDS; the chunk's scores leave in one burst of 16-byte stores at
 // the end.  Only key fragments are then in flight in the loop, so every wait is for a key group.
-template <bool FP8, int KS, int HBI>
+//
+// NTK (fp8 keys): the keys are loaded non-temporally.  Chosen when the call's key stream is at least
+// the Infinity Cache's size: such a stream cannot stay cached until the next step anyway, and
+// loading it normally would evict what the step's other launches reuse (1M-token cache, batch 8:
+// step 0.384 -> 0.379 ms).  Smaller streams load normally (a 128K-token cache, batch 32: the
+// non-temporal loads made the call 0.0725 -> 0.077 ms).
+template <bool FP8, int KS, int HBI, bool NTK>
 __global__ void __launch_bounds__(256, (FP8 || KS * HBI <= 8) ? 2 : 1)
 index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w_idx,
                           const void* __restrict__ ik, const float* __restrict__ ik_scale, int64_t ik_ld,
@@ -634,10 +640,15 @@ index_score_decode_kernel(const uint16_t* __restrict__ q_idx, const uint16_t* __
       if (FP8) {
         // bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16): each load instruction covers 64
         // contiguous bytes of 16 rows (the query codes use the same dim order)
-        // (non-temporal: each key is read once per step, and keeping the 277 MB stream of a 1M-token
-        // cache out of the caches' retention leaves them to the data the later launches reuse)
-        const intx4 x0 = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(ik8 + e * 128 + 16 * g));
-        const intx4 x1 = __builtin_nontemporal_load(reinterpret_cast<const intx4*>(ik8 + e * 128 + 64 + 16 * g));
+        const intx4* p = reinterpret_cast<const intx4*>(ik8 + e * 128 + 16 * g);
+        intx4 x0, x1;
+        if constexpr (NTK) {
+          x0 = __builtin_nontemporal_load(p);
+          x1 = __builtin_nontemporal_load(p + 4);
+        } else {
+          x0 = p[0];
+          x1 = p[4];
+        }
         intx8 v = intx8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         fr[u][0] = *reinterpret_cast<Frag*>(&v);
       } else {
@@ -1777,13 +1788,23 @@ int64_t decode_chunk(int64_t n_cap, int R) {
   return c;
 }
 
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;   // MI355X's memory-side cache
+
 template <bool FP8, int KS, int HBI>
 void launch_score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
   const int64_t chunk = decode_chunk(a.n_cap, a.B * a.Tq);
   dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * a.Tq));
-  LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI>), grid, dim3(256), 0, st,
-             a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
-             w.scores, w.hist, w.nsp);
+  // key bytes the call streams (codes and row scales of every visible-capacity entry of every row)
+  const bool ntk = FP8 && (int64_t)a.B * a.Tq * a.n_cap * (a.dI + 4) >= kInfinityCacheBytes;
+  if (FP8 && ntk) {
+    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, FP8>), grid, dim3(256), 0, st,
+               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
+               w.scores, w.hist, w.nsp);
+  } else {
+    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, false>), grid, dim3(256), 0, st,
+               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
+               w.scores, w.hist, w.nsp);
+  }
 }
 
 template <int KS, int HBI>
