@@ -21,7 +21,7 @@
 //   - PV: wave w accumulates O[the workgroup's heads, its 128 dims] += P V, V read from its own
 //     LDS slice (laid out so the key-major V fragment reads hit distinct banks).
 // The loop is software-pipelined with one barrier per tile: while tile t is scored, tile t-1 is
-// accumulated, tile t+1 is moved from registers to LDS and tiles t+2, t+3 are in flight from HBM.
+// accumulated, tile t+1 is moved from registers to LDS and tile t+2 is in flight from HBM.
 // Keys are split across workgroups (split-K); partial (max, sum, O) are merged by merge_kernel,
 // which adds the sink once.  With one split the workgroup finishes the output itself.
 #include <type_traits>
@@ -94,13 +94,6 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t c) {
 // hold real heads.  Its keys are the union of the rows' list entries (one bitmap per row over the
 // cache, at most kMaxBlockEntries entries), ascending, then the union of the rows' windows; each
 // slot keeps only the logits of its own row's keys (a per-row mask of every tile).  One split.
-// Selected-entry lists in the 32-head layout (one row per workgroup: the CSA decode shape, a few tiles
-// per split) keep one register buffer of tiles in flight instead of two: measured about 1 us (bf16
-// rows) and 1.7 us (fp8 rows) faster per launch than the two-buffer form, whose second buffer such
-// short splits barely use.
-template <bool LIST, bool F8, int HB, bool PAD, int QB>
-constexpr bool kOneTileBuffer = LIST && HB == 2 && QB == 1;
-
 template <bool LIST, bool F8, int HB, bool PAD, int QB = 1>
 __global__ void __launch_bounds__(256, 1)
 attend_kernel(AttnK a) {
@@ -209,11 +202,14 @@ attend_kernel(AttnK a) {
   // complete in order).  Dense ranges issue their first tiles before anything else; there the indexed
   // load, placed at its use, measured faster (the scalar table loads delay the tile loads' issue).
   const double rinv = LIST ? rope_inv(a.rf, (int)(threadIdx.x & 31)) : a.rf.inv[threadIdx.x & 31];
-  // HCA: the first two tiles are loaded speculatively at once, as entries e_begin .. e_begin+63
-  // (clamped into the cache); that holds whenever the split starts with 64 visible entries, which
+  // HCA: the first NB tiles are loaded speculatively at once, as entries e_begin .. e_begin+32 NB-1
+  // (clamped into the cache); that holds whenever the split starts with 32 NB visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
-  // Register buffers of tiles in flight (tiles t+2, t+3 while t is scored).
-  constexpr int NB = kOneTileBuffer<LIST, F8, HB, PAD, QB> ? 1 : 2;
+  // Register buffers of tiles in flight beyond the one being staged (the loop is written for 1 or 2).
+  // One measured faster than two on every layout and shape: CSA decode attention 16.9 -> 15.9 us
+  // (bf16 rows) and 19.1 -> 17.4 us (fp8 rows), HCA 31.3 -> 30.8 us, HCA at 64K context 34.5 -> 32.5
+  // us, the 1M chunked prefill 1.093 -> 1.082 ms, the 2K prefill's row blocks 0.110 -> 0.107 ms.
+  constexpr int NB = 1;
   uint4 kb0[2][4], kb1[2][4];
   float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};           // F8: scales of the buffers' keys kb*16 + c16
   uint32_t vb0 = 0, vb1 = 0;
