@@ -1794,17 +1794,19 @@ template <bool FP8, int KS, int HBI>
 void launch_score_decode(const IndexArgs& a, const Ws& w, hipStream_t st) {
   const int64_t chunk = decode_chunk(a.n_cap, a.B * a.Tq);
   dim3 grid((unsigned)((a.n_cap + chunk - 1) / chunk), (unsigned)(a.B * a.Tq));
-  // key bytes the call streams (codes and row scales of every visible-capacity entry of every row)
-  const bool ntk = FP8 && (int64_t)a.B * a.Tq * a.n_cap * (a.dI + 4) >= kInfinityCacheBytes;
-  if (FP8 && ntk) {
-    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, FP8>), grid, dim3(256), 0, st,
-               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
-               w.scores, w.hist, w.nsp);
-  } else {
-    LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, false>), grid, dim3(256), 0, st,
-               a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
-               w.scores, w.hist, w.nsp);
+  // key bytes the call streams (codes and row scales of every entry of every row's capacity)
+  const bool ntk = (int64_t)a.B * a.Tq * a.n_cap * (a.dI + 4) >= kInfinityCacheBytes;
+  if constexpr (FP8) {
+    if (ntk) {
+      LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, true>), grid, dim3(256), 0, st,
+                 a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
+                 w.scores, w.hist, w.nsp);
+      return;
+    }
   }
+  LCS_LAUNCH("index_score_kernel", (index_score_decode_kernel<FP8, KS, HBI, false>), grid, dim3(256), 0, st,
+             a.q_idx, a.w_idx, a.ik, a.ik_scale, a.ik_ld, a.q_pos, a.n_cap, a.Tq, a.H_I, a.dI, a.m, chunk,
+             w.scores, w.hist, w.nsp);
 }
 
 template <int KS, int HBI>
