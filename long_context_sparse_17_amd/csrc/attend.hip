@@ -202,8 +202,8 @@ attend_kernel(AttnK a) {
   // complete in order).  Dense ranges issue their first tiles before anything else; there the indexed
   // load, placed at its use, measured faster (the scalar table loads delay the tile loads' issue).
   const double rinv = LIST ? rope_inv(a.rf, (int)(threadIdx.x & 31)) : a.rf.inv[threadIdx.x & 31];
-  // HCA: the first NB tiles are loaded speculatively at once, as entries e_begin .. e_begin+32 NB-1
-  // (clamped into the cache); that holds whenever the split starts with 32 NB visible entries, which
+  // HCA: the first NB tiles are loaded speculatively at once, as entries e_begin .. e_begin + 32*NB - 1
+  // (clamped into the cache); that holds whenever the split starts with 32*NB visible entries, which
   // is checked once the query position is known (otherwise they are loaded again).
   // Register buffers of tiles in flight beyond the one being staged (the loop is written for 1 or 2).
   // One measured faster than two on every layout and shape: CSA decode attention 16.9 -> 15.9 us
