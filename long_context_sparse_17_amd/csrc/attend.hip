@@ -886,10 +886,12 @@ attend_kernel(AttnK a) {
 // barrier.  The lanes hold the splits' maxima (split lane + 64 i), the reference M = max(sink, split
 // maxima) is a wave reduction, each split's weight 2^(m_s - M) is formed in the lane that holds it
 // and broadcast with readlane, and the partial rows are read in rounds of kMergeChunk splits with
-// every load of a round issued before the first FMA.
+// every load of a round issued before the first FMA.  kMergeChunk (partial rows in flight per lane)
+// is 4, 8 or 16, the smallest that holds the call's splits (up to 16): loads past the last split
+// repeat its row, so a round sized to the split count issues none of them (HCA at 64K context, 4
+// splits: 32.8 -> 29.9 us per call).
 constexpr int kMergeWaves = 4;             // waves per workgroup
-constexpr int kMergeChunk = 16;            // partial rows in flight per lane
-
+template <int kMergeChunk>
 __global__ void __launch_bounds__(kMergeWaves * kWave)
 merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int R, int nsplit, int H,
              const float* __restrict__ sink, uint16_t* __restrict__ out) {
@@ -1095,8 +1097,10 @@ int launch_attend(const AttendArgs& x, int64_t max_keys, hipStream_t st) {
   }
   if (a.nsplit > 1) {
     const int64_t waves = (int64_t)R * x.H;
-    LCS_LAUNCH("attend_merge_kernel", merge_kernel, dim3((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)),
-               dim3(kMergeWaves * kWave), 0, st, a.part_o, a.part_ml, R, a.nsplit, x.H, x.sink, x.out);
+    const dim3 gm((unsigned)((waves + kMergeWaves - 1) / kMergeWaves)), bm(kMergeWaves * kWave);
+    if (a.nsplit <= 4) LCS_LAUNCH("attend_merge_kernel", merge_kernel<4>, gm, bm, 0, st, a.part_o, a.part_ml, R, a.nsplit, x.H, x.sink, x.out);
+    else if (a.nsplit <= 8) LCS_LAUNCH("attend_merge_kernel", merge_kernel<8>, gm, bm, 0, st, a.part_o, a.part_ml, R, a.nsplit, x.H, x.sink, x.out);
+    else LCS_LAUNCH("attend_merge_kernel", merge_kernel<16>, gm, bm, 0, st, a.part_o, a.part_ml, R, a.nsplit, x.H, x.sink, x.out);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
